@@ -1,0 +1,201 @@
+"""Seeded synthetic decode-attention workloads.
+
+This module only draws inputs. It holds none of the attention arithmetic, so
+the CPU oracle (``oracle/``) and the HIP path (``decode_phase_attention_amd``)
+can both be fed from it without sharing any code with each other.
+
+Workload shapes follow the pages' evaluation axes: single long-context decodes
+and ragged batches of unequal context lengths (LeanAttention talk summary,
+"Experimental Setup & Results", Workloads; xllm-io paper review, §5.2), over a
+KV cache laid out per request as (heads, seq_len, head_dim) (xllm-io paper
+review, §7.4).
+
+Packed layout. For request ``b`` with context ``n_b`` the K block is
+``[H, n_b, d]``; blocks follow each other in request order, so the whole cache
+is a 2-D ``[H * sum(n_b), d]`` tensor and request ``b`` starts at row
+``H * sum(n_{b'} for b' < b)``. For equal lengths this equals
+``[B, H, n, d]``. V uses the same layout.
+
+Values are i.i.d. N(0, 1), drawn in fp32 from torch generators seeded per
+(seed, tensor, request) and rounded to fp16/bf16 (round to nearest even).
+The draws do not depend on the order in which requests are generated.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+__all__ = [
+    "CONFIGS",
+    "Workload",
+    "Inputs",
+    "context_lengths",
+    "make_inputs",
+    "make_custom",
+    "to_bits",
+    "kv_bytes",
+    "algorithmic_bytes",
+]
+
+_TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+# tensor ids used in seed mixing
+_TID_Q, _TID_K, _TID_V, _TID_SHIFT = 1, 2, 3, 4
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    d: int
+    dtype: str                    # "f16" or "bf16"
+    ctx: int | None = None        # uniform context length, or None for ragged
+    ctx_lo: int = 0               # ragged: log-uniform range [ctx_lo, ctx_hi]
+    ctx_hi: int = 0
+    shift_frac: float = 0.0       # fraction of keys shifted toward q
+    shift_norm: float = 0.0       # length of that shift
+    note: str = ""
+
+
+CONFIGS: dict[str, Workload] = {
+    "tiny": Workload("tiny", B=1, H=4, d=64, dtype="f16", ctx=1024,
+                     shift_frac=0.01, shift_norm=8.0,
+                     note="1% of keys per head shifted by 8*q/|q| to stress max tracking"),
+    "65k": Workload("65k", B=1, H=32, d=128, dtype="bf16", ctx=65536),
+    "512k": Workload("512k", B=1, H=32, d=128, dtype="bf16", ctx=524288),
+    "ragged": Workload("ragged", B=16, H=32, d=128, dtype="bf16",
+                       ctx_lo=1024, ctx_hi=262144,
+                       note="per-request context log-uniform in [1024, 262144]"),
+    "many-heads": Workload("many-heads", B=8, H=128, d=64, dtype="f16", ctx=16384),
+}
+
+
+@dataclass
+class Inputs:
+    q: torch.Tensor               # [B, H, d]
+    k: torch.Tensor               # [H * sum(n_b), d] packed per request
+    v: torch.Tensor               # same layout as k
+    ctx_lens: list[int]
+    H: int
+    d: int
+    dtype: str
+    scale: float
+    seed: int
+    name: str = "custom"
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return len(self.ctx_lens)
+
+
+def _mix(*parts: int) -> int:
+    """Deterministic 63-bit seed from a tuple of small integers."""
+    h = 0x9E3779B97F4A7C15
+    for p in parts:
+        h ^= (int(p) + 0x632BE59BD9B4E019 + ((h << 6) & 0xFFFFFFFFFFFFFFFF) + (h >> 2))
+        h &= 0xFFFFFFFFFFFFFFFF
+    return h & 0x7FFFFFFFFFFFFFFF
+
+
+def _gen(device: str, *parts: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_mix(*parts))
+    return g
+
+
+def context_lengths(w: Workload, seed: int = 0) -> list[int]:
+    """Context length per request.
+
+    Ragged batches draw ``n_b = floor(exp(ln lo + u_b * ln(hi/lo)))`` with
+    ``u_b ~ U[0, 1)`` from ``numpy.random.default_rng(seed)``, clipped to
+    ``[lo, hi]``: log-uniform lengths, so the batch mixes short and long
+    requests the way the pages' ragged workloads do.
+    """
+    if w.ctx is not None:
+        return [int(w.ctx)] * w.B
+    u = np.random.default_rng(seed).random(w.B)
+    lo, hi = w.ctx_lo, w.ctx_hi
+    n = np.floor(np.exp(math.log(lo) + u * math.log(hi / lo))).astype(np.int64)
+    return [int(x) for x in np.clip(n, lo, hi)]
+
+
+def _draw_request(gq_row: torch.Tensor | None, H: int, n: int, d: int, seed: int,
+                  tid: int, b: int, device: str, w: Workload | None) -> torch.Tensor:
+    g = _gen(device, seed, tid, b)
+    x = torch.randn((H, n, d), generator=g, device=device, dtype=torch.float32)
+    if w is not None and tid == _TID_K and w.shift_frac > 0.0 and gq_row is not None:
+        cnt = max(1, int(round(w.shift_frac * n)))
+        for h in range(H):
+            gs = _gen("cpu", seed, _TID_SHIFT, b, h)
+            idx = torch.randperm(n, generator=gs)[:cnt].to(device)
+            qh = gq_row[h]
+            x[h, idx, :] += w.shift_norm * qh / torch.linalg.vector_norm(qh)
+    return x
+
+
+def make_custom(ctx_lens: list[int], H: int, d: int, dtype: str = "bf16", seed: int = 0,
+                device: str = "cpu", q_std: float = 1.0, scale: float | None = None,
+                workload: Workload | None = None, name: str = "custom") -> Inputs:
+    """Draw q, K, V for arbitrary request lengths.
+
+    ``q_std`` widens the score range (adversarial inputs): scores grow in
+    proportion to it.
+    """
+    if any(int(n) < 0 for n in ctx_lens):
+        raise ValueError("context lengths must be >= 0")
+    tdt = _TORCH_DTYPE[dtype]
+    B = len(ctx_lens)
+    qs = []
+    for b in range(B):
+        g = _gen(device, seed, _TID_Q, b)
+        qs.append(torch.randn((H, d), generator=g, device=device, dtype=torch.float32) * q_std)
+    q32 = torch.stack(qs) if B else torch.empty((0, H, d), device=device)
+    N = int(sum(ctx_lens))
+    k = torch.empty((H * N, d), dtype=tdt, device=device)
+    v = torch.empty((H * N, d), dtype=tdt, device=device)
+    row = 0
+    for b, n in enumerate(ctx_lens):
+        n = int(n)
+        if n == 0:
+            continue
+        kb = _draw_request(q32[b], H, n, d, seed, _TID_K, b, device, workload)
+        k[row:row + H * n] = kb.reshape(H * n, d).to(tdt)
+        del kb
+        vb = _draw_request(None, H, n, d, seed, _TID_V, b, device, None)
+        v[row:row + H * n] = vb.reshape(H * n, d).to(tdt)
+        del vb
+        row += H * n
+    sc = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    return Inputs(q=q32.to(tdt).contiguous(), k=k, v=v, ctx_lens=[int(n) for n in ctx_lens],
+                  H=H, d=d, dtype=dtype, scale=sc, seed=seed, name=name)
+
+
+def make_inputs(name: str, seed: int = 0, device: str = "cpu") -> Inputs:
+    """Inputs for one of the named workloads in ``CONFIGS``."""
+    w = CONFIGS[name]
+    lens = context_lengths(w, seed)
+    inp = make_custom(lens, w.H, w.d, w.dtype, seed=seed, device=device, workload=w, name=name)
+    inp.meta["workload"] = w
+    return inp
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw 16-bit patterns of an fp16/bf16 tensor as a host numpy uint16 array."""
+    if t.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"expected fp16/bf16, got {t.dtype}")
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def kv_bytes(ctx_lens: list[int], H: int, d: int, elem: int = 2) -> int:
+    return 2 * int(sum(ctx_lens)) * H * d * elem
+
+
+def algorithmic_bytes(ctx_lens: list[int], H: int, d: int, elem: int = 2) -> int:
+    """Bytes one decode step must move: K and V once, q once, fp32 output once."""
+    B = len(ctx_lens)
+    return kv_bytes(ctx_lens, H, d, elem) + B * H * d * elem + B * H * d * 4
