@@ -1,0 +1,274 @@
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 512k]
+
+One step is one decode-attention call over the whole workload: the host
+scheduler builds the stream-K tables, they are copied to the device, and the
+lean kernel runs. Inputs are seeded synthetic caches already resident in HBM.
+Prints one JSON line on stdout (the last line); progress goes to stderr.
+
+`value` is microseconds per step (host-observed, whole call). The `roofline`
+object prices the lean kernel alone: algorithmic bytes per launch (K and V
+once, q once, the fp32 output once) over the kernel's average duration,
+measured with HIP events recorded on the call's stream right around the
+launch. `cpu_baseline` times the fp64 oracle on a bounded sample of heads of
+the same workload and scales it to a whole step. `comparators` times the
+in-house fixed-split and per-head kernels on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode-attention µs/step + achieved HBM TB/s vs 8 TB/s peak (512k, ragged)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Timing events from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
+    """Host-observed µs/step and mean kernel µs (HIP events around the kernels)."""
+    B, H, d = inp.B, inp.H, inp.d
+    out = torch.empty((B, H, d), dtype=torch.float32, device=inp.q.device)
+
+    def call(ev0=None, ev1=None):
+        la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, B, H, d, inp.scale, out, kind=kind,
+                        ev_start=ev0, ev_stop=ev1, **opts)
+
+    for _ in range(warmup):
+        call()
+    la.la_sync_check()
+    pairs = evs.create(2 * steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(pairs[2 * i], pairs[2 * i + 1])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    la.la_sync_check()
+    kern = [evs.elapsed_ms(pairs[2 * i], pairs[2 * i + 1]) * 1e3 for i in range(steps)]
+    evs.destroy(pairs)
+    kern.sort()
+    return {
+        "us_per_step": (t1 - t0) * 1e6 / steps,
+        "kernel_us_mean": sum(kern) / len(kern),
+        "kernel_us_p10": kern[len(kern) // 10],
+        "kernel_us_p50": kern[len(kern) // 2],
+        "kernel_us_p90": kern[(9 * len(kern)) // 10],
+    }
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """fp64 oracle on whole heads of the workload until ~budget_s of wall time,
+    scaled by (all heads / heads done) to microseconds per step."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    B, H = inp.B, inp.H
+    starts = np.concatenate([[0], np.cumsum(inp.ctx_lens)]) * H
+    qb = W.to_bits(inp.q)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    done = 0
+    tokens_done = 0
+    spent = 0.0
+    i = 0
+    while i < len(heads) and spent < budget_s:
+        batch = heads[i:i + workers]
+        # host copies of just these heads, made outside the timed region
+        ks, vs, lens, qs = [], [], [], []
+        for (b, h) in batch:
+            n = inp.ctx_lens[b]
+            r0 = int(starts[b]) + h * n
+            ks.append(W.to_bits(inp.k[r0:r0 + n]))
+            vs.append(W.to_bits(inp.v[r0:r0 + n]))
+            lens.append(n)
+            qs.append(qb[b, h])
+        kcat, vcat = np.concatenate(ks), np.concatenate(vs)
+        qcat = np.stack(qs)[:, None, :]
+        t0 = time.perf_counter()
+        oracle.attend_fp64(qcat, kcat, vcat, lens, inp.scale, inp.dtype, workers=workers)
+        spent += time.perf_counter() - t0
+        done += len(batch)
+        tokens_done += sum(lens)
+        i += len(batch)
+        del ks, vs, kcat, vcat
+    total_tokens = H * sum(inp.ctx_lens)
+    value = spent * 1e6 * total_tokens / tokens_done
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(value, 1),
+        "unit": "us/step",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{done} of {B * H} heads ({tokens_done} of {total_tokens} head-tokens), "
+                  f"fp64 two-pass numpy oracle, {spent:.1f} s wall, scaled by head-tokens; "
+                  f"host {cpu}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="512k",
+                    choices=["tiny", "65k", "512k", "ragged", "many-heads"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="time only the lean kernel on the workload (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the stream-K decode path here is single-GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_phase_attention_amd as la
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    la.lib()
+    evs = HipEvents()
+    log(f"[bench] generating {args.workload} (seed {args.seed})")
+    inp = W.make_inputs(args.workload, seed=args.seed, device="cuda")
+    w = inp.meta["workload"]
+    torch.cuda.synchronize()
+    dt_code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
+    G = la.la_max_grid(w.d, dt_code)
+    L = la.la_default_tile(w.d)
+    I, Gu, _ = la.la_schedule_dims(inp.ctx_lens, inp.H, L, G)
+    alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d)
+    log(f"[bench] lens={inp.ctx_lens} I={I} G={Gu} L={L} bytes={alg_bytes}")
+
+    log("[bench] timing lean")
+    lean = time_kind(la, torch, evs, inp, "lean", args.steps, args.warmup)
+    achieved = alg_bytes / (lean["kernel_us_mean"] * 1e-6) / 1e9
+    log(f"[bench] lean: {lean}")
+
+    comparators = None
+    if not args.no_comparators and not args.kernel_only:
+        comparators = {}
+        comparators["per_head"] = time_kind(la, torch, evs, inp, "per_head", 10, 2)
+        log(f"[bench] per_head: {comparators['per_head']}")
+        comparators["fixed_split_heuristic"] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2)
+        sweep = {}
+        for K in (1, 2, 4, 8, 16, 32, 64):
+            sweep[K] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2, num_splits=K)
+        bestK = min(sweep, key=lambda k: sweep[k]["kernel_us_mean"])
+        comparators["fixed_split_best"] = dict(sweep[bestK], num_splits=bestK)
+        comparators["fixed_split_sweep_kernel_us"] = {str(k): round(v["kernel_us_mean"], 2)
+                                                      for k, v in sweep.items()}
+        log(f"[bench] fixed_split best K={bestK}: {comparators['fixed_split_best']}")
+        for v in comparators.values():
+            if isinstance(v, dict) and "kernel_us_mean" in v:
+                v["tbs"] = round(alg_bytes / (v["kernel_us_mean"] * 1e-6) / 1e12, 3)
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.kernel_only:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(inp)
+        log(f"[bench] cpu: {cpu}")
+
+    desc = {
+        "tiny": "tiny: B=1, H=4, d=64, n=1024, fp16",
+        "65k": "65k: B=1, H=32, d=128, n=65536, bf16",
+        "512k": "512k: B=1, H=32, d=128, n=524288, bf16",
+        "ragged": "ragged: B=16, H=32, d=128, n_b log-uniform in [1024, 262144], bf16",
+        "many-heads": "many-heads: B=8, H=128, d=64, n=16384, fp16",
+    }[args.workload]
+    rec = {
+        "metric": METRIC,
+        "value": round(lean["us_per_step"], 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(lean["us_per_step"] / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": desc,
+            "B": inp.B, "H": inp.H, "d": w.d, "ctx_lens": inp.ctx_lens, "seed": args.seed,
+            "inputs": w.dtype, "accumulate": "fp32", "output": "fp32",
+            "kind": "lean", "grid": Gu, "tile_tokens": L, "iterations": I,
+            "parallelism": "single GPU",
+        },
+        "achieved_tbs": round(achieved / 1e3, 3),
+        "kernel_us": {k: round(v, 2) for k, v in lean.items() if k.startswith("kernel")},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "lean_kernel",
+            "bytes_per_launch": alg_bytes,
+        },
+        "cpu_baseline": cpu,
+        "comparators": comparators,
+        "env": {"torch": torch.__version__, "python": platform.python_version(),
+                "device": torch.cuda.get_device_name(0)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,270 @@
+"""ctypes binding over libla_decode.so (include/la_decode.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library. There
+is no fallback: if the library is not built, every call raises.
+
+torch is imported before the library is loaded so that the process holds one
+HIP runtime (torch's), which the library then shares.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import numpy as np
+
+__all__ = [
+    "LaError", "LA_F16", "LA_BF16", "LA_KIND_LEAN", "LA_KIND_FIXED_SPLIT", "LA_KIND_PER_HEAD",
+    "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex", "la_schedule",
+    "la_schedule_dims", "la_default_tile", "la_max_grid", "la_sync_check", "la_last_error",
+    "la_shutdown", "la_set_wait_limit_us", "decode_attention", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_decode.so")
+
+LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP, LA_ETIMEOUT, LA_ENOMEM = range(6)
+LA_F16, LA_BF16 = 0, 1
+LA_KIND_LEAN, LA_KIND_FIXED_SPLIT, LA_KIND_PER_HEAD = 0, 1, 2
+_STATUS = {0: "LA_OK", 1: "LA_EINVAL", 2: "LA_EUNSUPPORTED", 3: "LA_EHIP", 4: "LA_ETIMEOUT",
+           5: "LA_ENOMEM"}
+_KINDS = {"lean": LA_KIND_LEAN, "fixed_split": LA_KIND_FIXED_SPLIT, "per_head": LA_KIND_PER_HEAD}
+
+
+class LaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class LaOpts(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("kind", ctypes.c_int),
+        ("tile_tokens", ctypes.c_int),
+        ("grid", ctypes.c_int),
+        ("num_splits", ctypes.c_int),
+        ("ordinary_launch", ctypes.c_int),
+        ("m_out", ctypes.c_void_p),
+        ("l_out", ctypes.c_void_p),
+        ("tile_owner", ctypes.c_void_p),
+        ("cta_timestamps", ctypes.c_void_p),
+        ("ev_start", ctypes.c_void_p),
+        ("ev_stop", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_SIG = {
+    "la_decode_bf16": (_I, [_P, _P, _P, _I32P, _I, _I, _I, ctypes.c_float, _P, _P]),
+    "la_decode_f16": (_I, [_P, _P, _P, _I32P, _I, _I, _I, ctypes.c_float, _P, _P]),
+    "la_decode": (_I, [_P, _P, _P, _I32P, _I, _I, _I, ctypes.c_float, _P, _P, _I]),
+    "la_opts_init": (None, [ctypes.POINTER(LaOpts)]),
+    "la_decode_ex": (_I, [_P, _P, _P, _I32P, _I, _I, _I, ctypes.c_float, _P, _P,
+                          ctypes.POINTER(LaOpts)]),
+    "la_schedule_dims": (_I, [_I32P, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_int64),
+                              ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "la_schedule": (_I, [_I32P, _I, _I, _I, _I, _I32P, _I32P, _I32P, _I, ctypes.POINTER(_I),
+                         _I32P, _I32P]),
+    "la_default_tile": (_I, [_I]),
+    "la_max_grid": (_I, [_I, _I]),
+    "la_sync_check": (_I, [_P]),
+    "la_last_error": (ctypes.c_char_p, []),
+    "la_shutdown": (None, []),
+    "la_set_wait_limit_us": (None, [ctypes.c_uint32]),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            import torch  # noqa: F401  (one HIP runtime per process: torch's)
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m decode_phase_attention_amd.build`")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIG.items():
+                fn = getattr(h, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = h
+    return _lib
+
+
+def la_last_error() -> str:
+    return (lib().la_last_error() or b"").decode()
+
+
+def _check(st: int):
+    if st != LA_OK:
+        raise LaError(st, la_last_error())
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    import torch
+    if isinstance(x, torch.Tensor):
+        if not x.is_cuda:
+            raise ValueError("device tensors expected")
+        if not x.is_contiguous():
+            raise ValueError("contiguous tensors expected")
+        return x.data_ptr()
+    raise TypeError(f"cannot pass {type(x).__name__} as a device pointer")
+
+
+def _lens(ctx_lens):
+    arr = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int64))
+    if arr.ndim != 1:
+        raise ValueError("ctx_lens must be one-dimensional")
+    if arr.size and (arr.min() < np.iinfo(np.int32).min or arr.max() > np.iinfo(np.int32).max):
+        raise ValueError("ctx_lens entries must fit in int32")
+    a32 = arr.astype(np.int32)
+    return a32, a32.ctypes.data_as(_I32P)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_of(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return LA_F16
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise ValueError(f"fp16 or bf16 expected, got {t.dtype}")
+
+
+def la_decode(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, dtype=None):
+    """la_decode(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream, dtype)."""
+    if dtype is None:
+        dtype = _dtype_of(q)
+    arr, p = _lens(ctx_lens)
+    _check(lib().la_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
+                           float(scale), _ptr(out), _stream(stream), int(dtype)))
+
+
+def la_decode_bf16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None):
+    arr, p = _lens(ctx_lens)
+    _check(lib().la_decode_bf16(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
+                                float(scale), _ptr(out), _stream(stream)))
+
+
+def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None):
+    arr, p = _lens(ctx_lens)
+    _check(lib().la_decode_f16(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
+                               float(scale), _ptr(out), _stream(stream)))
+
+
+def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
+                 kind="lean", tile_tokens=0, grid=0, num_splits=0, ordinary_launch=False,
+                 m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
+                 ev_stop=None):
+    o = LaOpts()
+    lib().la_opts_init(ctypes.byref(o))
+    o.dtype = _dtype_of(q) if dtype is None else int(dtype)
+    o.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
+    o.tile_tokens = int(tile_tokens)
+    o.grid = int(grid)
+    o.num_splits = int(num_splits)
+    o.ordinary_launch = int(bool(ordinary_launch))
+    o.m_out = _ptr(m_out)
+    o.l_out = _ptr(l_out)
+    o.tile_owner = _ptr(tile_owner)
+    o.cta_timestamps = _ptr(cta_timestamps)
+    o.ev_start = ev_start
+    o.ev_stop = ev_stop
+    arr, p = _lens(ctx_lens)
+    _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
+                              float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
+
+
+def la_schedule_dims(ctx_lens, H, tile_tokens, grid):
+    arr, p = _lens(ctx_lens)
+    I = ctypes.c_int64()
+    G = ctypes.c_int()
+    rows = ctypes.c_int()
+    _check(lib().la_schedule_dims(p, len(arr), int(H), int(tile_tokens), int(grid),
+                                  ctypes.byref(I), ctypes.byref(G), ctypes.byref(rows)))
+    return I.value, G.value, rows.value
+
+
+def la_schedule(ctx_lens, H, tile_tokens, grid) -> dict:
+    """Host scheduler tables as numpy arrays (keys as in the C header)."""
+    arr, p = _lens(ctx_lens)
+    I, G, rows = la_schedule_dims(arr, H, tile_tokens, grid)
+    B = len(arr)
+    cta_begin = np.zeros(G + 1, np.int32)
+    cta_seg = np.zeros(G + 1, np.int32)
+    seg = np.zeros((rows, 6), np.int32)
+    host = np.zeros(B * H, np.int32)
+    last = np.zeros(B * H, np.int32)
+    n = ctypes.c_int()
+    _check(lib().la_schedule(p, B, int(H), int(tile_tokens), int(grid),
+                             cta_begin.ctypes.data_as(_I32P), cta_seg.ctypes.data_as(_I32P),
+                             seg.ctypes.data_as(_I32P), rows, ctypes.byref(n),
+                             host.ctypes.data_as(_I32P), last.ctypes.data_as(_I32P)))
+    return {"I": I, "G": G, "cta_begin": cta_begin, "cta_seg": cta_seg, "seg": seg[:n.value],
+            "host_cta": host, "last_cta": last}
+
+
+def la_default_tile(d: int) -> int:
+    return int(lib().la_default_tile(int(d)))
+
+
+def la_max_grid(d: int, dtype: int) -> int:
+    g = int(lib().la_max_grid(int(d), int(dtype)))
+    if g <= 0:
+        raise LaError(LA_EHIP, la_last_error())
+    return g
+
+
+def la_sync_check(stream=None):
+    _check(lib().la_sync_check(_stream(stream)))
+
+
+def la_shutdown():
+    lib().la_shutdown()
+
+
+def la_set_wait_limit_us(us: int):
+    lib().la_set_wait_limit_us(int(us))
+
+
+def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, kind="lean", out=None,
+                     stream=None, **opts):
+    """Convenience wrapper: shapes from the tensors, fp32 output allocated if
+    not given. q is [B, H, d]; k_cache/v_cache are packed [H * sum(n_b), d]."""
+    import torch
+    B, H, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if len(ctx_lens) != B:
+        raise ValueError("ctx_lens must have B entries")
+    total = int(np.sum(np.asarray(ctx_lens, dtype=np.int64)))
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (H * total, d) or t.dtype != q.dtype:
+            raise ValueError("k_cache/v_cache must be [H * sum(ctx_lens), d] in q's dtype")
+    la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream, kind=kind, **opts)
+    return out

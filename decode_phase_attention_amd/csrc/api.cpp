@@ -1,0 +1,481 @@
+// C-ABI entry points of libla_decode (declared in include/la_decode.h).
+//
+// Per call: validate, run the host scheduler into a pinned staging slot, copy
+// the tables to the workspace's device buffer on the caller's stream, launch.
+// Workspaces are per (device, stream) so that concurrent streams never share a
+// partials buffer or flags.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/la_decode.h"
+#include "kernels.h"
+#include "sched.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+la_status fail(la_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess)                                                             \
+            return fail(LA_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));          \
+    } while (0)
+
+constexpr int kRing = 4;                    // pinned staging slots per workspace
+constexpr uint32_t kDefaultWaitUs = 2000000;  // bound on one device-side wait: 2 s
+
+struct Staging {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+};
+
+struct Workspace {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    float* part = nullptr;          // lean partial records
+    size_t part_cap = 0;            // floats
+    uint32_t* flags = nullptr;      // one per lean workgroup, zero between launches
+    size_t flags_cap = 0;
+    uint32_t* err = nullptr;        // device error word
+    float* split_part = nullptr;    // fixed-split partial records
+    size_t split_cap = 0;
+    void* tables = nullptr;         // device copy of the schedule tables
+    size_t tables_cap = 0;
+    Staging ring[kRing];
+    int next = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
+std::map<std::pair<int, const void*>, int> g_capacity;
+uint32_t g_wait_us = kDefaultWaitUs;
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+// Grows a device buffer. The old one may still be read by work queued on the
+// stream, so the stream is drained before it is freed.
+la_status grow(Workspace& w, void** p, size_t* cap, size_t need_bytes, bool zero) {
+    if (need_bytes <= *cap) return LA_OK;
+    if (*p != nullptr) {
+        HIP_TRY(hipStreamSynchronize(w.stream));
+        HIP_TRY(hipFree(*p));
+        *p = nullptr;
+        *cap = 0;
+    }
+    size_t bytes = need_bytes + need_bytes / 2;
+    if (hipMalloc(p, bytes) != hipSuccess) {
+        *p = nullptr;
+        return fail(LA_ENOMEM, "hipMalloc of %zu bytes failed", bytes);
+    }
+    if (zero) HIP_TRY(hipMemsetAsync(*p, 0, bytes, w.stream));
+    *cap = bytes;
+    return LA_OK;
+}
+
+la_status get_workspace(hipStream_t stream, Workspace** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    auto key = std::make_pair(dev, stream);
+    auto it = g_ws.find(key);
+    if (it != g_ws.end()) {
+        *out = it->second;
+        return LA_OK;
+    }
+    Workspace* w = new Workspace();
+    w->device = dev;
+    w->stream = stream;
+    size_t cap = 0;
+    la_status st = grow(*w, (void**)&w->err, &cap, 256, true);
+    if (st != LA_OK) {
+        delete w;
+        return st;
+    }
+    for (auto& s : w->ring) {
+        if (hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
+            delete w;
+            return fail(LA_EHIP, "hipEventCreate failed");
+        }
+    }
+    g_ws[key] = w;
+    *out = w;
+    return LA_OK;
+}
+
+la_status capacity(int dtype, int d, int* out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    const void* fn = la::lean_kernel_ptr(dtype, d);
+    auto key = std::make_pair(dev, fn);
+    auto it = g_capacity.find(key);
+    if (it != g_capacity.end()) {
+        *out = it->second;
+        return LA_OK;
+    }
+    int per_cu = 0, cus = 0;
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, la::kThreads, 0));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    if (per_cu < 1 || cus < 1) return fail(LA_EHIP, "lean kernel does not fit on this device");
+    g_capacity[key] = per_cu * cus;
+    *out = per_cu * cus;
+    return LA_OK;
+}
+
+// Pinned staging slot with room for `bytes`; waits until its previous copy is done.
+la_status staging(Workspace& w, size_t bytes, Staging** out) {
+    Staging& s = w.ring[w.next];
+    w.next = (w.next + 1) % kRing;
+    HIP_TRY(hipEventSynchronize(s.ev));
+    if (s.cap < bytes) {
+        if (s.host != nullptr) HIP_TRY(hipHostFree(s.host));
+        s.host = nullptr;
+        s.cap = 0;
+        size_t b = bytes + bytes / 2;
+        if (hipHostMalloc(&s.host, b, hipHostMallocDefault) != hipSuccess) {
+            s.host = nullptr;
+            return fail(LA_ENOMEM, "hipHostMalloc of %zu bytes failed", b);
+        }
+        s.cap = b;
+    }
+    *out = &s;
+    return LA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+la_status validate(const void* q, const void* k, const void* v, const int32_t* ctx_lens, int B,
+                   int H, int d, float scale, const float* out, int dtype) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || ctx_lens == nullptr)
+        return fail(LA_EINVAL, "null pointer argument");
+    if (B < 1 || H < 1) return fail(LA_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+    if (d != 64 && d != 128) return fail(LA_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
+    if (dtype != LA_F16 && dtype != LA_BF16) return fail(LA_EINVAL, "unknown dtype %d", dtype);
+    if (!isfinite(scale)) return fail(LA_EINVAL, "scale must be finite");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(LA_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
+    for (int b = 0; b < B; ++b) {
+        if (ctx_lens[b] < 1) return fail(LA_EINVAL, "ctx_lens[%d] = %d; must be >= 1", b, ctx_lens[b]);
+        // kernels address one head's rows with 32-bit byte offsets
+        if ((int64_t)ctx_lens[b] * d * 2 > (int64_t)UINT32_MAX)
+            return fail(LA_EUNSUPPORTED, "ctx_lens[%d] = %d: one head's cache exceeds 4 GiB", b,
+                        ctx_lens[b]);
+    }
+    if ((int64_t)B * H > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "too many heads");
+    return LA_OK;
+}
+
+// Request tables every kernel kind needs: n_b and the token prefix sums.
+struct ReqLayout {
+    size_t off_tok, off_ctx, bytes;
+};
+
+ReqLayout req_layout(size_t start, int B) {
+    ReqLayout r;
+    r.off_tok = align16(start);
+    r.off_ctx = align16(r.off_tok + sizeof(int64_t) * B);
+    r.bytes = align16(r.off_ctx + sizeof(int32_t) * B);
+    return r;
+}
+
+void fill_req(char* base, const ReqLayout& r, const int32_t* ctx_lens, int B) {
+    int64_t* tok = (int64_t*)(base + r.off_tok);
+    int32_t* ctx = (int32_t*)(base + r.off_ctx);
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+        tok[b] = acc;
+        ctx[b] = ctx_lens[b];
+        acc += ctx_lens[b];
+    }
+}
+
+la_status upload(Workspace& w, Staging* s, size_t bytes) {
+    la_status st = grow(w, &w.tables, &w.tables_cap, bytes, false);
+    if (st != LA_OK) return st;
+    HIP_TRY(hipMemcpyAsync(w.tables, s->host, bytes, hipMemcpyHostToDevice, w.stream));
+    HIP_TRY(hipEventRecord(s->ev, w.stream));
+    return LA_OK;
+}
+
+la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
+                   const int32_t* ctx_lens, int B, int H, int d, float scale, float* out,
+                   const la_opts& o) {
+    int cap = 0;
+    la_status st = capacity(o.dtype, d, &cap);
+    if (st != LA_OK) return st;
+    if (o.grid < 0 || o.grid > cap)
+        return fail(LA_EINVAL, "grid %d outside [1, %d] (co-resident capacity)", o.grid, cap);
+    const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
+    int64_t I = 0;
+    int G = 0, max_rows = 0;
+    const char* why = "";
+    const int rc = la::schedule_dims(ctx_lens, B, H, L, o.grid > 0 ? o.grid : cap, &I, &G,
+                                     &max_rows, &why);
+    if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+
+    // table layout in one buffer
+    const int BH = B * H;
+    const size_t off_seg = 0;
+    const size_t off_cta_seg = align16(off_seg + 16 * (size_t)max_rows);
+    const size_t off_cta_begin = align16(off_cta_seg + 4 * (size_t)(G + 1));
+    const size_t off_last = align16(off_cta_begin + 4 * (size_t)(G + 1));
+    const size_t off_host = align16(off_last + 4 * (size_t)BH);
+    const ReqLayout rl = req_layout(off_host + 4 * (size_t)BH, B);
+
+    Staging* s = nullptr;
+    if ((st = staging(w, rl.bytes, &s)) != LA_OK) return st;
+    char* hb = (char*)s->host;
+    la::build_schedule(ctx_lens, B, H, L, G, I, (int32_t*)(hb + off_cta_begin),
+                       (int32_t*)(hb + off_cta_seg), nullptr, (int32_t*)(hb + off_seg),
+                       (int32_t*)(hb + off_host), (int32_t*)(hb + off_last));
+    fill_req(hb, rl, ctx_lens, B);
+
+    if ((st = grow(w, (void**)&w.part, &w.part_cap, sizeof(float) * (size_t)G * la::part_stride(d),
+                   false)) != LA_OK)
+        return st;
+    if ((st = grow(w, (void**)&w.flags, &w.flags_cap, sizeof(uint32_t) * (size_t)G, true)) != LA_OK)
+        return st;
+    if ((st = upload(w, s, rl.bytes)) != LA_OK) return st;
+
+    char* db = (char*)w.tables;
+    la::LeanArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.out = out;
+    a.m_out = o.m_out;
+    a.l_out = o.l_out;
+    a.ctx = (const int32_t*)(db + rl.off_ctx);
+    a.tok_off = (const int64_t*)(db + rl.off_tok);
+    a.seg = (const int4*)(db + off_seg);
+    a.cta_seg = (const int32_t*)(db + off_cta_seg);
+    a.cta_begin = (const int32_t*)(db + off_cta_begin);
+    a.last_cta = (const int32_t*)(db + off_last);
+    a.part = w.part;
+    a.flags = w.flags;
+    a.err = w.err;
+    a.tile_owner = o.tile_owner;
+    a.ts = o.cta_timestamps;
+    a.H = H;
+    a.L = L;
+    a.sl2e = scale * 1.4426950408889634f;
+    a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
+    if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
+    HIP_TRY(la::launch_lean(o.dtype, d, a, G, w.stream, o.ordinary_launch == 0));
+    if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+    return LA_OK;
+}
+
+la_status run_split_or_head(Workspace& w, const void* q, const void* k, const void* v,
+                            const int32_t* ctx_lens, int B, int H, int d, float scale, float* out,
+                            const la_opts& o) {
+    const int BH = B * H;
+    const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
+    int splits = 1;
+    if (o.kind == LA_KIND_FIXED_SPLIT) {
+        if (o.num_splits < 0) return fail(LA_EINVAL, "num_splits must be >= 0");
+        splits = o.num_splits;
+        if (splits == 0) {
+            int cap = 0;
+            la_status st = capacity(o.dtype, d, &cap);
+            if (st != LA_OK) return st;
+            splits = 1;
+            while ((int64_t)BH * splits < cap && splits < 64) splits *= 2;
+        }
+        if ((int64_t)BH * splits > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "too many splits");
+    }
+    const ReqLayout rl = req_layout(0, B);
+    Staging* s = nullptr;
+    la_status st = staging(w, rl.bytes, &s);
+    if (st != LA_OK) return st;
+    fill_req((char*)s->host, rl, ctx_lens, B);
+    if (o.kind == LA_KIND_FIXED_SPLIT &&
+        (st = grow(w, (void**)&w.split_part, &w.split_cap,
+                   sizeof(float) * (size_t)BH * splits * la::part_stride(d), false)) != LA_OK)
+        return st;
+    if ((st = upload(w, s, rl.bytes)) != LA_OK) return st;
+
+    char* db = (char*)w.tables;
+    la::SplitArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.out = out;
+    a.m_out = o.m_out;
+    a.l_out = o.l_out;
+    a.ctx = (const int32_t*)(db + rl.off_ctx);
+    a.tok_off = (const int64_t*)(db + rl.off_tok);
+    a.part = w.split_part;
+    a.H = H;
+    a.L = L;
+    a.splits = splits;
+    a.sl2e = scale * 1.4426950408889634f;
+    if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
+    if (o.kind == LA_KIND_PER_HEAD) {
+        HIP_TRY(la::launch_per_head(o.dtype, d, a, BH, w.stream));
+    } else {
+        HIP_TRY(la::launch_split(o.dtype, d, a, BH * splits, w.stream));
+        la::CombineArgs c;
+        c.part = w.split_part;
+        c.out = out;
+        c.m_out = o.m_out;
+        c.l_out = o.l_out;
+        c.splits = splits;
+        HIP_TRY(la::launch_combine(d, c, BH, w.stream));
+    }
+    if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+    return LA_OK;
+}
+
+void free_workspace(Workspace* w) {
+    hipSetDevice(w->device);
+    hipDeviceSynchronize();
+    hipFree(w->part);
+    hipFree(w->flags);
+    hipFree(w->err);
+    hipFree(w->split_part);
+    hipFree(w->tables);
+    for (auto& s : w->ring) {
+        if (s.host != nullptr) hipHostFree(s.host);
+        if (s.ev != nullptr) hipEventDestroy(s.ev);
+    }
+    delete w;
+}
+
+}  // namespace
+
+extern "C" {
+
+void la_opts_init(la_opts* o) {
+    if (o != nullptr) memset(o, 0, sizeof(*o));
+}
+
+la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_t* ctx_lens,
+                       int B, int H, int d, float scale, float* out, void* stream,
+                       const la_opts* opts) {
+    g_msg[0] = 0;
+    la_opts o;
+    la_opts_init(&o);
+    if (opts != nullptr) o = *opts;
+    la_status st = validate(q, k, v, ctx_lens, B, H, d, scale, out, o.dtype);
+    if (st != LA_OK) return st;
+    if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_FIXED_SPLIT && o.kind != LA_KIND_PER_HEAD)
+        return fail(LA_EINVAL, "unknown kind %d", o.kind);
+    if (o.tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");
+    if (o.kind != LA_KIND_LEAN && (o.tile_owner != nullptr || o.cta_timestamps != nullptr))
+        return fail(LA_EINVAL, "tile_owner and cta_timestamps apply to the lean kind only");
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace* w = nullptr;
+    if ((st = get_workspace((hipStream_t)stream, &w)) != LA_OK) return st;
+    if (o.kind == LA_KIND_LEAN) return run_lean(*w, q, k, v, ctx_lens, B, H, d, scale, out, o);
+    return run_split_or_head(*w, q, k, v, ctx_lens, B, H, d, scale, out, o);
+}
+
+la_status la_decode(const void* q, const void* k, const void* v, const int32_t* ctx_lens, int B,
+                    int H, int d, float scale, float* out, void* stream, int dtype) {
+    la_opts o;
+    la_opts_init(&o);
+    o.dtype = dtype;
+    return la_decode_ex(q, k, v, ctx_lens, B, H, d, scale, out, stream, &o);
+}
+
+la_status la_decode_bf16(const void* q, const void* k, const void* v, const int32_t* ctx_lens,
+                         int B, int H, int d, float scale, float* out, void* stream) {
+    return la_decode(q, k, v, ctx_lens, B, H, d, scale, out, stream, LA_BF16);
+}
+
+la_status la_decode_f16(const void* q, const void* k, const void* v, const int32_t* ctx_lens,
+                        int B, int H, int d, float scale, float* out, void* stream) {
+    return la_decode(q, k, v, ctx_lens, B, H, d, scale, out, stream, LA_F16);
+}
+
+la_status la_schedule_dims(const int32_t* ctx_lens, int B, int H, int tile_tokens, int grid,
+                           int64_t* iters, int* grid_used, int* max_rows) {
+    g_msg[0] = 0;
+    if (iters == nullptr || grid_used == nullptr || max_rows == nullptr)
+        return fail(LA_EINVAL, "null output pointer");
+    const char* why = "";
+    const int rc = la::schedule_dims(ctx_lens, B, H, tile_tokens, grid, iters, grid_used, max_rows,
+                                     &why);
+    if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+    return LA_OK;
+}
+
+la_status la_schedule(const int32_t* ctx_lens, int B, int H, int tile_tokens, int grid,
+                      int32_t* cta_begin, int32_t* cta_seg, int32_t* seg, int max_rows,
+                      int* n_seg, int32_t* host_cta, int32_t* last_cta) {
+    int64_t I = 0;
+    int G = 0, rows = 0;
+    la_status st = la_schedule_dims(ctx_lens, B, H, tile_tokens, grid, &I, &G, &rows);
+    if (st != LA_OK) return st;
+    if (cta_begin == nullptr || cta_seg == nullptr || seg == nullptr || n_seg == nullptr ||
+        host_cta == nullptr || last_cta == nullptr)
+        return fail(LA_EINVAL, "null output pointer");
+    if (max_rows < rows) return fail(LA_EINVAL, "max_rows %d < required %d", max_rows, rows);
+    *n_seg = la::build_schedule(ctx_lens, B, H, tile_tokens, G, I, cta_begin, cta_seg, seg,
+                                nullptr, host_cta, last_cta);
+    return LA_OK;
+}
+
+int la_default_tile(int d) { return (d == 64 || d == 128) ? la::chunk_rows(d) : 0; }
+
+int la_max_grid(int d, int dtype) {
+    if ((d != 64 && d != 128) || (dtype != LA_F16 && dtype != LA_BF16)) {
+        fail(LA_EINVAL, "unsupported d/dtype");
+        return -1;
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cap = 0;
+    if (capacity(dtype, d, &cap) != LA_OK) return -1;
+    return cap;
+}
+
+la_status la_sync_check(void* stream) {
+    g_msg[0] = 0;
+    std::lock_guard<std::mutex> lock(g_mu);
+    HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    auto it = g_ws.find(std::make_pair(dev, (hipStream_t)stream));
+    if (it == g_ws.end()) return LA_OK;
+    Workspace& w = *it->second;
+    uint32_t err = 0;
+    HIP_TRY(hipMemcpy(&err, w.err, sizeof(err), hipMemcpyDeviceToHost));
+    if (err == 0) return LA_OK;
+    HIP_TRY(hipMemsetAsync(w.err, 0, sizeof(uint32_t), w.stream));
+    if (w.flags != nullptr) HIP_TRY(hipMemsetAsync(w.flags, 0, w.flags_cap, w.stream));
+    HIP_TRY(hipStreamSynchronize(w.stream));
+    return fail(LA_ETIMEOUT, "a device-side wait exceeded its bound (error word 0x%x)", err);
+}
+
+const char* la_last_error(void) { return g_msg; }
+
+void la_shutdown(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (auto& kv : g_ws) free_workspace(kv.second);
+    g_ws.clear();
+    g_capacity.clear();
+}
+
+// Bound on one device-side wait in microseconds (0 restores the default).
+// A small bound makes waits give up early; tests use it to force that path.
+void la_set_wait_limit_us(uint32_t us) { g_wait_us = us == 0 ? kDefaultWaitUs : us; }
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;     // workgroup size
+constexpr int kRows = 8;                  // K/V rows each lane group loads per step
+
+// Rows processed by one workgroup per step (the natural LeanTile size):
+// a row of d halves is d/8 lanes of 16 bytes, so a wave holds 512/d rows per
+// load and the workgroup 2048/d; each lane group takes kRows of them.
+constexpr int chunk_rows(int d) { return (2048 / d) * kRows; }
+
+// Stride in floats of one partial record (Obar[d], m, l), padded to 16 bytes.
+constexpr int part_stride(int d) { return d + 4; }
+
+struct LeanArgs {
+    const uint16_t* q;         // [B*H, d]
+    const uint16_t* k;         // packed rows [H * sum n_b, d]
+    const uint16_t* v;
+    float* out;                // [B*H, d]
+    float* m_out;              // optional [B*H]
+    float* l_out;              // optional [B*H]
+    const int32_t* ctx;        // [B] n_b
+    const int64_t* tok_off;    // [B] sum_{b'<b} n_b'
+    const int4* seg;           // [nseg] (u, t0, t1, host | finishing << 1)
+    const int32_t* cta_seg;    // [G+1]
+    const int32_t* cta_begin;  // [G+1]
+    const int32_t* last_cta;   // [B*H]
+    float* part;               // [G * part_stride(d)]
+    uint32_t* flags;           // [G], zero at launch, zero again at exit
+    uint32_t* err;             // device error word
+    int32_t* tile_owner;       // optional [I]
+    uint64_t* ts;              // optional [G*4]
+    int H;
+    int L;                     // tile tokens
+    float sl2e;                // scale * log2(e)
+    uint64_t wait_ticks;       // 100 MHz clock ticks before a wait gives up
+};
+
+struct SplitArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    float* out;                // per-head kernel: output; split kernel: unused
+    float* m_out;
+    float* l_out;
+    const int32_t* ctx;
+    const int64_t* tok_off;
+    float* part;               // split kernel: [B*H*splits * part_stride(d)]
+    int H;
+    int L;
+    int splits;
+    float sl2e;
+};
+
+struct CombineArgs {
+    const float* part;
+    float* out;
+    float* m_out;
+    float* l_out;
+    int splits;
+};
+
+const void* lean_kernel_ptr(int dtype, int d);
+hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_t s,
+                       bool cooperative);
+hipError_t launch_split(int dtype, int d, const SplitArgs& a, int blocks, hipStream_t s);
+hipError_t launch_combine(int d, const CombineArgs& a, int heads, hipStream_t s);
+hipError_t launch_per_head(int dtype, int d, const SplitArgs& a, int heads, hipStream_t s);
+
+}  // namespace la

@@ -1,0 +1,479 @@
+// Decode-attention kernels for gfx950 (CDNA4).
+//
+// Three kernels share one streaming routine:
+//   lean_kernel      stream-K over a persistent grid with in-launch merging
+//                    (xllm-io paper review of arXiv 2405.10480, §3.3-§3.5, §4.4)
+//   split_kernel +   fixed split of every head into `splits` pieces and a
+//   combine_kernel   second launch that merges them (the FlashDecoding scheme the
+//                    same review describes in §2.3)
+//   per_head_kernel  one workgroup per (request, head) over its whole context
+//                    (the FlashAttention-2 decode mapping, §2.2)
+//
+// Streaming routine. A K or V row of d halves is d/8 lanes x 16 bytes, so
+// d/8 consecutive lanes form a "lane group" that owns one row per load. Each
+// group keeps its own online-softmax state (m, l, Obar slice of 8 dims) over
+// the rows it sees (§3.3: update the statistics per tile, then
+// O_acc = P V + diag(rescale) O_acc). Scores are reduced across the group's
+// lanes with DPP; no barrier or LDS traffic happens inside a range. Decode
+// attention has a single query row, so K and V elements are each used by one
+// lane exactly once: they go straight from HBM to registers with 16-byte
+// loads and are never staged in LDS. Only at the end of a range do the
+// groups meet in LDS, where the reduction f (§3.2) folds them into one
+// (m, l, Obar[d]).
+//
+// Exponentials are taken base 2 with log2(e) folded into the scale; m is kept
+// in log2 units inside the kernels and converted back to natural-log units
+// for m_out.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace la {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ numerics
+
+// Dot product of 8 packed halves (one 16-byte load) with the lane's q slice,
+// accumulated in fp32 by the packed dot2 instructions.
+template <int DT>
+__device__ __forceinline__ float dot8(const uint4 k, const uint4 q) {
+    float a = 0.f;
+    if constexpr (DT == 0) {
+        a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.x), __builtin_bit_cast(half2_t, q.x), a, false);
+        a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.y), __builtin_bit_cast(half2_t, q.y), a, false);
+        a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.z), __builtin_bit_cast(half2_t, q.z), a, false);
+        a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.w), __builtin_bit_cast(half2_t, q.w), a, false);
+    } else {
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.x), __builtin_bit_cast(bf162_t, q.x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.y), __builtin_bit_cast(bf162_t, q.y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.z), __builtin_bit_cast(bf162_t, q.z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.w), __builtin_bit_cast(bf162_t, q.w), a, false);
+    }
+    return a;
+}
+
+template <int DT>
+__device__ __forceinline__ void widen2(uint32_t w, float& lo, float& hi) {
+    if constexpr (DT == 0) {
+        half2_t h = __builtin_bit_cast(half2_t, w);
+        lo = (float)h.x;
+        hi = (float)h.y;
+    } else {
+        lo = __uint_as_float(w << 16);
+        hi = __uint_as_float(w & 0xffff0000u);
+    }
+}
+
+// Sum over the lanes of one group: 8 lanes (d = 64) or 16 lanes (d = 128),
+// all inside one DPP row. Every lane ends with the same bits because each
+// step adds a pair of commuted operands.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    if constexpr (LPR == 16)
+        x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false);  // row_mirror
+    return x;
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct Acc {
+    float m;      // running max, log2 units
+    float l;      // running sum of 2^(s - m)
+    float o[8];   // running unnormalised output, this lane's 8 dims
+};
+
+__device__ __forceinline__ void acc_init(Acc& a) {
+    a.m = kNegInf;
+    a.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a.o[i] = 0.f;
+}
+
+template <int D>
+struct Geo {
+    static constexpr int LPR = D / 8;                 // lanes per row
+    static constexpr int GPW = 64 / LPR;              // groups per wave
+    static constexpr int NG = GPW * kWaves;           // groups per workgroup
+    static constexpr int CH = NG * kRows;             // rows per step
+};
+
+// One step of the streaming loop: kRows rows per lane group, K and V loads
+// issued back to back, then scores, one rescale, and the V accumulation.
+// Row r of group g in a step starting at `base` is base + r*NG + g, so one
+// load instruction of a wave reads GPW consecutive rows (1 KiB contiguous).
+// Full steps address rows as (uniform base) + (fixed 32-bit lane offset); the
+// last, partial step clamps rows at or past e to e-1 (never reading outside
+// the head) and masks their scores to -inf.
+template <int DT, int D, bool TAIL>
+__device__ __forceinline__ void stream_step(const char* __restrict__ kh, const char* __restrict__ vh,
+                                            int base, int e, uint32_t lane_off, const uint4 qv,
+                                            float sl2e, int grp, Acc& acc) {
+    using G = Geo<D>;
+    constexpr uint32_t kRowBytes = D * 2;
+    constexpr uint32_t kStepRowBytes = G::NG * kRowBytes;
+    uint4 kr[kRows], vr[kRows];
+    if constexpr (!TAIL) {
+        const uint32_t off = (uint32_t)base * kRowBytes + lane_off;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+            kr[r] = *reinterpret_cast<const uint4*>(kh + (uint64_t)(off + r * kStepRowBytes));
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+            vr[r] = *reinterpret_cast<const uint4*>(vh + (uint64_t)(off + r * kStepRowBytes));
+    } else {
+        const uint32_t col_off = lane_off - (uint32_t)grp * kRowBytes;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
+            kr[r] = *reinterpret_cast<const uint4*>(kh + (uint64_t)(j * kRowBytes + col_off));
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
+            vr[r] = *reinterpret_cast<const uint4*>(vh + (uint64_t)(j * kRowBytes + col_off));
+        }
+    }
+    float s[kRows];
+    float mx = kNegInf;
+    {
+        // The scaled score is rounded once and that same value feeds both the
+        // max and exp2(s - m): no contraction of the product into the
+        // subtraction, so the maximal row gets weight exactly 1.
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const float x = group_sum<G::LPR>(dot8<DT>(kr[r], qv)) * sl2e;
+            s[r] = (!TAIL || base + r * G::NG + grp < e) ? x : kNegInf;
+            mx = fmaxf(mx, s[r]);
+        }
+    }
+    const float mn = fmaxf(acc.m, mx);
+    const float mu = (mn == kNegInf) ? 0.f : mn;   // no -inf - -inf
+    const float alpha = fexp2(acc.m - mu);
+    acc.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc.o[i] *= alpha;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const float p = fexp2(s[r] - mu);
+        acc.l += p;
+        float f[8];
+        widen2<DT>(vr[r].x, f[0], f[1]);
+        widen2<DT>(vr[r].y, f[2], f[3]);
+        widen2<DT>(vr[r].z, f[4], f[5]);
+        widen2<DT>(vr[r].w, f[6], f[7]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc.o[i] = fmaf(p, f[i], acc.o[i]);
+    }
+    acc.m = mn;
+}
+
+// Stream rows [a, e) of one head (kh/vh point at its row 0) through the lane
+// group's online softmax. A head spans less than 4 GiB, so every offset
+// inside it fits in 32 bits.
+template <int DT, int D>
+__device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t* vh, int a, int e,
+                                             const uint4 qv, float sl2e, int grp, int sub, Acc& acc) {
+    using G = Geo<D>;
+    const uint32_t lane_off = (uint32_t)(grp * D + sub * 8) * 2u;
+    const char* kc = reinterpret_cast<const char*>(kh);
+    const char* vc = reinterpret_cast<const char*>(vh);
+    int base = a;
+    for (; base + G::CH <= e; base += G::CH)
+        stream_step<DT, D, false>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
+    if (base < e) stream_step<DT, D, true>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
+}
+
+template <int D>
+struct alignas(16) Smem {
+    float o[Geo<D>::NG][D];
+    float m[Geo<D>::NG];
+    float l[Geo<D>::NG];
+};
+
+// Fold the lane groups of the workgroup with f. Threads t < D receive
+// (m, l, Obar[t]) of everything the workgroup streamed for this range.
+template <int D>
+__device__ __forceinline__ void wg_fold(Smem<D>& sm, const Acc& a, int grp, int sub, float& M,
+                                        float& Ls, float& O) {
+    using G = Geo<D>;
+    float4* dst = reinterpret_cast<float4*>(&sm.o[grp][sub * 8]);
+    dst[0] = make_float4(a.o[0], a.o[1], a.o[2], a.o[3]);
+    dst[1] = make_float4(a.o[4], a.o[5], a.o[6], a.o[7]);
+    if (sub == 0) {
+        sm.m[grp] = a.m;
+        sm.l[grp] = a.l;
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < D) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int g = 0; g < G::NG; ++g) mx = fmaxf(mx, sm.m[g]);
+        const float mu = (mx == kNegInf) ? 0.f : mx;
+        float ls = 0.f, o = 0.f;
+#pragma unroll 8
+        for (int g = 0; g < G::NG; ++g) {
+            const float w = fexp2(sm.m[g] - mu);
+            ls = fmaf(w, sm.l[g], ls);
+            o = fmaf(w, sm.o[g][t], o);
+        }
+        M = mx;
+        Ls = ls;
+        O = o;
+    }
+    __syncthreads();
+}
+
+// f applied to a running (M, Ls, O) and one more (pm, pl, po).
+__device__ __forceinline__ void merge_into(float& M, float& Ls, float& O, float pm, float pl,
+                                           float po) {
+    const float mn = fmaxf(M, pm);
+    const float mu = (mn == kNegInf) ? 0.f : mn;
+    const float a = fexp2(M - mu), b = fexp2(pm - mu);
+    Ls = a * Ls + b * pl;
+    O = a * O + b * po;
+    M = mn;
+}
+
+// Wait until another workgroup has published its partial. Polls with
+// relaxed agent-scope loads, then one acquire fence so the partial's data is
+// read after the flag. A wait gives up after `limit` ticks of the 100 MHz
+// realtime clock, or at once when any wait has already given up, and raises
+// the error word: a missing peer cannot hang the launch.
+__device__ __forceinline__ void wait_flag(uint32_t* f, uint64_t limit, uint32_t* err) {
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (__builtin_amdgcn_s_memrealtime() - t0 > limit ||
+                __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                atomicOr(err, 1u);
+                break;
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+__device__ __forceinline__ uint4 load_q(const uint16_t* q, int u, int D, int sub) {
+    return *reinterpret_cast<const uint4*>(q + (int64_t)u * D + sub * 8);
+}
+
+__device__ __forceinline__ uint64_t hwreg_ids() {
+    // HW_ID (register 4) and XCC_ID (register 20), all 32 bits of each
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+    return ((uint64_t)xcc << 32) | hw;
+}
+
+// ------------------------------------------------------------------ lean
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
+    using G = Geo<D>;
+    __shared__ Smem<D> sm;
+    const int c = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int grp = (t >> 6) * G::GPW + lane / G::LPR;
+    const int sub = lane % G::LPR;
+    if (a.ts != nullptr && t == 0) {
+        a.ts[c * 4 + 0] = __builtin_amdgcn_s_memrealtime();
+        a.ts[c * 4 + 2] = hwreg_ids();
+    }
+    const int s0 = a.cta_seg[c], s1 = a.cta_seg[c + 1];
+    int iter = a.cta_begin[c];
+    for (int si = s0; si < s1; ++si) {
+        const int4 sg = a.seg[si];
+        const int u = sg.x;
+        const int b = u / a.H;
+        const int h = u - b * a.H;
+        const int n = a.ctx[b];
+        const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
+        const uint16_t* kh = a.k + row0 * D;
+        const uint16_t* vh = a.v + row0 * D;
+        const int tok0 = sg.y * a.L;
+        const int tok1 = (int)min((int64_t)sg.z * a.L, (int64_t)n);
+        Acc acc;
+        acc_init(acc);
+        stream_range<DT, D>(kh, vh, tok0, tok1, load_q(a.q, u, D, sub), a.sl2e, grp, sub, acc);
+        if (a.tile_owner != nullptr && t == 0)
+            for (int i = sg.y; i < sg.z; ++i) a.tile_owner[iter + i - sg.y] = c;
+        iter += sg.z - sg.y;
+
+        float M = kNegInf, Ls = 0.f, O = 0.f;
+        wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+        const bool host = sg.w & 1;
+        const bool fin = sg.w & 2;
+        if (!host) {
+            // a peer: publish (Obar, m, l) for the head's host, then raise the flag
+            float* p = a.part + (int64_t)c * part_stride(D);
+            if (t < D) p[t] = O;
+            if (t == 0) {
+                p[D] = M;
+                p[D + 1] = Ls;
+            }
+            __threadfence();
+            __syncthreads();
+            if (t == 0) __hip_atomic_store(&a.flags[c], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            continue;
+        }
+        if (!fin) {
+            // the host: fold the peers' partials in ascending workgroup order
+            const int last = a.last_cta[u];
+            if (t < D) {
+                for (int pc = c + 1; pc <= last; ++pc) {
+                    wait_flag(&a.flags[pc], a.wait_ticks, a.err);
+                    const float* p = a.part + (int64_t)pc * part_stride(D);
+                    merge_into(M, Ls, O, p[D], p[D + 1], p[t]);
+                }
+            }
+            __syncthreads();
+            if (t == 0)
+                for (int pc = c + 1; pc <= last; ++pc)
+                    __hip_atomic_store(&a.flags[pc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (t < D) a.out[(int64_t)u * D + t] = O / Ls;
+        if (t == 0) {
+            if (a.m_out != nullptr) a.m_out[u] = M * kLn2;
+            if (a.l_out != nullptr) a.l_out[u] = Ls;
+        }
+    }
+    if (a.ts != nullptr && t == 0) a.ts[c * 4 + 1] = __builtin_amdgcn_s_memrealtime();
+}
+
+// ------------------------------------------------------------------ fixed split
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
+    using G = Geo<D>;
+    __shared__ Smem<D> sm;
+    const int u = blockIdx.x / a.splits;
+    const int k = blockIdx.x - u * a.splits;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int grp = (t >> 6) * G::GPW + lane / G::LPR;
+    const int sub = lane % G::LPR;
+    const int b = u / a.H;
+    const int h = u - b * a.H;
+    const int n = a.ctx[b];
+    const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
+    const int64_t T = ((int64_t)n + a.L - 1) / a.L;
+    const int64_t t0 = (int64_t)k * T / a.splits, t1 = (int64_t)(k + 1) * T / a.splits;
+    const int tok0 = (int)(t0 * a.L);
+    const int tok1 = (int)min(t1 * a.L, (int64_t)n);
+    Acc acc;
+    acc_init(acc);
+    if (tok0 < tok1)
+        stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, load_q(a.q, u, D, sub),
+                            a.sl2e, grp, sub, acc);
+    float M = kNegInf, Ls = 0.f, O = 0.f;
+    wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+    float* p = a.part + (int64_t)blockIdx.x * part_stride(D);
+    if (t < D) p[t] = O;
+    if (t == 0) {
+        p[D] = M;
+        p[D + 1] = Ls;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void combine_kernel(const CombineArgs a) {
+    const int u = blockIdx.x;
+    const int t = threadIdx.x;
+    float M = kNegInf, Ls = 0.f, O = 0.f;
+    for (int k = 0; k < a.splits; ++k) {
+        const float* p = a.part + ((int64_t)u * a.splits + k) * part_stride(D);
+        merge_into(M, Ls, O, p[D], p[D + 1], p[t]);
+    }
+    a.out[(int64_t)u * D + t] = O / Ls;
+    if (t == 0) {
+        if (a.m_out != nullptr) a.m_out[u] = M * kLn2;
+        if (a.l_out != nullptr) a.l_out[u] = Ls;
+    }
+}
+
+// ------------------------------------------------------------------ per head
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
+    using G = Geo<D>;
+    __shared__ Smem<D> sm;
+    const int u = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int grp = (t >> 6) * G::GPW + lane / G::LPR;
+    const int sub = lane % G::LPR;
+    const int b = u / a.H;
+    const int h = u - b * a.H;
+    const int n = a.ctx[b];
+    const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
+    Acc acc;
+    acc_init(acc);
+    stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, 0, n, load_q(a.q, u, D, sub), a.sl2e,
+                        grp, sub, acc);
+    float M = kNegInf, Ls = 0.f, O = 0.f;
+    wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+    if (t < D) a.out[(int64_t)u * D + t] = O / Ls;
+    if (t == 0) {
+        if (a.m_out != nullptr) a.m_out[u] = M * kLn2;
+        if (a.l_out != nullptr) a.l_out[u] = Ls;
+    }
+}
+
+template <typename F>
+const void* pick(int dtype, int d, F f16_64, F f16_128, F bf16_64, F bf16_128) {
+    if (dtype == 0) return d == 64 ? (const void*)f16_64 : (const void*)f16_128;
+    return d == 64 ? (const void*)bf16_64 : (const void*)bf16_128;
+}
+
+}  // namespace
+
+const void* lean_kernel_ptr(int dtype, int d) {
+    return pick(dtype, d, &lean_kernel<0, 64>, &lean_kernel<0, 128>, &lean_kernel<1, 64>,
+                &lean_kernel<1, 128>);
+}
+
+hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_t s,
+                       bool cooperative) {
+    const void* fn = lean_kernel_ptr(dtype, d);
+    void* args[] = {const_cast<LeanArgs*>(&a)};
+    if (cooperative)
+        return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_split(int dtype, int d, const SplitArgs& a, int blocks, hipStream_t s) {
+    const void* fn = pick(dtype, d, &split_kernel<0, 64>, &split_kernel<0, 128>,
+                          &split_kernel<1, 64>, &split_kernel<1, 128>);
+    void* args[] = {const_cast<SplitArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3(blocks), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_combine(int d, const CombineArgs& a, int heads, hipStream_t s) {
+    const void* fn = d == 64 ? (const void*)&combine_kernel<64> : (const void*)&combine_kernel<128>;
+    void* args[] = {const_cast<CombineArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3(heads), dim3(d), args, 0, s);
+}
+
+hipError_t launch_per_head(int dtype, int d, const SplitArgs& a, int heads, hipStream_t s) {
+    const void* fn = pick(dtype, d, &per_head_kernel<0, 64>, &per_head_kernel<0, 128>,
+                          &per_head_kernel<1, 64>, &per_head_kernel<1, 128>);
+    void* args[] = {const_cast<SplitArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3(heads), dim3(kThreads), args, 0, s);
+}
+
+}  // namespace la

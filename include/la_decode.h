@@ -1,0 +1,200 @@
+/*
+ * la_decode.h -- exact decode-phase attention over a KV cache on MI355X
+ * (gfx950), with the LeanAttention stream-K decomposition.
+ *
+ * The operation (xllm-io paper review of arXiv 2405.10480, §3.1 and §3.2;
+ * LeanAttention talk summary, "Background"): for every request b and head h,
+ * one query row q = q[b,h,:] attends over the n_b cached keys and values of
+ * that request and head:
+ *
+ *     s_j = scale * (q . K_j)           j = 0 .. n_b - 1
+ *     m   = max_j s_j
+ *     l   = sum_j exp(s_j - m)
+ *     out = sum_j exp(s_j - m) V_j / l
+ *
+ * No mask other than the length: the decode query sees the whole cache.
+ *
+ * How it is computed (same pages, §3.3-§3.5): the context of every head is cut
+ * into LeanTiles of `tile_tokens` tokens; the tile iterations of all heads are
+ * laid end to end and split into equal contiguous ranges over a persistent grid
+ * of co-resident workgroups (a host-side scheduler builds these tables on every
+ * call); each workgroup streams its tiles with an online softmax, and partial
+ * (m, l, Obar) results of heads that span several workgroups are merged inside
+ * the same launch with the associative rescaling reduction
+ *     f(x, y): m = max(m_x, m_y), l = e^{m_x-m} l_x + e^{m_y-m} l_y,
+ *              Obar = e^{m_x-m} Obar_x + e^{m_y-m} Obar_y
+ * by the workgroup that holds the head's first tile (its "host").
+ *
+ * Conventions for every entry point:
+ *  - Device pointers: q, k_cache, v_cache, out and the optional outputs in
+ *    la_opts. They must be 16-byte aligned. The caller owns them.
+ *  - Host pointers: ctx_lens (B entries, each >= 1) and the la_schedule
+ *    tables. ctx_lens is read before the call returns, so the caller may reuse
+ *    it immediately.
+ *  - Layouts: q is [B, H, d] (fp16 or bf16). K and V are packed per request:
+ *    request b's block is [H, n_b, d] and starts at element
+ *    H * d * sum_{b' < b} n_{b'}; for equal lengths this is [B, H, n, d]
+ *    (the (batch, heads, seq_len, head_dim) layout of §7.4). out is
+ *    [B, H, d] fp32.
+ *  - d must be 64 or 128. scale must be finite. One head's K (or V) block,
+ *    n_b * d * 2 bytes, must not exceed 4 GiB (LA_EUNSUPPORTED otherwise).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; 0 is the null
+ *    stream). Argument and launch errors are returned synchronously. A
+ *    device-side wait that exceeds its bound sets an error word that
+ *    la_sync_check() reports.
+ *  - Nothing throws across this boundary. On failure la_last_error() returns a
+ *    message for the calling thread.
+ *  - Workspaces (partials buffer, flags, schedule tables, pinned staging) are
+ *    owned by the library, one per (device, stream), allocated on first use and
+ *    freed by la_shutdown(). Calls on the same stream are ordered; calls from
+ *    several host threads are serialised inside the library.
+ */
+#ifndef LA_DECODE_H
+#define LA_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_EINVAL = 1,        /* bad argument: null pointer, size < 1, misaligned, ... */
+    LA_EUNSUPPORTED = 2,  /* valid but not implemented: d not 64/128, too many tiles */
+    LA_EHIP = 3,          /* a HIP runtime call failed */
+    LA_ETIMEOUT = 4,      /* a device-side wait exceeded its bound (la_sync_check) */
+    LA_ENOMEM = 5         /* workspace allocation failed */
+} la_status;
+
+typedef enum { LA_F16 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum {
+    LA_KIND_LEAN = 0,         /* stream-K over a persistent grid, one launch */
+    LA_KIND_FIXED_SPLIT = 1,  /* each head cut into num_splits pieces + a combine launch */
+    LA_KIND_PER_HEAD = 2      /* one workgroup per (request, head), whole context */
+} la_kind;
+
+/*
+ * la_decode_bf16 / la_decode_f16: decode attention for bf16 or fp16 inputs,
+ * lean schedule, default tile size and grid. Arguments as described above;
+ * `stream` is a hipStream_t passed as void*.
+ */
+la_status la_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* ctx_lens, int B, int H, int d, float scale,
+                         float* out, void* stream);
+la_status la_decode_f16(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* ctx_lens, int B, int H, int d, float scale,
+                        float* out, void* stream);
+
+/* Same as above with the input dtype as a trailing argument (la_dtype). */
+la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* ctx_lens, int B, int H, int d, float scale,
+                    float* out, void* stream, int dtype);
+
+/*
+ * Options for la_decode_ex. Zero-initialise (or call la_opts_init) and set
+ * what you need.
+ *   kind        la_kind
+ *   tile_tokens LeanTile size in tokens; 0 = library default for d
+ *   grid        lean: workgroups in the persistent grid; 0 = co-resident
+ *               capacity (la_max_grid); larger than capacity -> LA_EINVAL
+ *   num_splits  fixed split: pieces per head; 0 = smallest power of two with
+ *               B*H*splits >= capacity, capped at 64
+ *   ordinary_launch  lean: 1 = launch without the cooperative guarantee
+ *               (grid still limited to capacity); 0 = cooperative launch
+ *   m_out, l_out     optional device [B*H] fp32: m (natural-log units, on
+ *               scaled logits) and l of every head
+ *   tile_owner  optional device int32 [I]: lean only; entry i receives the
+ *               workgroup that processed tile iteration i of the linearised
+ *               schedule (for checking the tables the kernel executed)
+ *   cta_timestamps optional device uint64 [grid*4]: lean only; per workgroup
+ *               start and end of the 100 MHz realtime clock, HW_ID and XCC_ID
+ *               registers
+ *   ev_start, ev_stop optional hipEvent_t: recorded on `stream` right before
+ *               the first and right after the last kernel of the call (the
+ *               schedule table copy is outside this pair)
+ */
+typedef struct la_opts {
+    int dtype;
+    int kind;
+    int tile_tokens;
+    int grid;
+    int num_splits;
+    int ordinary_launch;
+    float* m_out;
+    float* l_out;
+    int32_t* tile_owner;
+    uint64_t* cta_timestamps;
+    void* ev_start;
+    void* ev_stop;
+} la_opts;
+
+void la_opts_init(la_opts* opts);
+
+la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* ctx_lens, int B, int H, int d, float scale,
+                       float* out, void* stream, const la_opts* opts);
+
+/*
+ * la_schedule_dims: sizes of the stream-K tables for a batch, host only.
+ * Outputs: *iters = I = H * sum_b ceil(n_b / tile_tokens); *grid_used =
+ * min(grid, I); *max_rows = grid_used + B*H (an upper bound on segments).
+ * Returns LA_EUNSUPPORTED if I does not fit in int32.
+ */
+la_status la_schedule_dims(const int32_t* ctx_lens, int B, int H, int tile_tokens, int grid,
+                           int64_t* iters, int* grid_used, int* max_rows);
+
+/*
+ * la_schedule: the host-side stream-K scheduler (§3.4-§3.5), host only.
+ * Iterations are ordered request, then head, then tile; CTA c gets
+ * [c*q + min(c, r), (c+1)*q + min(c+1, r)) with q = I / G, r = I mod G.
+ * Outputs (caller-allocated host arrays):
+ *   cta_begin [G+1]   iteration bounds per CTA
+ *   cta_seg   [G+1]   segment-row bounds per CTA
+ *   seg       [max_rows * 6]  rows (cta, u = b*H + h, t0, t1, host, finishing)
+ *   host_cta, last_cta [B*H]  CTA holding each head's first and last tile
+ *   *n_seg            number of rows written
+ * `grid` is the requested G; the tables use min(grid, I) (la_schedule_dims).
+ */
+la_status la_schedule(const int32_t* ctx_lens, int B, int H, int tile_tokens, int grid,
+                      int32_t* cta_begin, int32_t* cta_seg, int32_t* seg, int max_rows,
+                      int* n_seg, int32_t* host_cta, int32_t* last_cta);
+
+/* Default LeanTile size (tokens) for head dim d; 0 if d is unsupported. */
+int la_default_tile(int d);
+
+/*
+ * Co-resident workgroup capacity of the lean kernel for (d, dtype) on the
+ * current device: occupancy per CU times the CU count. Returns <= 0 on error.
+ */
+int la_max_grid(int d, int dtype);
+
+/*
+ * Synchronises `stream` and reads the device error word of its workspace.
+ * LA_ETIMEOUT if a device-side wait exceeded its bound since the last check
+ * (the word and the flags are then reset); LA_EHIP if the stream reports an
+ * error; LA_OK otherwise.
+ */
+la_status la_sync_check(void* stream);
+
+/*
+ * Bound, in microseconds, on one device-side wait of a host workgroup for a
+ * peer's partial, for calls enqueued after this one (0 restores the default,
+ * 2 s). A wait that runs out -- or any wait after one has run out -- gives up
+ * and raises the error word reported by la_sync_check(); the output of that
+ * launch is then undefined. Small bounds force this path in tests.
+ */
+void la_set_wait_limit_us(uint32_t us);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* la_last_error(void);
+
+/* Frees every library-owned workspace after synchronising its stream. */
+void la_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_DECODE_H */

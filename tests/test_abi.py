@@ -1,0 +1,139 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every function
+include/la_decode.h declares, and its host-side scheduler produces the same
+tables as the schedule oracle, field for field. Argument validation is checked
+through calls that fail before any device work."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la_decode.h")
+
+la = pytest.importorskip("decode_phase_attention_amd")
+if not os.path.exists(la.binding.LIB_PATH):
+    pytest.skip("libla_decode.so not built", allow_module_level=True)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    h = ctypes.CDLL(la.binding.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+    # the binding wraps each of them under the same name
+    assert set(names) - {"la_opts_init"} <= set(la.binding.__all__)
+
+
+def compare_tables(lens, H, L, G):
+    want = oracle.lean_schedule(lens, H, L, G)
+    got = la.la_schedule(lens, H, L, G)
+    assert got["I"] == want["I"] and got["G"] == want["G"]
+    for key in ("cta_begin", "cta_seg", "host_cta", "last_cta"):
+        assert got[key].tolist() == want[key], key
+    assert [tuple(r) for r in got["seg"].tolist()] == want["seg"]
+
+
+def test_schedule_golden_cases():
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "schedule_cases.json")))["cases"]
+    for c in cases:
+        got = la.la_schedule(c["ctx_lens"], c["H"], c["L"], c["G_req"])
+        assert got["cta_begin"].tolist() == c["cta_begin"], c["name"]
+        assert got["seg"].tolist() == c["seg"], c["name"]
+        assert got["host_cta"].tolist() == c["host_cta"] and got["last_cta"].tolist() == c["last_cta"]
+
+
+def test_schedule_random_bit_exact():
+    rng = random.Random(2024)
+    for _ in range(3000):
+        B = rng.randint(1, 8)
+        H = rng.randint(1, 6)
+        L = rng.choice([1, 2, 5, 16, 64, 128, 256])
+        lens = [rng.randint(1, 3000) for _ in range(B)]
+        G = rng.randint(1, 1200)
+        compare_tables(lens, H, L, G)
+
+
+@pytest.mark.parametrize("name", ["tiny", "65k", "512k", "ragged", "many-heads"])
+@pytest.mark.parametrize("G", [1, 3, 255, 256, 1024, 1280, 2048])
+def test_schedule_bench_shapes(name, G):
+    w = W.CONFIGS[name]
+    for seed in ([0, 1, 2] if name == "ragged" else [0]):
+        lens = W.context_lengths(w, seed)
+        L = 128 if w.d == 128 else 256
+        compare_tables(lens, w.H, L, G)
+
+
+def test_default_tile():
+    assert la.la_default_tile(128) == 128
+    assert la.la_default_tile(64) == 256
+    assert la.la_default_tile(96) == 0
+
+
+def test_schedule_validation():
+    with pytest.raises(la.LaError) as e:
+        la.la_schedule([4, 0], 2, 4, 3)
+    assert e.value.status == 1 and "context" in str(e.value)
+    for args in (([4], 0, 4, 3), ([4], 1, 0, 3), ([4], 1, 4, 0)):
+        with pytest.raises(la.LaError) as e:
+            la.la_schedule(*args)
+        assert e.value.status == 1
+    with pytest.raises(la.LaError) as e:      # 2^31 tiles do not fit the int32 tables
+        la.la_schedule([2 ** 30, 2 ** 30], 2, 1, 64)
+    assert e.value.status == 2
+    # max_rows below the bound is rejected rather than overrun
+    lens = (ctypes.c_int32 * 2)(8, 8)
+    buf = (ctypes.c_int32 * 64)()
+    n = ctypes.c_int()
+    st = la.lib().la_schedule(lens, 2, 1, 4, 3, buf, buf, buf, 1, ctypes.byref(n), buf, buf)
+    assert st == 1
+
+
+def test_decode_validation_before_device_work():
+    """These calls fail in argument checking, before any HIP call."""
+    L = la.lib()
+    lens = (ctypes.c_int32 * 2)(16, 16)
+    fake = 1 << 20                       # aligned, never dereferenced
+    cases = [
+        (dict(q=None), 1),
+        (dict(B=0), 1),
+        (dict(H=0), 1),
+        (dict(d=96), 2),
+        (dict(scale=float("inf")), 1),
+        (dict(scale=float("nan")), 1),
+        (dict(k=fake + 8), 1),           # misaligned
+        (dict(dtype=7), 1),
+    ]
+    for over, want in cases:
+        a = dict(q=fake, k=fake, v=fake, B=2, H=4, d=128, scale=0.1, out=fake, dtype=1)
+        a.update(over)
+        st = L.la_decode(a["q"], a["k"], a["v"], lens, a["B"], a["H"], a["d"], a["scale"],
+                         a["out"], None, a["dtype"])
+        assert st == want, (over, st, la.la_last_error())
+    bad = (ctypes.c_int32 * 2)(16, 0)
+    assert L.la_decode(fake, fake, fake, bad, 2, 4, 128, 0.1, fake, None, 1) == 1
+    huge = (ctypes.c_int32 * 1)(1 << 24)        # one head's cache > 4 GiB at d = 128
+    assert L.la_decode(fake, fake, fake, huge, 1, 1, 128, 0.1, fake, None, 1) == 2
+    o = la.binding.LaOpts()
+    L.la_opts_init(ctypes.byref(o))
+    o.kind = 9
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    o.kind = 1
+    o.tile_owner = fake
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "lean" in la.la_last_error()

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max |O_gpu - O_ref| <= 1e-3 on the fp32 output; l within 1e-5 relative
+after rescaling to the oracle's max (l_gpu * exp(m_gpu - m_ref) vs l_ref) and
+|m_gpu - m_ref| <= 1e-5 * max(1, |m_ref|). The lean kernel's executed
+tile-to-workgroup map must equal the schedule oracle's bit for bit.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 1e-3
+L_RTOL = 1e-5
+M_RTOL = 1e-5
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def la():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_phase_attention_amd as la
+    la.lib()
+    return la
+
+
+def run(la, inp, kind="lean", **opts):
+    B, H, d = inp.B, inp.H, inp.d
+    dev = inp.q.device
+    out = torch.full((B, H, d), float("nan"), dtype=torch.float32, device=dev)
+    m = torch.full((B * H,), float("nan"), dtype=torch.float32, device=dev)
+    l = torch.full((B * H,), float("nan"), dtype=torch.float32, device=dev)
+    la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, B, H, d, inp.scale, out, kind=kind,
+                    m_out=m, l_out=l, **opts)
+    la.la_sync_check()
+    return out.cpu().numpy(), m.view(B, H).cpu().numpy(), l.view(B, H).cpu().numpy()
+
+
+def reference(inp, heads=None):
+    return oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), inp.ctx_lens,
+                              inp.scale, inp.dtype, heads=heads, workers=WORKERS)
+
+
+def sampled_reference(inp, heads):
+    """Oracle on a subset of heads, copying only those heads' rows to the host."""
+    B, H, d = inp.B, inp.H, inp.d
+    starts = np.concatenate([[0], np.cumsum(inp.ctx_lens)]) * H
+    qb = W.to_bits(inp.q)
+    O = np.full((B, H, d), np.nan)
+    M = np.full((B, H), np.nan)
+    L = np.full((B, H), np.nan)
+    for (b, h) in heads:
+        n = inp.ctx_lens[b]
+        r0 = int(starts[b]) + h * n
+        kb = W.to_bits(inp.k[r0:r0 + n])
+        vb = W.to_bits(inp.v[r0:r0 + n])
+        o, m, l = oracle.attend_fp64(qb[b:b + 1, h:h + 1], kb, vb, [n], inp.scale, inp.dtype,
+                                     workers=1)
+        O[b, h], M[b, h], L[b, h] = o[0, 0], m[0, 0], l[0, 0]
+    return O, M, L
+
+
+def check(got, ref, heads=None, tag=""):
+    O, m, l = got
+    Or, mr, lr = ref
+    if heads is not None:
+        idx = tuple(np.array(heads).T)
+        O, m, l, Or, mr, lr = O[idx], m[idx], l[idx], Or[idx], mr[idx], lr[idx]
+    assert np.isfinite(O).all(), tag
+    err = float(np.max(np.abs(O - Or)))
+    assert err <= O_TOL, f"{tag}: max |dO| = {err}"
+    assert np.all(np.abs(m - mr) <= M_RTOL * np.maximum(1.0, np.abs(mr))), f"{tag}: m"
+    lrel = np.abs(l * np.exp(m.astype(np.float64) - mr) - lr) / lr
+    assert float(np.max(lrel)) <= L_RTOL, f"{tag}: l rel err {float(np.max(lrel))}"
+    return err
+
+
+def tile_owner_ref(lens, H, L, G):
+    s = oracle.lean_schedule(lens, H, L, G)
+    own = np.empty(s["I"], np.int32)
+    for (c, u, t0, t1, _h, _f) in s["seg"]:
+        own[s["S"][u] + t0:s["S"][u] + t1] = c
+    return own, s["G"]
+
+
+# ------------------------------------------------------------------ small shapes
+
+KINDS = ["lean", "fixed_split", "per_head"]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_tiny_config(la, kind):
+    inp = W.make_inputs("tiny", seed=0, device="cuda")
+    say(f"[tiny/{kind}]")
+    check(run(la, inp, kind), reference(inp), tag=f"tiny/{kind}")
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 64), ("f16", 128), ("bf16", 128)])
+@pytest.mark.parametrize("kind", KINDS)
+def test_ragged_small(la, dtype, d, kind):
+    lens = [1, 7, 129, 1000, 4097, 300]
+    inp = W.make_custom(lens, H=3, d=d, dtype=dtype, seed=11, device="cuda")
+    say(f"[ragged-small {dtype} d={d} {kind}]")
+    ref = reference(inp)
+    check(run(la, inp, kind), ref, tag=f"{dtype}/{d}/{kind}")
+
+
+@pytest.mark.parametrize("grid", [1, 2, 3, 7, 255, 0])
+@pytest.mark.parametrize("tile", [0, 16, 100, 384])
+def test_lean_schedule_invariance(la, grid, tile):
+    """Any grid and LeanTile size gives the oracle's result, and the kernel
+    executes exactly the oracle's tile-to-workgroup map."""
+    lens = [33, 1, 700, 2048, 5]
+    H, d = 4, 128
+    inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=3, device="cuda")
+    L = tile if tile else la.la_default_tile(d)
+    G_req = grid if grid else la.la_max_grid(d, la.LA_BF16)
+    own_ref, G = tile_owner_ref(lens, H, L, G_req)
+    owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
+    say(f"[invariance grid={grid} tile={tile}]")
+    got = run(la, inp, "lean", grid=grid, tile_tokens=tile, tile_owner=owner)
+    check(got, reference(inp), tag=f"grid={grid} tile={tile}")
+    assert np.array_equal(owner.cpu().numpy(), own_ref)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 16, 64])
+def test_fixed_split_counts(la, splits):
+    lens = [3, 1000, 40000]
+    inp = W.make_custom(lens, H=2, d=64, dtype="f16", seed=5, device="cuda")
+    check(run(la, inp, "fixed_split", num_splits=splits), reference(inp), tag=f"splits={splits}")
+
+
+def test_ordinary_launch(la):
+    lens = [5000, 17, 60000]
+    inp = W.make_custom(lens, H=8, d=128, dtype="bf16", seed=9, device="cuda")
+    check(run(la, inp, "lean", ordinary_launch=True), reference(inp), tag="ordinary")
+
+
+def test_adversarial_scores(la):
+    """Scores spread over tens of units (q scaled up) in fp16 and bf16."""
+    for dtype in ("f16", "bf16"):
+        inp = W.make_custom([3000, 20000], H=4, d=128, dtype=dtype, seed=21, device="cuda",
+                            q_std=6.0)
+        got = run(la, inp, "lean", grid=37)
+        check(got, reference(inp), tag=f"adversarial/{dtype}")
+
+
+# ------------------------------------------------------------------ closed forms
+
+def _inputs_from(la, q, K, V, lens, H, d, dtype):
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    return W.Inputs(q=q.to(tdt).cuda().contiguous(), k=K.to(tdt).cuda().contiguous(),
+                    v=V.to(tdt).cuda().contiguous(), ctx_lens=lens, H=H, d=d, dtype=dtype,
+                    scale=1.0 / math.sqrt(d), seed=0)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_closed_forms(la, kind):
+    g = torch.Generator().manual_seed(1)
+    H, d = 2, 128
+    lens = [1, 5000]
+    N = sum(lens)
+    q = torch.randn((2, H, d), generator=g)
+    K = torch.randn((H * N, d), generator=g)
+    # constant V: the output is that constant
+    c = torch.randn(d, generator=g).to(torch.bfloat16).float()
+    inp = _inputs_from(la, q, K, c.expand(H * N, d), lens, H, d, "bf16")
+    O, m, l = run(la, inp, kind)
+    assert np.max(np.abs(O - c.numpy())) <= 1e-4
+    # one token: O = V_0 and l = 1 (request 0 has n = 1)
+    V = torch.randn((H * N, d), generator=g)
+    inp = _inputs_from(la, q, K, V, lens, H, d, "bf16")
+    O, m, l = run(la, inp, kind)
+    v0 = inp.v[:H].float().cpu().numpy()
+    assert np.max(np.abs(O[0] - v0)) <= 1e-6 and np.all(l[0] == 1.0)
+    # q = 0: m = 0, l = n, O = the mean of V
+    inp = _inputs_from(la, torch.zeros_like(q), K, V, lens, H, d, "bf16")
+    O, m, l = run(la, inp, kind)
+    Vb = inp.v.float().cpu().numpy()
+    mean = Vb[H:H + 5000].mean(axis=0)
+    assert np.max(np.abs(O[1, 0] - mean)) <= 1e-4
+    assert np.all(m == 0.0) and abs(l[1, 0] - 5000) <= 5000 * 1e-5
+    # a dominant logit: O = that V row
+    Kd = K.clone()
+    j = 4321
+    qn = q[1, 0].norm()
+    Kd[H + j] = (100.0 * math.sqrt(d) / qn) * (q[1, 0] / qn)    # s_j = 100, others ~ N(0, 1)
+    inp = _inputs_from(la, q, Kd, V, lens, H, d, "bf16")
+    O, m, l = run(la, inp, kind)
+    assert np.max(np.abs(O[1, 0] - inp.v[H + j].float().cpu().numpy())) <= 1e-4
+    assert 1.0 <= float(l[1, 0]) <= 1.0 + 1e-4
+
+
+def test_determinism(la):
+    inp = W.make_custom([777, 31000, 1], H=6, d=128, dtype="bf16", seed=8, device="cuda")
+    first = run(la, inp, "lean")
+    for _ in range(20):
+        again = run(la, inp, "lean")
+        for a, b in zip(first, again):
+            assert np.array_equal(a, b, equal_nan=True)
+
+
+def test_timeout_path_recovers(la):
+    """A 1 us wait bound makes hosts give up waiting (forced from the host);
+    the launch still ends, la_sync_check reports or not, and after the reset
+    the next call is exact again."""
+    inp = W.make_custom([30000, 30000], H=2, d=128, dtype="bf16", seed=2, device="cuda")
+    try:
+        la.la_set_wait_limit_us(1)
+        for _ in range(3):
+            out = torch.empty((2, 2, 128), dtype=torch.float32, device="cuda")
+            la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, 2, 2, 128, inp.scale, out)
+            try:
+                la.la_sync_check()
+            except la.LaError as e:
+                assert e.status == 4
+    finally:
+        la.la_set_wait_limit_us(0)
+    check(run(la, inp, "lean"), reference(inp), tag="after-timeout")
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_heads(B, H, k, seed):
+    rng = np.random.default_rng(seed)
+    allh = [(b, h) for b in range(B) for h in range(H)]
+    pick = {allh[0], allh[-1]}
+    for i in rng.choice(len(allh), size=min(k, len(allh)), replace=False):
+        pick.add(allh[int(i)])
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name,nheads", [("65k", 32), ("512k", 32), ("ragged", 64),
+                                         ("many-heads", 64)])
+def test_full_size(la, name, nheads):
+    say(f"[full {name}] generating")
+    inp = W.make_inputs(name, seed=0, device="cuda")
+    w = inp.meta["workload"]
+    heads = _sample_heads(inp.B, inp.H, nheads, seed=1)
+    say(f"[full {name}] lens={inp.ctx_lens[:4]}... heads checked={len(heads)}")
+    res = {}
+    for kind in KINDS:
+        res[kind] = run(la, inp, kind)
+        say(f"[full {name}] {kind} done")
+    ref = sampled_reference(inp, heads)
+    say(f"[full {name}] oracle done")
+    for kind in KINDS:
+        err = check(res[kind], ref, heads=heads, tag=f"{name}/{kind}")
+        say(f"[full {name}] {kind} max|dO|={err:.2e}")
+    # the lean kernel executed the oracle's tile map
+    L = la.la_default_tile(w.d)
+    G_req = la.la_max_grid(w.d, la.LA_BF16 if w.dtype == "bf16" else la.LA_F16)
+    own_ref, G = tile_owner_ref(inp.ctx_lens, inp.H, L, G_req)
+    owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
+    run(la, inp, "lean", tile_owner=owner)
+    assert np.array_equal(owner.cpu().numpy(), own_ref)
+    del inp
+    torch.cuda.empty_cache()
