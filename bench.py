@@ -188,7 +188,7 @@ def main():
     w = inp.meta["workload"]
     torch.cuda.synchronize()
     dt_code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
-    G = la.la_max_grid(w.d, dt_code)
+    G = la.la_default_grid(w.d, dt_code)
     L = la.la_default_tile(w.d)
     I, Gu, _ = la.la_schedule_dims(inp.ctx_lens, inp.H, L, G)
     alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d)

@@ -19,7 +19,8 @@ import numpy as np
 __all__ = [
     "LaError", "LA_F16", "LA_BF16", "LA_KIND_LEAN", "LA_KIND_FIXED_SPLIT", "LA_KIND_PER_HEAD",
     "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex", "la_schedule",
-    "la_schedule_dims", "la_default_tile", "la_max_grid", "la_sync_check", "la_last_error",
+    "la_schedule_dims", "la_default_tile", "la_max_grid", "la_default_grid", "la_sync_check",
+    "la_last_error",
     "la_shutdown", "la_set_wait_limit_us", "decode_attention", "LIB_PATH",
 ]
 
@@ -46,7 +47,7 @@ class LaOpts(ctypes.Structure):
         ("tile_tokens", ctypes.c_int),
         ("grid", ctypes.c_int),
         ("num_splits", ctypes.c_int),
-        ("ordinary_launch", ctypes.c_int),
+        ("cooperative", ctypes.c_int),
         ("m_out", ctypes.c_void_p),
         ("l_out", ctypes.c_void_p),
         ("tile_owner", ctypes.c_void_p),
@@ -75,6 +76,7 @@ _SIG = {
                          _I32P, _I32P]),
     "la_default_tile": (_I, [_I]),
     "la_max_grid": (_I, [_I, _I]),
+    "la_default_grid": (_I, [_I, _I]),
     "la_sync_check": (_I, [_P]),
     "la_last_error": (ctypes.c_char_p, []),
     "la_shutdown": (None, []),
@@ -176,7 +178,7 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
 
 
 def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
-                 kind="lean", tile_tokens=0, grid=0, num_splits=0, ordinary_launch=False,
+                 kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
                  ev_stop=None):
     o = LaOpts()
@@ -186,7 +188,7 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
     o.tile_tokens = int(tile_tokens)
     o.grid = int(grid)
     o.num_splits = int(num_splits)
-    o.ordinary_launch = int(bool(ordinary_launch))
+    o.cooperative = int(bool(cooperative))
     o.m_out = _ptr(m_out)
     o.l_out = _ptr(l_out)
     o.tile_owner = _ptr(tile_owner)
@@ -233,6 +235,13 @@ def la_default_tile(d: int) -> int:
 
 def la_max_grid(d: int, dtype: int) -> int:
     g = int(lib().la_max_grid(int(d), int(dtype)))
+    if g <= 0:
+        raise LaError(LA_EHIP, la_last_error())
+    return g
+
+
+def la_default_grid(d: int, dtype: int) -> int:
+    g = int(lib().la_default_grid(int(d), int(dtype)))
     if g <= 0:
         raise LaError(LA_EHIP, la_last_error())
     return g

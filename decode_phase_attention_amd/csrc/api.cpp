@@ -16,7 +16,7 @@
 #include <utility>
 #include <vector>
 
-#include "../../include/la_decode.h"
+#include "la_decode.h"
 #include "kernels.h"
 #include "sched.h"
 
@@ -66,7 +66,17 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
-std::map<std::pair<int, const void*>, int> g_capacity;
+struct Capacity {
+    int coresident;   // occupancy per CU x CUs: the largest grid a launch may use
+    int preferred;    // default grid: kWgPerCu workgroups on every CU
+};
+std::map<std::pair<int, const void*>, Capacity> g_capacity;
+
+// One lean workgroup per CU by default. Each workgroup already keeps
+// 2*kRows 16-byte loads per lane in flight; more workgroups per CU add
+// concurrent sequential streams without adding bandwidth (measured on MI355X:
+// 1 per CU streams fastest on the long-context and ragged workloads).
+constexpr int kWgPerCu = 1;
 uint32_t g_wait_us = kDefaultWaitUs;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -120,7 +130,7 @@ la_status get_workspace(hipStream_t stream, Workspace** out) {
     return LA_OK;
 }
 
-la_status capacity(int dtype, int d, int* out) {
+la_status capacity(int dtype, int d, Capacity* out) {
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
     const void* fn = la::lean_kernel_ptr(dtype, d);
@@ -134,8 +144,11 @@ la_status capacity(int dtype, int d, int* out) {
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, la::kThreads, 0));
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     if (per_cu < 1 || cus < 1) return fail(LA_EHIP, "lean kernel does not fit on this device");
-    g_capacity[key] = per_cu * cus;
-    *out = per_cu * cus;
+    Capacity c;
+    c.coresident = per_cu * cus;
+    c.preferred = (per_cu < kWgPerCu ? per_cu : kWgPerCu) * cus;
+    g_capacity[key] = c;
+    *out = c;
     return LA_OK;
 }
 
@@ -217,17 +230,18 @@ la_status upload(Workspace& w, Staging* s, size_t bytes) {
 la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
                    const int32_t* ctx_lens, int B, int H, int d, float scale, float* out,
                    const la_opts& o) {
-    int cap = 0;
+    Capacity cap;
     la_status st = capacity(o.dtype, d, &cap);
     if (st != LA_OK) return st;
-    if (o.grid < 0 || o.grid > cap)
-        return fail(LA_EINVAL, "grid %d outside [1, %d] (co-resident capacity)", o.grid, cap);
+    if (o.grid < 0 || o.grid > cap.coresident)
+        return fail(LA_EINVAL, "grid %d outside [1, %d] (co-resident capacity)", o.grid,
+                    cap.coresident);
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
     int64_t I = 0;
     int G = 0, max_rows = 0;
     const char* why = "";
-    const int rc = la::schedule_dims(ctx_lens, B, H, L, o.grid > 0 ? o.grid : cap, &I, &G,
-                                     &max_rows, &why);
+    const int rc = la::schedule_dims(ctx_lens, B, H, L, o.grid > 0 ? o.grid : cap.preferred, &I,
+                                     &G, &max_rows, &why);
     if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
 
     // table layout in one buffer
@@ -278,7 +292,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     a.sl2e = scale * 1.4426950408889634f;
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
-    HIP_TRY(la::launch_lean(o.dtype, d, a, G, w.stream, o.ordinary_launch == 0));
+    HIP_TRY(la::launch_lean(o.dtype, d, a, G, w.stream, o.cooperative != 0));
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
     return LA_OK;
 }
@@ -293,11 +307,11 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
         if (o.num_splits < 0) return fail(LA_EINVAL, "num_splits must be >= 0");
         splits = o.num_splits;
         if (splits == 0) {
-            int cap = 0;
+            Capacity cap;
             la_status st = capacity(o.dtype, d, &cap);
             if (st != LA_OK) return st;
             splits = 1;
-            while ((int64_t)BH * splits < cap && splits < 64) splits *= 2;
+            while ((int64_t)BH * splits < cap.coresident && splits < 64) splits *= 2;
         }
         if ((int64_t)BH * splits > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "too many splits");
     }
@@ -442,9 +456,20 @@ int la_max_grid(int d, int dtype) {
         return -1;
     }
     std::lock_guard<std::mutex> lock(g_mu);
-    int cap = 0;
+    Capacity cap;
     if (capacity(dtype, d, &cap) != LA_OK) return -1;
-    return cap;
+    return cap.coresident;
+}
+
+int la_default_grid(int d, int dtype) {
+    if ((d != 64 && d != 128) || (dtype != LA_F16 && dtype != LA_BF16)) {
+        fail(LA_EINVAL, "unsupported d/dtype");
+        return -1;
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    Capacity cap;
+    if (capacity(dtype, d, &cap) != LA_OK) return -1;
+    return cap.preferred;
 }
 
 la_status la_sync_check(void* stream) {

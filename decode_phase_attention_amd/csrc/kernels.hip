@@ -21,6 +21,12 @@
 // groups meet in LDS, where the reduction f (§3.2) folds them into one
 // (m, l, Obar[d]).
 //
+// Epilogues run in wave 0 only. In the lean kernel a peer (a workgroup that
+// holds a head's tiles but not its first one) publishes its (Obar, m, l)
+// record and raises a flag; the head's host polls all its peers' flags at
+// once and folds their records in ascending workgroup order (§3.5). The other
+// waves meanwhile go on to the workgroup's next segment.
+//
 // Exponentials are taken base 2 with log2(e) folded into the scale; m is kept
 // in log2 units inside the kernels and converted back to natural-log units
 // for m_out.
@@ -88,6 +94,14 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load with the non-temporal hint: K and V are streamed exactly once,
+// so they should not displace other lines in the caches.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const char* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 struct Acc {
     float m;      // running max, log2 units
     float l;      // running sum of 2^(s - m)
@@ -127,24 +141,26 @@ __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const c
     if constexpr (!TAIL) {
         const uint32_t off = (uint32_t)base * kRowBytes + lane_off;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
-            kr[r] = *reinterpret_cast<const uint4*>(kh + (uint64_t)(off + r * kStepRowBytes));
+        for (int r = 0; r < kRows; ++r) kr[r] = load_nt(kh + (uint64_t)(off + r * kStepRowBytes));
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
-            vr[r] = *reinterpret_cast<const uint4*>(vh + (uint64_t)(off + r * kStepRowBytes));
+        for (int r = 0; r < kRows; ++r) vr[r] = load_nt(vh + (uint64_t)(off + r * kStepRowBytes));
     } else {
         const uint32_t col_off = lane_off - (uint32_t)grp * kRowBytes;
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
-            kr[r] = *reinterpret_cast<const uint4*>(kh + (uint64_t)(j * kRowBytes + col_off));
+            kr[r] = load_nt(kh + (uint64_t)(j * kRowBytes + col_off));
         }
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
-            vr[r] = *reinterpret_cast<const uint4*>(vh + (uint64_t)(j * kRowBytes + col_off));
+            vr[r] = load_nt(vh + (uint64_t)(j * kRowBytes + col_off));
         }
     }
+    // Keep all 2*kRows loads of the step in flight before any of them is
+    // consumed; without this the scheduler interleaves loads with the math
+    // and fewer bytes are outstanding per wave.
+    __builtin_amdgcn_sched_barrier(0);
     float s[kRows];
     float mx = kNegInf;
     {
@@ -203,11 +219,17 @@ struct alignas(16) Smem {
     float l[Geo<D>::NG];
 };
 
-// Fold the lane groups of the workgroup with f. Threads t < D receive
-// (m, l, Obar[t]) of everything the workgroup streamed for this range.
+// Dims of the output each lane of wave 0 holds after a fold: lane i holds
+// dims i, i + 64, ... (coalesced 256-byte rows per k).
+template <int D>
+constexpr int kDpl = D / 64;
+
+// Fold the lane groups of the workgroup with f. Wave 0 receives
+// (m, l, Obar[lane + 64k]) of everything the workgroup streamed for this
+// range; the other waves return at once after the second barrier.
 template <int D>
 __device__ __forceinline__ void wg_fold(Smem<D>& sm, const Acc& a, int grp, int sub, float& M,
-                                        float& Ls, float& O) {
+                                        float& Ls, float (&O)[kDpl<D>]) {
     using G = Geo<D>;
     float4* dst = reinterpret_cast<float4*>(&sm.o[grp][sub * 8]);
     dst[0] = make_float4(a.o[0], a.o[1], a.o[2], a.o[3]);
@@ -218,54 +240,78 @@ __device__ __forceinline__ void wg_fold(Smem<D>& sm, const Acc& a, int grp, int 
     }
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < D) {
+    if (t < 64) {
         float mx = kNegInf;
 #pragma unroll
         for (int g = 0; g < G::NG; ++g) mx = fmaxf(mx, sm.m[g]);
         const float mu = (mx == kNegInf) ? 0.f : mx;
-        float ls = 0.f, o = 0.f;
+        float ls = 0.f, o[kDpl<D>];
+#pragma unroll
+        for (int k = 0; k < kDpl<D>; ++k) o[k] = 0.f;
 #pragma unroll 8
         for (int g = 0; g < G::NG; ++g) {
             const float w = fexp2(sm.m[g] - mu);
             ls = fmaf(w, sm.l[g], ls);
-            o = fmaf(w, sm.o[g][t], o);
+#pragma unroll
+            for (int k = 0; k < kDpl<D>; ++k) o[k] = fmaf(w, sm.o[g][t + 64 * k], o[k]);
         }
         M = mx;
         Ls = ls;
-        O = o;
+#pragma unroll
+        for (int k = 0; k < kDpl<D>; ++k) O[k] = o[k];
     }
     __syncthreads();
 }
 
-// f applied to a running (M, Ls, O) and one more (pm, pl, po).
-__device__ __forceinline__ void merge_into(float& M, float& Ls, float& O, float pm, float pl,
-                                           float po) {
+// f applied to a running (M, Ls, O) and one more record (pm, pl, po).
+template <int N>
+__device__ __forceinline__ void merge_into(float& M, float& Ls, float (&O)[N], float pm, float pl,
+                                           const float (&po)[N]) {
     const float mn = fmaxf(M, pm);
     const float mu = (mn == kNegInf) ? 0.f : mn;
     const float a = fexp2(M - mu), b = fexp2(pm - mu);
     Ls = a * Ls + b * pl;
-    O = a * O + b * po;
+#pragma unroll
+    for (int k = 0; k < N; ++k) O[k] = a * O[k] + b * po[k];
     M = mn;
 }
 
-// Wait until another workgroup has published its partial. Polls with
-// relaxed agent-scope loads, then one acquire fence so the partial's data is
-// read after the flag. A wait gives up after `limit` ticks of the 100 MHz
-// realtime clock, or at once when any wait has already given up, and raises
-// the error word: a missing peer cannot hang the launch.
+// Cross-workgroup exchange. Peers and hosts run on different XCDs, whose L2
+// caches are not coherent with each other. Instead of release/acquire fences
+// (which write back / invalidate a whole L2 and stall every other workgroup
+// on that XCD), every access to the exchange buffers is an agent-scope atomic
+// (stores write through to the device coherence point, loads bypass stale
+// lines), and ordering comes from completion: a peer waits until its data
+// stores have completed (s_waitcnt vmcnt(0)) before it stores its flag, and a
+// host loads a peer's data only after it has observed the flag.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_flag(uint32_t* f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void drain_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);   // every memory operation of this wave has completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until a peer's flag is raised. Gives up after `limit` ticks of the
+// 100 MHz realtime clock, or at once when any wait has already given up, and
+// raises the error word: a missing peer cannot hang the launch.
 __device__ __forceinline__ void wait_flag(uint32_t* f, uint64_t limit, uint32_t* err) {
-    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
-            if (__builtin_amdgcn_s_memrealtime() - t0 > limit ||
-                __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                atomicOr(err, 1u);
-                break;
-            }
+    if (load_flag(f) != 0u) return;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (load_flag(f) == 0u) {
+        __builtin_amdgcn_s_sleep(2);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > limit || load_flag(err) != 0u) {
+            atomicOr(err, 1u);
+            return;
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 __device__ __forceinline__ uint4 load_q(const uint16_t* q, int u, int D, int sub) {
@@ -279,11 +325,25 @@ __device__ __forceinline__ uint64_t hwreg_ids() {
     return ((uint64_t)xcc << 32) | hw;
 }
 
+// Wave 0 writes out = Obar / l (and m in natural-log units, l) for head u.
+template <int D>
+__device__ __forceinline__ void write_out(float* out, float* m_out, float* l_out, int u, int lane,
+                                          float M, float Ls, const float (&O)[kDpl<D>]) {
+    const float inv = 1.f / Ls;
+#pragma unroll
+    for (int k = 0; k < kDpl<D>; ++k) out[(int64_t)u * D + lane + 64 * k] = O[k] * inv;
+    if (lane == 0) {
+        if (m_out != nullptr) m_out[u] = M * kLn2;
+        if (l_out != nullptr) l_out[u] = Ls;
+    }
+}
+
 // ------------------------------------------------------------------ lean
 
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     using G = Geo<D>;
+    constexpr int P = kDpl<D>;
     __shared__ Smem<D> sm;
     const int c = blockIdx.x;
     const int t = threadIdx.x;
@@ -303,54 +363,61 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         const int h = u - b * a.H;
         const int n = a.ctx[b];
         const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
-        const uint16_t* kh = a.k + row0 * D;
-        const uint16_t* vh = a.v + row0 * D;
         const int tok0 = sg.y * a.L;
         const int tok1 = (int)min((int64_t)sg.z * a.L, (int64_t)n);
         Acc acc;
         acc_init(acc);
-        stream_range<DT, D>(kh, vh, tok0, tok1, load_q(a.q, u, D, sub), a.sl2e, grp, sub, acc);
+        stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, load_q(a.q, u, D, sub),
+                            a.sl2e, grp, sub, acc);
         if (a.tile_owner != nullptr && t == 0)
             for (int i = sg.y; i < sg.z; ++i) a.tile_owner[iter + i - sg.y] = c;
         iter += sg.z - sg.y;
 
-        float M = kNegInf, Ls = 0.f, O = 0.f;
+        float M = kNegInf, Ls = 0.f, O[P];
         wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
-        const bool host = sg.w & 1;
-        const bool fin = sg.w & 2;
-        if (!host) {
+        if (t >= 64) continue;   // the epilogue is wave 0's; the others go on streaming
+
+        if (!(sg.w & 1)) {
             // a peer: publish (Obar, m, l) for the head's host, then raise the flag
             float* p = a.part + (int64_t)c * part_stride(D);
-            if (t < D) p[t] = O;
-            if (t == 0) {
-                p[D] = M;
-                p[D + 1] = Ls;
+#pragma unroll
+            for (int k = 0; k < P; ++k) store_agent(p + lane + 64 * k, O[k]);
+            if (lane == 0) {
+                store_agent(p + D, M);
+                store_agent(p + D + 1, Ls);
             }
-            __threadfence();
-            __syncthreads();
-            if (t == 0) __hip_atomic_store(&a.flags[c], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            drain_stores();
+            if (lane == 0) __hip_atomic_store(&a.flags[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
         }
-        if (!fin) {
-            // the host: fold the peers' partials in ascending workgroup order
+        if (!(sg.w & 2)) {
+            // The host. Its peers (c, last] each publish one partial: wait for
+            // all of them at once (one flag per lane), then fold them in
+            // ascending workgroup order with their loads issued in batches.
             const int last = a.last_cta[u];
-            if (t < D) {
-                for (int pc = c + 1; pc <= last; ++pc) {
-                    wait_flag(&a.flags[pc], a.wait_ticks, a.err);
-                    const float* p = a.part + (int64_t)pc * part_stride(D);
-                    merge_into(M, Ls, O, p[D], p[D + 1], p[t]);
+            const int np = last - c;
+            for (int i = lane; i < np; i += 64) wait_flag(&a.flags[c + 1 + i], a.wait_ticks, a.err);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            constexpr int kBatch = 8;
+            for (int p0 = c + 1; p0 <= last; p0 += kBatch) {
+                float pm[kBatch], pl[kBatch], po[kBatch][P];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const float* p = a.part + (int64_t)min(p0 + j, last) * part_stride(D);
+                    pm[j] = load_agent(p + D);
+                    pl[j] = load_agent(p + D + 1);
+#pragma unroll
+                    for (int k = 0; k < P; ++k) po[j][k] = load_agent(p + lane + 64 * k);
                 }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (p0 + j <= last) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
             }
-            __syncthreads();
-            if (t == 0)
-                for (int pc = c + 1; pc <= last; ++pc)
-                    __hip_atomic_store(&a.flags[pc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // consumed: lower the flags for the next launch
+            for (int i = lane; i < np; i += 64)
+                __hip_atomic_store(&a.flags[c + 1 + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (t < D) a.out[(int64_t)u * D + t] = O / Ls;
-        if (t == 0) {
-            if (a.m_out != nullptr) a.m_out[u] = M * kLn2;
-            if (a.l_out != nullptr) a.l_out[u] = Ls;
-        }
+        write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
     }
     if (a.ts != nullptr && t == 0) a.ts[c * 4 + 1] = __builtin_amdgcn_s_memrealtime();
 }
@@ -360,6 +427,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     using G = Geo<D>;
+    constexpr int P = kDpl<D>;
     __shared__ Smem<D> sm;
     const int u = blockIdx.x / a.splits;
     const int k = blockIdx.x - u * a.splits;
@@ -380,30 +448,35 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     if (tok0 < tok1)
         stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, load_q(a.q, u, D, sub),
                             a.sl2e, grp, sub, acc);
-    float M = kNegInf, Ls = 0.f, O = 0.f;
+    float M = kNegInf, Ls = 0.f, O[P];
     wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+    if (t >= 64) return;
     float* p = a.part + (int64_t)blockIdx.x * part_stride(D);
-    if (t < D) p[t] = O;
-    if (t == 0) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) p[lane + 64 * j] = O[j];
+    if (lane == 0) {
         p[D] = M;
         p[D + 1] = Ls;
     }
 }
 
+// One wave per head: folds the head's `splits` partial records in order.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(const CombineArgs a) {
+__global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
+    constexpr int P = kDpl<D>;
     const int u = blockIdx.x;
-    const int t = threadIdx.x;
-    float M = kNegInf, Ls = 0.f, O = 0.f;
+    const int lane = threadIdx.x;
+    float M = kNegInf, Ls = 0.f, O[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) O[j] = 0.f;
     for (int k = 0; k < a.splits; ++k) {
         const float* p = a.part + ((int64_t)u * a.splits + k) * part_stride(D);
-        merge_into(M, Ls, O, p[D], p[D + 1], p[t]);
+        float po[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) po[j] = p[lane + 64 * j];
+        merge_into<P>(M, Ls, O, p[D], p[D + 1], po);
     }
-    a.out[(int64_t)u * D + t] = O / Ls;
-    if (t == 0) {
-        if (a.m_out != nullptr) a.m_out[u] = M * kLn2;
-        if (a.l_out != nullptr) a.l_out[u] = Ls;
-    }
+    write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
 }
 
 // ------------------------------------------------------------------ per head
@@ -425,13 +498,9 @@ __global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
     acc_init(acc);
     stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, 0, n, load_q(a.q, u, D, sub), a.sl2e,
                         grp, sub, acc);
-    float M = kNegInf, Ls = 0.f, O = 0.f;
+    float M = kNegInf, Ls = 0.f, O[kDpl<D>];
     wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
-    if (t < D) a.out[(int64_t)u * D + t] = O / Ls;
-    if (t == 0) {
-        if (a.m_out != nullptr) a.m_out[u] = M * kLn2;
-        if (a.l_out != nullptr) a.l_out[u] = Ls;
-    }
+    if (t < 64) write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
 }
 
 template <typename F>
@@ -466,7 +535,7 @@ hipError_t launch_split(int dtype, int d, const SplitArgs& a, int blocks, hipStr
 hipError_t launch_combine(int d, const CombineArgs& a, int heads, hipStream_t s) {
     const void* fn = d == 64 ? (const void*)&combine_kernel<64> : (const void*)&combine_kernel<128>;
     void* args[] = {const_cast<CombineArgs*>(&a)};
-    return hipLaunchKernel(fn, dim3(heads), dim3(d), args, 0, s);
+    return hipLaunchKernel(fn, dim3(heads), dim3(64), args, 0, s);
 }
 
 hipError_t launch_per_head(int dtype, int d, const SplitArgs& a, int heads, hipStream_t s) {

@@ -97,12 +97,15 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  * what you need.
  *   kind        la_kind
  *   tile_tokens LeanTile size in tokens; 0 = library default for d
- *   grid        lean: workgroups in the persistent grid; 0 = co-resident
- *               capacity (la_max_grid); larger than capacity -> LA_EINVAL
+ *   grid        lean: workgroups in the persistent grid; 0 = la_default_grid
+ *               (one per CU); larger than la_max_grid -> LA_EINVAL
  *   num_splits  fixed split: pieces per head; 0 = smallest power of two with
  *               B*H*splits >= capacity, capped at 64
- *   ordinary_launch  lean: 1 = launch without the cooperative guarantee
- *               (grid still limited to capacity); 0 = cooperative launch
+ *   cooperative lean: 1 = hipLaunchCooperativeKernel, which refuses a grid
+ *               that cannot be co-resident; 0 = ordinary launch. Both cap the
+ *               grid at la_max_grid, so every workgroup a host waits for can be
+ *               resident; the cooperative form also guarantees it while other
+ *               work shares the device, at the cost of a slower launch.
  *   m_out, l_out     optional device [B*H] fp32: m (natural-log units, on
  *               scaled logits) and l of every head
  *   tile_owner  optional device int32 [I]: lean only; entry i receives the
@@ -121,7 +124,7 @@ typedef struct la_opts {
     int tile_tokens;
     int grid;
     int num_splits;
-    int ordinary_launch;
+    int cooperative;
     float* m_out;
     float* l_out;
     int32_t* tile_owner;
@@ -169,6 +172,12 @@ int la_default_tile(int d);
  * current device: occupancy per CU times the CU count. Returns <= 0 on error.
  */
 int la_max_grid(int d, int dtype);
+
+/*
+ * Grid the lean kind uses when la_opts.grid is 0: one workgroup per CU on the
+ * current device (never more than la_max_grid). Returns <= 0 on error.
+ */
+int la_default_grid(int d, int dtype);
 
 /*
  * Synchronises `stream` and reads the device error word of its workspace.

@@ -120,16 +120,19 @@ def test_ragged_small(la, dtype, d, kind):
     check(run(la, inp, kind), ref, tag=f"{dtype}/{d}/{kind}")
 
 
-@pytest.mark.parametrize("grid", [1, 2, 3, 7, 255, 0])
+@pytest.mark.parametrize("grid", [1, 2, 3, 7, 255, 0, -1])
 @pytest.mark.parametrize("tile", [0, 16, 100, 384])
 def test_lean_schedule_invariance(la, grid, tile):
-    """Any grid and LeanTile size gives the oracle's result, and the kernel
-    executes exactly the oracle's tile-to-workgroup map."""
+    """Any grid (0: the default, -1: the co-resident maximum) and LeanTile size
+    gives the oracle's result, and the kernel executes exactly the oracle's
+    tile-to-workgroup map."""
     lens = [33, 1, 700, 2048, 5]
     H, d = 4, 128
     inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=3, device="cuda")
     L = tile if tile else la.la_default_tile(d)
-    G_req = grid if grid else la.la_max_grid(d, la.LA_BF16)
+    if grid == -1:
+        grid = la.la_max_grid(d, la.LA_BF16)
+    G_req = grid if grid else la.la_default_grid(d, la.LA_BF16)
     own_ref, G = tile_owner_ref(lens, H, L, G_req)
     owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
     say(f"[invariance grid={grid} tile={tile}]")
@@ -145,10 +148,12 @@ def test_fixed_split_counts(la, splits):
     check(run(la, inp, "fixed_split", num_splits=splits), reference(inp), tag=f"splits={splits}")
 
 
-def test_ordinary_launch(la):
+@pytest.mark.parametrize("grid", [0, -1])
+def test_cooperative_launch(la, grid):
     lens = [5000, 17, 60000]
     inp = W.make_custom(lens, H=8, d=128, dtype="bf16", seed=9, device="cuda")
-    check(run(la, inp, "lean", ordinary_launch=True), reference(inp), tag="ordinary")
+    g = la.la_max_grid(128, la.LA_BF16) if grid == -1 else 0
+    check(run(la, inp, "lean", cooperative=True, grid=g), reference(inp), tag="cooperative")
 
 
 def test_adversarial_scores(la):
@@ -264,7 +269,7 @@ def test_full_size(la, name, nheads):
         say(f"[full {name}] {kind} max|dO|={err:.2e}")
     # the lean kernel executed the oracle's tile map
     L = la.la_default_tile(w.d)
-    G_req = la.la_max_grid(w.d, la.LA_BF16 if w.dtype == "bf16" else la.LA_F16)
+    G_req = la.la_default_grid(w.d, la.LA_BF16 if w.dtype == "bf16" else la.LA_F16)
     own_ref, G = tile_owner_ref(inp.ctx_lens, inp.H, L, G_req)
     owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
     run(la, inp, "lean", tile_owner=owner)

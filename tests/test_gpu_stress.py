@@ -1,0 +1,76 @@
+"""Stress of the in-launch exchange between workgroups (GPU).
+
+Many launches with grids drawn at random -- up to the co-resident maximum, so
+a head can have hundreds of peers whose partials its host must see -- each
+checked against the fp64 oracle computed once per input. A missing or stale
+partial (an ordering bug in the flag/data protocol) shows up as a wrong
+output or a raised error word.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def la():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_phase_attention_amd as la
+    la.lib()
+    return la
+
+
+CASES = [
+    ("bf16", 128, [300000, 3, 50000], 2),
+    ("f16", 64, [1, 90000, 777, 4096, 120000], 3),
+]
+
+
+@pytest.mark.parametrize("dtype,d,lens,H", CASES)
+def test_random_grids(la, dtype, d, lens, H):
+    inp = W.make_custom(lens, H=H, d=d, dtype=dtype, seed=17, device="cuda")
+    ref, _, _ = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                                   inp.scale, dtype, workers=8)
+    dt = la.LA_BF16 if dtype == "bf16" else la.LA_F16
+    cap = la.la_max_grid(d, dt)
+    rng = np.random.default_rng(5)
+    grids = [cap, cap - 1, 1, 2] + [int(g) for g in rng.integers(1, cap + 1, size=146)]
+    tiles = [0, 0, 64, 512] + [int(x) for x in rng.choice([0, 32, 128, 200, 1024], size=146)]
+    out = torch.empty((len(lens), H, d), dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for i, (g, tl) in enumerate(zip(grids, tiles)):
+        out.fill_(float("nan"))
+        la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out, grid=g,
+                        tile_tokens=tl, cooperative=(i % 7 == 0))
+        la.la_sync_check()
+        err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+        assert err <= 1e-3, (i, g, tl, err)
+        worst = max(worst, err)
+    print(f"{dtype} d={d}: {len(grids)} launches, worst max|dO| = {worst:.2e}", file=sys.stderr)
+
+
+def test_back_to_back_without_sync(la):
+    """Launches queued back to back on one stream reuse the flags; each must
+    see only its own peers' partials."""
+    lens = [200000, 1000]
+    H, d = 4, 128
+    inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=23, device="cuda")
+    ref, _, _ = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                                   inp.scale, "bf16", workers=8)
+    cap = la.la_max_grid(d, la.LA_BF16)
+    outs = [torch.empty((2, H, d), dtype=torch.float32, device="cuda") for _ in range(64)]
+    for i, o in enumerate(outs):
+        la.la_decode_ex(inp.q, inp.k, inp.v, lens, 2, H, d, inp.scale, o,
+                        grid=[cap, 256, 1000, 37][i % 4])
+    la.la_sync_check()
+    for o in outs:
+        assert float(np.max(np.abs(o.cpu().numpy() - ref))) <= 1e-3
