@@ -30,6 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_phase_attention_amd", "csrc", f)
+                  for f in ("kernels.hip", "kernels.h")]
 METRIC = "decode-attention µs/step + achieved HBM TB/s vs 8 TB/s peak (512k, ragged)"
 
 
@@ -97,6 +100,46 @@ def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
         "kernel_us_p50": kern[len(kern) // 2],
         "kernel_us_p90": kern[(9 * len(kern)) // 10],
     }
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per lean launch from the committed counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"lean_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters (FETCH_SIZE should read nbytes, WRITE_SIZE nbytes)."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes")
 
 
 def cpu_baseline(inp, budget_s=12.0):
@@ -169,6 +212,8 @@ def main():
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only the lean kernel on the workload (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (scales the HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -198,6 +243,9 @@ def main():
     lean = time_kind(la, torch, evs, inp, "lean", args.steps, args.warmup)
     achieved = alg_bytes / (lean["kernel_us_mean"] * 1e-6) / 1e9
     log(f"[bench] lean: {lean}")
+
+    if args.copy_calibration:
+        copy_calibration(torch)
 
     comparators = None
     if not args.no_comparators and not args.kernel_only:
@@ -258,9 +306,10 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": committed_traffic(args.workload),
             "kernel": "lean_kernel",
             "bytes_per_launch": alg_bytes,
+            "kernel_source_sha256_16": kernel_source_hash(),
         },
         "cpu_baseline": cpu,
         "comparators": comparators,
