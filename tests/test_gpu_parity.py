@@ -276,3 +276,61 @@ def test_full_size(la, name, nheads):
     assert np.array_equal(owner.cpu().numpy(), own_ref)
     del inp
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_all_single_token_requests(la, kind):
+    lens = [1] * 37
+    inp = W.make_custom(lens, H=5, d=64, dtype="f16", seed=31, device="cuda")
+    check(run(la, inp, kind), reference(inp), tag=f"n=1/{kind}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_many_small_requests(la, kind):
+    """512 requests of 1..300 tokens: each lean workgroup holds many segments
+    (whole heads between a peer segment and a host segment)."""
+    rng = np.random.default_rng(4)
+    lens = [int(x) for x in rng.integers(1, 301, size=512)]
+    inp = W.make_custom(lens, H=2, d=128, dtype="bf16", seed=41, device="cuda")
+    check(run(la, inp, kind), reference(inp), tag=f"many-small/{kind}")
+
+
+def test_grid_larger_than_work(la):
+    """Fewer tile iterations than the requested grid: G is cut to I."""
+    lens = [3, 200]
+    inp = W.make_custom(lens, H=2, d=128, dtype="bf16", seed=43, device="cuda")
+    own_ref, G = tile_owner_ref(lens, 2, 16, 999)
+    assert G == own_ref.size
+    owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
+    check(run(la, inp, "lean", grid=999, tile_tokens=16, tile_owner=owner), reference(inp),
+          tag="G>I")
+    assert np.array_equal(owner.cpu().numpy(), own_ref)
+
+
+def test_largest_head(la):
+    """One head at the 4 GiB limit of a head's block (n = 2^24 - 1 at d = 128):
+    the last rows sit right below the 32-bit offset boundary."""
+    n = (1 << 24) - 1
+    say(f"[largest head] n={n}")
+    inp = W.make_custom([n], H=1, d=128, dtype="bf16", seed=47, device="cuda")
+    got = {k: run(la, inp, k) for k in ("lean", "fixed_split")}
+    ref = sampled_reference(inp, [(0, 0)])
+    for k, g in got.items():
+        check(g, ref, heads=[(0, 0)], tag=f"largest/{k}")
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_rejects_without_launch(la):
+    inp = W.make_custom([4, 4], H=1, d=128, dtype="bf16", seed=1, device="cuda")
+    out = torch.empty((2, 1, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_ex(inp.q, inp.k, inp.v, [4, 0], 2, 1, 128, 0.1, out)
+    assert e.value.status == 1
+    cap = la.la_max_grid(128, la.LA_BF16)
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_ex(inp.q, inp.k, inp.v, [4, 4], 2, 1, 128, 0.1, out, grid=cap + 1)
+    assert e.value.status == 1
+    la.la_sync_check()
