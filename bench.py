@@ -142,6 +142,46 @@ def copy_calibration(torch, nbytes=1 << 30, reps=3):
     log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes")
 
 
+def occupancy(la, torch, inp, kind, blocks, **opts):
+    """Per-CU busy time of one launch, from the per-workgroup timestamps: for
+    every CU the union of its workgroups' [entry, exit] intervals, as a
+    fraction of the kernel's span (first entry to last exit)."""
+    import numpy as np
+    ts = torch.zeros(blocks * 4, dtype=torch.int64, device=inp.q.device)
+    out = torch.empty((inp.B, inp.H, inp.d), dtype=torch.float32, device=inp.q.device)
+    la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
+                    kind=kind, cta_timestamps=ts, **opts)
+    la.la_sync_check()
+    a = ts.view(blocks, 4).cpu().numpy().astype(np.int64)
+    start, end, ids = a[:, 0], a[:, 1], a[:, 2]
+    t0, t1 = int(start.min()), int(end.max())
+    span = max(1, t1 - t0)
+    # XCC_ID, then HW_ID bits 8..15 (CU, SH and SE ids): one key per CU
+    keys = ((ids >> 32) & 0xFF) * 256 + ((ids >> 8) & 0xFF)
+    busy = {}
+    for k in np.unique(keys):
+        sel = np.argsort(start[keys == k])
+        s_, e_ = start[keys == k][sel], end[keys == k][sel]
+        tot, cs, ce = 0, int(s_[0]), int(e_[0])
+        for x, y in zip(s_[1:], e_[1:]):
+            if x > ce:
+                tot += ce - cs
+                cs, ce = int(x), int(y)
+            else:
+                ce = max(ce, int(y))
+        busy[int(k)] = tot + ce - cs
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fr = np.array(list(busy.values())) / span
+    return {
+        "workgroups": blocks,
+        "cus_used": len(busy),
+        "cus": n_cus,
+        "busy_frac_mean_all_cus": round(float(fr.sum() / n_cus), 4),
+        "busy_frac_min_used": round(float(fr.min()), 4),
+        "span_us": round(span / 100.0, 1),     # realtime clock: 100 MHz
+    }
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """fp64 oracle on whole heads of the workload until ~budget_s of wall time,
     scaled by (all heads / heads done) to microseconds per step."""
@@ -265,6 +305,21 @@ def main():
             if isinstance(v, dict) and "kernel_us_mean" in v:
                 v["tbs"] = round(alg_bytes / (v["kernel_us_mean"] * 1e-6) / 1e12, 3)
 
+    occ = None
+    splits = None
+    if not args.kernel_only:
+        import numpy as np
+        sch = la.la_schedule(inp.ctx_lens, inp.H, L, G)
+        per_head = np.bincount(sch["seg"][:, 1], minlength=inp.B * inp.H)
+        splits = {"max": int(per_head.max()), "mean": round(float(per_head.mean()), 3)}
+        occ = {"lean": occupancy(la, torch, inp, "lean", Gu),
+               "per_head": occupancy(la, torch, inp, "per_head", inp.B * inp.H)}
+        if comparators is not None:
+            K = comparators["fixed_split_best"]["num_splits"]
+            occ["fixed_split_best"] = occupancy(la, torch, inp, "fixed_split", inp.B * inp.H * K,
+                                                num_splits=K)
+        log(f"[bench] occupancy: {occ}")
+
     cpu = None
     if not args.no_cpu_baseline and not args.kernel_only:
         log("[bench] cpu baseline (oracle)")
@@ -313,6 +368,8 @@ def main():
         },
         "cpu_baseline": cpu,
         "comparators": comparators,
+        "occupancy": occ,
+        "lean_splits_per_head": splits,
         "env": {"torch": torch.__version__, "python": platform.python_version(),
                 "device": torch.cuda.get_device_name(0)},
     }

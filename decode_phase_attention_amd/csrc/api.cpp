@@ -337,6 +337,7 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
     a.ctx = (const int32_t*)(db + rl.off_ctx);
     a.tok_off = (const int64_t*)(db + rl.off_tok);
     a.part = w.split_part;
+    a.ts = o.cta_timestamps;
     a.H = H;
     a.L = L;
     a.splits = splits;
@@ -393,8 +394,10 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_FIXED_SPLIT && o.kind != LA_KIND_PER_HEAD)
         return fail(LA_EINVAL, "unknown kind %d", o.kind);
     if (o.tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");
-    if (o.kind != LA_KIND_LEAN && (o.tile_owner != nullptr || o.cta_timestamps != nullptr))
-        return fail(LA_EINVAL, "tile_owner and cta_timestamps apply to the lean kind only");
+    if (o.kind != LA_KIND_LEAN && o.tile_owner != nullptr)
+        return fail(LA_EINVAL, "tile_owner applies to the lean kind only");
+    if (o.kind == LA_KIND_FIXED_SPLIT && o.cta_timestamps != nullptr && o.num_splits < 1)
+        return fail(LA_EINVAL, "cta_timestamps with fixed_split needs an explicit num_splits");
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace* w = nullptr;
     if ((st = get_workspace((hipStream_t)stream, &w)) != LA_OK) return st;

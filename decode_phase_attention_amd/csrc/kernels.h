@@ -35,7 +35,7 @@ struct LeanArgs {
     uint32_t* flags;           // [G], zero at launch, zero again at exit
     uint32_t* err;             // device error word
     int32_t* tile_owner;       // optional [I]
-    uint64_t* ts;              // optional [G*4]
+    uint64_t* ts;              // optional [G*4]: start, end, HW_ID/XCC_ID, 0
     int H;
     int L;                     // tile tokens
     float sl2e;                // scale * log2(e)
@@ -52,6 +52,7 @@ struct SplitArgs {
     const int32_t* ctx;
     const int64_t* tok_off;
     float* part;               // split kernel: [B*H*splits * part_stride(d)]
+    uint64_t* ts;              // optional [blocks*4]: start, end, HW_ID/XCC_ID, 0
     int H;
     int L;
     int splits;

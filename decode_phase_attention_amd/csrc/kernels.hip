@@ -325,6 +325,19 @@ __device__ __forceinline__ uint64_t hwreg_ids() {
     return ((uint64_t)xcc << 32) | hw;
 }
 
+// Per-workgroup trace: realtime clock at entry and exit plus the hardware
+// ids of the CU it ran on (thread 0 only).
+__device__ __forceinline__ void stamp_start(uint64_t* ts, int blk) {
+    if (ts != nullptr && threadIdx.x == 0) {
+        ts[blk * 4 + 0] = __builtin_amdgcn_s_memrealtime();
+        ts[blk * 4 + 2] = hwreg_ids();
+        ts[blk * 4 + 3] = 0;
+    }
+}
+__device__ __forceinline__ void stamp_end(uint64_t* ts, int blk) {
+    if (ts != nullptr && threadIdx.x == 0) ts[blk * 4 + 1] = __builtin_amdgcn_s_memrealtime();
+}
+
 // Wave 0 writes out = Obar / l (and m in natural-log units, l) for head u.
 template <int D>
 __device__ __forceinline__ void write_out(float* out, float* m_out, float* l_out, int u, int lane,
@@ -350,10 +363,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     const int lane = t & 63;
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
-    if (a.ts != nullptr && t == 0) {
-        a.ts[c * 4 + 0] = __builtin_amdgcn_s_memrealtime();
-        a.ts[c * 4 + 2] = hwreg_ids();
-    }
+    stamp_start(a.ts, c);
     const int s0 = a.cta_seg[c], s1 = a.cta_seg[c + 1];
     int iter = a.cta_begin[c];
     for (int si = s0; si < s1; ++si) {
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         }
         write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
     }
-    if (a.ts != nullptr && t == 0) a.ts[c * 4 + 1] = __builtin_amdgcn_s_memrealtime();
+    stamp_end(a.ts, c);
 }
 
 // ------------------------------------------------------------------ fixed split
@@ -429,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     using G = Geo<D>;
     constexpr int P = kDpl<D>;
     __shared__ Smem<D> sm;
+    stamp_start(a.ts, blockIdx.x);
     const int u = blockIdx.x / a.splits;
     const int k = blockIdx.x - u * a.splits;
     const int t = threadIdx.x;
@@ -458,6 +469,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
         p[D] = M;
         p[D + 1] = Ls;
     }
+    stamp_end(a.ts, blockIdx.x);
 }
 
 // One wave per head: folds the head's `splits` partial records in order.
@@ -485,6 +497,7 @@ template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
     using G = Geo<D>;
     __shared__ Smem<D> sm;
+    stamp_start(a.ts, blockIdx.x);
     const int u = blockIdx.x;
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -501,6 +514,7 @@ __global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
     float M = kNegInf, Ls = 0.f, O[kDpl<D>];
     wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
     if (t < 64) write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
+    stamp_end(a.ts, blockIdx.x);
 }
 
 template <typename F>

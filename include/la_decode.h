@@ -111,9 +111,11 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *   tile_owner  optional device int32 [I]: lean only; entry i receives the
  *               workgroup that processed tile iteration i of the linearised
  *               schedule (for checking the tables the kernel executed)
- *   cta_timestamps optional device uint64 [grid*4]: lean only; per workgroup
- *               start and end of the 100 MHz realtime clock, HW_ID and XCC_ID
- *               registers
+ *   cta_timestamps optional device uint64 [blocks*4], blocks = the grid of
+ *               the call's first kernel (lean: min(grid, I); fixed split:
+ *               B*H*num_splits, which must then be given; per head: B*H). Per
+ *               workgroup: realtime clock (100 MHz) at entry and at exit, then
+ *               XCC_ID << 32 | HW_ID of the CU it ran on, then 0
  *   ev_start, ev_stop optional hipEvent_t: recorded on `stream` right before
  *               the first and right after the last kernel of the call (the
  *               schedule table copy is outside this pair)

@@ -137,3 +137,7 @@ def test_decode_validation_before_device_work():
     o.tile_owner = fake
     assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
     assert "lean" in la.la_last_error()
+    o.tile_owner = None
+    o.cta_timestamps = fake            # fixed split with timestamps needs num_splits
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "num_splits" in la.la_last_error()

@@ -334,3 +334,26 @@ def test_rejects_without_launch(la):
         la.la_decode_ex(inp.q, inp.k, inp.v, [4, 4], 2, 1, 128, 0.1, out, grid=cap + 1)
     assert e.value.status == 1
     la.la_sync_check()
+
+
+@pytest.mark.parametrize("kind,blocks", [("lean", None), ("fixed_split", 4), ("per_head", None)])
+def test_timestamps(la, kind, blocks):
+    lens = [20000, 3000]
+    H, d = 4, 128
+    inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=53, device="cuda")
+    opts = {}
+    if kind == "lean":
+        _, n, _ = la.la_schedule_dims(lens, H, la.la_default_tile(d), la.la_default_grid(d, la.LA_BF16))
+    elif kind == "fixed_split":
+        n = len(lens) * H * blocks
+        opts["num_splits"] = blocks
+    else:
+        n = len(lens) * H
+    ts = torch.zeros(n * 4, dtype=torch.int64, device="cuda")
+    got = run(la, inp, kind, cta_timestamps=ts, **opts)
+    check(got, reference(inp), tag=f"timestamps/{kind}")
+    a = ts.view(n, 4).cpu().numpy()
+    assert np.all(a[:, 0] > 0) and np.all(a[:, 1] >= a[:, 0])
+    assert np.all(a[:, 3] == 0)
+    span_us = (a[:, 1].max() - a[:, 0].min()) / 100.0
+    assert 0 < span_us < 1e6
