@@ -159,26 +159,39 @@ def _head_from_packed(kbits, vbits, row0: int, n: int, q: np.ndarray, scale: flo
 
 
 def attend_fp64(qbits: np.ndarray, kbits: np.ndarray, vbits: np.ndarray, ctx_lens,
-                scale: float, dtype: str, heads=None, workers: int | None = None):
+                scale: float, dtype: str, heads=None, workers: int | None = None,
+                kv_heads: int | None = None):
     """Decode attention for a packed batch, in fp64.
 
-    ``qbits`` [B, H, d] and ``kbits``/``vbits`` [H * sum(n_b), d] hold raw
-    fp16/bf16 patterns. Request b's K block is [H, n_b, d] starting at row
-    H * sum(n_{b'} for b' < b) (layout (batch, heads, seq_len, head_dim),
-    xllm-io paper review §7.4, with requests packed back to back).
+    ``qbits`` [B, H, d] and ``kbits``/``vbits`` [Hk * sum(n_b), d] hold raw
+    fp16/bf16 patterns, with Hk = ``kv_heads`` (default H). Request b's K
+    block is [Hk, n_b, d] starting at row Hk * sum(n_{b'} for b' < b) (layout
+    (batch, heads, seq_len, head_dim), xllm-io paper review §7.4, with
+    requests packed back to back).
+
+    Grouped-query attention (named as a direction in the review, §7.4, and as
+    a qualification case in the siliconandsystems digest, "Exactness and
+    numerical qualification"): with g = H / Hk, query head h attends over KV
+    head h // g, so each run of g consecutive query heads shares one KV head;
+    Hk = 1 is multi-query attention. The arithmetic per query head is the
+    plain definition above.
 
     ``heads`` optionally restricts the work to a list of (b, h) pairs; other
     entries of the outputs are NaN. Returns (O[B,H,d], m[B,H], l[B,H]) in fp64.
     """
     qbits = np.asarray(qbits)
     B, H, d = qbits.shape
+    Hk = H if kv_heads is None else int(kv_heads)
+    if Hk < 1 or H % Hk:
+        raise ValueError("kv_heads must divide the number of query heads")
+    g = H // Hk
     lens = [int(n) for n in ctx_lens]
     if len(lens) != B:
         raise ValueError("ctx_lens must have one entry per request")
-    if kbits.shape != (H * sum(lens), d) or vbits.shape != kbits.shape:
-        raise ValueError("packed K/V shape does not match ctx_lens, H and d")
+    if kbits.shape != (Hk * sum(lens), d) or vbits.shape != kbits.shape:
+        raise ValueError("packed K/V shape does not match ctx_lens, kv_heads and d")
     q64 = decode_half(qbits.reshape(B * H, d), dtype).reshape(B, H, d)
-    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64) * H
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64) * Hk
     work = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     O = np.full((B, H, d), np.nan)
     M = np.full((B, H), np.nan)
@@ -187,7 +200,7 @@ def attend_fp64(qbits: np.ndarray, kbits: np.ndarray, vbits: np.ndarray, ctx_len
     def one(bh):
         b, h = bh
         n = lens[b]
-        r0 = int(starts[b]) + h * n
+        r0 = int(starts[b]) + (h // g) * n
         return bh, _head_from_packed(kbits, vbits, r0, n, q64[b, h], scale, dtype)
 
     if workers is None:

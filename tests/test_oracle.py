@@ -349,3 +349,69 @@ def test_pins_catch_planted_mistakes():
     assert np.max(np.abs(oracle.attend_head(q3, K3.T, V3, 0.6)[0] - Ob3)) > 1e-3
     assert np.max(np.abs(oracle.attend_head(q, K, V, 1.0)[0] - Ob)) > 1e-3
     assert np.max(np.abs(oracle.attend_head(q, K, V, 0.6)[0] - Ob)) < 1e-12
+
+
+# ----------------------------------------------------------------- grouped-query heads
+
+@pytest.mark.parametrize("H,Hk", [(4, 2), (6, 1), (8, 8)])
+def test_grouped_query_against_brute_force(H, Hk):
+    """Query head h reads K/V head h // (H / Hk); checked head by head against
+    brute force on the K/V head's own source arrays."""
+    rng = np.random.default_rng(H * 10 + Hk)
+    d = 8
+    lens = [4, 1, 13]
+    g = H // Hk
+
+    def bits_and_vals(shape):
+        x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+        return (x.view(torch.int16).numpy().view(np.uint16), x.to(torch.float64).numpy())
+
+    qb, qv = bits_and_vals((len(lens), H, d))
+    kbl = [bits_and_vals((Hk, n, d)) for n in lens]
+    vbl = [bits_and_vals((Hk, n, d)) for n in lens]
+    kp = np.concatenate([k.reshape(-1, d) for k, _ in kbl])
+    vp = np.concatenate([v.reshape(-1, d) for v, _ in vbl])
+    O, M, L = oracle.attend_fp64(qb, kp, vp, lens, 0.4, "bf16", workers=1, kv_heads=Hk)
+    for b in range(len(lens)):
+        for h in range(H):
+            Ob, mb, lb = brute_mp(qv[b, h], kbl[b][1][h // g], vbl[b][1][h // g], 0.4)
+            np.testing.assert_allclose(O[b, h], Ob, rtol=1e-12, atol=1e-12)
+            assert abs(M[b, h] - mb) <= 1e-12 * max(1.0, abs(mb))
+            assert abs(L[b, h] - lb) <= 1e-12 * lb
+
+
+def test_grouped_query_against_torch_sdpa():
+    """torch's scaled_dot_product_attention with enable_gqa (fp64, CPU)."""
+    rng = np.random.default_rng(77)
+    H, Hk, d, n = 16, 4, 64, 3000
+    q = torch.from_numpy(rng.standard_normal((1, H, 1, d)).astype(np.float32)).to(torch.float16)
+    k = torch.from_numpy(rng.standard_normal((1, Hk, n, d)).astype(np.float32)).to(torch.float16)
+    v = torch.from_numpy(rng.standard_normal((1, Hk, n, d)).astype(np.float32)).to(torch.float16)
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    O, _, _ = oracle.attend_fp64(bits(q).reshape(1, H, d), bits(k).reshape(Hk * n, d),
+                                 bits(v).reshape(Hk * n, d), [n], 0.125, "f16", workers=2,
+                                 kv_heads=Hk)
+    t = torch.nn.functional.scaled_dot_product_attention(
+        q.double(), k.double(), v.double(), scale=0.125, enable_gqa=True)
+    np.testing.assert_allclose(O[0], t[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.attend_fp64(bits(q).reshape(1, H, d), bits(k).reshape(Hk * n, d),
+                           bits(v).reshape(Hk * n, d), [n], 0.125, "f16", kv_heads=3)
+
+
+def test_grouping_mistake_is_caught():
+    """A plausible slip -- query head h reading K/V head h % Hk instead of
+    h // g -- disagrees with torch's grouped-query attention."""
+    rng = np.random.default_rng(78)
+    H, Hk, d, n = 8, 2, 16, 50
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal((Hk, n, d))
+    v = rng.standard_normal((Hk, n, d))
+    t = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).view(1, H, 1, d), torch.from_numpy(k).view(1, Hk, n, d),
+        torch.from_numpy(v).view(1, Hk, n, d), scale=0.3, enable_gqa=True)[0, :, 0].numpy()
+    good = np.stack([oracle.attend_head(q[h], k[h // (H // Hk)], v[h // (H // Hk)], 0.3)[0]
+                     for h in range(H)])
+    bad = np.stack([oracle.attend_head(q[h], k[h % Hk], v[h % Hk], 0.3)[0] for h in range(H)])
+    np.testing.assert_allclose(good, t, rtol=1e-12, atol=1e-12)
+    assert np.max(np.abs(bad - t)) > 1e-3

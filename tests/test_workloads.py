@@ -4,13 +4,16 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import workloads as W
 
 
 def test_named_configs_shapes():
-    assert set(W.CONFIGS) == {"tiny", "65k", "512k", "ragged", "many-heads"}
+    assert {"tiny", "65k", "512k", "ragged", "many-heads"} <= set(W.CONFIGS)
+    for name, w in W.CONFIGS.items():
+        assert w.kv_heads is None or w.H % w.kv_heads == 0, name
     inp = W.make_inputs("tiny", seed=0)
     assert inp.q.shape == (1, 4, 64) and inp.q.dtype == torch.float16
     assert inp.k.shape == (4 * 1024, 64) and inp.v.shape == inp.k.shape
@@ -58,3 +61,11 @@ def test_bits_roundtrip():
     bits = W.to_bits(inp.k)
     assert bits.dtype == np.uint16 and bits.shape == (4, 8)
     assert np.array_equal(bits.view(np.float16).astype(np.float32), inp.k.float().numpy())
+
+
+def test_grouped_query_shapes():
+    inp = W.make_custom([5, 9], H=8, d=16, dtype="bf16", seed=2, kv_heads=2)
+    assert inp.q.shape == (2, 8, 16) and inp.k.shape == (2 * 14, 16) and inp.Hk == 2
+    assert W.algorithmic_bytes([5, 9], 8, 16, kv_heads=2) == 2 * 14 * 2 * 16 * 2 + 2 * 8 * 16 * 6
+    with pytest.raises(ValueError):
+        W.make_custom([4], H=6, d=16, kv_heads=4)

@@ -58,6 +58,7 @@ class Workload:
     ctx_hi: int = 0
     shift_frac: float = 0.0       # fraction of keys shifted toward q
     shift_norm: float = 0.0       # length of that shift
+    kv_heads: int | None = None   # K/V heads per request (None: H, plain multi-head)
     note: str = ""
 
 
@@ -71,6 +72,14 @@ CONFIGS: dict[str, Workload] = {
                        ctx_lo=1024, ctx_hi=262144,
                        note="per-request context log-uniform in [1024, 262144]"),
     "many-heads": Workload("many-heads", B=8, H=128, d=64, dtype="f16", ctx=16384),
+    # grouped-query layouts: g = H / kv_heads query heads share each K/V head
+    "gqa-512k": Workload("gqa-512k", B=1, H=32, d=128, dtype="bf16", ctx=524288, kv_heads=8,
+                         note="32 query heads over 8 K/V heads (g = 4)"),
+    "gqa8-ragged": Workload("gqa8-ragged", B=16, H=64, d=128, dtype="bf16", ctx_lo=1024,
+                            ctx_hi=262144, kv_heads=8,
+                            note="64 query heads over 8 K/V heads (g = 8), log-uniform lengths"),
+    "mqa-32k": Workload("mqa-32k", B=8, H=16, d=64, dtype="f16", ctx=32768, kv_heads=1,
+                        note="16 query heads over one K/V head (g = 16)"),
 }
 
 
@@ -91,6 +100,11 @@ class Inputs:
     @property
     def B(self) -> int:
         return len(self.ctx_lens)
+
+    @property
+    def Hk(self) -> int:
+        """K/V heads per request (H for plain multi-head attention)."""
+        return int(self.meta.get("kv_heads", self.H))
 
 
 def _mix(*parts: int) -> int:
@@ -140,12 +154,18 @@ def _draw_request(gq_row: torch.Tensor | None, H: int, n: int, d: int, seed: int
 
 def make_custom(ctx_lens: list[int], H: int, d: int, dtype: str = "bf16", seed: int = 0,
                 device: str = "cpu", q_std: float = 1.0, scale: float | None = None,
-                workload: Workload | None = None, name: str = "custom") -> Inputs:
+                workload: Workload | None = None, name: str = "custom",
+                kv_heads: int | None = None) -> Inputs:
     """Draw q, K, V for arbitrary request lengths.
 
     ``q_std`` widens the score range (adversarial inputs): scores grow in
-    proportion to it.
+    proportion to it. ``kv_heads`` (default H) sets the number of K/V heads
+    per request for grouped-query layouts: K and V are then
+    [kv_heads * sum(n_b), d] while q keeps H heads.
     """
+    Hk = H if kv_heads is None else int(kv_heads)
+    if Hk < 1 or H % Hk:
+        raise ValueError("kv_heads must divide H")
     if any(int(n) < 0 for n in ctx_lens):
         raise ValueError("context lengths must be >= 0")
     tdt = _TORCH_DTYPE[dtype]
@@ -156,30 +176,34 @@ def make_custom(ctx_lens: list[int], H: int, d: int, dtype: str = "bf16", seed: 
         qs.append(torch.randn((H, d), generator=g, device=device, dtype=torch.float32) * q_std)
     q32 = torch.stack(qs) if B else torch.empty((0, H, d), device=device)
     N = int(sum(ctx_lens))
-    k = torch.empty((H * N, d), dtype=tdt, device=device)
-    v = torch.empty((H * N, d), dtype=tdt, device=device)
+    k = torch.empty((Hk * N, d), dtype=tdt, device=device)
+    v = torch.empty((Hk * N, d), dtype=tdt, device=device)
     row = 0
     for b, n in enumerate(ctx_lens):
         n = int(n)
         if n == 0:
             continue
-        kb = _draw_request(q32[b], H, n, d, seed, _TID_K, b, device, workload)
-        k[row:row + H * n] = kb.reshape(H * n, d).to(tdt)
+        kb = _draw_request(q32[b] if Hk == H else None, Hk, n, d, seed, _TID_K, b, device,
+                           workload)
+        k[row:row + Hk * n] = kb.reshape(Hk * n, d).to(tdt)
         del kb
-        vb = _draw_request(None, H, n, d, seed, _TID_V, b, device, None)
-        v[row:row + H * n] = vb.reshape(H * n, d).to(tdt)
+        vb = _draw_request(None, Hk, n, d, seed, _TID_V, b, device, None)
+        v[row:row + Hk * n] = vb.reshape(Hk * n, d).to(tdt)
         del vb
-        row += H * n
+        row += Hk * n
     sc = (1.0 / math.sqrt(d)) if scale is None else float(scale)
-    return Inputs(q=q32.to(tdt).contiguous(), k=k, v=v, ctx_lens=[int(n) for n in ctx_lens],
-                  H=H, d=d, dtype=dtype, scale=sc, seed=seed, name=name)
+    inp = Inputs(q=q32.to(tdt).contiguous(), k=k, v=v, ctx_lens=[int(n) for n in ctx_lens],
+                 H=H, d=d, dtype=dtype, scale=sc, seed=seed, name=name)
+    inp.meta["kv_heads"] = Hk
+    return inp
 
 
 def make_inputs(name: str, seed: int = 0, device: str = "cpu") -> Inputs:
     """Inputs for one of the named workloads in ``CONFIGS``."""
     w = CONFIGS[name]
     lens = context_lengths(w, seed)
-    inp = make_custom(lens, w.H, w.d, w.dtype, seed=seed, device=device, workload=w, name=name)
+    inp = make_custom(lens, w.H, w.d, w.dtype, seed=seed, device=device, workload=w, name=name,
+                      kv_heads=w.kv_heads)
     inp.meta["workload"] = w
     return inp
 
@@ -195,7 +219,10 @@ def kv_bytes(ctx_lens: list[int], H: int, d: int, elem: int = 2) -> int:
     return 2 * int(sum(ctx_lens)) * H * d * elem
 
 
-def algorithmic_bytes(ctx_lens: list[int], H: int, d: int, elem: int = 2) -> int:
-    """Bytes one decode step must move: K and V once, q once, fp32 output once."""
+def algorithmic_bytes(ctx_lens: list[int], H: int, d: int, elem: int = 2,
+                      kv_heads: int | None = None) -> int:
+    """Bytes one decode step must move: K and V once (kv_heads heads), q once
+    and the fp32 output once (H heads)."""
     B = len(ctx_lens)
-    return kv_bytes(ctx_lens, H, d, elem) + B * H * d * elem + B * H * d * 4
+    Hk = H if kv_heads is None else kv_heads
+    return kv_bytes(ctx_lens, Hk, d, elem) + B * H * d * elem + B * H * d * 4
