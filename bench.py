@@ -77,7 +77,7 @@ def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
 
     def call(ev0=None, ev1=None):
         la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, B, H, d, inp.scale, out, kind=kind,
-                        ev_start=ev0, ev_stop=ev1, **opts)
+                        ev_start=ev0, ev_stop=ev1, kv_heads=inp.Hk, **opts)
 
     for _ in range(warmup):
         call()
@@ -150,7 +150,7 @@ def occupancy(la, torch, inp, kind, blocks, **opts):
     ts = torch.zeros(blocks * 4, dtype=torch.int64, device=inp.q.device)
     out = torch.empty((inp.B, inp.H, inp.d), dtype=torch.float32, device=inp.q.device)
     la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
-                    kind=kind, cta_timestamps=ts, **opts)
+                    kind=kind, cta_timestamps=ts, kv_heads=inp.Hk, **opts)
     la.la_sync_check()
     a = ts.view(blocks, 4).cpu().numpy().astype(np.int64)
     start, end, ids = a[:, 0], a[:, 1], a[:, 2]
@@ -191,8 +191,9 @@ def cpu_baseline(inp, budget_s=12.0):
     import workloads as W
 
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    B, H = inp.B, inp.H
-    starts = np.concatenate([[0], np.cumsum(inp.ctx_lens)]) * H
+    B, H, Hk = inp.B, inp.H, inp.Hk
+    g = H // Hk
+    starts = np.concatenate([[0], np.cumsum(inp.ctx_lens)]) * Hk
     qb = W.to_bits(inp.q)
     heads = [(b, h) for b in range(B) for h in range(H)]
     done = 0
@@ -205,7 +206,7 @@ def cpu_baseline(inp, budget_s=12.0):
         ks, vs, lens, qs = [], [], [], []
         for (b, h) in batch:
             n = inp.ctx_lens[b]
-            r0 = int(starts[b]) + h * n
+            r0 = int(starts[b]) + (h // g) * n
             ks.append(W.to_bits(inp.k[r0:r0 + n]))
             vs.append(W.to_bits(inp.v[r0:r0 + n]))
             lens.append(n)
@@ -246,7 +247,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="512k",
-                    choices=["tiny", "65k", "512k", "ragged", "many-heads"])
+                    choices=["tiny", "65k", "512k", "ragged", "many-heads", "gqa-512k",
+                             "gqa8-ragged", "mqa-32k"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
@@ -275,8 +277,11 @@ def main():
     dt_code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
     G = la.la_default_grid(w.d, dt_code)
     L = la.la_default_tile(w.d)
-    I, Gu, _ = la.la_schedule_dims(inp.ctx_lens, inp.H, L, G)
-    alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d)
+    Hk = inp.Hk
+    g = inp.H // Hk
+    units = inp.H if g == 1 else Hk * ((g + 15) // 16)   # schedule units per request
+    I, Gu, _ = la.la_schedule_dims(inp.ctx_lens, units, L, G)
+    alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d, kv_heads=Hk)
     log(f"[bench] lens={inp.ctx_lens} I={I} G={Gu} L={L} bytes={alg_bytes}")
 
     log("[bench] timing lean")
@@ -309,14 +314,14 @@ def main():
     splits = None
     if not args.kernel_only:
         import numpy as np
-        sch = la.la_schedule(inp.ctx_lens, inp.H, L, G)
-        per_head = np.bincount(sch["seg"][:, 1], minlength=inp.B * inp.H)
+        sch = la.la_schedule(inp.ctx_lens, units, L, G)
+        per_head = np.bincount(sch["seg"][:, 1], minlength=inp.B * units)
         splits = {"max": int(per_head.max()), "mean": round(float(per_head.mean()), 3)}
         occ = {"lean": occupancy(la, torch, inp, "lean", Gu),
-               "per_head": occupancy(la, torch, inp, "per_head", inp.B * inp.H)}
+               "per_head": occupancy(la, torch, inp, "per_head", inp.B * units)}
         if comparators is not None:
             K = comparators["fixed_split_best"]["num_splits"]
-            occ["fixed_split_best"] = occupancy(la, torch, inp, "fixed_split", inp.B * inp.H * K,
+            occ["fixed_split_best"] = occupancy(la, torch, inp, "fixed_split", inp.B * units * K,
                                                 num_splits=K)
         log(f"[bench] occupancy: {occ}")
 
@@ -332,6 +337,10 @@ def main():
         "512k": "512k: B=1, H=32, d=128, n=524288, bf16",
         "ragged": "ragged: B=16, H=32, d=128, n_b log-uniform in [1024, 262144], bf16",
         "many-heads": "many-heads: B=8, H=128, d=64, n=16384, fp16",
+        "gqa-512k": "gqa-512k: B=1, H=32 over 8 K/V heads, d=128, n=524288, bf16",
+        "gqa8-ragged": "gqa8-ragged: B=16, H=64 over 8 K/V heads, d=128, n_b log-uniform "
+                       "in [1024, 262144], bf16",
+        "mqa-32k": "mqa-32k: B=8, H=16 over 1 K/V head, d=64, n=32768, fp16",
     }[args.workload]
     rec = {
         "metric": METRIC,
@@ -348,7 +357,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": desc,
-            "B": inp.B, "H": inp.H, "d": w.d, "ctx_lens": inp.ctx_lens, "seed": args.seed,
+            "B": inp.B, "H": inp.H, "kv_heads": Hk, "d": w.d, "ctx_lens": inp.ctx_lens,
+            "seed": args.seed,
             "inputs": w.dtype, "accumulate": "fp32", "output": "fp32",
             "kind": "lean", "grid": Gu, "tile_tokens": L, "iterations": I,
             "parallelism": "single GPU",

@@ -54,6 +54,7 @@ class LaOpts(ctypes.Structure):
         ("cta_timestamps", ctypes.c_void_p),
         ("ev_start", ctypes.c_void_p),
         ("ev_stop", ctypes.c_void_p),
+        ("kv_heads", ctypes.c_int),
     ]
 
 
@@ -180,7 +181,7 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
 def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
-                 ev_stop=None):
+                 ev_stop=None, kv_heads=0):
     o = LaOpts()
     lib().la_opts_init(ctypes.byref(o))
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
@@ -195,6 +196,7 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
     o.cta_timestamps = _ptr(cta_timestamps)
     o.ev_start = ev_start
     o.ev_stop = ev_stop
+    o.kv_heads = int(kv_heads or 0)
     arr, p = _lens(ctx_lens)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
@@ -272,8 +274,9 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, kind="lean", out
     if len(ctx_lens) != B:
         raise ValueError("ctx_lens must have B entries")
     total = int(np.sum(np.asarray(ctx_lens, dtype=np.int64)))
+    Hk = int(opts.get("kv_heads") or H)
     for t in (k_cache, v_cache):
-        if tuple(t.shape) != (H * total, d) or t.dtype != q.dtype:
-            raise ValueError("k_cache/v_cache must be [H * sum(ctx_lens), d] in q's dtype")
+        if tuple(t.shape) != (Hk * total, d) or t.dtype != q.dtype:
+            raise ValueError("k_cache/v_cache must be [kv_heads * sum(ctx_lens), d] in q's dtype")
     la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream, kind=kind, **opts)
     return out

@@ -130,10 +130,10 @@ la_status get_workspace(hipStream_t stream, Workspace** out) {
     return LA_OK;
 }
 
-la_status capacity(int dtype, int d, Capacity* out) {
+la_status capacity(int dtype, int d, bool grouped, Capacity* out) {
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
-    const void* fn = la::lean_kernel_ptr(dtype, d);
+    const void* fn = grouped ? la::lean_gqa_kernel_ptr(dtype, d) : la::lean_kernel_ptr(dtype, d);
     auto key = std::make_pair(dev, fn);
     auto it = g_capacity.find(key);
     if (it != g_capacity.end()) {
@@ -227,41 +227,82 @@ la_status upload(Workspace& w, Staging* s, size_t bytes) {
     return LA_OK;
 }
 
+// Heads of a call: H query heads over Hk K/V heads. With g = H / Hk > 1 the
+// grouped kernels run and the schedule unit is (request, K/V head, block of up
+// to 16 query heads); otherwise the unit is (request, head).
+struct Heads {
+    int H, Hk, g, QB;
+    bool grouped;
+    int units_per_req() const { return grouped ? Hk * QB : H; }
+};
+
+Heads heads_of(int H, int kv_heads) {
+    Heads h;
+    h.H = H;
+    h.Hk = kv_heads > 0 ? kv_heads : H;
+    h.g = H / h.Hk;
+    h.QB = (h.g + 15) / 16;
+    h.grouped = h.g > 1;
+    return h;
+}
+
+void fill_gqa(la::GqaArgs& a, const void* q, const void* k, const void* v, float* out,
+              const la_opts& o, const Heads& hd, int L, float scale) {
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.out = out;
+    a.m_out = o.m_out;
+    a.l_out = o.l_out;
+    a.tile_owner = o.tile_owner;
+    a.ts = o.cta_timestamps;
+    a.H = hd.H;
+    a.Hk = hd.Hk;
+    a.g = hd.g;
+    a.QB = hd.QB;
+    a.L = L;
+    a.splits = 1;
+    a.sl2e = scale * 1.4426950408889634f;
+    a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
+}
+
 la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
-                   const int32_t* ctx_lens, int B, int H, int d, float scale, float* out,
-                   const la_opts& o) {
+                   const int32_t* ctx_lens, int B, const Heads& hd, int d, float scale,
+                   float* out, const la_opts& o) {
     Capacity cap;
-    la_status st = capacity(o.dtype, d, &cap);
+    la_status st = capacity(o.dtype, d, hd.grouped, &cap);
     if (st != LA_OK) return st;
     if (o.grid < 0 || o.grid > cap.coresident)
         return fail(LA_EINVAL, "grid %d outside [1, %d] (co-resident capacity)", o.grid,
                     cap.coresident);
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
+    const int U = hd.units_per_req();
     int64_t I = 0;
     int G = 0, max_rows = 0;
     const char* why = "";
-    const int rc = la::schedule_dims(ctx_lens, B, H, L, o.grid > 0 ? o.grid : cap.preferred, &I,
+    const int rc = la::schedule_dims(ctx_lens, B, U, L, o.grid > 0 ? o.grid : cap.preferred, &I,
                                      &G, &max_rows, &why);
     if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
 
     // table layout in one buffer
-    const int BH = B * H;
+    const int BU = B * U;
     const size_t off_seg = 0;
     const size_t off_cta_seg = align16(off_seg + 16 * (size_t)max_rows);
     const size_t off_cta_begin = align16(off_cta_seg + 4 * (size_t)(G + 1));
     const size_t off_last = align16(off_cta_begin + 4 * (size_t)(G + 1));
-    const size_t off_host = align16(off_last + 4 * (size_t)BH);
-    const ReqLayout rl = req_layout(off_host + 4 * (size_t)BH, B);
+    const size_t off_host = align16(off_last + 4 * (size_t)BU);
+    const ReqLayout rl = req_layout(off_host + 4 * (size_t)BU, B);
 
     Staging* s = nullptr;
     if ((st = staging(w, rl.bytes, &s)) != LA_OK) return st;
     char* hb = (char*)s->host;
-    la::build_schedule(ctx_lens, B, H, L, G, I, (int32_t*)(hb + off_cta_begin),
+    la::build_schedule(ctx_lens, B, U, L, G, I, (int32_t*)(hb + off_cta_begin),
                        (int32_t*)(hb + off_cta_seg), nullptr, (int32_t*)(hb + off_seg),
                        (int32_t*)(hb + off_host), (int32_t*)(hb + off_last));
     fill_req(hb, rl, ctx_lens, B);
 
-    if ((st = grow(w, (void**)&w.part, &w.part_cap, sizeof(float) * (size_t)G * la::part_stride(d),
+    const size_t records = (size_t)G * (hd.grouped ? 16 : 1);
+    if ((st = grow(w, (void**)&w.part, &w.part_cap, sizeof(float) * records * la::part_stride(d),
                    false)) != LA_OK)
         return st;
     if ((st = grow(w, (void**)&w.flags, &w.flags_cap, sizeof(uint32_t) * (size_t)G, true)) != LA_OK)
@@ -269,6 +310,24 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     if ((st = upload(w, s, rl.bytes)) != LA_OK) return st;
 
     char* db = (char*)w.tables;
+    const bool coop = o.cooperative != 0;
+    if (hd.grouped) {
+        la::GqaArgs a;
+        fill_gqa(a, q, k, v, out, o, hd, L, scale);
+        a.ctx = (const int32_t*)(db + rl.off_ctx);
+        a.tok_off = (const int64_t*)(db + rl.off_tok);
+        a.seg = (const int4*)(db + off_seg);
+        a.cta_seg = (const int32_t*)(db + off_cta_seg);
+        a.cta_begin = (const int32_t*)(db + off_cta_begin);
+        a.last_cta = (const int32_t*)(db + off_last);
+        a.part = w.part;
+        a.flags = w.flags;
+        a.err = w.err;
+        if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
+        HIP_TRY(la::launch_lean_gqa(o.dtype, d, a, G, w.stream, coop));
+        if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+        return LA_OK;
+    }
     la::LeanArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -287,20 +346,20 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     a.err = w.err;
     a.tile_owner = o.tile_owner;
     a.ts = o.cta_timestamps;
-    a.H = H;
+    a.H = hd.H;
     a.L = L;
     a.sl2e = scale * 1.4426950408889634f;
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
-    HIP_TRY(la::launch_lean(o.dtype, d, a, G, w.stream, o.cooperative != 0));
+    HIP_TRY(la::launch_lean(o.dtype, d, a, G, w.stream, coop));
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
     return LA_OK;
 }
 
 la_status run_split_or_head(Workspace& w, const void* q, const void* k, const void* v,
-                            const int32_t* ctx_lens, int B, int H, int d, float scale, float* out,
-                            const la_opts& o) {
-    const int BH = B * H;
+                            const int32_t* ctx_lens, int B, const Heads& hd, int d, float scale,
+                            float* out, const la_opts& o) {
+    const int BU = B * hd.units_per_req();
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
     int splits = 1;
     if (o.kind == LA_KIND_FIXED_SPLIT) {
@@ -308,25 +367,44 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
         splits = o.num_splits;
         if (splits == 0) {
             Capacity cap;
-            la_status st = capacity(o.dtype, d, &cap);
+            la_status st = capacity(o.dtype, d, hd.grouped, &cap);
             if (st != LA_OK) return st;
             splits = 1;
-            while ((int64_t)BH * splits < cap.coresident && splits < 64) splits *= 2;
+            while ((int64_t)BU * splits < cap.coresident && splits < 64) splits *= 2;
         }
-        if ((int64_t)BH * splits > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "too many splits");
+        if ((int64_t)BU * splits > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many splits");
     }
     const ReqLayout rl = req_layout(0, B);
     Staging* s = nullptr;
     la_status st = staging(w, rl.bytes, &s);
     if (st != LA_OK) return st;
     fill_req((char*)s->host, rl, ctx_lens, B);
+    const size_t records = (size_t)BU * splits * (hd.grouped ? 16 : 1);
     if (o.kind == LA_KIND_FIXED_SPLIT &&
         (st = grow(w, (void**)&w.split_part, &w.split_cap,
-                   sizeof(float) * (size_t)BH * splits * la::part_stride(d), false)) != LA_OK)
+                   sizeof(float) * records * la::part_stride(d), false)) != LA_OK)
         return st;
     if ((st = upload(w, s, rl.bytes)) != LA_OK) return st;
 
     char* db = (char*)w.tables;
+    if (hd.grouped) {
+        la::GqaArgs a;
+        fill_gqa(a, q, k, v, out, o, hd, L, scale);
+        a.ctx = (const int32_t*)(db + rl.off_ctx);
+        a.tok_off = (const int64_t*)(db + rl.off_tok);
+        a.part = w.split_part;
+        a.splits = splits;
+        if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
+        if (o.kind == LA_KIND_PER_HEAD) {
+            HIP_TRY(la::launch_per_head_gqa(o.dtype, d, a, BU, w.stream));
+        } else {
+            HIP_TRY(la::launch_split_gqa(o.dtype, d, a, BU * splits, w.stream));
+            a.ts = nullptr;
+            HIP_TRY(la::launch_combine_gqa(d, a, BU, w.stream));
+        }
+        if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+        return LA_OK;
+    }
     la::SplitArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -338,22 +416,22 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
     a.tok_off = (const int64_t*)(db + rl.off_tok);
     a.part = w.split_part;
     a.ts = o.cta_timestamps;
-    a.H = H;
+    a.H = hd.H;
     a.L = L;
     a.splits = splits;
     a.sl2e = scale * 1.4426950408889634f;
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
     if (o.kind == LA_KIND_PER_HEAD) {
-        HIP_TRY(la::launch_per_head(o.dtype, d, a, BH, w.stream));
+        HIP_TRY(la::launch_per_head(o.dtype, d, a, BU, w.stream));
     } else {
-        HIP_TRY(la::launch_split(o.dtype, d, a, BH * splits, w.stream));
+        HIP_TRY(la::launch_split(o.dtype, d, a, BU * splits, w.stream));
         la::CombineArgs c;
         c.part = w.split_part;
         c.out = out;
         c.m_out = o.m_out;
         c.l_out = o.l_out;
         c.splits = splits;
-        HIP_TRY(la::launch_combine(d, c, BH, w.stream));
+        HIP_TRY(la::launch_combine(d, c, BU, w.stream));
     }
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
     return LA_OK;
@@ -398,11 +476,15 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
         return fail(LA_EINVAL, "tile_owner applies to the lean kind only");
     if (o.kind == LA_KIND_FIXED_SPLIT && o.cta_timestamps != nullptr && o.num_splits < 1)
         return fail(LA_EINVAL, "cta_timestamps with fixed_split needs an explicit num_splits");
+    if (o.kv_heads < 0 || (o.kv_heads > 0 && H % o.kv_heads != 0))
+        return fail(LA_EINVAL, "kv_heads %d must divide H = %d", o.kv_heads, H);
+    const Heads hd = heads_of(H, o.kv_heads);
+    if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace* w = nullptr;
     if ((st = get_workspace((hipStream_t)stream, &w)) != LA_OK) return st;
-    if (o.kind == LA_KIND_LEAN) return run_lean(*w, q, k, v, ctx_lens, B, H, d, scale, out, o);
-    return run_split_or_head(*w, q, k, v, ctx_lens, B, H, d, scale, out, o);
+    if (o.kind == LA_KIND_LEAN) return run_lean(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
+    return run_split_or_head(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
 }
 
 la_status la_decode(const void* q, const void* k, const void* v, const int32_t* ctx_lens, int B,
@@ -460,7 +542,7 @@ int la_max_grid(int d, int dtype) {
     }
     std::lock_guard<std::mutex> lock(g_mu);
     Capacity cap;
-    if (capacity(dtype, d, &cap) != LA_OK) return -1;
+    if (capacity(dtype, d, false, &cap) != LA_OK) return -1;
     return cap.coresident;
 }
 
@@ -471,7 +553,7 @@ int la_default_grid(int d, int dtype) {
     }
     std::lock_guard<std::mutex> lock(g_mu);
     Capacity cap;
-    if (capacity(dtype, d, &cap) != LA_OK) return -1;
+    if (capacity(dtype, d, false, &cap) != LA_OK) return -1;
     return cap.preferred;
 }
 

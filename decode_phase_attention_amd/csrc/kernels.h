@@ -67,7 +67,44 @@ struct CombineArgs {
     int splits;
 };
 
+// Grouped-query heads: g = H / Hk query heads share a K/V head. The schedule
+// unit is (request, K/V head, block of up to 16 of its query heads); a unit
+// produces 16 partial records (one per query column) of part_stride(d) floats.
+struct GqaArgs {
+    const uint16_t* q;         // [B*H, d]
+    const uint16_t* k;         // packed rows [Hk * sum n_b, d]
+    const uint16_t* v;
+    float* out;                // [B*H, d]
+    float* m_out;              // optional [B*H]
+    float* l_out;              // optional [B*H]
+    const int32_t* ctx;        // [B]
+    const int64_t* tok_off;    // [B]
+    const int4* seg;           // lean tables, as in LeanArgs (units instead of heads)
+    const int32_t* cta_seg;
+    const int32_t* cta_begin;
+    const int32_t* last_cta;
+    float* part;               // lean: [G*16]; split: [units*splits*16] records
+    uint32_t* flags;
+    uint32_t* err;
+    int32_t* tile_owner;
+    uint64_t* ts;
+    int H;                     // query heads per request
+    int Hk;                    // K/V heads per request
+    int g;                     // H / Hk
+    int QB;                    // query blocks of 16 per K/V head: ceil(g / 16)
+    int L;
+    int splits;
+    float sl2e;
+    uint64_t wait_ticks;
+};
+
 const void* lean_kernel_ptr(int dtype, int d);
+const void* lean_gqa_kernel_ptr(int dtype, int d);
+hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,
+                           bool cooperative);
+hipError_t launch_split_gqa(int dtype, int d, const GqaArgs& a, int blocks, hipStream_t s);
+hipError_t launch_combine_gqa(int d, const GqaArgs& a, int units, hipStream_t s);
+hipError_t launch_per_head_gqa(int dtype, int d, const GqaArgs& a, int units, hipStream_t s);
 hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_t s,
                        bool cooperative);
 hipError_t launch_split(int dtype, int d, const SplitArgs& a, int blocks, hipStream_t s);

@@ -34,14 +34,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "kernels.h"
 
 namespace la {
 
 namespace {
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.693147180559945309f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -90,16 +88,6 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (LPR == 16)
         x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false);  // row_mirror
     return x;
-}
-
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// 16-byte load with the non-temporal hint: K and V are streamed exactly once,
-// so they should not displace other lines in the caches.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_nt(const char* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 struct Acc {
@@ -263,79 +251,8 @@ __device__ __forceinline__ void wg_fold(Smem<D>& sm, const Acc& a, int grp, int 
     __syncthreads();
 }
 
-// f applied to a running (M, Ls, O) and one more record (pm, pl, po).
-template <int N>
-__device__ __forceinline__ void merge_into(float& M, float& Ls, float (&O)[N], float pm, float pl,
-                                           const float (&po)[N]) {
-    const float mn = fmaxf(M, pm);
-    const float mu = (mn == kNegInf) ? 0.f : mn;
-    const float a = fexp2(M - mu), b = fexp2(pm - mu);
-    Ls = a * Ls + b * pl;
-#pragma unroll
-    for (int k = 0; k < N; ++k) O[k] = a * O[k] + b * po[k];
-    M = mn;
-}
-
-// Cross-workgroup exchange. Peers and hosts run on different XCDs, whose L2
-// caches are not coherent with each other. Instead of release/acquire fences
-// (which write back / invalidate a whole L2 and stall every other workgroup
-// on that XCD), every access to the exchange buffers is an agent-scope atomic
-// (stores write through to the device coherence point, loads bypass stale
-// lines), and ordering comes from completion: a peer waits until its data
-// stores have completed (s_waitcnt vmcnt(0)) before it stores its flag, and a
-// host loads a peer's data only after it has observed the flag.
-__device__ __forceinline__ void store_agent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_flag(uint32_t* f) {
-    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void drain_stores() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);   // every memory operation of this wave has completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Wait until a peer's flag is raised. Gives up after `limit` ticks of the
-// 100 MHz realtime clock, or at once when any wait has already given up, and
-// raises the error word: a missing peer cannot hang the launch.
-__device__ __forceinline__ void wait_flag(uint32_t* f, uint64_t limit, uint32_t* err) {
-    if (load_flag(f) != 0u) return;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (load_flag(f) == 0u) {
-        __builtin_amdgcn_s_sleep(2);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > limit || load_flag(err) != 0u) {
-            atomicOr(err, 1u);
-            return;
-        }
-    }
-}
-
 __device__ __forceinline__ uint4 load_q(const uint16_t* q, int u, int D, int sub) {
     return *reinterpret_cast<const uint4*>(q + (int64_t)u * D + sub * 8);
-}
-
-__device__ __forceinline__ uint64_t hwreg_ids() {
-    // HW_ID (register 4) and XCC_ID (register 20), all 32 bits of each
-    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
-    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
-    return ((uint64_t)xcc << 32) | hw;
-}
-
-// Per-workgroup trace: realtime clock at entry and exit plus the hardware
-// ids of the CU it ran on (thread 0 only).
-__device__ __forceinline__ void stamp_start(uint64_t* ts, int blk) {
-    if (ts != nullptr && threadIdx.x == 0) {
-        ts[blk * 4 + 0] = __builtin_amdgcn_s_memrealtime();
-        ts[blk * 4 + 2] = hwreg_ids();
-        ts[blk * 4 + 3] = 0;
-    }
-}
-__device__ __forceinline__ void stamp_end(uint64_t* ts, int blk) {
-    if (ts != nullptr && threadIdx.x == 0) ts[blk * 4 + 1] = __builtin_amdgcn_s_memrealtime();
 }
 
 // Wave 0 writes out = Obar / l (and m in natural-log units, l) for head u.

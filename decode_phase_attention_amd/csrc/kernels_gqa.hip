@@ -1,0 +1,551 @@
+// Grouped-query decode attention on gfx950: g = H / Hk query heads share one
+// K/V head, so every K/V row meets up to 16 query rows at once and the scores
+// and the weighted sum form dense tiles. Both go through the 16x16x32 MFMA:
+//
+//   S^T (keys x q)  = K (keys x d)  . Q^T (d x q)        k-dim: head dim
+//   O^T (d x q)    += V^T (d x keys) . P^T (keys x q)    k-dim: keys
+//
+// Operand layout of v_mfma_f32_16x16x32_{bf16,f16} (lane l, w = l/16,
+// c = l%16): A[c][8w + j], B[8w + j][c], C[4w + r][c]. Two freedoms make every
+// operand a direct 16-byte load from HBM (no LDS staging):
+//   - the order of a contraction is free, so lane (w, c) loads K row c at
+//     16-byte piece w + 4kk and Q row c at the same piece;
+//   - the d index of a row of O^T is free, so O^T row i of block nb is head
+//     dim NB*i + nb: lane (w, c) then needs V[key][NB*c .. NB*c + NB) -- one
+//     contiguous load per key -- and an in-register 8 x NB transpose (v_perm)
+//     turns its 8 keys x NB dims into the A operands of the NB blocks.
+// The S^T accumulator leaves lane (w, c) holding query c's scores for keys
+// 4w + r + 16sb, exactly the 8 keys it loaded V for, so P^T needs no shuffle.
+// P is split into a 16-bit high and low part (two MFMAs) so that the weighted
+// sum keeps ~16 significant bits of every weight instead of 8.
+//
+// Query rows beyond the group (c >= g) are zero and never written. Groups of
+// more than 16 query heads are cut into blocks of 16, each a unit of the
+// schedule (the K/V head is then streamed once per block).
+//
+// Each wave streams 32 keys per step with its own online softmax (per query
+// column: m, a per-lane partial l, O^T); waves meet in LDS only at the end of
+// a range. The epilogue uses all 256 threads: thread t owns query t % 16 and
+// head dims [(t / 16) * D/16, +D/16). The exchange between workgroups is the
+// same agent-scope, completion-ordered protocol as the single-head kernels,
+// with 16 records (one per query column) per workgroup.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace la {
+
+namespace {
+
+static_assert(kThreads == 256, "the grouped epilogue maps 16 queries x 16 dim chunks to 256 threads");
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct GGeo {
+    static constexpr int RB = D * 2;            // bytes per K/V row
+    static constexpr int KK = D / 32;           // MFMA k-chunks of the head dim: 4 or 2
+    static constexpr int NB = D / 16;           // 16-row blocks of O^T: 8 or 4
+    static constexpr int KEYS = 32;             // keys per wave step
+    static constexpr int CH = KEYS * kWaves;    // keys per workgroup step: 128
+    static constexpr int DPT = D / 16;          // epilogue dims per thread: 8 or 4
+    static constexpr int VW = NB / 2;           // 32-bit words of V per lane per key: 4 or 2
+};
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma(const u32x4_t a, const u32x4_t b, const f32x4_t c) {
+    if constexpr (DT == 0)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Round p to the 16-bit input type, and the remainder too: hi + lo carries
+// ~16 significant bits of p into the MFMA.
+template <int DT>
+__device__ __forceinline__ void split_p(const float (&p)[8], u32x4_t& hi, u32x4_t& lo) {
+    if constexpr (DT == 0) {
+        f16x8_t h, l;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            h[j] = (_Float16)p[j];
+            l[j] = (_Float16)(p[j] - (float)h[j]);
+        }
+        hi = __builtin_bit_cast(u32x4_t, h);
+        lo = __builtin_bit_cast(u32x4_t, l);
+    } else {
+        bf16x8_t h, l;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            h[j] = (__bf16)p[j];
+            l[j] = (__bf16)(p[j] - (float)h[j]);
+        }
+        hi = __builtin_bit_cast(u32x4_t, h);
+        lo = __builtin_bit_cast(u32x4_t, l);
+    }
+}
+
+__device__ __forceinline__ u32x4_t load16(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+template <int D>
+struct GState {
+    float m;                        // running max of query c, log2 units
+    float l;                        // this lane's partial sum of 2^(s - m)
+    f32x4_t o[GGeo<D>::NB];         // O^T blocks: o[nb][r] = O[c][NB*(4w + r) + nb]
+};
+
+template <int D>
+__device__ __forceinline__ void gstate_init(GState<D>& st) {
+    st.m = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < GGeo<D>::NB; ++nb) st.o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// One wave step over keys [kb, kb + 32) of a head (rows of kh/vh), keys >= e
+// masked. qt[kk] is the B operand of Q^T for head-dim chunk kk.
+template <int DT, int D, bool TAIL>
+__device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char* __restrict__ vh,
+                                         int kb, int e, int w, int c,
+                                         const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
+                                         GState<D>& st) {
+    using G = GGeo<D>;
+    // K: lane (w, c) loads key c (+16 sb), 16-byte piece w + 4kk
+    u32x4_t kr[2][G::KK];
+    // V: lane (w, c) loads keys 4w + r + 16sb (j = r + 4sb), dims [NB*c, NB*c + NB)
+    uint32_t vr[8][G::VW];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        int key = kb + c + 16 * sb;
+        if constexpr (TAIL) key = min(key, e - 1);
+#pragma unroll
+        for (int kk = 0; kk < G::KK; ++kk)
+            kr[sb][kk] = load16(kh + (uint64_t)((uint32_t)key * G::RB + (uint32_t)(w + 4 * kk) * 16u));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        int key = kb + 4 * w + (j & 3) + 16 * (j >> 2);
+        if constexpr (TAIL) key = min(key, e - 1);
+        const char* src = vh + (uint64_t)((uint32_t)key * G::RB + (uint32_t)c * (G::NB * 2));
+        if constexpr (G::VW == 4) {
+            const u32x4_t x = load16(src);
+            vr[j][0] = x.x; vr[j][1] = x.y; vr[j][2] = x.z; vr[j][3] = x.w;
+        } else {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src));
+            vr[j][0] = x.x; vr[j][1] = x.y;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads of the step in flight first
+
+    // scores S^T: lane holds s[j] = S[q = c][key = kb + 4w + (j & 3) + 16 (j >> 2)]
+    float s[8];
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < G::KK; ++kk) acc = mfma<DT>(kr[sb][kk], qt[kk], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = acc[r] * sl2e;
+                s[r + 4 * sb] = (!TAIL || kb + 4 * w + r + 16 * sb < e) ? x : kNegInf;
+            }
+        }
+    }
+    // online softmax of query c across the 4 lanes (w = 0..3) that hold its keys
+    float mx = s[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, s[j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(st.m, mx);
+    const float mu = (mn == kNegInf) ? 0.f : mn;
+    const float alpha = fexp2(st.m - mu);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p[j] = fexp2(s[j] - mu);
+        ps += p[j];
+    }
+    st.l = st.l * alpha + ps;
+    st.m = mn;
+    u32x4_t phi, plo;
+    split_p<DT>(p, phi, plo);
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) {
+        // A operand of block nb: V[key(j)][NB*c + nb] for j = 0..7 (8 x NB transpose)
+        const int wd = nb >> 1;
+        const uint32_t sel = (nb & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t a;
+        a.x = __builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel);
+        a.y = __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel);
+        a.z = __builtin_amdgcn_perm(vr[5][wd], vr[4][wd], sel);
+        a.w = __builtin_amdgcn_perm(vr[7][wd], vr[6][wd], sel);
+        f32x4_t o = st.o[nb] * alpha;
+        o = mfma<DT>(a, phi, o);
+        o = mfma<DT>(a, plo, o);
+        st.o[nb] = o;
+    }
+}
+
+// Stream keys [a, e) of one K/V head for the 16 query columns of qt.
+template <int DT, int D>
+__device__ __forceinline__ void gqa_range(const uint16_t* kh, const uint16_t* vh, int a, int e,
+                                          int wave, int w, int c,
+                                          const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
+                                          GState<D>& st) {
+    using G = GGeo<D>;
+    const char* kc = reinterpret_cast<const char*>(kh);
+    const char* vc = reinterpret_cast<const char*>(vh);
+    int base = a;
+    for (; base + G::CH <= e; base += G::CH)
+        gqa_step<DT, D, false>(kc, vc, base + G::KEYS * wave, e, w, c, qt, sl2e, st);
+    if (base < e) gqa_step<DT, D, true>(kc, vc, base + G::KEYS * wave, e, w, c, qt, sl2e, st);
+}
+
+// Q^T operands of a unit: lane (w, c) holds query row c (if c < geff) at
+// head-dim pieces w + 4kk; rows beyond the group are zero.
+template <int D>
+__device__ __forceinline__ void load_qt(const uint16_t* q, int64_t qrow0, int geff, int w, int c,
+                                        u32x4_t (&qt)[GGeo<D>::KK]) {
+#pragma unroll
+    for (int kk = 0; kk < GGeo<D>::KK; ++kk) {
+        if (c < geff)
+            qt[kk] = *reinterpret_cast<const u32x4_t*>(
+                reinterpret_cast<const char*>(q) +
+                (uint64_t)((qrow0 + c) * (int64_t)(D * 2) + (w + 4 * kk) * 16));
+        else
+            qt[kk] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int D>
+struct alignas(16) GSmem {
+    float o[kWaves][16][D + 4];   // padded rows: conflict-free float4 traffic
+    float m[kWaves][16];
+    float l[kWaves][16];
+};
+
+// Fold the waves' states with f. Thread t = 16*dc + q receives (M, L, O) of
+// query column q for head dims [dc*DPT, dc*DPT + DPT).
+template <int D>
+__device__ __forceinline__ void gqa_fold(GSmem<D>& sm, GState<D>& st, int wave, int w, int c,
+                                         float& M, float& L, float (&O)[GGeo<D>::DPT]) {
+    using G = GGeo<D>;
+    // the lanes of query c split its keys over w = 0..3: add their partial sums
+    float l = st.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int nb0 = 0; nb0 < G::NB; nb0 += 4) {
+            float4 v = make_float4(st.o[nb0][r], st.o[nb0 + 1][r], st.o[nb0 + 2][r], st.o[nb0 + 3][r]);
+            *reinterpret_cast<float4*>(&sm.o[wave][c][G::NB * (4 * w + r) + nb0]) = v;
+        }
+    }
+    if (w == 0) {
+        sm.m[wave][c] = st.m;
+        sm.l[wave][c] = l;
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int q = t & 15;
+    const int dc = t >> 4;
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) mx = fmaxf(mx, sm.m[v][q]);
+    const float mu = (mx == kNegInf) ? 0.f : mx;
+    float ls = 0.f, o[G::DPT];
+#pragma unroll
+    for (int i = 0; i < G::DPT; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const float wt = fexp2(sm.m[v][q] - mu);
+        ls = fmaf(wt, sm.l[v][q], ls);
+#pragma unroll
+        for (int i0 = 0; i0 < G::DPT; i0 += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(&sm.o[v][q][dc * G::DPT + i0]);
+            o[i0 + 0] = fmaf(wt, x.x, o[i0 + 0]);
+            o[i0 + 1] = fmaf(wt, x.y, o[i0 + 1]);
+            o[i0 + 2] = fmaf(wt, x.z, o[i0 + 2]);
+            o[i0 + 3] = fmaf(wt, x.w, o[i0 + 3]);
+        }
+    }
+    M = mx;
+    L = ls;
+#pragma unroll
+    for (int i = 0; i < G::DPT; ++i) O[i] = o[i];
+    __syncthreads();
+}
+
+struct Unit {
+    int b, kvh, qb, geff;
+    int64_t qrow0;   // row of the unit's first query head in q / out
+    int64_t kvrow0;  // row of the K/V head's first key
+    int n;
+};
+
+__device__ __forceinline__ Unit decode_unit(const GqaArgs& a, int u) {
+    Unit x;
+    const int upr = a.Hk * a.QB;
+    x.b = u / upr;
+    const int rem = u - x.b * upr;
+    x.kvh = rem / a.QB;
+    x.qb = rem - x.kvh * a.QB;
+    x.geff = min(16, a.g - 16 * x.qb);
+    x.qrow0 = (int64_t)x.b * a.H + (int64_t)x.kvh * a.g + 16 * x.qb;
+    x.n = a.ctx[x.b];
+    x.kvrow0 = (int64_t)a.Hk * a.tok_off[x.b] + (int64_t)x.kvh * x.n;
+    return x;
+}
+
+template <int D>
+__device__ __forceinline__ void write_out_gqa(const GqaArgs& a, const Unit& x, int q, int dc,
+                                              float M, float L, const float (&O)[GGeo<D>::DPT]) {
+    if (q >= x.geff) return;
+    const int64_t row = x.qrow0 + q;
+    const float inv = 1.f / L;
+    float* dst = a.out + row * D + dc * GGeo<D>::DPT;
+#pragma unroll
+    for (int i0 = 0; i0 < GGeo<D>::DPT; i0 += 4)
+        *reinterpret_cast<float4*>(dst + i0) =
+            make_float4(O[i0] * inv, O[i0 + 1] * inv, O[i0 + 2] * inv, O[i0 + 3] * inv);
+    if (dc == 0) {
+        if (a.m_out != nullptr) a.m_out[row] = M * kLn2;
+        if (a.l_out != nullptr) a.l_out[row] = L;
+    }
+}
+
+// ------------------------------------------------------------------ lean
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
+    using G = GGeo<D>;
+    __shared__ GSmem<D> sm;
+    const int cta = blockIdx.x;
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    const int w = (t >> 4) & 3;
+    const int c = t & 15;
+    const int q = t & 15;
+    const int dc = t >> 4;
+    stamp_start(a.ts, cta);
+    const int s0 = a.cta_seg[cta], s1 = a.cta_seg[cta + 1];
+    int iter = a.cta_begin[cta];
+    for (int si = s0; si < s1; ++si) {
+        const int4 sg = a.seg[si];
+        const int u = sg.x;
+        const Unit x = decode_unit(a, u);
+        const int tok0 = sg.y * a.L;
+        const int tok1 = (int)min((int64_t)sg.z * a.L, (int64_t)x.n);
+        u32x4_t qt[G::KK];
+        load_qt<D>(a.q, x.qrow0, x.geff, w, c, qt);
+        GState<D> st;
+        gstate_init<D>(st);
+        gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, wave, w, c, qt,
+                         a.sl2e, st);
+        if (a.tile_owner != nullptr && t == 0)
+            for (int i = sg.y; i < sg.z; ++i) a.tile_owner[iter + i - sg.y] = cta;
+        iter += sg.z - sg.y;
+
+        float M, L, O[G::DPT];
+        gqa_fold<D>(sm, st, wave, w, c, M, L, O);
+
+        if (!(sg.w & 1)) {
+            // a peer: publish one record per query column, then raise the flag
+            if (q < x.geff) {
+                float* p = a.part + ((int64_t)cta * 16 + q) * part_stride(D);
+#pragma unroll
+                for (int i = 0; i < G::DPT; ++i) store_agent(p + dc * G::DPT + i, O[i]);
+                if (dc == 0) {
+                    store_agent(p + D, M);
+                    store_agent(p + D + 1, L);
+                }
+            }
+            drain_stores();
+            __syncthreads();
+            if (t == 0) __hip_atomic_store(&a.flags[cta], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            continue;
+        }
+        if (!(sg.w & 2)) {
+            // the host: wait for every peer at once, then fold their records in
+            // ascending workgroup order, four peers' loads in flight at a time
+            const int last = a.last_cta[u];
+            const int np = last - cta;
+            for (int i = t; i < np; i += kThreads) wait_flag(&a.flags[cta + 1 + i], a.wait_ticks, a.err);
+            __syncthreads();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            constexpr int kBatch = 4;
+            const int qq = min(q, x.geff - 1);   // columns past the group read a valid record
+            for (int p0 = cta + 1; p0 <= last; p0 += kBatch) {
+                float pm[kBatch], pl[kBatch], po[kBatch][G::DPT];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const float* p = a.part + ((int64_t)min(p0 + j, last) * 16 + qq) * part_stride(D);
+                    pm[j] = load_agent(p + D);
+                    pl[j] = load_agent(p + D + 1);
+#pragma unroll
+                    for (int i = 0; i < G::DPT; ++i) po[j][i] = load_agent(p + dc * G::DPT + i);
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (p0 + j <= last) merge_into<G::DPT>(M, L, O, pm[j], pl[j], po[j]);
+            }
+            __syncthreads();
+            for (int i = t; i < np; i += kThreads)
+                __hip_atomic_store(&a.flags[cta + 1 + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        write_out_gqa<D>(a, x, q, dc, M, L, O);
+    }
+    stamp_end(a.ts, cta);
+}
+
+// ------------------------------------------------------------------ fixed split
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void split_gqa_kernel(const GqaArgs a) {
+    using G = GGeo<D>;
+    __shared__ GSmem<D> sm;
+    stamp_start(a.ts, blockIdx.x);
+    const int u = blockIdx.x / a.splits;
+    const int k = blockIdx.x - u * a.splits;
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    const int w = (t >> 4) & 3;
+    const int c = t & 15;
+    const Unit x = decode_unit(a, u);
+    const int64_t T = ((int64_t)x.n + a.L - 1) / a.L;
+    const int64_t t0 = (int64_t)k * T / a.splits, t1 = (int64_t)(k + 1) * T / a.splits;
+    const int tok0 = (int)(t0 * a.L);
+    const int tok1 = (int)min(t1 * a.L, (int64_t)x.n);
+    u32x4_t qt[G::KK];
+    load_qt<D>(a.q, x.qrow0, x.geff, w, c, qt);
+    GState<D> st;
+    gstate_init<D>(st);
+    if (tok0 < tok1)
+        gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, wave, w, c, qt,
+                         a.sl2e, st);
+    float M, L, O[G::DPT];
+    gqa_fold<D>(sm, st, wave, w, c, M, L, O);
+    const int q = t & 15, dc = t >> 4;
+    if (q < x.geff) {
+        float* p = a.part + ((int64_t)blockIdx.x * 16 + q) * part_stride(D);
+#pragma unroll
+        for (int i = 0; i < G::DPT; ++i) p[dc * G::DPT + i] = O[i];
+        if (dc == 0) {
+            p[D] = M;
+            p[D + 1] = L;
+        }
+    }
+    stamp_end(a.ts, blockIdx.x);
+}
+
+// One wave per (unit, query column): folds the unit's `splits` records in order.
+template <int D>
+__global__ __launch_bounds__(64) void combine_gqa_kernel(const GqaArgs a) {
+    constexpr int P = D / 64;
+    const int u = blockIdx.x >> 4;
+    const int q = blockIdx.x & 15;
+    const int lane = threadIdx.x;
+    const Unit x = decode_unit(a, u);
+    if (q >= x.geff) return;
+    float M = kNegInf, L = 0.f, O[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) O[j] = 0.f;
+    for (int k = 0; k < a.splits; ++k) {
+        const float* p = a.part + (((int64_t)u * a.splits + k) * 16 + q) * part_stride(D);
+        float po[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) po[j] = p[lane + 64 * j];
+        merge_into<P>(M, L, O, p[D], p[D + 1], po);
+    }
+    const int64_t row = x.qrow0 + q;
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int j = 0; j < P; ++j) a.out[row * D + lane + 64 * j] = O[j] * inv;
+    if (lane == 0) {
+        if (a.m_out != nullptr) a.m_out[row] = M * kLn2;
+        if (a.l_out != nullptr) a.l_out[row] = L;
+    }
+}
+
+// ------------------------------------------------------------------ per head
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void per_head_gqa_kernel(const GqaArgs a) {
+    using G = GGeo<D>;
+    __shared__ GSmem<D> sm;
+    stamp_start(a.ts, blockIdx.x);
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    const int w = (t >> 4) & 3;
+    const int c = t & 15;
+    const Unit x = decode_unit(a, blockIdx.x);
+    u32x4_t qt[G::KK];
+    load_qt<D>(a.q, x.qrow0, x.geff, w, c, qt);
+    GState<D> st;
+    gstate_init<D>(st);
+    gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, 0, x.n, wave, w, c, qt, a.sl2e, st);
+    float M, L, O[G::DPT];
+    gqa_fold<D>(sm, st, wave, w, c, M, L, O);
+    write_out_gqa<D>(a, x, t & 15, t >> 4, M, L, O);
+    stamp_end(a.ts, blockIdx.x);
+}
+
+template <typename F>
+const void* pick_g(int dtype, int d, F f16_64, F f16_128, F bf16_64, F bf16_128) {
+    if (dtype == 0) return d == 64 ? (const void*)f16_64 : (const void*)f16_128;
+    return d == 64 ? (const void*)bf16_64 : (const void*)bf16_128;
+}
+
+}  // namespace
+
+const void* lean_gqa_kernel_ptr(int dtype, int d) {
+    return pick_g(dtype, d, &lean_gqa_kernel<0, 64>, &lean_gqa_kernel<0, 128>,
+                  &lean_gqa_kernel<1, 64>, &lean_gqa_kernel<1, 128>);
+}
+
+hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,
+                           bool cooperative) {
+    const void* fn = lean_gqa_kernel_ptr(dtype, d);
+    void* args[] = {const_cast<GqaArgs*>(&a)};
+    if (cooperative)
+        return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_split_gqa(int dtype, int d, const GqaArgs& a, int blocks, hipStream_t s) {
+    const void* fn = pick_g(dtype, d, &split_gqa_kernel<0, 64>, &split_gqa_kernel<0, 128>,
+                            &split_gqa_kernel<1, 64>, &split_gqa_kernel<1, 128>);
+    void* args[] = {const_cast<GqaArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3(blocks), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_combine_gqa(int d, const GqaArgs& a, int units, hipStream_t s) {
+    const void* fn =
+        d == 64 ? (const void*)&combine_gqa_kernel<64> : (const void*)&combine_gqa_kernel<128>;
+    void* args[] = {const_cast<GqaArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3(units * 16), dim3(64), args, 0, s);
+}
+
+hipError_t launch_per_head_gqa(int dtype, int d, const GqaArgs& a, int units, hipStream_t s) {
+    const void* fn = pick_g(dtype, d, &per_head_gqa_kernel<0, 64>, &per_head_gqa_kernel<0, 128>,
+                            &per_head_gqa_kernel<1, 64>, &per_head_gqa_kernel<1, 128>);
+    void* args[] = {const_cast<GqaArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3(units), dim3(kThreads), args, 0, s);
+}
+
+}  // namespace la

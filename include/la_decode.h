@@ -119,6 +119,14 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *   ev_start, ev_stop optional hipEvent_t: recorded on `stream` right before
  *               the first and right after the last kernel of the call (the
  *               schedule table copy is outside this pair)
+ *   kv_heads    grouped-query attention: K/V heads per request, dividing H
+ *               (0 = H, plain multi-head attention). Query head h attends over
+ *               K/V head h / (H / kv_heads); k_cache and v_cache are then
+ *               packed as [kv_heads, n_b, d] per request while q and out keep
+ *               H heads. Groups of more than 16 query heads stream their K/V
+ *               head once per 16 query heads. With kv_heads < H the lean
+ *               schedule's units (tables, tile_owner, grid) are
+ *               (request, K/V head, block of 16 query heads).
  */
 typedef struct la_opts {
     int dtype;
@@ -133,6 +141,7 @@ typedef struct la_opts {
     uint64_t* cta_timestamps;
     void* ev_start;
     void* ev_stop;
+    int kv_heads;
 } la_opts;
 
 void la_opts_init(la_opts* opts);
