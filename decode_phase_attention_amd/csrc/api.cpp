@@ -321,6 +321,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         a.cta_begin = (const int32_t*)(db + off_cta_begin);
         a.last_cta = (const int32_t*)(db + off_last);
         a.part = w.part;
+        a.part_bytes = w.part_cap > (size_t)INT32_MAX ? (uint32_t)INT32_MAX : (uint32_t)w.part_cap;
         a.flags = w.flags;
         a.err = w.err;
         if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
@@ -393,6 +394,7 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
         a.ctx = (const int32_t*)(db + rl.off_ctx);
         a.tok_off = (const int64_t*)(db + rl.off_tok);
         a.part = w.split_part;
+        a.part_bytes = 0;   // the split kernels use plain accesses
         a.splits = splits;
         if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
         if (o.kind == LA_KIND_PER_HEAD) {

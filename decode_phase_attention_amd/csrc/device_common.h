@@ -50,6 +50,33 @@ __device__ __forceinline__ float load_agent(const float* p) {
 __device__ __forceinline__ uint32_t load_flag(uint32_t* f) {
     return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16- and 8-byte exchange accesses with the same device-scope coherence
+// (cache policy sc1), through a raw buffer resource over the exchange buffer
+// (offsets in bytes; the resource also bounds every access to `bytes`).
+constexpr int kCoherentPolicy = 16;   // sc1
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t exchange_rsrc(float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+    const u32x4_t x = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                       __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)off, 0, kCoherentPolicy);
+}
+__device__ __forceinline__ void store8_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b) {
+    const u32x2_t x = {__float_as_uint(a), __float_as_uint(b)};
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)off, 0, kCoherentPolicy);
+}
+__device__ __forceinline__ float4 load16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t x = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherentPolicy));
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                       __uint_as_float(x.w));
+}
+__device__ __forceinline__ float2 load8_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x2_t x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCoherentPolicy));
+    return make_float2(__uint_as_float(x.x), __uint_as_float(x.y));
+}
+
 __device__ __forceinline__ void drain_stores() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);   // every memory operation of this wave has completed

@@ -84,6 +84,7 @@ struct GqaArgs {
     const int32_t* cta_begin;
     const int32_t* last_cta;
     float* part;               // lean: [G*16]; split: [units*splits*16] records
+    uint32_t part_bytes;       // size of the lean exchange buffer (bounds its accesses)
     uint32_t* flags;
     uint32_t* err;
     int32_t* tile_owner;

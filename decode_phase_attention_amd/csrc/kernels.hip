@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
             const int np = last - c;
             for (int i = lane; i < np; i += 64) wait_flag(&a.flags[c + 1 + i], a.wait_ticks, a.err);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            constexpr int kBatch = 8;
+            constexpr int kBatch = 16;
             for (int p0 = c + 1; p0 <= last; p0 += kBatch) {
                 float pm[kBatch], pl[kBatch], po[kBatch][P];
 #pragma unroll

@@ -25,10 +25,11 @@
 //
 // Each wave streams 32 keys per step with its own online softmax (per query
 // column: m, a per-lane partial l, O^T); waves meet in LDS only at the end of
-// a range. The epilogue uses all 256 threads: thread t owns query t % 16 and
-// head dims [(t / 16) * D/16, +D/16). The exchange between workgroups is the
-// same agent-scope, completion-ordered protocol as the single-head kernels,
-// with 16 records (one per query column) per workgroup.
+// a range. The epilogue uses all 256 threads: thread t owns query t / 16 and
+// head dims [(t % 16) * D/16, +D/16), so a wave covers four whole records.
+// The exchange between workgroups is the same agent-scope, completion-ordered
+// protocol as the single-head kernels, with 16 records (one per query column)
+// per workgroup, moved in 16-byte device-coherent buffer accesses.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -238,7 +239,7 @@ struct alignas(16) GSmem {
     float l[kWaves][16];
 };
 
-// Fold the waves' states with f. Thread t = 16*dc + q receives (M, L, O) of
+// Fold the waves' states with f. Thread t = 16*q + dc receives (M, L, O) of
 // query column q for head dims [dc*DPT, dc*DPT + DPT).
 template <int D>
 __device__ __forceinline__ void gqa_fold(GSmem<D>& sm, GState<D>& st, int wave, int w, int c,
@@ -262,8 +263,8 @@ __device__ __forceinline__ void gqa_fold(GSmem<D>& sm, GState<D>& st, int wave, 
     }
     __syncthreads();
     const int t = threadIdx.x;
-    const int q = t & 15;
-    const int dc = t >> 4;
+    const int q = t >> 4;
+    const int dc = t & 15;
     float mx = kNegInf;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) mx = fmaxf(mx, sm.m[v][q]);
@@ -340,8 +341,9 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     const int wave = t >> 6;
     const int w = (t >> 4) & 3;
     const int c = t & 15;
-    const int q = t & 15;
-    const int dc = t >> 4;
+    const int q = t >> 4;
+    const int dc = t & 15;
+    const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
     stamp_start(a.ts, cta);
     const int s0 = a.cta_seg[cta], s1 = a.cta_seg[cta + 1];
     int iter = a.cta_begin[cta];
@@ -367,13 +369,12 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
         if (!(sg.w & 1)) {
             // a peer: publish one record per query column, then raise the flag
             if (q < x.geff) {
-                float* p = a.part + ((int64_t)cta * 16 + q) * part_stride(D);
+                const uint32_t rec = (uint32_t)(cta * 16 + q) * (uint32_t)(part_stride(D) * 4);
 #pragma unroll
-                for (int i = 0; i < G::DPT; ++i) store_agent(p + dc * G::DPT + i, O[i]);
-                if (dc == 0) {
-                    store_agent(p + D, M);
-                    store_agent(p + D + 1, L);
-                }
+                for (int i = 0; i < G::DPT; i += 4)
+                    store16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u,
+                                  make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]));
+                if (dc == 0) store8_agent(xr, rec + (uint32_t)D * 4u, M, L);
             }
             drain_stores();
             __syncthreads();
@@ -382,23 +383,32 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
         }
         if (!(sg.w & 2)) {
             // the host: wait for every peer at once, then fold their records in
-            // ascending workgroup order, four peers' loads in flight at a time
+            // ascending workgroup order, a batch of peers' loads in flight at a
+            // time (the streaming registers are free by now)
             const int last = a.last_cta[u];
             const int np = last - cta;
             for (int i = t; i < np; i += kThreads) wait_flag(&a.flags[cta + 1 + i], a.wait_ticks, a.err);
             __syncthreads();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            constexpr int kBatch = 4;
+            constexpr int kBatch = 128 / D * 8;   // 16 peers at d = 64, 8 at d = 128
             const int qq = min(q, x.geff - 1);   // columns past the group read a valid record
             for (int p0 = cta + 1; p0 <= last; p0 += kBatch) {
                 float pm[kBatch], pl[kBatch], po[kBatch][G::DPT];
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
-                    const float* p = a.part + ((int64_t)min(p0 + j, last) * 16 + qq) * part_stride(D);
-                    pm[j] = load_agent(p + D);
-                    pl[j] = load_agent(p + D + 1);
+                    const uint32_t rec =
+                        (uint32_t)(min(p0 + j, last) * 16 + qq) * (uint32_t)(part_stride(D) * 4);
+                    const float2 ml = load8_agent(xr, rec + (uint32_t)D * 4u);
+                    pm[j] = ml.x;
+                    pl[j] = ml.y;
 #pragma unroll
-                    for (int i = 0; i < G::DPT; ++i) po[j][i] = load_agent(p + dc * G::DPT + i);
+                    for (int i = 0; i < G::DPT; i += 4) {
+                        const float4 v = load16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u);
+                        po[j][i] = v.x;
+                        po[j][i + 1] = v.y;
+                        po[j][i + 2] = v.z;
+                        po[j][i + 3] = v.w;
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j)
@@ -440,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void split_gqa_kernel(const GqaArgs a) {
                          a.sl2e, st);
     float M, L, O[G::DPT];
     gqa_fold<D>(sm, st, wave, w, c, M, L, O);
-    const int q = t & 15, dc = t >> 4;
+    const int q = t >> 4, dc = t & 15;
     if (q < x.geff) {
         float* p = a.part + ((int64_t)blockIdx.x * 16 + q) * part_stride(D);
 #pragma unroll
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void per_head_gqa_kernel(const GqaArgs a)
     gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, 0, x.n, wave, w, c, qt, a.sl2e, st);
     float M, L, O[G::DPT];
     gqa_fold<D>(sm, st, wave, w, c, M, L, O);
-    write_out_gqa<D>(a, x, t & 15, t >> 4, M, L, O);
+    write_out_gqa<D>(a, x, t >> 4, t & 15, M, L, O);
     stamp_end(a.ts, blockIdx.x);
 }
 
