@@ -6,8 +6,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 What it computes is the plain definition of scaled dot-product attention for a
 single query row per (request, head) -- the decode shape Nq = 1 (xllm-io paper
 review of arXiv 2405.10480, §2.1 and §3.1; LeanAttention talk summary,
-"Background"). LeanAttention reaches this result exactly, up to floating-point
-rounding order (xllm-io paper review, §4.1; siliconandsystems digest,
+"Background") -- and, for several new tokens per request, the same definition
+over each token's causally visible prefix (see ``attend_fp64``). LeanAttention
+reaches this result exactly, up to floating-point rounding order (xllm-io paper review, §4.1; siliconandsystems digest,
 "Exactness and numerical qualification"), so the oracle is the definition
 itself, not the tiled algorithm:
 
@@ -45,6 +46,7 @@ __all__ = [
     "identity",
     "normalise",
     "attend_fp64",
+    "visible_rows",
 ]
 
 _CHUNK = 65536  # tokens decoded to fp64 at a time, to bound memory per head
@@ -139,6 +141,12 @@ def normalise(t):
     return np.asarray(o, dtype=np.float64) / l
 
 
+def visible_rows(n: int, Nq: int, t: int) -> int:
+    """Rows of an n-row cache that new token t of Nq sees: the token sits at
+    position n - Nq + t and attends causally to positions 0 .. n - Nq + t."""
+    return n - Nq + 1 + t
+
+
 def _head_from_packed(kbits, vbits, row0: int, n: int, q: np.ndarray, scale: float,
                       dtype: str):
     """Two-pass attention for one head whose rows are kbits[row0:row0+n]."""
@@ -176,11 +184,27 @@ def attend_fp64(qbits: np.ndarray, kbits: np.ndarray, vbits: np.ndarray, ctx_len
     Hk = 1 is multi-query attention. The arithmetic per query head is the
     plain definition above.
 
-    ``heads`` optionally restricts the work to a list of (b, h) pairs; other
-    entries of the outputs are NaN. Returns (O[B,H,d], m[B,H], l[B,H]) in fp64.
+    Several new tokens per request (the review, §7.4, names combining the
+    method with speculative decoding as a direction; the digest lists masked
+    tokens among the cases to qualify): ``qbits`` [B, Nq, H, d] holds Nq
+    query tokens per request. They occupy the last Nq of the request's n_b
+    cached positions (their own K/V rows end the cache), and token t
+    (0-based) attends causally, to the first n_b - Nq + 1 + t rows of its K/V
+    head: exactly the rows a one-token decode at that position would see.
+    Then every n_b must be >= Nq.
+
+    ``heads`` optionally restricts the work to a list of (b, h) pairs --
+    (b, t, h) triples with several tokens; other entries of the outputs are
+    NaN. Returns (O[B,H,d], m[B,H], l[B,H]) in fp64, or O[B,Nq,H,d],
+    m[B,Nq,H], l[B,Nq,H] with several tokens.
     """
     qbits = np.asarray(qbits)
-    B, H, d = qbits.shape
+    multi = qbits.ndim == 4
+    if multi:
+        B, Nq, H, d = qbits.shape
+    else:
+        B, H, d = qbits.shape
+        Nq = 1
     Hk = H if kv_heads is None else int(kv_heads)
     if Hk < 1 or H % Hk:
         raise ValueError("kv_heads must divide the number of query heads")
@@ -188,20 +212,28 @@ def attend_fp64(qbits: np.ndarray, kbits: np.ndarray, vbits: np.ndarray, ctx_len
     lens = [int(n) for n in ctx_lens]
     if len(lens) != B:
         raise ValueError("ctx_lens must have one entry per request")
+    if Nq < 1 or any(n < Nq for n in lens):
+        raise ValueError("every context must hold the request's new tokens (n_b >= Nq)")
     if kbits.shape != (Hk * sum(lens), d) or vbits.shape != kbits.shape:
         raise ValueError("packed K/V shape does not match ctx_lens, kv_heads and d")
-    q64 = decode_half(qbits.reshape(B * H, d), dtype).reshape(B, H, d)
+    q64 = decode_half(qbits.reshape(B * Nq * H, d), dtype).reshape(B, Nq, H, d)
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64) * Hk
-    work = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
-    O = np.full((B, H, d), np.nan)
-    M = np.full((B, H), np.nan)
-    L = np.full((B, H), np.nan)
+    if heads is None:
+        work = [(b, t, h) for b in range(B) for t in range(Nq) for h in range(H)]
+    elif multi:
+        work = [tuple(x) for x in heads]
+    else:
+        work = [(b, 0, h) for b, h in heads]
+    O = np.full((B, Nq, H, d), np.nan)
+    M = np.full((B, Nq, H), np.nan)
+    L = np.full((B, Nq, H), np.nan)
 
-    def one(bh):
-        b, h = bh
+    def one(bth):
+        b, t, h = bth
         n = lens[b]
         r0 = int(starts[b]) + (h // g) * n
-        return bh, _head_from_packed(kbits, vbits, r0, n, q64[b, h], scale, dtype)
+        return bth, _head_from_packed(kbits, vbits, r0, visible_rows(n, Nq, t), q64[b, t, h],
+                                      scale, dtype)
 
     if workers is None:
         workers = max(1, min(len(work), len(os.sched_getaffinity(0))))
@@ -211,9 +243,11 @@ def attend_fp64(qbits: np.ndarray, kbits: np.ndarray, vbits: np.ndarray, ctx_len
         with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
             results = list(ex.map(one, work))
     else:
-        results = [one(bh) for bh in work]
-    for (b, h), (o, m, l) in results:
-        O[b, h] = o
-        M[b, h] = m
-        L[b, h] = l
+        results = [one(x) for x in work]
+    for (b, t, h), (o, m, l) in results:
+        O[b, t, h] = o
+        M[b, t, h] = m
+        L[b, t, h] = l
+    if not multi:
+        return O[:, 0], M[:, 0], L[:, 0]
     return O, M, L

@@ -69,3 +69,20 @@ def test_grouped_query_shapes():
     assert W.algorithmic_bytes([5, 9], 8, 16, kv_heads=2) == 2 * 14 * 2 * 16 * 2 + 2 * 8 * 16 * 6
     with pytest.raises(ValueError):
         W.make_custom([4], H=6, d=16, kv_heads=4)
+
+
+def test_several_new_tokens_shapes():
+    a = W.make_custom([6, 3], H=4, d=8, dtype="bf16", seed=2, kv_heads=2, q_tokens=3)
+    assert a.q.shape == (2, 3, 4, 8) and a.Nq == 3 and a.Hk == 2
+    assert a.k.shape == (2 * 9, 8)
+    # token 0 of the batch is the single-token draw: the token axis extends it
+    b = W.make_custom([6, 3], H=4, d=8, dtype="bf16", seed=2, kv_heads=2)
+    assert torch.equal(a.q[:, 0].view(torch.int16), b.q.view(torch.int16))
+    assert torch.equal(a.k.view(torch.int16), b.k.view(torch.int16))
+    with pytest.raises(ValueError):
+        W.make_custom([6, 2], H=4, d=8, q_tokens=3)
+    assert W.algorithmic_bytes([6, 3], 4, 8, kv_heads=2, q_tokens=3) == \
+        2 * 9 * 2 * 8 * 2 + 2 * 3 * 4 * 8 * (2 + 4)
+    for name in ("spec4-ragged", "spec8-64k"):
+        w = W.CONFIGS[name]
+        assert w.q_tokens > 1 and min(W.context_lengths(w)) >= w.q_tokens

@@ -59,6 +59,7 @@ class Workload:
     shift_frac: float = 0.0       # fraction of keys shifted toward q
     shift_norm: float = 0.0       # length of that shift
     kv_heads: int | None = None   # K/V heads per request (None: H, plain multi-head)
+    q_tokens: int = 1             # new tokens per request decoded together (speculative verification)
     note: str = ""
 
 
@@ -80,12 +81,19 @@ CONFIGS: dict[str, Workload] = {
                             note="64 query heads over 8 K/V heads (g = 8), log-uniform lengths"),
     "mqa-32k": Workload("mqa-32k", B=8, H=16, d=64, dtype="f16", ctx=32768, kv_heads=1,
                         note="16 query heads over one K/V head (g = 16)"),
+    # several new tokens per request (draft tokens under verification); the
+    # last q_tokens positions of each cache are those tokens' own K/V rows
+    "spec4-ragged": Workload("spec4-ragged", B=16, H=32, d=128, dtype="bf16", ctx_lo=1024,
+                             ctx_hi=262144, kv_heads=8, q_tokens=4,
+                             note="4 new tokens per request, 32 query heads over 8 K/V heads"),
+    "spec8-64k": Workload("spec8-64k", B=4, H=32, d=128, dtype="bf16", ctx=65536, q_tokens=8,
+                          note="8 new tokens per request, plain multi-head"),
 }
 
 
 @dataclass
 class Inputs:
-    q: torch.Tensor               # [B, H, d]
+    q: torch.Tensor               # [B, H, d], or [B, Nq, H, d] with several new tokens
     k: torch.Tensor               # [H * sum(n_b), d] packed per request
     v: torch.Tensor               # same layout as k
     ctx_lens: list[int]
@@ -105,6 +113,11 @@ class Inputs:
     def Hk(self) -> int:
         """K/V heads per request (H for plain multi-head attention)."""
         return int(self.meta.get("kv_heads", self.H))
+
+    @property
+    def Nq(self) -> int:
+        """New tokens per request (1 for plain decode)."""
+        return int(self.meta.get("q_tokens", 1))
 
 
 def _mix(*parts: int) -> int:
@@ -155,26 +168,34 @@ def _draw_request(gq_row: torch.Tensor | None, H: int, n: int, d: int, seed: int
 def make_custom(ctx_lens: list[int], H: int, d: int, dtype: str = "bf16", seed: int = 0,
                 device: str = "cpu", q_std: float = 1.0, scale: float | None = None,
                 workload: Workload | None = None, name: str = "custom",
-                kv_heads: int | None = None) -> Inputs:
+                kv_heads: int | None = None, q_tokens: int = 1) -> Inputs:
     """Draw q, K, V for arbitrary request lengths.
 
     ``q_std`` widens the score range (adversarial inputs): scores grow in
     proportion to it. ``kv_heads`` (default H) sets the number of K/V heads
     per request for grouped-query layouts: K and V are then
-    [kv_heads * sum(n_b), d] while q keeps H heads.
+    [kv_heads * sum(n_b), d] while q keeps H heads. ``q_tokens`` > 1 draws
+    that many query tokens per request, q then being [B, q_tokens, H, d]
+    (token-major, as a batch of new tokens arrives); every n_b must be at
+    least q_tokens, since the new tokens' own K/V rows end each cache.
     """
     Hk = H if kv_heads is None else int(kv_heads)
     if Hk < 1 or H % Hk:
         raise ValueError("kv_heads must divide H")
     if any(int(n) < 0 for n in ctx_lens):
         raise ValueError("context lengths must be >= 0")
+    Nq = int(q_tokens)
+    if Nq < 1 or (Nq > 1 and any(int(n) < Nq for n in ctx_lens)):
+        raise ValueError("q_tokens must be >= 1 and at most every context length")
     tdt = _TORCH_DTYPE[dtype]
     B = len(ctx_lens)
     qs = []
     for b in range(B):
         g = _gen(device, seed, _TID_Q, b)
-        qs.append(torch.randn((H, d), generator=g, device=device, dtype=torch.float32) * q_std)
-    q32 = torch.stack(qs) if B else torch.empty((0, H, d), device=device)
+        qs.append(torch.randn((Nq * H, d), generator=g, device=device, dtype=torch.float32) * q_std)
+    q32 = torch.stack(qs) if B else torch.empty((0, Nq * H, d), device=device)
+    if Nq > 1:
+        q32 = q32.view(B, Nq, H, d)
     N = int(sum(ctx_lens))
     k = torch.empty((Hk * N, d), dtype=tdt, device=device)
     v = torch.empty((Hk * N, d), dtype=tdt, device=device)
@@ -183,8 +204,8 @@ def make_custom(ctx_lens: list[int], H: int, d: int, dtype: str = "bf16", seed: 
         n = int(n)
         if n == 0:
             continue
-        kb = _draw_request(q32[b] if Hk == H else None, Hk, n, d, seed, _TID_K, b, device,
-                           workload)
+        kb = _draw_request(q32[b] if Hk == H and Nq == 1 else None, Hk, n, d, seed, _TID_K, b,
+                           device, workload)
         k[row:row + Hk * n] = kb.reshape(Hk * n, d).to(tdt)
         del kb
         vb = _draw_request(None, Hk, n, d, seed, _TID_V, b, device, None)
@@ -195,6 +216,7 @@ def make_custom(ctx_lens: list[int], H: int, d: int, dtype: str = "bf16", seed: 
     inp = Inputs(q=q32.to(tdt).contiguous(), k=k, v=v, ctx_lens=[int(n) for n in ctx_lens],
                  H=H, d=d, dtype=dtype, scale=sc, seed=seed, name=name)
     inp.meta["kv_heads"] = Hk
+    inp.meta["q_tokens"] = Nq
     return inp
 
 
@@ -203,7 +225,7 @@ def make_inputs(name: str, seed: int = 0, device: str = "cpu") -> Inputs:
     w = CONFIGS[name]
     lens = context_lengths(w, seed)
     inp = make_custom(lens, w.H, w.d, w.dtype, seed=seed, device=device, workload=w, name=name,
-                      kv_heads=w.kv_heads)
+                      kv_heads=w.kv_heads, q_tokens=w.q_tokens)
     inp.meta["workload"] = w
     return inp
 
@@ -220,9 +242,10 @@ def kv_bytes(ctx_lens: list[int], H: int, d: int, elem: int = 2) -> int:
 
 
 def algorithmic_bytes(ctx_lens: list[int], H: int, d: int, elem: int = 2,
-                      kv_heads: int | None = None) -> int:
+                      kv_heads: int | None = None, q_tokens: int = 1) -> int:
     """Bytes one decode step must move: K and V once (kv_heads heads), q once
-    and the fp32 output once (H heads)."""
+    and the fp32 output once (q_tokens x H query rows per request)."""
     B = len(ctx_lens)
     Hk = H if kv_heads is None else kv_heads
-    return kv_bytes(ctx_lens, Hk, d, elem) + B * H * d * elem + B * H * d * 4
+    rows = B * q_tokens * H
+    return kv_bytes(ctx_lens, Hk, d, elem) + rows * d * elem + rows * d * 4
