@@ -55,6 +55,7 @@ class LaOpts(ctypes.Structure):
         ("ev_start", ctypes.c_void_p),
         ("ev_stop", ctypes.c_void_p),
         ("kv_heads", ctypes.c_int),
+        ("q_tokens", ctypes.c_int),
     ]
 
 
@@ -181,7 +182,7 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
 def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
-                 ev_stop=None, kv_heads=0):
+                 ev_stop=None, kv_heads=0, q_tokens=0):
     o = LaOpts()
     lib().la_opts_init(ctypes.byref(o))
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
@@ -197,6 +198,7 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
     o.ev_start = ev_start
     o.ev_stop = ev_stop
     o.kv_heads = int(kv_heads or 0)
+    o.q_tokens = int(q_tokens or 0)
     arr, p = _lens(ctx_lens)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
@@ -264,11 +266,16 @@ def la_set_wait_limit_us(us: int):
 def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, kind="lean", out=None,
                      stream=None, **opts):
     """Convenience wrapper: shapes from the tensors, fp32 output allocated if
-    not given. q is [B, H, d]; k_cache/v_cache are packed [H * sum(n_b), d]."""
+    not given. q is [B, H, d], or [B, Nq, H, d] for Nq new tokens per request;
+    k_cache/v_cache are packed [kv_heads * sum(n_b), d]."""
     import torch
-    B, H, d = q.shape
+    if q.dim() == 4:
+        B, Nq, H, d = q.shape
+        opts["q_tokens"] = Nq
+    else:
+        B, H, d = q.shape
     if out is None:
-        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if len(ctx_lens) != B:

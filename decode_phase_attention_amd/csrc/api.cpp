@@ -78,6 +78,7 @@ std::map<std::pair<int, const void*>, Capacity> g_capacity;
 // concurrent sequential streams without adding bandwidth (measured on MI355X:
 // 1 per CU streams fastest on the long-context and ragged workloads).
 constexpr int kWgPerCu = 1;
+constexpr int kMaxQTokens = 64;
 uint32_t g_wait_us = kDefaultWaitUs;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -243,22 +244,25 @@ la_status upload(Workspace& w, const char* host, size_t bytes) {
 // Host scratch for building tables before they are compared and uploaded.
 thread_local std::vector<char> g_build;
 
-// Heads of a call: H query heads over Hk K/V heads. With g = H / Hk > 1 the
-// grouped kernels run and the schedule unit is (request, K/V head, block of up
-// to 16 query heads); otherwise the unit is (request, head).
+// Query columns of a call: H query heads over Hk K/V heads, times Nq new
+// tokens per request. With more than one column per K/V head (g * Nq > 1) the
+// grouped kernels run and the schedule unit is (request, K/V head, block of
+// up to 16 columns); otherwise the unit is (request, head).
 struct Heads {
-    int H, Hk, g, QB;
+    int H, Hk, g, Nq, cols, QB;
     bool grouped;
     int units_per_req() const { return grouped ? Hk * QB : H; }
 };
 
-Heads heads_of(int H, int kv_heads) {
+Heads heads_of(int H, int kv_heads, int q_tokens) {
     Heads h;
     h.H = H;
     h.Hk = kv_heads > 0 ? kv_heads : H;
     h.g = H / h.Hk;
-    h.QB = (h.g + 15) / 16;
-    h.grouped = h.g > 1;
+    h.Nq = q_tokens > 0 ? q_tokens : 1;
+    h.cols = h.g * h.Nq;
+    h.QB = (h.cols + 15) / 16;
+    h.grouped = h.cols > 1;
     return h;
 }
 
@@ -275,6 +279,8 @@ void fill_gqa(la::GqaArgs& a, const void* q, const void* k, const void* v, float
     a.H = hd.H;
     a.Hk = hd.Hk;
     a.g = hd.g;
+    a.Nq = hd.Nq;
+    a.cols = hd.cols;
     a.QB = hd.QB;
     a.L = L;
     a.splits = 1;
@@ -494,7 +500,13 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
         return fail(LA_EINVAL, "cta_timestamps with fixed_split needs an explicit num_splits");
     if (o.kv_heads < 0 || (o.kv_heads > 0 && H % o.kv_heads != 0))
         return fail(LA_EINVAL, "kv_heads %d must divide H = %d", o.kv_heads, H);
-    const Heads hd = heads_of(H, o.kv_heads);
+    if (o.q_tokens < 0 || o.q_tokens > kMaxQTokens)
+        return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", o.q_tokens, kMaxQTokens);
+    for (int b = 0; b < B && o.q_tokens > 1; ++b)
+        if (ctx_lens[b] < o.q_tokens)
+            return fail(LA_EINVAL, "ctx_lens[%d] = %d is shorter than the %d new tokens it must hold",
+                        b, ctx_lens[b], o.q_tokens);
+    const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace* w = nullptr;

@@ -67,16 +67,18 @@ struct CombineArgs {
     int splits;
 };
 
-// Grouped-query heads: g = H / Hk query heads share a K/V head. The schedule
-// unit is (request, K/V head, block of up to 16 of its query heads); a unit
-// produces 16 partial records (one per query column) of part_stride(d) floats.
+// Grouped-query heads and several new tokens per request: the g = H / Hk
+// query heads sharing a K/V head, times the Nq new tokens, are that K/V head's
+// g * Nq query columns. The schedule unit is (request, K/V head, block of up
+// to 16 columns); a unit produces 16 partial records (one per column) of
+// part_stride(d) floats.
 struct GqaArgs {
-    const uint16_t* q;         // [B*H, d]
+    const uint16_t* q;         // [B*Nq*H, d]
     const uint16_t* k;         // packed rows [Hk * sum n_b, d]
     const uint16_t* v;
-    float* out;                // [B*H, d]
-    float* m_out;              // optional [B*H]
-    float* l_out;              // optional [B*H]
+    float* out;                // [B*Nq*H, d]
+    float* m_out;              // optional [B*Nq*H]
+    float* l_out;              // optional [B*Nq*H]
     const int32_t* ctx;        // [B]
     const int64_t* tok_off;    // [B]
     const int4* seg;           // lean tables, as in LeanArgs (units instead of heads)
@@ -92,7 +94,9 @@ struct GqaArgs {
     int H;                     // query heads per request
     int Hk;                    // K/V heads per request
     int g;                     // H / Hk
-    int QB;                    // query blocks of 16 per K/V head: ceil(g / 16)
+    int Nq;                    // new tokens per request
+    int cols;                  // query columns per K/V head: g * Nq
+    int QB;                    // column blocks of 16 per K/V head: ceil(cols / 16)
     int L;
     int splits;
     float sl2e;

@@ -19,8 +19,12 @@
 // P is split into a 16-bit high and low part (two MFMAs) so that the weighted
 // sum keeps ~16 significant bits of every weight instead of 8.
 //
-// Query rows beyond the group (c >= g) are zero and never written. Groups of
-// more than 16 query heads are cut into blocks of 16, each a unit of the
+// The query columns of a K/V head are its g query heads times the Nq new
+// tokens of the request, ordered (head in group, token). Token t of Nq sits
+// at cache position n - Nq + t and sees keys [0, n - Nq + t], so keys below
+// n - Nq + 1 are seen by every column and only the last steps of a head mask
+// per column. Columns beyond the g * Nq live ones are zero and never
+// written. More than 16 columns are cut into blocks of 16, each a unit of the
 // schedule (the K/V head is then streamed once per block).
 //
 // Each wave streams 32 keys per step with its own online softmax (per query
@@ -112,11 +116,12 @@ __device__ __forceinline__ void gstate_init(GState<D>& st) {
     for (int nb = 0; nb < GGeo<D>::NB; ++nb) st.o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// One wave step over keys [kb, kb + 32) of a head (rows of kh/vh), keys >= e
-// masked. qt[kk] is the B operand of Q^T for head-dim chunk kk.
+// One wave step over keys [kb, kb + 32) of a head (rows of kh/vh). With TAIL,
+// loads stay below e and this lane's query column masks keys >= lim (lim <= e).
+// qt[kk] is the B operand of Q^T for head-dim chunk kk.
 template <int DT, int D, bool TAIL>
 __device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char* __restrict__ vh,
-                                         int kb, int e, int w, int c,
+                                         int kb, int e, int lim, int w, int c,
                                          const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
                                          GState<D>& st) {
     using G = GGeo<D>;
@@ -160,7 +165,7 @@ __device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float x = acc[r] * sl2e;
-                s[r + 4 * sb] = (!TAIL || kb + 4 * w + r + 16 * sb < e) ? x : kNegInf;
+                s[r + 4 * sb] = (!TAIL || kb + 4 * w + r + 16 * sb < lim) ? x : kNegInf;
             }
         }
     }
@@ -201,32 +206,35 @@ __device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char
     }
 }
 
-// Stream keys [a, e) of one K/V head for the 16 query columns of qt.
+// Stream keys [a, e) of one K/V head for the 16 query columns of qt. Keys
+// below `full` (uniform) are seen by every column; this lane's column sees
+// keys below lim (full <= lim <= e), which only the last steps test.
 template <int DT, int D>
 __device__ __forceinline__ void gqa_range(const uint16_t* kh, const uint16_t* vh, int a, int e,
-                                          int wave, int w, int c,
+                                          int full, int lim, int wave, int w, int c,
                                           const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
                                           GState<D>& st) {
     using G = GGeo<D>;
     const char* kc = reinterpret_cast<const char*>(kh);
     const char* vc = reinterpret_cast<const char*>(vh);
     int base = a;
-    for (; base + G::CH <= e; base += G::CH)
-        gqa_step<DT, D, false>(kc, vc, base + G::KEYS * wave, e, w, c, qt, sl2e, st);
-    if (base < e) gqa_step<DT, D, true>(kc, vc, base + G::KEYS * wave, e, w, c, qt, sl2e, st);
+    for (; base + G::CH <= full; base += G::CH)
+        gqa_step<DT, D, false>(kc, vc, base + G::KEYS * wave, e, lim, w, c, qt, sl2e, st);
+    for (; base < e; base += G::CH)
+        gqa_step<DT, D, true>(kc, vc, base + G::KEYS * wave, e, lim, w, c, qt, sl2e, st);
 }
 
-// Q^T operands of a unit: lane (w, c) holds query row c (if c < geff) at
-// head-dim pieces w + 4kk; rows beyond the group are zero.
+// Q^T operands of a unit: lane (w, c) holds the query row of column c (row
+// `row`, if live) at head-dim pieces w + 4kk; dead columns are zero.
 template <int D>
-__device__ __forceinline__ void load_qt(const uint16_t* q, int64_t qrow0, int geff, int w, int c,
+__device__ __forceinline__ void load_qt(const uint16_t* q, int64_t row, bool live, int w,
                                         u32x4_t (&qt)[GGeo<D>::KK]) {
 #pragma unroll
     for (int kk = 0; kk < GGeo<D>::KK; ++kk) {
-        if (c < geff)
+        if (live)
             qt[kk] = *reinterpret_cast<const u32x4_t*>(
                 reinterpret_cast<const char*>(q) +
-                (uint64_t)((qrow0 + c) * (int64_t)(D * 2) + (w + 4 * kk) * 16));
+                (uint64_t)(row * (int64_t)(D * 2) + (w + 4 * kk) * 16));
         else
             qt[kk] = u32x4_t{0u, 0u, 0u, 0u};
     }
@@ -293,9 +301,8 @@ __device__ __forceinline__ void gqa_fold(GSmem<D>& sm, GState<D>& st, int wave, 
 }
 
 struct Unit {
-    int b, kvh, qb, geff;
-    int64_t qrow0;   // row of the unit's first query head in q / out
-    int64_t kvrow0;  // row of the K/V head's first key
+    int b, kvh, qb, geff;   // geff: live query columns of this block (<= 16)
+    int64_t kvrow0;         // row of the K/V head's first key
     int n;
 };
 
@@ -306,18 +313,39 @@ __device__ __forceinline__ Unit decode_unit(const GqaArgs& a, int u) {
     const int rem = u - x.b * upr;
     x.kvh = rem / a.QB;
     x.qb = rem - x.kvh * a.QB;
-    x.geff = min(16, a.g - 16 * x.qb);
-    x.qrow0 = (int64_t)x.b * a.H + (int64_t)x.kvh * a.g + 16 * x.qb;
+    x.geff = min(16, a.cols - 16 * x.qb);
     x.n = a.ctx[x.b];
     x.kvrow0 = (int64_t)a.Hk * a.tok_off[x.b] + (int64_t)x.kvh * x.n;
     return x;
+}
+
+// Row in q / out (and m_out / l_out) of live column c of a unit: column
+// 16 qb + c is (query head hq of the group, token t), row (b Nq + t) H + kvh g + hq.
+__device__ __forceinline__ int64_t col_row(const GqaArgs& a, const Unit& x, int c) {
+    const int cg = 16 * x.qb + c;
+    const int hq = cg / a.Nq;
+    const int t = cg - hq * a.Nq;
+    return ((int64_t)x.b * a.Nq + t) * a.H + (int64_t)x.kvh * a.g + hq;
+}
+
+// Keys column c sees: its token t sits at position n - Nq + t.
+__device__ __forceinline__ int col_visible(const GqaArgs& a, const Unit& x, int c) {
+    return x.n - a.Nq + 1 + (16 * x.qb + c) % a.Nq;
+}
+
+// Key bounds of a range [tok0, tok1) for lane column c: keys below `full` are
+// seen by every column, keys below `lim` by column c.
+__device__ __forceinline__ void col_bounds(const GqaArgs& a, const Unit& x, int c, int tok1,
+                                           int& full, int& lim) {
+    full = min(tok1, x.n - a.Nq + 1);
+    lim = min(tok1, col_visible(a, x, c));
 }
 
 template <int D>
 __device__ __forceinline__ void write_out_gqa(const GqaArgs& a, const Unit& x, int q, int dc,
                                               float M, float L, const float (&O)[GGeo<D>::DPT]) {
     if (q >= x.geff) return;
-    const int64_t row = x.qrow0 + q;
+    const int64_t row = col_row(a, x, q);
     const float inv = 1.f / L;
     float* dst = a.out + row * D + dc * GGeo<D>::DPT;
 #pragma unroll
@@ -354,11 +382,13 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
         const int tok0 = sg.y * a.L;
         const int tok1 = (int)min((int64_t)sg.z * a.L, (int64_t)x.n);
         u32x4_t qt[G::KK];
-        load_qt<D>(a.q, x.qrow0, x.geff, w, c, qt);
+        load_qt<D>(a.q, c < x.geff ? col_row(a, x, c) : 0, c < x.geff, w, qt);
+        int full, lim;
+        col_bounds(a, x, c, tok1, full, lim);
         GState<D> st;
         gstate_init<D>(st);
-        gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, wave, w, c, qt,
-                         a.sl2e, st);
+        gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, full, lim, wave, w,
+                         c, qt, a.sl2e, st);
         if (a.tile_owner != nullptr && t == 0)
             for (int i = sg.y; i < sg.z; ++i) a.tile_owner[iter + i - sg.y] = cta;
         iter += sg.z - sg.y;
@@ -442,12 +472,14 @@ __global__ __launch_bounds__(kThreads) void split_gqa_kernel(const GqaArgs a) {
     const int tok0 = (int)(t0 * a.L);
     const int tok1 = (int)min(t1 * a.L, (int64_t)x.n);
     u32x4_t qt[G::KK];
-    load_qt<D>(a.q, x.qrow0, x.geff, w, c, qt);
+    load_qt<D>(a.q, c < x.geff ? col_row(a, x, c) : 0, c < x.geff, w, qt);
+    int full, lim;
+    col_bounds(a, x, c, tok1, full, lim);
     GState<D> st;
     gstate_init<D>(st);
     if (tok0 < tok1)
-        gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, wave, w, c, qt,
-                         a.sl2e, st);
+        gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, full, lim, wave, w,
+                         c, qt, a.sl2e, st);
     float M, L, O[G::DPT];
     gqa_fold<D>(sm, st, wave, w, c, M, L, O);
     const int q = t >> 4, dc = t & 15;
@@ -482,7 +514,7 @@ __global__ __launch_bounds__(64) void combine_gqa_kernel(const GqaArgs a) {
         for (int j = 0; j < P; ++j) po[j] = p[lane + 64 * j];
         merge_into<P>(M, L, O, p[D], p[D + 1], po);
     }
-    const int64_t row = x.qrow0 + q;
+    const int64_t row = col_row(a, x, q);
     const float inv = 1.f / L;
 #pragma unroll
     for (int j = 0; j < P; ++j) a.out[row * D + lane + 64 * j] = O[j] * inv;
@@ -505,10 +537,13 @@ __global__ __launch_bounds__(kThreads) void per_head_gqa_kernel(const GqaArgs a)
     const int c = t & 15;
     const Unit x = decode_unit(a, blockIdx.x);
     u32x4_t qt[G::KK];
-    load_qt<D>(a.q, x.qrow0, x.geff, w, c, qt);
+    load_qt<D>(a.q, c < x.geff ? col_row(a, x, c) : 0, c < x.geff, w, qt);
+    int full, lim;
+    col_bounds(a, x, c, x.n, full, lim);
     GState<D> st;
     gstate_init<D>(st);
-    gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, 0, x.n, wave, w, c, qt, a.sl2e, st);
+    gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, 0, x.n, full, lim, wave, w, c, qt,
+                     a.sl2e, st);
     float M, L, O[G::DPT];
     gqa_fold<D>(sm, st, wave, w, c, M, L, O);
     write_out_gqa<D>(a, x, t >> 4, t & 15, M, L, O);

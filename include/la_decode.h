@@ -127,6 +127,22 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               head once per 16 query heads. With kv_heads < H the lean
  *               schedule's units (tables, tile_owner, grid) are
  *               (request, K/V head, block of 16 query heads).
+ *   q_tokens    new tokens per request decoded together, as when a draft of
+ *               several tokens is verified (0 or 1 = one token; at most 64).
+ *               q is then [B, q_tokens, H, d] (token-major) and out
+ *               [B, q_tokens, H, d] fp32, m_out/l_out [B*q_tokens*H]. The new
+ *               tokens are the last q_tokens positions of each request's
+ *               cache (their own K/V rows are already in it, so every
+ *               ctx_lens[b] >= q_tokens, else LA_EINVAL), and token t attends
+ *               causally to cache positions 0 .. ctx_lens[b] - q_tokens + t.
+ *               A K/V head's query columns are then its H/kv_heads query
+ *               heads times q_tokens, ordered (head, token); the schedule's
+ *               units are (request, K/V head, block of 16 columns) whenever
+ *               there is more than one column. The causal mask among the new
+ *               tokens is a reading: the pages name combining the method with
+ *               speculative decoding (xllm-io paper review, §7.4) and masked
+ *               tokens as a case to qualify (siliconandsystems digest,
+ *               "Exactness and numerical qualification") but fix no mask.
  */
 typedef struct la_opts {
     int dtype;
@@ -142,6 +158,7 @@ typedef struct la_opts {
     void* ev_start;
     void* ev_stop;
     int kv_heads;
+    int q_tokens;
 } la_opts;
 
 void la_opts_init(la_opts* opts);

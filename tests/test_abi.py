@@ -141,3 +141,13 @@ def test_decode_validation_before_device_work():
     o.cta_timestamps = fake            # fixed split with timestamps needs num_splits
     assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
     assert "num_splits" in la.la_last_error()
+    o.cta_timestamps = None
+    o.kind = 0
+    o.q_tokens = 65                    # more new tokens than supported
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "q_tokens" in la.la_last_error()
+    o.q_tokens = 17                    # contexts of 16 cannot hold 17 new tokens
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "new tokens" in la.la_last_error()
+    o.q_tokens = -1
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
