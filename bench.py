@@ -73,11 +73,11 @@ class HipEvents:
 def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
     """Host-observed µs/step and mean kernel µs (HIP events around the kernels)."""
     B, H, d = inp.B, inp.H, inp.d
-    out = torch.empty((B, H, d), dtype=torch.float32, device=inp.q.device)
+    out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device=inp.q.device)
 
     def call(ev0=None, ev1=None):
         la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, B, H, d, inp.scale, out, kind=kind,
-                        ev_start=ev0, ev_stop=ev1, kv_heads=inp.Hk, **opts)
+                        ev_start=ev0, ev_stop=ev1, kv_heads=inp.Hk, q_tokens=inp.Nq, **opts)
 
     for _ in range(warmup):
         call()
@@ -148,9 +148,9 @@ def occupancy(la, torch, inp, kind, blocks, **opts):
     fraction of the kernel's span (first entry to last exit)."""
     import numpy as np
     ts = torch.zeros(blocks * 4, dtype=torch.int64, device=inp.q.device)
-    out = torch.empty((inp.B, inp.H, inp.d), dtype=torch.float32, device=inp.q.device)
+    out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device=inp.q.device)
     la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
-                    kind=kind, cta_timestamps=ts, kv_heads=inp.Hk, **opts)
+                    kind=kind, cta_timestamps=ts, kv_heads=inp.Hk, q_tokens=inp.Nq, **opts)
     la.la_sync_check()
     a = ts.view(blocks, 4).cpu().numpy().astype(np.int64)
     start, end, ids = a[:, 0], a[:, 1], a[:, 2]
@@ -183,34 +183,37 @@ def occupancy(la, torch, inp, kind, blocks, **opts):
 
 
 def cpu_baseline(inp, budget_s=12.0):
-    """fp64 oracle on whole heads of the workload until ~budget_s of wall time,
-    scaled by (all heads / heads done) to microseconds per step."""
+    """fp64 oracle on whole query rows of the workload until ~budget_s of wall
+    time, scaled by (all head-tokens / head-tokens done) to microseconds per
+    step. A query row is (request, head), or (request, new token, head) with
+    several new tokens; it attends over its visible prefix of the cache."""
     import numpy as np
 
     import oracle
     import workloads as W
 
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    B, H, Hk = inp.B, inp.H, inp.Hk
+    B, H, Hk, Nq = inp.B, inp.H, inp.Hk, inp.Nq
     g = H // Hk
     starts = np.concatenate([[0], np.cumsum(inp.ctx_lens)]) * Hk
-    qb = W.to_bits(inp.q)
-    heads = [(b, h) for b in range(B) for h in range(H)]
+    qb = W.to_bits(inp.q).reshape(B, Nq, H, inp.d)
+    heads = [(b, t, h) for b in range(B) for t in range(Nq) for h in range(H)]
     done = 0
     tokens_done = 0
     spent = 0.0
     i = 0
     while i < len(heads) and spent < budget_s:
         batch = heads[i:i + workers]
-        # host copies of just these heads, made outside the timed region
+        # host copies of just these rows, made outside the timed region
         ks, vs, lens, qs = [], [], [], []
-        for (b, h) in batch:
+        for (b, t, h) in batch:
             n = inp.ctx_lens[b]
+            vis = n - Nq + 1 + t
             r0 = int(starts[b]) + (h // g) * n
-            ks.append(W.to_bits(inp.k[r0:r0 + n]))
-            vs.append(W.to_bits(inp.v[r0:r0 + n]))
-            lens.append(n)
-            qs.append(qb[b, h])
+            ks.append(W.to_bits(inp.k[r0:r0 + vis]))
+            vs.append(W.to_bits(inp.v[r0:r0 + vis]))
+            lens.append(vis)
+            qs.append(qb[b, t, h])
         kcat, vcat = np.concatenate(ks), np.concatenate(vs)
         qcat = np.stack(qs)[:, None, :]
         t0 = time.perf_counter()
@@ -220,7 +223,7 @@ def cpu_baseline(inp, budget_s=12.0):
         tokens_done += sum(lens)
         i += len(batch)
         del ks, vs, kcat, vcat
-    total_tokens = H * sum(inp.ctx_lens)
+    total_tokens = H * sum(Nq * n - Nq * (Nq - 1) // 2 for n in inp.ctx_lens)
     value = spent * 1e6 * total_tokens / tokens_done
     cpu = "unknown"
     try:
@@ -235,7 +238,8 @@ def cpu_baseline(inp, budget_s=12.0):
         "unit": "us/step",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"{done} of {B * H} heads ({tokens_done} of {total_tokens} head-tokens), "
+        "sample": f"{done} of {len(heads)} query rows ({tokens_done} of {total_tokens} "
+                  f"head-tokens), "
                   f"fp64 two-pass numpy oracle, {spent:.1f} s wall, scaled by head-tokens; "
                   f"host {cpu}",
     }
@@ -248,7 +252,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="512k",
                     choices=["tiny", "65k", "512k", "ragged", "many-heads", "gqa-512k",
-                             "gqa8-ragged", "mqa-32k"])
+                             "gqa8-ragged", "mqa-32k", "spec4-ragged", "spec8-64k"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
@@ -277,11 +281,12 @@ def main():
     dt_code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
     G = la.la_default_grid(w.d, dt_code)
     L = la.la_default_tile(w.d)
-    Hk = inp.Hk
-    g = inp.H // Hk
-    units = inp.H if g == 1 else Hk * ((g + 15) // 16)   # schedule units per request
+    Hk, Nq = inp.Hk, inp.Nq
+    cols = inp.H // Hk * Nq                                # query columns per K/V head
+    grouped = cols > 1
+    units = Hk * ((cols + 15) // 16) if grouped else inp.H  # schedule units per request
     I, Gu, _ = la.la_schedule_dims(inp.ctx_lens, units, L, G)
-    alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d, kv_heads=Hk)
+    alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d, kv_heads=Hk, q_tokens=Nq)
     log(f"[bench] lens={inp.ctx_lens} I={I} G={Gu} L={L} bytes={alg_bytes}")
 
     log("[bench] timing lean")
@@ -341,6 +346,10 @@ def main():
         "gqa8-ragged": "gqa8-ragged: B=16, H=64 over 8 K/V heads, d=128, n_b log-uniform "
                        "in [1024, 262144], bf16",
         "mqa-32k": "mqa-32k: B=8, H=16 over 1 K/V head, d=64, n=32768, fp16",
+        "spec4-ragged": "spec4-ragged: B=16, 4 new tokens each, H=32 over 8 K/V heads, d=128, "
+                        "n_b log-uniform in [1024, 262144], causal among the new tokens, bf16",
+        "spec8-64k": "spec8-64k: B=4, 8 new tokens each, H=32, d=128, n=65536, causal among "
+                     "the new tokens, bf16",
     }[args.workload]
     rec = {
         "metric": METRIC,
@@ -357,7 +366,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": desc,
-            "B": inp.B, "H": inp.H, "kv_heads": Hk, "d": w.d, "ctx_lens": inp.ctx_lens,
+            "B": inp.B, "H": inp.H, "kv_heads": Hk, "q_tokens": Nq, "d": w.d,
+            "ctx_lens": inp.ctx_lens,
             "seed": args.seed,
             "inputs": w.dtype, "accumulate": "fp32", "output": "fp32",
             "kind": "lean", "grid": Gu, "tile_tokens": L, "iterations": I,
@@ -372,7 +382,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": committed_traffic(args.workload),
-            "kernel": "lean_kernel",
+            "kernel": "lean_gqa_kernel" if grouped else "lean_kernel",
             "bytes_per_launch": alg_bytes,
             "kernel_source_sha256_16": kernel_source_hash(),
         },
