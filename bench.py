@@ -245,6 +245,103 @@ def cpu_baseline(inp, budget_s=12.0):
     }
 
 
+def selector_shapes():
+    """Decode shapes for measuring kind="auto" against every kernel: one long
+    head to thousands of short ones, uniform and log-uniform lengths, d = 64
+    and 128, grouped K/V heads and several new tokens."""
+    import numpy as np
+
+    def loguni(B, lo, hi, seed):
+        u = np.random.default_rng(seed).random(B)
+        return [int(math.exp(math.log(lo) + x * math.log(hi / lo))) for x in u]
+
+    S = [dict(lens=[n], H=32, d=128, dt="bf16") for n in (4096, 65536)]
+    S += [dict(lens=[131072], H=8, d=128, dt="bf16"),
+          dict(lens=[16384] * 4, H=32, d=128, dt="bf16"),
+          dict(lens=[4096] * 16, H=32, d=128, dt="bf16"),
+          dict(lens=[4096] * 64, H=32, d=128, dt="bf16"),
+          dict(lens=[512] * 256, H=32, d=128, dt="bf16"),
+          dict(lens=[256] * 512, H=8, d=128, dt="bf16"),
+          dict(lens=[16384] * 8, H=128, d=64, dt="f16"),
+          dict(lens=[65536] * 2, H=16, d=64, dt="f16"),
+          dict(lens=loguni(4, 1024, 262144, 1), H=32, d=128, dt="bf16"),
+          dict(lens=loguni(16, 1024, 262144, 2), H=32, d=128, dt="bf16"),
+          dict(lens=loguni(128, 128, 8192, 4), H=32, d=128, dt="bf16"),
+          dict(lens=loguni(32, 256, 32768, 5), H=16, d=64, dt="f16"),
+          dict(lens=[131072], H=32, Hk=8, d=128, dt="bf16"),
+          dict(lens=[4096] * 32, H=32, Hk=8, d=128, dt="bf16"),
+          dict(lens=[2048] * 64, H=64, Hk=8, d=128, dt="bf16"),
+          dict(lens=[32768] * 8, H=16, Hk=1, d=64, dt="f16"),
+          dict(lens=loguni(16, 1024, 262144, 6), H=32, Hk=4, d=128, dt="bf16"),
+          dict(lens=loguni(16, 1024, 65536, 7), H=32, Hk=8, Nq=4, d=128, dt="bf16"),
+          dict(lens=[8192] * 32, H=32, Nq=4, d=128, dt="bf16")]
+    return S
+
+
+def selector_sweep(steps=10, warmup=2, rounds=3):
+    """kind="auto" against lean (one and two workgroups per CU), per-head and
+    fixed-split (heuristic K and K = 2..32) on every selector shape; prints one
+    JSON line with each shape's kernel times and auto's regret (its kernel
+    time over the fastest)."""
+    import torch
+
+    import decode_phase_attention_amd as la
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    la.lib()
+    evs = HipEvents()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = []
+    for i, s in enumerate(selector_shapes()):
+        Hk, Nq = s.get("Hk", s["H"]), s.get("Nq", 1)
+        log(f"[selector {i}] B={len(s['lens'])} H={s['H']} Hk={Hk} Nq={Nq} d={s['d']} "
+            f"N={sum(s['lens'])}")
+        inp = W.make_custom(s["lens"], s["H"], s["d"], s["dt"], seed=0, device="cuda",
+                            kv_heads=Hk, q_tokens=Nq)
+        dt = la.LA_BF16 if s["dt"] == "bf16" else la.LA_F16
+        pick, grid = la.la_select(inp.ctx_lens, inp.H, inp.d, dt, kv_heads=Hk, q_tokens=Nq)
+        kinds = [("auto", "auto", {}), ("lean_1cu", "lean", {"grid": cus}),
+                 ("lean_2cu", "lean", {"grid": 2 * cus}),
+                 ("per_head", "per_head", {}), ("fixed_split_heuristic", "fixed_split", {})]
+        kinds += [(f"fixed_split_{K}", "fixed_split", {"num_splits": K}) for K in (2, 4, 8, 16, 32)]
+        # rounds over all kinds, each round starting at another kind, so that
+        # no kind is always timed first; a kind's time is its best round's median
+        t = {}
+        for r in range(rounds):
+            for j in range(len(kinds)):
+                tag, kind, o = kinds[(j + r * 3) % len(kinds)]
+                try:
+                    us = time_kind(la, torch, evs, inp, kind, steps, warmup, **o)["kernel_us_p50"]
+                except la.LaError:
+                    continue                   # grid above the kernel's co-resident capacity
+                t[tag] = round(min(us, t.get(tag, float("inf"))), 2)
+        best = min((v, k) for k, v in t.items() if k != "auto")
+        # auto runs the same kernel and grid as one explicit kind: both are
+        # samples of that configuration
+        same = "per_head" if pick == "per_head" else ("lean_1cu" if grid == cus else "lean_2cu")
+        auto_us = min(t["auto"], t.get(same, t["auto"]))
+        rows.append({"B": inp.B, "H": inp.H, "kv_heads": Hk, "q_tokens": Nq, "d": inp.d,
+                     "dtype": s["dt"], "sum_n": sum(inp.ctx_lens),
+                     "uniform": len(set(inp.ctx_lens)) == 1, "auto_pick": pick, "auto_grid": grid,
+                     "kernel_us_p50": t, "best": best[1],
+                     "auto_regret": round(auto_us / best[0], 4),
+                     "lean_1cu_regret": round(t["lean_1cu"] / best[0], 4)})
+        log(f"   auto={pick}@{grid} {t['auto']} us, best {best[1]} {best[0]} us, "
+            f"regret {rows[-1]['auto_regret']}")
+        del inp
+        torch.cuda.empty_cache()
+    reg = [r["auto_regret"] for r in rows]
+    reg1 = [r["lean_1cu_regret"] for r in rows]
+    print(json.dumps({"metric": "kind=auto kernel time over the fastest kind, per shape",
+                      "shapes": len(rows), "auto_regret_max": max(reg),
+                      "auto_regret_mean": round(sum(reg) / len(reg), 4),
+                      "lean_1cu_regret_max": max(reg1),
+                      "lean_1cu_regret_mean": round(sum(reg1) / len(reg1), 4),
+                      "device": torch.cuda.get_device_name(0), "cus": cus, "rows": rows}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,11 +357,17 @@ def main():
                     help="time only the lean kernel on the workload (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (scales the HBM counters)")
+    ap.add_argument("--selector-sweep", action="store_true",
+                    help="instead of the workload: measure kind=auto against every kind "
+                         "on a sweep of shapes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the stream-K decode path here is single-GPU)", file=sys.stderr)
         sys.exit(2)
+    if args.selector_sweep:
+        selector_sweep()
+        return
 
     import torch
 

@@ -18,7 +18,8 @@ import numpy as np
 
 __all__ = [
     "LaError", "LA_F16", "LA_BF16", "LA_KIND_LEAN", "LA_KIND_FIXED_SPLIT", "LA_KIND_PER_HEAD",
-    "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex", "la_schedule",
+    "LA_KIND_AUTO", "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex",
+    "la_select", "la_select_for", "la_schedule",
     "la_schedule_dims", "la_default_tile", "la_max_grid", "la_default_grid", "la_sync_check",
     "la_last_error",
     "la_shutdown", "la_set_wait_limit_us", "decode_attention", "LIB_PATH",
@@ -28,10 +29,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_decod
 
 LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP, LA_ETIMEOUT, LA_ENOMEM = range(6)
 LA_F16, LA_BF16 = 0, 1
-LA_KIND_LEAN, LA_KIND_FIXED_SPLIT, LA_KIND_PER_HEAD = 0, 1, 2
+LA_KIND_LEAN, LA_KIND_FIXED_SPLIT, LA_KIND_PER_HEAD, LA_KIND_AUTO = 0, 1, 2, 3
 _STATUS = {0: "LA_OK", 1: "LA_EINVAL", 2: "LA_EUNSUPPORTED", 3: "LA_EHIP", 4: "LA_ETIMEOUT",
            5: "LA_ENOMEM"}
-_KINDS = {"lean": LA_KIND_LEAN, "fixed_split": LA_KIND_FIXED_SPLIT, "per_head": LA_KIND_PER_HEAD}
+_KINDS = {"lean": LA_KIND_LEAN, "fixed_split": LA_KIND_FIXED_SPLIT, "per_head": LA_KIND_PER_HEAD,
+          "auto": LA_KIND_AUTO}
+KIND_NAMES = {v: k for k, v in _KINDS.items()}
 
 
 class LaError(RuntimeError):
@@ -76,6 +79,10 @@ _SIG = {
                               ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "la_schedule": (_I, [_I32P, _I, _I, _I, _I, _I32P, _I32P, _I32P, _I, ctypes.POINTER(_I),
                          _I32P, _I32P]),
+    "la_select_for": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I),
+                           ctypes.POINTER(_I)]),
+    "la_select": (_I, [_I32P, _I, _I, _I, ctypes.POINTER(LaOpts), ctypes.POINTER(_I),
+                       ctypes.POINTER(_I)]),
     "la_default_tile": (_I, [_I]),
     "la_max_grid": (_I, [_I, _I]),
     "la_default_grid": (_I, [_I, _I]),
@@ -231,6 +238,31 @@ def la_schedule(ctx_lens, H, tile_tokens, grid) -> dict:
                              host.ctypes.data_as(_I32P), last.ctypes.data_as(_I32P)))
     return {"I": I, "G": G, "cta_begin": cta_begin, "cta_seg": cta_seg, "seg": seg[:n.value],
             "host_cta": host, "last_cta": last}
+
+
+def la_select_for(ctx_lens, H, d, cus, coresident, kv_heads=0, q_tokens=0, tile_tokens=0):
+    """(kind name, grid) that kind="auto" picks on a device of this size (host only)."""
+    arr, p = _lens(ctx_lens)
+    kind, grid = ctypes.c_int(), ctypes.c_int()
+    _check(lib().la_select_for(p, len(arr), int(H), int(d), int(kv_heads), int(q_tokens),
+                               int(tile_tokens), int(cus), int(coresident), ctypes.byref(kind),
+                               ctypes.byref(grid)))
+    return KIND_NAMES[kind.value], grid.value
+
+
+def la_select(ctx_lens, H, d, dtype, kv_heads=0, q_tokens=0, tile_tokens=0):
+    """(kind name, grid) that kind="auto" picks on the current device."""
+    arr, p = _lens(ctx_lens)
+    o = LaOpts()
+    lib().la_opts_init(ctypes.byref(o))
+    o.dtype = int(dtype)
+    o.kv_heads = int(kv_heads)
+    o.q_tokens = int(q_tokens)
+    o.tile_tokens = int(tile_tokens)
+    kind, grid = ctypes.c_int(), ctypes.c_int()
+    _check(lib().la_select(p, len(arr), int(H), int(d), ctypes.byref(o), ctypes.byref(kind),
+                           ctypes.byref(grid)))
+    return KIND_NAMES[kind.value], grid.value
 
 
 def la_default_tile(d: int) -> int:

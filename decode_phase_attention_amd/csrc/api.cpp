@@ -19,6 +19,7 @@
 #include "la_decode.h"
 #include "kernels.h"
 #include "sched.h"
+#include "select.h"
 
 namespace {
 
@@ -459,6 +460,23 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
     return LA_OK;
 }
 
+// la_select_for with the current device's CU count and lean capacity.
+la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int d,
+                           const la_opts& o, int* kind, int* grid) {
+    Capacity cap;
+    la_status st = capacity(o.dtype, d, hd.grouped, &cap);
+    if (st != LA_OK) return st;
+    int dev = 0, cus = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
+    const char* why = "";
+    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, cus, cap.coresident, kind,
+                                   grid, &why);
+    if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+    return LA_OK;
+}
+
 void free_workspace(Workspace* w) {
     hipSetDevice(w->device);
     hipDeviceSynchronize();
@@ -491,8 +509,11 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     if (opts != nullptr) o = *opts;
     la_status st = validate(q, k, v, ctx_lens, B, H, d, scale, out, o.dtype);
     if (st != LA_OK) return st;
-    if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_FIXED_SPLIT && o.kind != LA_KIND_PER_HEAD)
+    if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_FIXED_SPLIT && o.kind != LA_KIND_PER_HEAD &&
+        o.kind != LA_KIND_AUTO)
         return fail(LA_EINVAL, "unknown kind %d", o.kind);
+    if (o.kind == LA_KIND_AUTO && (o.tile_owner != nullptr || o.cta_timestamps != nullptr))
+        return fail(LA_EINVAL, "tile_owner and cta_timestamps need an explicit kind");
     if (o.tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");
     if (o.kind != LA_KIND_LEAN && o.tile_owner != nullptr)
         return fail(LA_EINVAL, "tile_owner applies to the lean kind only");
@@ -509,6 +530,12 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
     std::lock_guard<std::mutex> lock(g_mu);
+    if (o.kind == LA_KIND_AUTO) {
+        int kind = 0, grid = 0;
+        if ((st = select_on_device(ctx_lens, B, hd, d, o, &kind, &grid)) != LA_OK) return st;
+        o.kind = kind;
+        if (o.grid == 0) o.grid = grid;
+    }
     Workspace* w = nullptr;
     if ((st = get_workspace((hipStream_t)stream, &w)) != LA_OK) return st;
     if (o.kind == LA_KIND_LEAN) return run_lean(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
@@ -559,6 +586,47 @@ la_status la_schedule(const int32_t* ctx_lens, int B, int H, int tile_tokens, in
     *n_seg = la::build_schedule(ctx_lens, B, H, tile_tokens, G, I, cta_begin, cta_seg, seg,
                                 nullptr, host_cta, last_cta);
     return LA_OK;
+}
+
+la_status la_select_for(const int32_t* ctx_lens, int B, int H, int d, int kv_heads, int q_tokens,
+                        int tile_tokens, int cus, int coresident, int* kind, int* grid) {
+    g_msg[0] = 0;
+    if (ctx_lens == nullptr || kind == nullptr || grid == nullptr)
+        return fail(LA_EINVAL, "null pointer argument");
+    if (B < 1 || H < 1) return fail(LA_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+    if (d != 64 && d != 128) return fail(LA_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
+    if (kv_heads < 0 || (kv_heads > 0 && H % kv_heads != 0))
+        return fail(LA_EINVAL, "kv_heads %d must divide H = %d", kv_heads, H);
+    if (q_tokens < 0 || q_tokens > kMaxQTokens)
+        return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", q_tokens, kMaxQTokens);
+    if (tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");
+    const Heads hd = heads_of(H, kv_heads, q_tokens);
+    const int L = tile_tokens > 0 ? tile_tokens : la::chunk_rows(d);
+    const char* why = "";
+    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, cus, coresident, kind, grid,
+                                   &why);
+    if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+    return LA_OK;
+}
+
+la_status la_select(const int32_t* ctx_lens, int B, int H, int d, const la_opts* opts, int* kind,
+                    int* grid) {
+    g_msg[0] = 0;
+    la_opts o;
+    la_opts_init(&o);
+    if (opts != nullptr) o = *opts;
+    if (ctx_lens == nullptr || kind == nullptr || grid == nullptr)
+        return fail(LA_EINVAL, "null pointer argument");
+    if (B < 1 || H < 1) return fail(LA_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+    if (d != 64 && d != 128) return fail(LA_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
+    if (o.dtype != LA_F16 && o.dtype != LA_BF16) return fail(LA_EINVAL, "unknown dtype %d", o.dtype);
+    if (o.kv_heads < 0 || (o.kv_heads > 0 && H % o.kv_heads != 0))
+        return fail(LA_EINVAL, "kv_heads %d must divide H = %d", o.kv_heads, H);
+    if (o.q_tokens < 0 || o.q_tokens > kMaxQTokens)
+        return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", o.q_tokens, kMaxQTokens);
+    if (o.tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");
+    std::lock_guard<std::mutex> lock(g_mu);
+    return select_on_device(ctx_lens, B, heads_of(H, o.kv_heads, o.q_tokens), d, o, kind, grid);
 }
 
 int la_default_tile(int d) { return (d == 64 || d == 128) ? la::chunk_rows(d) : 0; }

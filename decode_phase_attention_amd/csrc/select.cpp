@@ -1,0 +1,63 @@
+// Shape-driven selection among the decompositions (siliconandsystems digest,
+// "A useful control policy": pick a FlashAttention-style, fixed-split or
+// stream-K schedule from the actual shape; xllm-io paper review §4.3: the
+// stream-K schedule reduces to the per-head one when every workgroup holds
+// whole heads, and to a fixed split of K = G / (B H) pieces when the lengths
+// are uniform and B H divides G).
+//
+// The choice, from measurements of all three kernels over shapes from one
+// 512k-token head to thousands of 256-token heads:
+//   1. Grid. One lean workgroup per CU keeps a CU's loads in flight from a
+//      single stream, which is fastest while a workgroup's range holds few
+//      heads. With at least two heads per CU, every workgroup switches heads,
+//      and the fixed costs of a switch (loading q, the cross-wave fold, the
+//      epilogue) stall a CU that runs one workgroup; two per CU hide them.
+//   2. Kind. If the lean schedule on that grid splits no head, every
+//      workgroup holds whole heads: the per-head decomposition (review §4.3's
+//      FlashAttention-2 case) does the same work with no tables, partials or
+//      flags, and the hardware dispatcher balances it, so per head is chosen
+//      -- provided heads average at least kMinTilesPerHead tiles. Shorter
+//      heads make per-head workgroups spend a large share of their life in
+//      their prologue and epilogue, which the persistent grid amortises over
+//      many heads (measured: 2-tile heads 6% faster on lean). Otherwise lean.
+//      A fixed split is never chosen: on uniform lengths the lean schedule
+//      already is the best fixed split, in one launch instead of two, and on
+//      ragged lengths its balance is better.
+#include "select.h"
+
+#include <vector>
+
+#include "sched.h"
+
+namespace la {
+
+constexpr int64_t kMinTilesPerHead = 8;
+
+int select_kind(const int32_t* ctx_lens, int B, int units, int L, int cus, int coresident,
+                int* kind, int* grid, const char** why) {
+    if (cus < 1 || coresident < 1 || B < 1 || units < 1) {
+        *why = "select: cus, coresident, B and units must be >= 1";
+        return 1;
+    }
+    const int64_t U = (int64_t)B * units;
+    int G = U >= 2 * (int64_t)cus ? 2 * cus : cus;
+    if (G > coresident) G = coresident;
+    int64_t I = 0;
+    int Gu = 0, rows = 0;
+    const int rc = schedule_dims(ctx_lens, B, units, L, G, &I, &Gu, &rows, why);
+    if (rc != 0) return rc;
+    thread_local std::vector<int32_t> cb, cs, host, last;
+    cb.resize((size_t)Gu + 1);
+    cs.resize((size_t)Gu + 1);
+    host.resize((size_t)U);
+    last.resize((size_t)U);
+    build_schedule(ctx_lens, B, units, L, Gu, I, cb.data(), cs.data(), nullptr, nullptr,
+                   host.data(), last.data());
+    bool split = false;
+    for (int64_t u = 0; u < U && !split; ++u) split = host[u] != last[u];
+    *kind = (split || I < kMinTilesPerHead * U) ? 0 : 2;
+    *grid = G;
+    return 0;
+}
+
+}  // namespace la

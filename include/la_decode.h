@@ -72,7 +72,8 @@ typedef enum { LA_F16 = 0, LA_BF16 = 1 } la_dtype;
 typedef enum {
     LA_KIND_LEAN = 0,         /* stream-K over a persistent grid, one launch */
     LA_KIND_FIXED_SPLIT = 1,  /* each head cut into num_splits pieces + a combine launch */
-    LA_KIND_PER_HEAD = 2      /* one workgroup per (request, head), whole context */
+    LA_KIND_PER_HEAD = 2,     /* one workgroup per (request, head), whole context */
+    LA_KIND_AUTO = 3          /* one of the above, chosen from the shape (la_select) */
 } la_kind;
 
 /*
@@ -95,7 +96,9 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
 /*
  * Options for la_decode_ex. Zero-initialise (or call la_opts_init) and set
  * what you need.
- *   kind        la_kind
+ *   kind        la_kind. LA_KIND_AUTO resolves kind and (if grid is 0) the
+ *               grid with la_select; it takes no tile_owner or
+ *               cta_timestamps, since those depend on the kind
  *   tile_tokens LeanTile size in tokens; 0 = library default for d
  *   grid        lean: workgroups in the persistent grid; 0 = la_default_grid
  *               (one per CU); larger than la_max_grid -> LA_EINVAL
@@ -166,6 +169,32 @@ void la_opts_init(la_opts* opts);
 la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* ctx_lens, int B, int H, int d, float scale,
                        float* out, void* stream, const la_opts* opts);
+
+/*
+ * la_select_for: the kind and lean grid that LA_KIND_AUTO uses, for a device
+ * with `cus` compute units whose lean kernel fits `coresident` workgroups at
+ * once. Host only: reads nothing from a device. A shape-driven control policy
+ * in the spirit of the siliconandsystems digest ("A useful control policy"),
+ * built on the reductions of xllm-io paper review §4.3:
+ *   grid  = 2*cus if B * units >= 2*cus (at least two heads per CU, whose
+ *           switches a second workgroup per CU hides), else cus; capped at
+ *           coresident. units = H, or with kv_heads / q_tokens the grouped
+ *           units (K/V head x block of 16 query columns).
+ *   kind  = LA_KIND_PER_HEAD if the lean schedule on that grid splits no
+ *           head (every workgroup holds whole heads) and heads average at
+ *           least 8 tiles, else LA_KIND_LEAN. LA_KIND_FIXED_SPLIT is never
+ *           chosen.
+ * tile_tokens 0 = la_default_tile(d). Returns LA_EINVAL on bad arguments
+ * (as la_decode_ex validates kv_heads, q_tokens, d), LA_EUNSUPPORTED if the
+ * iteration count does not fit in int32.
+ */
+la_status la_select_for(const int32_t* ctx_lens, int B, int H, int d, int kv_heads, int q_tokens,
+                        int tile_tokens, int cus, int coresident, int* kind, int* grid);
+
+/* la_select: la_select_for on the current device, with d, dtype, kv_heads,
+ * q_tokens and tile_tokens taken from `opts` (which may be null: defaults). */
+la_status la_select(const int32_t* ctx_lens, int B, int H, int d, const la_opts* opts, int* kind,
+                    int* grid);
 
 /*
  * la_schedule_dims: sizes of the stream-K tables for a batch, host only.
