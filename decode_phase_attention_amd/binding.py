@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "LaError", "LA_F16", "LA_BF16", "LA_KIND_LEAN", "LA_KIND_FIXED_SPLIT", "LA_KIND_PER_HEAD",
-    "LA_KIND_AUTO", "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex",
+    "LA_KIND_AUTO", "LA_KIND_PULL", "LA_KIND_CHUNKS", "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex",
     "la_select", "la_select_for", "la_schedule",
     "la_schedule_dims", "la_default_tile", "la_max_grid", "la_default_grid", "la_sync_check",
     "la_last_error",
@@ -30,10 +30,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_decod
 LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP, LA_ETIMEOUT, LA_ENOMEM = range(6)
 LA_F16, LA_BF16 = 0, 1
 LA_KIND_LEAN, LA_KIND_FIXED_SPLIT, LA_KIND_PER_HEAD, LA_KIND_AUTO = 0, 1, 2, 3
+LA_KIND_PULL, LA_KIND_CHUNKS = 4, 5
 _STATUS = {0: "LA_OK", 1: "LA_EINVAL", 2: "LA_EUNSUPPORTED", 3: "LA_EHIP", 4: "LA_ETIMEOUT",
            5: "LA_ENOMEM"}
 _KINDS = {"lean": LA_KIND_LEAN, "fixed_split": LA_KIND_FIXED_SPLIT, "per_head": LA_KIND_PER_HEAD,
-          "auto": LA_KIND_AUTO}
+          "auto": LA_KIND_AUTO, "pull": LA_KIND_PULL, "chunks": LA_KIND_CHUNKS}
 KIND_NAMES = {v: k for k, v in _KINDS.items()}
 
 
@@ -59,6 +60,7 @@ class LaOpts(ctypes.Structure):
         ("ev_stop", ctypes.c_void_p),
         ("kv_heads", ctypes.c_int),
         ("q_tokens", ctypes.c_int),
+        ("chunk_tiles", ctypes.c_int),
     ]
 
 
@@ -189,7 +191,7 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
 def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
-                 ev_stop=None, kv_heads=0, q_tokens=0):
+                 ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0):
     o = LaOpts()
     lib().la_opts_init(ctypes.byref(o))
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
@@ -206,6 +208,7 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
     o.ev_stop = ev_stop
     o.kv_heads = int(kv_heads or 0)
     o.q_tokens = int(q_tokens or 0)
+    o.chunk_tiles = int(chunk_tiles or 0)
     arr, p = _lens(ctx_lens)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))

@@ -11,6 +11,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -53,12 +54,18 @@ struct Workspace {
     int device = 0;
     hipStream_t stream = nullptr;
     float* part = nullptr;          // lean partial records
-    size_t part_cap = 0;            // floats
+    size_t part_cap = 0;            // bytes
     uint32_t* flags = nullptr;      // one per lean workgroup, zero between launches
     size_t flags_cap = 0;
     uint32_t* err = nullptr;        // device error word
     float* split_part = nullptr;    // fixed-split partial records
     size_t split_cap = 0;
+    float* pull_part = nullptr;     // dynamic-pull partial records, two per chunk
+    size_t pull_part_cap = 0;
+    uint32_t* arrive = nullptr;     // dynamic pull: pieces arrived per head, zero between launches
+    size_t arrive_cap = 0;
+    uint32_t* pull_ctr = nullptr;   // dynamic pull: next chunk, workgroups done; zero between launches
+    size_t pull_ctr_cap = 0;
     void* tables = nullptr;         // device copy of the schedule tables
     size_t tables_cap = 0;
     std::vector<char> last_tables;  // host copy of what `tables` holds (valid while non-empty)
@@ -80,6 +87,7 @@ std::map<std::pair<int, const void*>, Capacity> g_capacity;
 // 1 per CU streams fastest on the long-context and ragged workloads).
 constexpr int kWgPerCu = 1;
 constexpr int kMaxQTokens = 64;
+constexpr int kMaxPullGrid = 65536;
 uint32_t g_wait_us = kDefaultWaitUs;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -460,6 +468,94 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
     return LA_OK;
 }
 
+// Dynamic tile pull (LA_KIND_PULL) and one chunk per workgroup
+// (LA_KIND_CHUNKS): the tile sequence of the lean schedule cut into fixed
+// chunks; heads spanning chunks are merged by their last piece's workgroup.
+la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
+                   const int32_t* ctx_lens, int B, const Heads& hd, int d, float scale,
+                   float* out, const la_opts& o) {
+    Capacity cap;
+    la_status st = capacity(o.dtype, d, false, &cap);
+    if (st != LA_OK) return st;
+    const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
+    const int U = hd.units_per_req();
+    const int BU = B * U;
+    int64_t I = 0;
+    for (int b = 0; b < B; ++b) I += (int64_t)U * ((ctx_lens[b] + L - 1) / L);
+    if (I > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "%lld tile iterations do not fit", (long long)I);
+    const bool dynamic = o.kind == LA_KIND_PULL;
+    // default chunk: about four chunks per workgroup of a one-per-CU grid
+    const int G0 = dynamic && o.grid > 0 ? o.grid : cap.preferred;
+    int C = o.chunk_tiles;
+    if (C == 0) C = (int)std::max<int64_t>(1, (I + 4 * (int64_t)G0 - 1) / (4 * (int64_t)G0));
+    const int64_t nchunks = (I + C - 1) / C;
+    if (nchunks > kMaxPullGrid * 64) return fail(LA_EUNSUPPORTED, "too many chunks (%lld)", (long long)nchunks);
+    const int grid = dynamic ? (int)std::min<int64_t>(G0, nchunks) : (int)nchunks;
+
+    const size_t off_start = 0;
+    const size_t off_chunk = align16(off_start + 4 * ((size_t)BU + 1));
+    const ReqLayout rl = req_layout(off_chunk + 4 * (size_t)nchunks, B);
+    g_build.assign(rl.bytes, 0);
+    char* hb = g_build.data();
+    int32_t* S = (int32_t*)(hb + off_start);
+    int32_t* CH = (int32_t*)(hb + off_chunk);
+    {
+        int64_t acc = 0;
+        int u = 0;
+        for (int b = 0; b < B; ++b) {
+            const int T = (ctx_lens[b] + L - 1) / L;
+            for (int h = 0; h < U; ++h, ++u) {
+                S[u] = (int32_t)acc;
+                acc += T;
+            }
+        }
+        S[BU] = (int32_t)acc;
+        int head = 0;
+        for (int64_t c = 0; c < nchunks; ++c) {
+            while (S[head + 1] <= c * C) ++head;
+            CH[c] = head;
+        }
+    }
+    fill_req(hb, rl, ctx_lens, B);
+
+    if ((st = grow(w, (void**)&w.pull_part, &w.pull_part_cap,
+                   sizeof(float) * 2 * (size_t)nchunks * la::part_stride(d), false)) != LA_OK)
+        return st;
+    if ((st = grow(w, (void**)&w.arrive, &w.arrive_cap, sizeof(uint32_t) * (size_t)BU, true)) != LA_OK)
+        return st;
+    if ((st = grow(w, (void**)&w.pull_ctr, &w.pull_ctr_cap, 2 * sizeof(uint32_t), true)) != LA_OK)
+        return st;
+    if ((st = upload(w, hb, rl.bytes)) != LA_OK) return st;
+    char* db = (char*)w.tables;
+    la::PullArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.out = out;
+    a.m_out = o.m_out;
+    a.l_out = o.l_out;
+    a.ctx = (const int32_t*)(db + rl.off_ctx);
+    a.tok_off = (const int64_t*)(db + rl.off_tok);
+    a.head_start = (const int32_t*)(db + off_start);
+    a.chunk_head = (const int32_t*)(db + off_chunk);
+    a.part = w.pull_part;
+    a.arrive = w.arrive;
+    a.pull = w.pull_ctr;
+    a.tile_owner = o.tile_owner;
+    a.ts = o.cta_timestamps;
+    a.H = hd.H;
+    a.L = L;
+    a.C = C;
+    a.I = (int)I;
+    a.nchunks = (int)nchunks;
+    a.dynamic = dynamic ? 1 : 0;
+    a.sl2e = scale * 1.4426950408889634f;
+    if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
+    HIP_TRY(la::launch_pull(o.dtype, d, a, grid, w.stream));
+    if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+    return LA_OK;
+}
+
 // la_select_for with the current device's CU count and lean capacity.
 la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int d,
                            const la_opts& o, int* kind, int* grid) {
@@ -484,6 +580,9 @@ void free_workspace(Workspace* w) {
     hipFree(w->flags);
     hipFree(w->err);
     hipFree(w->split_part);
+    hipFree(w->pull_part);
+    hipFree(w->arrive);
+    hipFree(w->pull_ctr);
     hipFree(w->tables);
     for (auto& s : w->ring) {
         if (s.host != nullptr) hipHostFree(s.host);
@@ -510,15 +609,23 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     la_status st = validate(q, k, v, ctx_lens, B, H, d, scale, out, o.dtype);
     if (st != LA_OK) return st;
     if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_FIXED_SPLIT && o.kind != LA_KIND_PER_HEAD &&
-        o.kind != LA_KIND_AUTO)
+        o.kind != LA_KIND_AUTO && o.kind != LA_KIND_PULL && o.kind != LA_KIND_CHUNKS)
         return fail(LA_EINVAL, "unknown kind %d", o.kind);
     if (o.kind == LA_KIND_AUTO && (o.tile_owner != nullptr || o.cta_timestamps != nullptr))
         return fail(LA_EINVAL, "tile_owner and cta_timestamps need an explicit kind");
     if (o.tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");
-    if (o.kind != LA_KIND_LEAN && o.tile_owner != nullptr)
-        return fail(LA_EINVAL, "tile_owner applies to the lean kind only");
+    if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_PULL && o.kind != LA_KIND_CHUNKS &&
+        o.tile_owner != nullptr)
+        return fail(LA_EINVAL, "tile_owner applies to the lean and pull kinds only");
     if (o.kind == LA_KIND_FIXED_SPLIT && o.cta_timestamps != nullptr && o.num_splits < 1)
         return fail(LA_EINVAL, "cta_timestamps with fixed_split needs an explicit num_splits");
+    if (o.chunk_tiles < 0) return fail(LA_EINVAL, "chunk_tiles must be >= 0");
+    if ((o.kind == LA_KIND_PULL || o.kind == LA_KIND_CHUNKS) && (o.grid < 0 || o.grid > kMaxPullGrid))
+        return fail(LA_EINVAL, "grid %d outside [0, %d]", o.grid, kMaxPullGrid);
+    if (o.kind == LA_KIND_PULL && o.cta_timestamps != nullptr && o.grid < 1)
+        return fail(LA_EINVAL, "cta_timestamps with pull needs an explicit grid");
+    if (o.kind == LA_KIND_CHUNKS && o.cta_timestamps != nullptr && o.chunk_tiles < 1)
+        return fail(LA_EINVAL, "cta_timestamps with chunks needs an explicit chunk_tiles");
     if (o.kv_heads < 0 || (o.kv_heads > 0 && H % o.kv_heads != 0))
         return fail(LA_EINVAL, "kv_heads %d must divide H = %d", o.kv_heads, H);
     if (o.q_tokens < 0 || o.q_tokens > kMaxQTokens)
@@ -529,6 +636,9 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
                         b, ctx_lens[b], o.q_tokens);
     const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
+    if ((o.kind == LA_KIND_PULL || o.kind == LA_KIND_CHUNKS) && hd.grouped)
+        return fail(LA_EUNSUPPORTED, "the pull kinds take one query column per K/V head "
+                                     "(no kv_heads < H, no q_tokens > 1)");
     std::lock_guard<std::mutex> lock(g_mu);
     if (o.kind == LA_KIND_AUTO) {
         int kind = 0, grid = 0;
@@ -539,6 +649,8 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     Workspace* w = nullptr;
     if ((st = get_workspace((hipStream_t)stream, &w)) != LA_OK) return st;
     if (o.kind == LA_KIND_LEAN) return run_lean(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
+    if (o.kind == LA_KIND_PULL || o.kind == LA_KIND_CHUNKS)
+        return run_pull(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
     return run_split_or_head(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
 }
 

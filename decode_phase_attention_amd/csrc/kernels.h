@@ -103,7 +103,40 @@ struct GqaArgs {
     uint64_t wait_ticks;
 };
 
+// Dynamic tile pull. The linearised tile sequence (as in the lean schedule)
+// is cut into fixed chunks of C tiles; workgroups take chunks from an atomic
+// counter (dynamic) or one chunk each (grid = nchunks). A head spanning
+// several chunks leaves one partial record per chunk, at slot (chunk, side):
+// side 0 if its piece starts the chunk, else 1. The workgroup whose piece
+// arrives last (per-head arrival counter) merges the head's pieces in chunk
+// order and writes the output; nothing ever waits.
+struct PullArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    float* out;
+    float* m_out;
+    float* l_out;
+    const int32_t* ctx;        // [B]
+    const int64_t* tok_off;    // [B]
+    const int32_t* head_start; // [BU + 1]: first tile iteration of each head; [BU] = I
+    const int32_t* chunk_head; // [nchunks]: head holding the chunk's first tile
+    float* part;               // [nchunks * 2 * part_stride(d)]
+    uint32_t* arrive;          // [BU], zero at launch and at exit
+    uint32_t* pull;            // [2]: next chunk, workgroups done; zero at launch and at exit
+    int32_t* tile_owner;       // optional [I]
+    uint64_t* ts;              // optional [grid*4]
+    int H;
+    int L;
+    int C;                     // tiles per chunk
+    int I;                     // tile iterations
+    int nchunks;
+    int dynamic;               // 1: pull chunks from the counter; 0: chunk = blockIdx.x
+    float sl2e;
+};
+
 const void* lean_kernel_ptr(int dtype, int d);
+hipError_t launch_pull(int dtype, int d, const PullArgs& a, int grid, hipStream_t s);
 const void* lean_gqa_kernel_ptr(int dtype, int d);
 hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,
                            bool cooperative);

@@ -349,6 +349,122 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     stamp_end(a.ts, c);
 }
 
+// ------------------------------------------------------------------ dynamic pull
+
+// Stream-K over fixed chunks of the tile sequence, taken dynamically (the
+// digest's CTAs that pull the next tile instead of holding a fixed split) or
+// one per workgroup (a non-persistent grid). Pieces of a head that spans
+// several chunks are merged by whichever workgroup finishes the last of them,
+// in chunk order, so the result does not depend on which workgroup took which
+// chunk. No workgroup waits for another: any grid size is safe.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
+    using G = Geo<D>;
+    constexpr int P = kDpl<D>;
+    __shared__ Smem<D> sm;
+    __shared__ int s_chunk;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int grp = (t >> 6) * G::GPW + lane / G::LPR;
+    const int sub = lane % G::LPR;
+    stamp_start(a.ts, blockIdx.x);
+    int next = blockIdx.x;
+    for (;;) {
+        int k;
+        if (a.dynamic) {
+            if (t == 0)
+                s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            k = s_chunk;
+            __syncthreads();
+        } else {
+            k = next;
+            next = a.nchunks;
+        }
+        if (k >= a.nchunks) break;
+        const int c0 = k * a.C;
+        const int c1 = min(c0 + a.C, a.I);
+        int u = a.chunk_head[k];
+        for (int it = c0; it < c1; ++u) {
+            const int Su = a.head_start[u], Se = a.head_start[u + 1];
+            const int t1 = min(Se, c1);
+            const int b = u / a.H;
+            const int h = u - b * a.H;
+            const int n = a.ctx[b];
+            const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
+            const int tok0 = (it - Su) * a.L;
+            const int tok1 = (int)min((int64_t)(t1 - Su) * a.L, (int64_t)n);
+            Acc acc;
+            acc_init(acc);
+            stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1,
+                                load_q(a.q, u, D, sub), a.sl2e, grp, sub, acc);
+            if (a.tile_owner != nullptr)
+                for (int i = it + t; i < t1; i += kThreads) a.tile_owner[i] = blockIdx.x;
+            float M = kNegInf, Ls = 0.f, O[P];
+            wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+            const int side = it == c0 ? 0 : 1;
+            it = t1;
+            if (t >= 64) continue;   // the epilogue is wave 0's
+
+            const int kf = Su / a.C, kl = (Se - 1) / a.C;   // chunks holding head u
+            if (kf != kl) {
+                // one piece of a head spread over chunks kf..kl: publish it,
+                // then count it in; the last piece's workgroup merges them all
+                float* p = a.part + ((int64_t)k * 2 + side) * part_stride(D);
+#pragma unroll
+                for (int j = 0; j < P; ++j) store_agent(p + lane + 64 * j, O[j]);
+                if (lane == 0) {
+                    store_agent(p + D, M);
+                    store_agent(p + D + 1, Ls);
+                }
+                drain_stores();
+                uint32_t before = 0;
+                if (lane == 0)
+                    before = __hip_atomic_fetch_add(&a.arrive[u], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+                before = __shfl(before, 0);
+                if (before != (uint32_t)(kl - kf)) continue;
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                M = kNegInf;
+                Ls = 0.f;
+#pragma unroll
+                for (int j = 0; j < P; ++j) O[j] = 0.f;
+                constexpr int kBatch = 16;
+                for (int j0 = kf; j0 <= kl; j0 += kBatch) {
+                    float pm[kBatch], pl[kBatch], po[kBatch][P];
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j) {
+                        const int ch = min(j0 + j, kl);
+                        const int sd = max(Su, ch * a.C) == ch * a.C ? 0 : 1;
+                        const float* rp = a.part + ((int64_t)ch * 2 + sd) * part_stride(D);
+                        pm[j] = load_agent(rp + D);
+                        pl[j] = load_agent(rp + D + 1);
+#pragma unroll
+                        for (int x = 0; x < P; ++x) po[j][x] = load_agent(rp + lane + 64 * x);
+                    }
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j)
+                        if (j0 + j <= kl) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
+                }
+                if (lane == 0)
+                    __hip_atomic_store(&a.arrive[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
+        }
+    }
+    if (a.dynamic && t == 0) {
+        // the last workgroup out re-arms the counters for the next launch
+        const uint32_t done = __hip_atomic_fetch_add(&a.pull[1], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&a.pull[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.pull[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    stamp_end(a.ts, blockIdx.x);
+}
+
 // ------------------------------------------------------------------ fixed split
 
 template <int DT, int D>
@@ -453,6 +569,13 @@ hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_
     void* args[] = {const_cast<LeanArgs*>(&a)};
     if (cooperative)
         return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_pull(int dtype, int d, const PullArgs& a, int grid, hipStream_t s) {
+    const void* fn = pick(dtype, d, &pull_kernel<0, 64>, &pull_kernel<0, 128>, &pull_kernel<1, 64>,
+                          &pull_kernel<1, 128>);
+    void* args[] = {const_cast<PullArgs*>(&a)};
     return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 

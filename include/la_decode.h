@@ -73,7 +73,10 @@ typedef enum {
     LA_KIND_LEAN = 0,         /* stream-K over a persistent grid, one launch */
     LA_KIND_FIXED_SPLIT = 1,  /* each head cut into num_splits pieces + a combine launch */
     LA_KIND_PER_HEAD = 2,     /* one workgroup per (request, head), whole context */
-    LA_KIND_AUTO = 3          /* one of the above, chosen from the shape (la_select) */
+    LA_KIND_AUTO = 3,         /* one of the above, chosen from the shape (la_select) */
+    LA_KIND_PULL = 4,         /* fixed chunks of the tile sequence pulled dynamically by a
+                                 persistent grid */
+    LA_KIND_CHUNKS = 5        /* the same chunks, one workgroup each (non-persistent) */
 } la_kind;
 
 /*
@@ -146,6 +149,24 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               speculative decoding (xllm-io paper review, §7.4) and masked
  *               tokens as a case to qualify (siliconandsystems digest,
  *               "Exactness and numerical qualification") but fix no mask.
+ *   chunk_tiles pull kinds: tiles per chunk; 0 = about four chunks per
+ *               workgroup of a one-per-CU grid.
+ *
+ * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
+ * pieces": workgroups pull the next piece of the global tile order instead of
+ * holding a fixed split; "The hardware-aware part": persistent and
+ * non-persistent scheduling). The tile sequence of the lean schedule is cut
+ * into chunks of chunk_tiles tiles. LA_KIND_PULL: a persistent grid of `grid`
+ * workgroups (0 = la_default_grid, at most 65536) takes chunks from an atomic
+ * counter until none is left. LA_KIND_CHUNKS: one workgroup per chunk. A head
+ * spread over several chunks leaves one partial record per chunk; the
+ * workgroup whose piece of it arrives last merges them with f in chunk order,
+ * so outputs are bitwise the same whichever workgroup took which chunk. No
+ * workgroup ever waits for another (any grid is safe, co-resident or not).
+ * One query column per K/V head only (kv_heads = H or 0, q_tokens <= 1), else
+ * LA_EUNSUPPORTED. tile_owner receives the workgroup that processed each
+ * tile; cta_timestamps needs an explicit grid (pull: grid*4 entries) or
+ * chunk_tiles (chunks: ceil(I / chunk_tiles)*4 entries).
  */
 typedef struct la_opts {
     int dtype;
@@ -162,6 +183,7 @@ typedef struct la_opts {
     void* ev_stop;
     int kv_heads;
     int q_tokens;
+    int chunk_tiles;
 } la_opts;
 
 void la_opts_init(la_opts* opts);

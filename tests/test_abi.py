@@ -151,3 +151,21 @@ def test_decode_validation_before_device_work():
     assert "new tokens" in la.la_last_error()
     o.q_tokens = -1
     assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+
+
+def test_pull_kinds_validation():
+    L = la.lib()
+    lens = (ctypes.c_int32 * 2)(16, 16)
+    fake = 1 << 20
+    o = la.binding.LaOpts()
+    L.la_opts_init(ctypes.byref(o))
+    o.kind = la.LA_KIND_PULL
+    o.chunk_tiles = -1
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    o.chunk_tiles = 0
+    o.cta_timestamps = fake               # needs an explicit grid
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "grid" in la.la_last_error()
+    o.kind = la.LA_KIND_CHUNKS            # needs an explicit chunk size
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "chunk_tiles" in la.la_last_error()
