@@ -342,6 +342,81 @@ def selector_sweep(steps=10, warmup=2, rounds=3):
           flush=True)
 
 
+def masked_stream(hip, torch, n_cus, total):
+    """A stream whose kernels may use only the first n_cus CUs of the device
+    (hipExtStreamCreateWithCUMask; default priority)."""
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    words = (total + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for i in range(n_cus):
+        mask[i // 32] |= 1 << (i % 32)
+    s = ctypes.c_void_p()
+    if hip.hipExtStreamCreateWithCUMask(ctypes.byref(s), words, mask) != 0:
+        raise RuntimeError("hipExtStreamCreateWithCUMask failed")
+    return torch.cuda.ExternalStream(s.value)
+
+
+def contention(workloads, steps=10, warmup=3):
+    """Each kind on streams that may use only part of the CUs, as when other
+    kernels of a serving step hold the rest: the static schedules keep their
+    one-per-CU grid and split, the pull kinds rebalance. Prints one JSON line
+    with kernel p50 (us) per kind and available-CU count."""
+    import torch
+
+    import decode_phase_attention_amd as la
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    la.lib()
+    evs = HipEvents()
+    total = torch.cuda.get_device_properties(0).multi_processor_count
+    fracs = (8, 7, 6, 5, 4)                      # eighths of the CUs available
+    table = {}
+    for name in workloads:
+        log(f"[contention] {name}")
+        inp = W.make_inputs(name, seed=0, device="cuda")
+        out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device="cuda")
+        L = la.la_default_tile(inp.d)
+        I = inp.H * sum((n + L - 1) // L for n in inp.ctx_lens)
+        G = la.la_default_grid(inp.d, la.LA_BF16 if inp.dtype == "bf16" else la.LA_F16)
+        kinds = [("lean", "lean", {}), ("pull", "pull", {}),
+                 ("chunks", "chunks", {"chunk_tiles": -(-I // G)}),
+                 ("fixed_split_8", "fixed_split", {"num_splits": 8}),
+                 ("fixed_split_16", "fixed_split", {"num_splits": 16})]
+        rows = {}
+        for f in fracs:
+            n = total * f // 8
+            st = masked_stream(evs.hip, torch, n, total)
+            row = {}
+            for tag, kind, o in kinds:
+                with torch.cuda.stream(st):
+                    for _ in range(warmup):
+                        la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d,
+                                        inp.scale, out, kind=kind, **o)
+                    pairs = evs.create(2 * steps)
+                    for i in range(steps):
+                        la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d,
+                                        inp.scale, out, kind=kind, ev_start=pairs[2 * i],
+                                        ev_stop=pairs[2 * i + 1], **o)
+                    st.synchronize()
+                    la.la_sync_check()
+                ks = sorted(evs.elapsed_ms(pairs[2 * i], pairs[2 * i + 1]) * 1e3
+                            for i in range(steps))
+                evs.destroy(pairs)
+                row[tag] = round(ks[steps // 2], 1)
+            rows[str(n)] = row
+            log(f"   {n} CUs: {row}")
+        table[name] = rows
+        del inp, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode kernel p50 us when only part of the CUs is available",
+                      "device": torch.cuda.get_device_name(0), "cus": total,
+                      "grid": "lean/pull one workgroup per CU of the whole device; chunks "
+                              "ceil(I / that grid) tiles each; fixed split K pieces per head",
+                      "table": table}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -360,6 +435,9 @@ def main():
     ap.add_argument("--selector-sweep", action="store_true",
                     help="instead of the workload: measure kind=auto against every kind "
                          "on a sweep of shapes")
+    ap.add_argument("--contention", action="store_true",
+                    help="instead of the headline line: every kind on streams confined to "
+                         "part of the CUs (512k and ragged, or --workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -367,6 +445,9 @@ def main():
         sys.exit(2)
     if args.selector_sweep:
         selector_sweep()
+        return
+    if args.contention:
+        contention(["512k", "ragged"] if args.workload == "512k" else [args.workload])
         return
 
     import torch
@@ -406,6 +487,9 @@ def main():
         comparators["per_head"] = time_kind(la, torch, evs, inp, "per_head", 10, 2)
         log(f"[bench] per_head: {comparators['per_head']}")
         comparators["fixed_split_heuristic"] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2)
+        if not grouped:
+            comparators["pull"] = time_kind(la, torch, evs, inp, "pull", 10, 2)
+            log(f"[bench] pull: {comparators['pull']}")
         sweep = {}
         for K in (1, 2, 4, 8, 16, 32, 64):
             sweep[K] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2, num_splits=K)

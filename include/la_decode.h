@@ -149,8 +149,8 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               speculative decoding (xllm-io paper review, §7.4) and masked
  *               tokens as a case to qualify (siliconandsystems digest,
  *               "Exactness and numerical qualification") but fix no mask.
- *   chunk_tiles pull kinds: tiles per chunk; 0 = about four chunks per
- *               workgroup of a one-per-CU grid.
+ *   chunk_tiles pull kinds: tiles per chunk; 0 = ceil(I / (8 G)) with G the
+ *               pull grid (or one workgroup per CU), and at least 16.
  *
  * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
  * pieces": workgroups pull the next piece of the global tile order instead of

@@ -113,7 +113,7 @@ def test_pull_parity_and_tile_map(la, lens, H, d, dtype, grid, C):
     I = tiles(lens, H, L)
     owner = torch.full((I,), -1, dtype=torch.int32, device="cuda")
     check(run(la, inp, "pull", owner, grid=grid, chunk_tiles=C), ref, tag=f"pull grid={grid}")
-    Ceff = C if C > 0 else max(1, -(-I // (4 * grid)))
+    Ceff = C if C > 0 else max(16, -(-I // (8 * grid)))
     check_owner(owner, I, Ceff, "pull", grid)
 
 
