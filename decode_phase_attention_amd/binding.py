@@ -139,7 +139,19 @@ def _ptr(x) -> int | None:
     raise TypeError(f"cannot pass {type(x).__name__} as a device pointer")
 
 
+_I32_MIN, _I32_MAX = -(1 << 31), (1 << 31) - 1
+
+
 def _lens(ctx_lens):
+    if isinstance(ctx_lens, (list, tuple)):
+        # the common case, a list of integers: no numpy round trip
+        if ctx_lens and (min(ctx_lens) < _I32_MIN or max(ctx_lens) > _I32_MAX):
+            raise ValueError("ctx_lens entries must fit in int32")
+        try:
+            arr = (ctypes.c_int32 * len(ctx_lens))(*ctx_lens)
+            return arr, ctypes.cast(arr, _I32P)
+        except TypeError:
+            pass                  # not integers: let numpy convert (or reject) them
     arr = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int64))
     if arr.ndim != 1:
         raise ValueError("ctx_lens must be one-dimensional")
@@ -152,6 +164,9 @@ def _lens(ctx_lens):
 def _stream(stream) -> int | None:
     if stream is None:
         import torch
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(torch.cuda.current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream
@@ -192,23 +207,36 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
                  ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0):
-    o = LaOpts()
-    lib().la_opts_init(ctypes.byref(o))
+    o = LaOpts()              # ctypes zero-fills it: the same as la_opts_init
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
     o.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
-    o.tile_tokens = int(tile_tokens)
-    o.grid = int(grid)
-    o.num_splits = int(num_splits)
-    o.cooperative = int(bool(cooperative))
-    o.m_out = _ptr(m_out)
-    o.l_out = _ptr(l_out)
-    o.tile_owner = _ptr(tile_owner)
-    o.cta_timestamps = _ptr(cta_timestamps)
-    o.ev_start = ev_start
-    o.ev_stop = ev_stop
-    o.kv_heads = int(kv_heads or 0)
-    o.q_tokens = int(q_tokens or 0)
-    o.chunk_tiles = int(chunk_tiles or 0)
+    # only the fields that differ from zero (each ctypes field store costs)
+    if tile_tokens:
+        o.tile_tokens = int(tile_tokens)
+    if grid:
+        o.grid = int(grid)
+    if num_splits:
+        o.num_splits = int(num_splits)
+    if cooperative:
+        o.cooperative = 1
+    if m_out is not None:
+        o.m_out = _ptr(m_out)
+    if l_out is not None:
+        o.l_out = _ptr(l_out)
+    if tile_owner is not None:
+        o.tile_owner = _ptr(tile_owner)
+    if cta_timestamps is not None:
+        o.cta_timestamps = _ptr(cta_timestamps)
+    if ev_start is not None:
+        o.ev_start = ev_start
+    if ev_stop is not None:
+        o.ev_stop = ev_stop
+    if kv_heads:
+        o.kv_heads = int(kv_heads)
+    if q_tokens:
+        o.q_tokens = int(q_tokens)
+    if chunk_tiles:
+        o.chunk_tiles = int(chunk_tiles)
     arr, p = _lens(ctx_lens)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
