@@ -487,9 +487,8 @@ def main():
         comparators["per_head"] = time_kind(la, torch, evs, inp, "per_head", 10, 2)
         log(f"[bench] per_head: {comparators['per_head']}")
         comparators["fixed_split_heuristic"] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2)
-        if not grouped:
-            comparators["pull"] = time_kind(la, torch, evs, inp, "pull", 10, 2)
-            log(f"[bench] pull: {comparators['pull']}")
+        comparators["pull"] = time_kind(la, torch, evs, inp, "pull", 10, 2)
+        log(f"[bench] pull: {comparators['pull']}")
         sweep = {}
         for K in (1, 2, 4, 8, 16, 32, 64):
             sweep[K] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2, num_splits=K)

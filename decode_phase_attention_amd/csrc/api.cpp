@@ -343,7 +343,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     char* db = (char*)w.tables;
     const bool coop = o.cooperative != 0;
     if (hd.grouped) {
-        la::GqaArgs a;
+        la::GqaArgs a{};
         fill_gqa(a, q, k, v, out, o, hd, L, scale);
         a.ctx = (const int32_t*)(db + rl.off_ctx);
         a.tok_off = (const int64_t*)(db + rl.off_tok);
@@ -360,7 +360,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
         return LA_OK;
     }
-    la::LeanArgs a;
+    la::LeanArgs a{};
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.v = (const uint16_t*)v;
@@ -419,7 +419,7 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
 
     char* db = (char*)w.tables;
     if (hd.grouped) {
-        la::GqaArgs a;
+        la::GqaArgs a{};
         fill_gqa(a, q, k, v, out, o, hd, L, scale);
         a.ctx = (const int32_t*)(db + rl.off_ctx);
         a.tok_off = (const int64_t*)(db + rl.off_tok);
@@ -437,7 +437,7 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
         if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
         return LA_OK;
     }
-    la::SplitArgs a;
+    la::SplitArgs a{};
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.v = (const uint16_t*)v;
@@ -457,7 +457,7 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
         HIP_TRY(la::launch_per_head(o.dtype, d, a, BU, w.stream));
     } else {
         HIP_TRY(la::launch_split(o.dtype, d, a, BU * splits, w.stream));
-        la::CombineArgs c;
+        la::CombineArgs c{};
         c.part = w.split_part;
         c.out = out;
         c.m_out = o.m_out;
@@ -476,7 +476,7 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
                    const int32_t* ctx_lens, int B, const Heads& hd, int d, float scale,
                    float* out, const la_opts& o) {
     Capacity cap;
-    la_status st = capacity(o.dtype, d, false, &cap);
+    la_status st = capacity(o.dtype, d, hd.grouped, &cap);
     if (st != LA_OK) return st;
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
     const int U = hd.units_per_req();
@@ -525,8 +525,12 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     }
     fill_req(hb, rl, ctx_lens, B);
 
-    if ((st = grow(w, (void**)&w.pull_part, &w.pull_part_cap,
-                   sizeof(float) * 2 * (size_t)nchunks * la::part_stride(d), false)) != LA_OK)
+    const size_t part_bytes =
+        sizeof(float) * 2 * (size_t)nchunks * (hd.grouped ? 16 : 1) * la::part_stride(d);
+    if (hd.grouped && part_bytes > (size_t)INT32_MAX)
+        return fail(LA_EUNSUPPORTED, "%lld chunks of 16 records exceed the 2 GiB exchange buffer",
+                    (long long)nchunks);
+    if ((st = grow(w, (void**)&w.pull_part, &w.pull_part_cap, part_bytes, false)) != LA_OK)
         return st;
     if ((st = grow(w, (void**)&w.arrive, &w.arrive_cap, sizeof(uint32_t) * (size_t)BU, true)) != LA_OK)
         return st;
@@ -534,7 +538,27 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
         return st;
     if ((st = upload(w, hb, rl.bytes)) != LA_OK) return st;
     char* db = (char*)w.tables;
-    la::PullArgs a;
+    if (hd.grouped) {
+        la::GqaArgs a{};
+        fill_gqa(a, q, k, v, out, o, hd, L, scale);
+        a.ctx = (const int32_t*)(db + rl.off_ctx);
+        a.tok_off = (const int64_t*)(db + rl.off_tok);
+        a.part = w.pull_part;
+        a.part_bytes = (uint32_t)std::min<size_t>(w.pull_part_cap, (size_t)INT32_MAX);
+        a.head_start = (const int32_t*)(db + off_start);
+        a.chunk_head = (const int32_t*)(db + off_chunk);
+        a.arrive = w.arrive;
+        a.pull = w.pull_ctr;
+        a.C = C;
+        a.I = (int)I;
+        a.nchunks = (int)nchunks;
+        a.dynamic = dynamic ? 1 : 0;
+        if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
+        HIP_TRY(la::launch_pull_gqa(o.dtype, d, a, grid, w.stream));
+        if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+        return LA_OK;
+    }
+    la::PullArgs a{};
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.v = (const uint16_t*)v;
@@ -643,9 +667,6 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
                         b, ctx_lens[b], o.q_tokens);
     const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
-    if ((o.kind == LA_KIND_PULL || o.kind == LA_KIND_CHUNKS) && hd.grouped)
-        return fail(LA_EUNSUPPORTED, "the pull kinds take one query column per K/V head "
-                                     "(no kv_heads < H, no q_tokens > 1)");
     std::lock_guard<std::mutex> lock(g_mu);
     if (o.kind == LA_KIND_AUTO) {
         int kind = 0, grid = 0;

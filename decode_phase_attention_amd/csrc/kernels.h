@@ -101,6 +101,15 @@ struct GqaArgs {
     int splits;
     float sl2e;
     uint64_t wait_ticks;
+    // dynamic pull (as in PullArgs; part then holds [nchunks * 2 * 16] records)
+    const int32_t* head_start;
+    const int32_t* chunk_head;
+    uint32_t* arrive;
+    uint32_t* pull;
+    int C;
+    int I;
+    int nchunks;
+    int dynamic;
 };
 
 // Dynamic tile pull. The linearised tile sequence (as in the lean schedule)
@@ -143,6 +152,7 @@ hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStre
 hipError_t launch_split_gqa(int dtype, int d, const GqaArgs& a, int blocks, hipStream_t s);
 hipError_t launch_combine_gqa(int d, const GqaArgs& a, int units, hipStream_t s);
 hipError_t launch_per_head_gqa(int dtype, int d, const GqaArgs& a, int units, hipStream_t s);
+hipError_t launch_pull_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s);
 hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_t s,
                        bool cooperative);
 hipError_t launch_split(int dtype, int d, const SplitArgs& a, int blocks, hipStream_t s);

@@ -453,6 +453,129 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     stamp_end(a.ts, cta);
 }
 
+// ------------------------------------------------------------------ dynamic pull
+
+// Chunks of the unit tile sequence, taken from an atomic counter (dynamic) or
+// one per workgroup; a unit spread over chunks leaves 16 records (one per
+// query column) per chunk at slot (chunk, side), and the workgroup whose
+// piece arrives last merges them in chunk order. Nothing waits.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void pull_gqa_kernel(const GqaArgs a) {
+    using G = GGeo<D>;
+    __shared__ GSmem<D> sm;
+    __shared__ int s_chunk, s_arrived;
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    const int w = (t >> 4) & 3;
+    const int c = t & 15;
+    const int q = t >> 4;
+    const int dc = t & 15;
+    const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
+    stamp_start(a.ts, blockIdx.x);
+    int next = blockIdx.x;
+    for (;;) {
+        int k;
+        if (a.dynamic) {
+            if (t == 0)
+                s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            k = s_chunk;
+            __syncthreads();
+        } else {
+            k = next;
+            next = a.nchunks;
+        }
+        if (k >= a.nchunks) break;
+        const int c0 = k * a.C;
+        const int c1 = min(c0 + a.C, a.I);
+        int u = a.chunk_head[k];
+        for (int it = c0; it < c1; ++u) {
+            const int Su = a.head_start[u], Se = a.head_start[u + 1];
+            const int t1 = min(Se, c1);
+            const Unit x = decode_unit(a, u);
+            const int tok0 = (it - Su) * a.L;
+            const int tok1 = (int)min((int64_t)(t1 - Su) * a.L, (int64_t)x.n);
+            u32x4_t qt[G::KK];
+            load_qt<D>(a.q, c < x.geff ? col_row(a, x, c) : 0, c < x.geff, w, qt);
+            int full, lim;
+            col_bounds(a, x, c, tok1, full, lim);
+            GState<D> st;
+            gstate_init<D>(st);
+            gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, full, lim, wave,
+                             w, c, qt, a.sl2e, st);
+            if (a.tile_owner != nullptr)
+                for (int i = it + t; i < t1; i += kThreads) a.tile_owner[i] = blockIdx.x;
+            float M, L, O[G::DPT];
+            gqa_fold<D>(sm, st, wave, w, c, M, L, O);
+            const int side = it == c0 ? 0 : 1;
+            it = t1;
+            const int kf = Su / a.C, kl = (Se - 1) / a.C;   // chunks holding unit u
+            if (kf != kl) {
+                if (q < x.geff) {
+                    const uint32_t rec =
+                        (uint32_t)(((k * 2 + side) * 16) + q) * (uint32_t)(part_stride(D) * 4);
+#pragma unroll
+                    for (int i = 0; i < G::DPT; i += 4)
+                        store16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u,
+                                      make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]));
+                    if (dc == 0) store8_agent(xr, rec + (uint32_t)D * 4u, M, L);
+                }
+                drain_stores();
+                __syncthreads();
+                if (t == 0)
+                    s_arrived = (int)__hip_atomic_fetch_add(&a.arrive[u], 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                if (s_arrived != kl - kf) continue;
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                M = kNegInf;
+                L = 0.f;
+#pragma unroll
+                for (int i = 0; i < G::DPT; ++i) O[i] = 0.f;
+                constexpr int kBatch = 128 / D * 8;
+                const int qq = min(q, x.geff - 1);   // columns past the block read a valid record
+                for (int j0 = kf; j0 <= kl; j0 += kBatch) {
+                    float pm[kBatch], pl[kBatch], po[kBatch][G::DPT];
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j) {
+                        const int ch = min(j0 + j, kl);
+                        const int sd = max(Su, ch * a.C) == ch * a.C ? 0 : 1;
+                        const uint32_t rec =
+                            (uint32_t)((ch * 2 + sd) * 16 + qq) * (uint32_t)(part_stride(D) * 4);
+                        const float2 ml = load8_agent(xr, rec + (uint32_t)D * 4u);
+                        pm[j] = ml.x;
+                        pl[j] = ml.y;
+#pragma unroll
+                        for (int i = 0; i < G::DPT; i += 4) {
+                            const float4 v = load16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u);
+                            po[j][i] = v.x;
+                            po[j][i + 1] = v.y;
+                            po[j][i + 2] = v.z;
+                            po[j][i + 3] = v.w;
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j)
+                        if (j0 + j <= kl) merge_into<G::DPT>(M, L, O, pm[j], pl[j], po[j]);
+                }
+                if (t == 0)
+                    __hip_atomic_store(&a.arrive[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            write_out_gqa<D>(a, x, q, dc, M, L, O);
+        }
+    }
+    if (a.dynamic && t == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&a.pull[1], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&a.pull[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.pull[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    stamp_end(a.ts, blockIdx.x);
+}
+
 // ------------------------------------------------------------------ fixed split
 
 template <int DT, int D>
@@ -569,6 +692,13 @@ hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStre
     void* args[] = {const_cast<GqaArgs*>(&a)};
     if (cooperative)
         return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_pull_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s) {
+    const void* fn = pick_g(dtype, d, &pull_gqa_kernel<0, 64>, &pull_gqa_kernel<0, 128>,
+                            &pull_gqa_kernel<1, 64>, &pull_gqa_kernel<1, 128>);
+    void* args[] = {const_cast<GqaArgs*>(&a)};
     return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 

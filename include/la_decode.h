@@ -163,7 +163,8 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  * workgroup whose piece of it arrives last merges them with f in chunk order,
  * so outputs are bitwise the same whichever workgroup took which chunk. No
  * workgroup ever waits for another (any grid is safe, co-resident or not).
- * One query column per K/V head only (kv_heads = H or 0, q_tokens <= 1), else
+ * With kv_heads or q_tokens the chunks cut the grouped units' tiles, and the
+ * grouped exchange (16 records per chunk side) must fit 2 GiB, else
  * LA_EUNSUPPORTED. tile_owner receives the workgroup that processed each
  * tile; cta_timestamps needs an explicit grid (pull: grid*4 entries) or
  * chunk_tiles (chunks: ceil(I / chunk_tiles)*4 entries).

@@ -148,26 +148,63 @@ def test_back_to_back_reuses_counters(la):
         assert err <= O_TOL, (i, err)
 
 
-def test_grouped_calls_unsupported(la):
-    inp = W.make_custom([100], 8, 64, "f16", seed=8, device="cuda", kv_heads=2)
-    out = torch.empty((1, 8, 64), dtype=torch.float32, device="cuda")
-    with pytest.raises(la.LaError) as e:
-        la.la_decode_ex(inp.q, inp.k, inp.v, [100], 1, 8, 64, inp.scale, out, kind="pull",
-                        kv_heads=2)
-    assert e.value.status == 2
+@pytest.mark.parametrize("H,Hk,Nq,d,dtype", [(8, 2, 1, 64, "f16"), (32, 8, 1, 128, "bf16"),
+                                              (4, 4, 4, 128, "bf16"), (16, 2, 3, 64, "f16")])
+@pytest.mark.parametrize("kind,grid,C", [("pull", 0, 0), ("pull", 5, 1), ("pull", 700, 3),
+                                         ("chunks", 0, 2), ("chunks", 0, 40)])
+def test_grouped_and_several_tokens(la, H, Hk, Nq, d, dtype, kind, grid, C):
+    """The grouped MFMA kernel pulled the same way: units (K/V head, block of
+    16 query columns) instead of heads."""
+    L = la.la_default_tile(d)
+    lens = [Nq, 3 * L + 1, 5000, 700]
+    say(f"[pull grouped] H={H} Hk={Hk} Nq={Nq} d={d} {kind} grid={grid} C={C}")
+    inp = W.make_custom(lens, H, d, dtype, seed=H + Hk + Nq + C, device="cuda", kv_heads=Hk,
+                        q_tokens=Nq)
+    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                             inp.scale, dtype, workers=16, kv_heads=Hk)
+    shape = tuple(inp.q.shape)
+    out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    rows = int(np.prod(shape[:-1]))
+    m = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    l = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    U = Hk * ((H // Hk * Nq + 15) // 16)
+    I = U * sum((n + L - 1) // L for n in lens)
+    owner = torch.full((I,), -1, dtype=torch.int32, device="cuda")
+    la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out, kind=kind,
+                    grid=grid, chunk_tiles=C, m_out=m, l_out=l, tile_owner=owner, kv_heads=Hk,
+                    q_tokens=Nq)
+    la.la_sync_check()
+    check((out.cpu().numpy(), m.cpu().numpy().reshape(ref[1].shape),
+           l.cpu().numpy().reshape(ref[2].shape)), ref, tag=f"grouped {kind}")
+    G = grid if grid > 0 else la.la_default_grid(d, la.LA_BF16 if dtype == "bf16" else la.LA_F16)
+    Ceff = C if C > 0 else max(16, -(-I // (8 * G)))
+    check_owner(owner, I, Ceff, kind, grid if kind == "pull" and grid > 0 else 1 << 30)
 
 
-@pytest.mark.parametrize("name", ["512k", "ragged"])
+@pytest.mark.parametrize("name", ["512k", "ragged", "gqa8-ragged", "spec4-ragged"])
 def test_full_size(la, name):
     say(f"[pull full {name}]")
     inp = W.make_inputs(name, seed=0, device="cuda")
     rng = np.random.default_rng(9)
-    allh = [(b, h) for b in range(inp.B) for h in range(inp.H)]
+    Nq = inp.Nq
+    allh = [(b, t, h) for b in range(inp.B) for t in range(Nq) for h in range(inp.H)]
     heads = sorted({allh[0], allh[-1]} | {allh[int(i)] for i in rng.choice(len(allh), 24, replace=False)})
+    if Nq == 1:
+        heads = [(b, h) for b, _, h in heads]
     ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), inp.ctx_lens,
-                             inp.scale, inp.dtype, heads=heads, workers=16)
+                             inp.scale, inp.dtype, heads=heads, workers=16, kv_heads=inp.Hk)
+    shape = tuple(inp.q.shape)
+    rows = int(np.prod(shape[:-1]))
     for kind in ("pull", "chunks"):
-        err = check(run(la, inp, kind), ref, heads=heads, tag=f"{name}/{kind}")
+        out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+        m = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+        l = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+        la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
+                        kind=kind, m_out=m, l_out=l, kv_heads=inp.Hk, q_tokens=Nq)
+        la.la_sync_check()
+        got = (out.cpu().numpy(), m.cpu().numpy().reshape(ref[1].shape),
+               l.cpu().numpy().reshape(ref[2].shape))
+        err = check(got, ref, heads=heads, tag=f"{name}/{kind}")
         say(f"[pull full {name}] {kind} max|dO|={err:.2e}")
     del inp
     torch.cuda.empty_cache()
