@@ -378,7 +378,9 @@ def contention(workloads, steps=10, warmup=3):
         inp = W.make_inputs(name, seed=0, device="cuda")
         out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device="cuda")
         L = la.la_default_tile(inp.d)
-        I = inp.H * sum((n + L - 1) // L for n in inp.ctx_lens)
+        cols = inp.H // inp.Hk * inp.Nq
+        units = inp.Hk * ((cols + 15) // 16) if cols > 1 else inp.H
+        I = units * sum((n + L - 1) // L for n in inp.ctx_lens)
         G = la.la_default_grid(inp.d, la.LA_BF16 if inp.dtype == "bf16" else la.LA_F16)
         kinds = [("lean", "lean", {}), ("pull", "pull", {}),
                  ("chunks", "chunks", {"chunk_tiles": -(-I // G)}),
@@ -393,12 +395,14 @@ def contention(workloads, steps=10, warmup=3):
                 with torch.cuda.stream(st):
                     for _ in range(warmup):
                         la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d,
-                                        inp.scale, out, kind=kind, **o)
+                                        inp.scale, out, kind=kind, kv_heads=inp.Hk,
+                                        q_tokens=inp.Nq, **o)
                     pairs = evs.create(2 * steps)
                     for i in range(steps):
                         la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d,
                                         inp.scale, out, kind=kind, ev_start=pairs[2 * i],
-                                        ev_stop=pairs[2 * i + 1], **o)
+                                        ev_stop=pairs[2 * i + 1], kv_heads=inp.Hk,
+                                        q_tokens=inp.Nq, **o)
                     st.synchronize()
                     la.la_sync_check()
                 ks = sorted(evs.elapsed_ms(pairs[2 * i], pairs[2 * i + 1]) * 1e3

@@ -173,6 +173,25 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+def _check_sizes(q, k_cache, v_cache, out, ctx_lens, B, H, d, kv_heads=0, q_tokens=0,
+                 m_out=None, l_out=None):
+    """For torch tensors, reject a call that would read or write past them (the
+    library sees only pointers and cannot check)."""
+    import torch
+    if not any(isinstance(t, torch.Tensor) for t in (q, k_cache, v_cache, out)):
+        return
+    rows = int(B) * int(q_tokens or 1) * int(H)
+    kv = int(kv_heads or H) * int(sum(int(n) for n in ctx_lens)) * int(d)
+    for name, t, need, size in (("q", q, rows * int(d), 2), ("k_cache", k_cache, kv, 2),
+                                ("v_cache", v_cache, kv, 2), ("out", out, rows * int(d), 4),
+                                ("m_out", m_out, rows, 4), ("l_out", l_out, rows, 4)):
+        if isinstance(t, torch.Tensor):
+            if t.element_size() != size:
+                raise ValueError(f"{name}: {size}-byte elements expected, got {t.dtype}")
+            if t.numel() < need:
+                raise ValueError(f"{name} holds {t.numel()} elements; this call uses {need}")
+
+
 def _dtype_of(t) -> int:
     import torch
     if t.dtype == torch.float16:
@@ -187,18 +206,21 @@ def la_decode(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, d
     if dtype is None:
         dtype = _dtype_of(q)
     arr, p = _lens(ctx_lens)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d)
     _check(lib().la_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                            float(scale), _ptr(out), _stream(stream), int(dtype)))
 
 
 def la_decode_bf16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None):
     arr, p = _lens(ctx_lens)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d)
     _check(lib().la_decode_bf16(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                                 float(scale), _ptr(out), _stream(stream)))
 
 
 def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None):
     arr, p = _lens(ctx_lens)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d)
     _check(lib().la_decode_f16(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                                float(scale), _ptr(out), _stream(stream)))
 
@@ -238,6 +260,7 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
     if chunk_tiles:
         o.chunk_tiles = int(chunk_tiles)
     arr, p = _lens(ctx_lens)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, kv_heads, q_tokens, m_out, l_out)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
 

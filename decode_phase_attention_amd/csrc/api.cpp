@@ -66,6 +66,8 @@ struct Workspace {
     size_t arrive_cap = 0;
     uint32_t* pull_ctr = nullptr;   // dynamic pull: next chunk, workgroups done; zero between launches
     size_t pull_ctr_cap = 0;
+    uint32_t* gcount = nullptr;     // dynamic pull: pieces arrived per group, zero between launches
+    size_t gcount_cap = 0;
     void* tables = nullptr;         // device copy of the schedule tables
     size_t tables_cap = 0;
     std::vector<char> last_tables;  // host copy of what `tables` holds (valid while non-empty)
@@ -88,7 +90,7 @@ std::map<std::pair<int, const void*>, Capacity> g_capacity;
 constexpr int kWgPerCu = 1;
 constexpr int kMaxQTokens = 64;
 constexpr int kMaxPullGrid = 65536;
-constexpr int kMinChunkTiles = 16;
+constexpr int kMinChunkTiles = 32;   // 2 MiB of K and V at either head dim
 uint32_t g_wait_us = kDefaultWaitUs;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -486,15 +488,19 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     if (I > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "%lld tile iterations do not fit", (long long)I);
     const bool dynamic = o.kind == LA_KIND_PULL;
     // Default chunk: about eight chunks per workgroup of a one-per-CU grid,
-    // and at least kMinChunkTiles tiles. Measured on MI355X with part of the
-    // CUs taken away (a CU-masked stream): eight to sixteen chunks per
-    // workgroup keep a 512k-token decode within 4% of its full-GPU time with
-    // 7/8 of the CUs, where a static split of the same grid loses a third;
-    // shorter chunks than 16 tiles spend too long in the per-chunk merge.
+    // and at least kMinChunkTiles tiles (or one chunk per workgroup).
+    // Measured on MI355X with part of the CUs taken away (a CU-masked
+    // stream): eight to sixteen chunks per workgroup keep a 512k-token decode
+    // within 6% of its full-GPU time with 7/8 of the CUs, where a static split
+    // of the same grid loses a third; chunks of less than about 2 MiB spend
+    // too large a share in the per-chunk fold, publish and merge.
     const int G0 = dynamic && o.grid > 0 ? o.grid : cap.preferred;
     int C = o.chunk_tiles;
-    if (C == 0)
-        C = (int)std::max<int64_t>(kMinChunkTiles, (I + 8 * (int64_t)G0 - 1) / (8 * (int64_t)G0));
+    if (C == 0) {
+        const int64_t per_wg = (I + G0 - 1) / G0;   // never fewer chunks than workgroups
+        C = (int)std::max<int64_t>(std::min<int64_t>(kMinChunkTiles, per_wg),
+                                   (I + 8 * (int64_t)G0 - 1) / (8 * (int64_t)G0));
+    }
     const int64_t nchunks = (I + C - 1) / C;
     if (nchunks > kMaxPullGrid * 64) return fail(LA_EUNSUPPORTED, "too many chunks (%lld)", (long long)nchunks);
     const int grid = dynamic ? (int)std::min<int64_t>(G0, nchunks) : (int)nchunks;
@@ -525,14 +531,18 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     }
     fill_req(hb, rl, ctx_lens, B);
 
+    // two levels of records (pieces, then groups of pieces), two slots per chunk
     const size_t part_bytes =
-        sizeof(float) * 2 * (size_t)nchunks * (hd.grouped ? 16 : 1) * la::part_stride(d);
+        sizeof(float) * 4 * (size_t)nchunks * (hd.grouped ? 16 : 1) * la::part_stride(d);
     if (hd.grouped && part_bytes > (size_t)INT32_MAX)
         return fail(LA_EUNSUPPORTED, "%lld chunks of 16 records exceed the 2 GiB exchange buffer",
                     (long long)nchunks);
     if ((st = grow(w, (void**)&w.pull_part, &w.pull_part_cap, part_bytes, false)) != LA_OK)
         return st;
     if ((st = grow(w, (void**)&w.arrive, &w.arrive_cap, sizeof(uint32_t) * (size_t)BU, true)) != LA_OK)
+        return st;
+    if ((st = grow(w, (void**)&w.gcount, &w.gcount_cap, sizeof(uint32_t) * 2 * (size_t)nchunks,
+                   true)) != LA_OK)
         return st;
     if ((st = grow(w, (void**)&w.pull_ctr, &w.pull_ctr_cap, 2 * sizeof(uint32_t), true)) != LA_OK)
         return st;
@@ -548,6 +558,7 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
         a.head_start = (const int32_t*)(db + off_start);
         a.chunk_head = (const int32_t*)(db + off_chunk);
         a.arrive = w.arrive;
+        a.gcount = w.gcount;
         a.pull = w.pull_ctr;
         a.C = C;
         a.I = (int)I;
@@ -571,6 +582,7 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     a.chunk_head = (const int32_t*)(db + off_chunk);
     a.part = w.pull_part;
     a.arrive = w.arrive;
+    a.gcount = w.gcount;
     a.pull = w.pull_ctr;
     a.tile_owner = o.tile_owner;
     a.ts = o.cta_timestamps;
@@ -614,6 +626,7 @@ void free_workspace(Workspace* w) {
     hipFree(w->pull_part);
     hipFree(w->arrive);
     hipFree(w->pull_ctr);
+    hipFree(w->gcount);
     hipFree(w->tables);
     for (auto& s : w->ring) {
         if (s.host != nullptr) hipHostFree(s.host);

@@ -101,9 +101,10 @@ struct GqaArgs {
     int splits;
     float sl2e;
     uint64_t wait_ticks;
-    // dynamic pull (as in PullArgs; part then holds [nchunks * 2 * 16] records)
+    // dynamic pull (as in PullArgs; part then holds [2 * nchunks * 2 * 16] records)
     const int32_t* head_start;
     const int32_t* chunk_head;
+    uint32_t* gcount;
     uint32_t* arrive;
     uint32_t* pull;
     int C;
@@ -116,9 +117,12 @@ struct GqaArgs {
 // is cut into fixed chunks of C tiles; workgroups take chunks from an atomic
 // counter (dynamic) or one chunk each (grid = nchunks). A head spanning
 // several chunks leaves one partial record per chunk, at slot (chunk, side):
-// side 0 if its piece starts the chunk, else 1. The workgroup whose piece
-// arrives last (per-head arrival counter) merges the head's pieces in chunk
-// order and writes the output; nothing ever waits.
+// side 0 if its piece starts the chunk, else 1. The head's chunks form groups
+// of kMergeFanIn: the last piece of a group to arrive (group counter at the
+// slot of the group's first chunk) folds the group and stores the group's
+// record at that slot of the second level; the last group (per-head counter)
+// folds the group records and writes the output. Nothing ever waits.
+constexpr int kMergeFanIn = 16;
 struct PullArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -130,7 +134,8 @@ struct PullArgs {
     const int64_t* tok_off;    // [B]
     const int32_t* head_start; // [BU + 1]: first tile iteration of each head; [BU] = I
     const int32_t* chunk_head; // [nchunks]: head holding the chunk's first tile
-    float* part;               // [nchunks * 2 * part_stride(d)]
+    float* part;               // [2 levels * nchunks * 2 * part_stride(d)]
+    uint32_t* gcount;          // [nchunks * 2] group counters, zero at launch and at exit
     uint32_t* arrive;          // [BU], zero at launch and at exit
     uint32_t* pull;            // [2]: next chunk, workgroups done; zero at launch and at exit
     int32_t* tile_owner;       // optional [I]

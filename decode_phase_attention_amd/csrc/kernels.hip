@@ -351,6 +351,66 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
 
 // ------------------------------------------------------------------ dynamic pull
 
+// Record slot of a head's piece in chunk ch: (ch, 0) if the piece starts the
+// chunk, else (ch, 1) -- the chunk's last, partial segment.
+__device__ __forceinline__ int piece_slot(int ch, int Su, int C) {
+    return ch * 2 + (max(Su, ch * C) == ch * C ? 0 : 1);
+}
+
+// Wave 0 stores a record (Obar, m, l) with device-coherent stores.
+template <int D>
+__device__ __forceinline__ void publish_rec(float* p, int lane, float M, float Ls,
+                                            const float (&O)[kDpl<D>]) {
+#pragma unroll
+    for (int j = 0; j < kDpl<D>; ++j) store_agent(p + lane + 64 * j, O[j]);
+    if (lane == 0) {
+        store_agent(p + D, M);
+        store_agent(p + D + 1, Ls);
+    }
+}
+
+// After this wave's records are stored: wait for them to complete, then add
+// one to the counter. True for the wave whose add brings it to `last` + 1
+// (the last arrival), which then owns the merge.
+__device__ __forceinline__ bool count_in(uint32_t* ctr, uint32_t last, int lane) {
+    drain_stores();
+    uint32_t before = 0;
+    if (lane == 0)
+        before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __shfl(before, 0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return before == last;
+}
+
+// Wave 0 folds, in order, the records of chunks ch0, ch0 + step, ... (n of
+// them) of one head from `base` into (M, Ls, O), replacing what they held.
+template <int D>
+__device__ __forceinline__ void fold_slots(const float* base, int ch0, int n, int step, int Su,
+                                           int C, int lane, float& M, float& Ls,
+                                           float (&O)[kDpl<D>]) {
+    constexpr int P = kDpl<D>;
+    constexpr int kBatch = 16;
+    M = kNegInf;
+    Ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < P; ++j) O[j] = 0.f;
+    for (int i0 = 0; i0 < n; i0 += kBatch) {
+        float pm[kBatch], pl[kBatch], po[kBatch][P];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int ch = ch0 + min(i0 + j, n - 1) * step;
+            const float* rp = base + (int64_t)piece_slot(ch, Su, C) * part_stride(D);
+            pm[j] = load_agent(rp + D);
+            pl[j] = load_agent(rp + D + 1);
+#pragma unroll
+            for (int x = 0; x < P; ++x) po[j][x] = load_agent(rp + lane + 64 * x);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (i0 + j < n) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
+    }
+}
+
 // Stream-K over fixed chunks of the tile sequence, taken dynamically (the
 // digest's CTAs that pull the next tile instead of holding a fixed split) or
 // one per workgroup (a non-persistent grid). Pieces of a head that spans
@@ -368,20 +428,20 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
     stamp_start(a.ts, blockIdx.x);
+    // A workgroup takes its next chunk only when it has finished the last one
+    // (taking it earlier hands chunks to workgroups that are still busy while
+    // others, started later, find none).
     int next = blockIdx.x;
+    if (a.dynamic) {
+        if (t == 0)
+            s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        next = s_chunk;
+        __syncthreads();
+    }
     for (;;) {
-        int k;
-        if (a.dynamic) {
-            if (t == 0)
-                s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            k = s_chunk;
-            __syncthreads();
-        } else {
-            k = next;
-            next = a.nchunks;
-        }
+        const int k = next;
         if (k >= a.nchunks) break;
         const int c0 = k * a.C;
         const int c1 = min(c0 + a.C, a.I);
@@ -409,48 +469,42 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
 
             const int kf = Su / a.C, kl = (Se - 1) / a.C;   // chunks holding head u
             if (kf != kl) {
-                // one piece of a head spread over chunks kf..kl: publish it,
-                // then count it in; the last piece's workgroup merges them all
-                float* p = a.part + ((int64_t)k * 2 + side) * part_stride(D);
-#pragma unroll
-                for (int j = 0; j < P; ++j) store_agent(p + lane + 64 * j, O[j]);
-                if (lane == 0) {
-                    store_agent(p + D, M);
-                    store_agent(p + D + 1, Ls);
+                // A piece of a head spread over chunks kf..kl. Level 1: the
+                // chunks form groups of kMergeFanIn; the last piece of a group
+                // to arrive folds the group's pieces in chunk order. Level 2:
+                // the last group folds the group results in order. The tree is
+                // fixed, so the bits do not depend on who arrives last.
+                const int g0 = kf + (k - kf) / kMergeFanIn * kMergeFanIn;
+                const int g1 = min(g0 + kMergeFanIn - 1, kl);
+                const int ngroups = (kl - kf) / kMergeFanIn + 1;
+                const int gslot = piece_slot(g0, Su, a.C);
+                if (g1 > g0) {
+                    publish_rec<D>(a.part + (int64_t)(k * 2 + side) * part_stride(D), lane, M, Ls, O);
+                    if (!count_in(&a.gcount[gslot], (uint32_t)(g1 - g0), lane)) continue;
+                    fold_slots<D>(a.part, g0, g1 - g0 + 1, 1, Su, a.C, lane, M, Ls, O);
+                    if (lane == 0)
+                        __hip_atomic_store(&a.gcount[gslot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                drain_stores();
-                uint32_t before = 0;
-                if (lane == 0)
-                    before = __hip_atomic_fetch_add(&a.arrive[u], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-                before = __shfl(before, 0);
-                if (before != (uint32_t)(kl - kf)) continue;
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                M = kNegInf;
-                Ls = 0.f;
-#pragma unroll
-                for (int j = 0; j < P; ++j) O[j] = 0.f;
-                constexpr int kBatch = 16;
-                for (int j0 = kf; j0 <= kl; j0 += kBatch) {
-                    float pm[kBatch], pl[kBatch], po[kBatch][P];
-#pragma unroll
-                    for (int j = 0; j < kBatch; ++j) {
-                        const int ch = min(j0 + j, kl);
-                        const int sd = max(Su, ch * a.C) == ch * a.C ? 0 : 1;
-                        const float* rp = a.part + ((int64_t)ch * 2 + sd) * part_stride(D);
-                        pm[j] = load_agent(rp + D);
-                        pl[j] = load_agent(rp + D + 1);
-#pragma unroll
-                        for (int x = 0; x < P; ++x) po[j][x] = load_agent(rp + lane + 64 * x);
-                    }
-#pragma unroll
-                    for (int j = 0; j < kBatch; ++j)
-                        if (j0 + j <= kl) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
+                if (ngroups > 1) {
+                    float* l1 = a.part + (int64_t)2 * a.nchunks * part_stride(D);
+                    publish_rec<D>(l1 + (int64_t)gslot * part_stride(D), lane, M, Ls, O);
+                    if (!count_in(&a.arrive[u], (uint32_t)(ngroups - 1), lane)) continue;
+                    fold_slots<D>(l1, kf, ngroups, kMergeFanIn, Su, a.C, lane, M, Ls, O);
+                    if (lane == 0)
+                        __hip_atomic_store(&a.arrive[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (lane == 0)
-                    __hip_atomic_store(&a.arrive[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
+        }
+        if (a.dynamic) {
+            __syncthreads();
+            if (t == 0)
+                s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            next = s_chunk;
+        } else {
+            next = a.nchunks;
         }
     }
     if (a.dynamic && t == 0) {

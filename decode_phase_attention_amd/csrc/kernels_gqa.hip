@@ -455,6 +455,81 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
 
 // ------------------------------------------------------------------ dynamic pull
 
+// Slot of a unit's piece in chunk ch: (ch, 0) if the piece starts the chunk,
+// else (ch, 1). A slot holds 16 records, one per query column.
+__device__ __forceinline__ int piece_slot_g(int ch, int Su, int C) {
+    return ch * 2 + (max(Su, ch * C) == ch * C ? 0 : 1);
+}
+
+__device__ __forceinline__ uint32_t rec_off(int slot, int q, int D) {
+    return (uint32_t)(slot * 16 + q) * (uint32_t)(part_stride(D) * 4);
+}
+
+// Thread (q, dc) stores its slice of column q's record of `slot`.
+template <int D>
+__device__ __forceinline__ void publish_rec_g(__amdgpu_buffer_rsrc_t xr, int slot, int q, int dc,
+                                              int geff, float M, float L,
+                                              const float (&O)[GGeo<D>::DPT]) {
+    using G = GGeo<D>;
+    if (q >= geff) return;
+    const uint32_t rec = rec_off(slot, q, D);
+#pragma unroll
+    for (int i = 0; i < G::DPT; i += 4)
+        store16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u,
+                      make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]));
+    if (dc == 0) store8_agent(xr, rec + (uint32_t)D * 4u, M, L);
+}
+
+// Workgroup-wide: once every wave's record stores have completed, add one to
+// the counter; true in every thread when that add was the last (`last` + 1).
+__device__ __forceinline__ bool count_in_wg(uint32_t* ctr, int last, int& s_word) {
+    drain_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_word = (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const bool mine = s_word == last;
+    __syncthreads();   // s_word is read by all before it can be written again
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return mine;
+}
+
+// Fold, in order, column qq's records of chunks ch0, ch0 + step, ... (n of
+// them) at slot level `lvl` into (M, L, O), replacing what they held.
+template <int D>
+__device__ __forceinline__ void fold_slots_g(__amdgpu_buffer_rsrc_t xr, int lvl, int ch0, int n,
+                                             int step, int Su, int C, int qq, int dc, float& M,
+                                             float& L, float (&O)[GGeo<D>::DPT]) {
+    using G = GGeo<D>;
+    constexpr int kBatch = 128 / D * 8;   // 16 records in flight at d = 64, 8 at d = 128
+    M = kNegInf;
+    L = 0.f;
+#pragma unroll
+    for (int i = 0; i < G::DPT; ++i) O[i] = 0.f;
+    for (int i0 = 0; i0 < n; i0 += kBatch) {
+        float pm[kBatch], pl[kBatch], po[kBatch][G::DPT];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int ch = ch0 + min(i0 + j, n - 1) * step;
+            const uint32_t rec = rec_off(lvl + piece_slot_g(ch, Su, C), qq, D);
+            const float2 ml = load8_agent(xr, rec + (uint32_t)D * 4u);
+            pm[j] = ml.x;
+            pl[j] = ml.y;
+#pragma unroll
+            for (int i = 0; i < G::DPT; i += 4) {
+                const float4 v = load16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u);
+                po[j][i] = v.x;
+                po[j][i + 1] = v.y;
+                po[j][i + 2] = v.z;
+                po[j][i + 3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (i0 + j < n) merge_into<G::DPT>(M, L, O, pm[j], pl[j], po[j]);
+    }
+}
+
 // Chunks of the unit tile sequence, taken from an atomic counter (dynamic) or
 // one per workgroup; a unit spread over chunks leaves 16 records (one per
 // query column) per chunk at slot (chunk, side), and the workgroup whose
@@ -472,20 +547,20 @@ __global__ __launch_bounds__(kThreads) void pull_gqa_kernel(const GqaArgs a) {
     const int dc = t & 15;
     const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
     stamp_start(a.ts, blockIdx.x);
+    // A workgroup takes its next chunk only when it has finished the last one
+    // (taking it earlier hands chunks to workgroups that are still busy while
+    // others, started later, find none).
     int next = blockIdx.x;
+    if (a.dynamic) {
+        if (t == 0)
+            s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        next = s_chunk;
+        __syncthreads();
+    }
     for (;;) {
-        int k;
-        if (a.dynamic) {
-            if (t == 0)
-                s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            k = s_chunk;
-            __syncthreads();
-        } else {
-            k = next;
-            next = a.nchunks;
-        }
+        const int k = next;
         if (k >= a.nchunks) break;
         const int c0 = k * a.C;
         const int c1 = min(c0 + a.C, a.I);
@@ -512,57 +587,43 @@ __global__ __launch_bounds__(kThreads) void pull_gqa_kernel(const GqaArgs a) {
             it = t1;
             const int kf = Su / a.C, kl = (Se - 1) / a.C;   // chunks holding unit u
             if (kf != kl) {
-                if (q < x.geff) {
-                    const uint32_t rec =
-                        (uint32_t)(((k * 2 + side) * 16) + q) * (uint32_t)(part_stride(D) * 4);
-#pragma unroll
-                    for (int i = 0; i < G::DPT; i += 4)
-                        store16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u,
-                                      make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]));
-                    if (dc == 0) store8_agent(xr, rec + (uint32_t)D * 4u, M, L);
+                // two-level merge tree over the unit's chunks (groups of
+                // kMergeFanIn), as in the single-head pull kernel
+                const int g0 = kf + (k - kf) / kMergeFanIn * kMergeFanIn;
+                const int g1 = min(g0 + kMergeFanIn - 1, kl);
+                const int ngroups = (kl - kf) / kMergeFanIn + 1;
+                const int gslot = piece_slot_g(g0, Su, a.C);
+                if (g1 > g0) {
+                    publish_rec_g<D>(xr, k * 2 + side, q, dc, x.geff, M, L, O);
+                    if (!count_in_wg(&a.gcount[gslot], g1 - g0, s_arrived)) continue;
+                    fold_slots_g<D>(xr, 0, g0, g1 - g0 + 1, 1, Su, a.C, min(q, x.geff - 1), dc,
+                                    M, L, O);
+                    if (t == 0)
+                        __hip_atomic_store(&a.gcount[gslot], 0u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 }
-                drain_stores();
-                __syncthreads();
-                if (t == 0)
-                    s_arrived = (int)__hip_atomic_fetch_add(&a.arrive[u], 1u, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
-                __syncthreads();
-                if (s_arrived != kl - kf) continue;
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                M = kNegInf;
-                L = 0.f;
-#pragma unroll
-                for (int i = 0; i < G::DPT; ++i) O[i] = 0.f;
-                constexpr int kBatch = 128 / D * 8;
-                const int qq = min(q, x.geff - 1);   // columns past the block read a valid record
-                for (int j0 = kf; j0 <= kl; j0 += kBatch) {
-                    float pm[kBatch], pl[kBatch], po[kBatch][G::DPT];
-#pragma unroll
-                    for (int j = 0; j < kBatch; ++j) {
-                        const int ch = min(j0 + j, kl);
-                        const int sd = max(Su, ch * a.C) == ch * a.C ? 0 : 1;
-                        const uint32_t rec =
-                            (uint32_t)((ch * 2 + sd) * 16 + qq) * (uint32_t)(part_stride(D) * 4);
-                        const float2 ml = load8_agent(xr, rec + (uint32_t)D * 4u);
-                        pm[j] = ml.x;
-                        pl[j] = ml.y;
-#pragma unroll
-                        for (int i = 0; i < G::DPT; i += 4) {
-                            const float4 v = load16_agent(xr, rec + (uint32_t)(dc * G::DPT + i) * 4u);
-                            po[j][i] = v.x;
-                            po[j][i + 1] = v.y;
-                            po[j][i + 2] = v.z;
-                            po[j][i + 3] = v.w;
-                        }
-                    }
-#pragma unroll
-                    for (int j = 0; j < kBatch; ++j)
-                        if (j0 + j <= kl) merge_into<G::DPT>(M, L, O, pm[j], pl[j], po[j]);
+                if (ngroups > 1) {
+                    const int l1 = 2 * a.nchunks;   // second-level slots follow the first
+                    publish_rec_g<D>(xr, l1 + gslot, q, dc, x.geff, M, L, O);
+                    if (!count_in_wg(&a.arrive[u], ngroups - 1, s_arrived)) continue;
+                    fold_slots_g<D>(xr, l1, kf, ngroups, kMergeFanIn, Su, a.C, min(q, x.geff - 1),
+                                    dc, M, L, O);
+                    if (t == 0)
+                        __hip_atomic_store(&a.arrive[u], 0u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (t == 0)
-                    __hip_atomic_store(&a.arrive[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             write_out_gqa<D>(a, x, q, dc, M, L, O);
+        }
+        if (a.dynamic) {
+            __syncthreads();
+            if (t == 0)
+                s_chunk = (int)__hip_atomic_fetch_add(&a.pull[0], 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            next = s_chunk;
+        } else {
+            next = a.nchunks;
         }
     }
     if (a.dynamic && t == 0) {

@@ -150,7 +150,8 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               tokens as a case to qualify (siliconandsystems digest,
  *               "Exactness and numerical qualification") but fix no mask.
  *   chunk_tiles pull kinds: tiles per chunk; 0 = ceil(I / (8 G)) with G the
- *               pull grid (or one workgroup per CU), and at least 16.
+ *               pull grid (or one workgroup per CU), and at least
+ *               min(32, ceil(I / G)).
  *
  * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
  * pieces": workgroups pull the next piece of the global tile order instead of
@@ -159,9 +160,11 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  * into chunks of chunk_tiles tiles. LA_KIND_PULL: a persistent grid of `grid`
  * workgroups (0 = la_default_grid, at most 65536) takes chunks from an atomic
  * counter until none is left. LA_KIND_CHUNKS: one workgroup per chunk. A head
- * spread over several chunks leaves one partial record per chunk; the
- * workgroup whose piece of it arrives last merges them with f in chunk order,
- * so outputs are bitwise the same whichever workgroup took which chunk. No
+ * spread over several chunks leaves one partial record per chunk; its chunks
+ * form groups of 16, the workgroup whose piece arrives last in a group folds
+ * the group with f in chunk order, and the last group folds the groups in
+ * order. The tree is fixed, so outputs are bitwise the same whichever
+ * workgroup took which chunk. No
  * workgroup ever waits for another (any grid is safe, co-resident or not).
  * With kv_heads or q_tokens the chunks cut the grouped units' tiles, and the
  * grouped exchange (16 records per chunk side) must fit 2 GiB, else

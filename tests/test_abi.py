@@ -169,3 +169,20 @@ def test_pull_kinds_validation():
     o.kind = la.LA_KIND_CHUNKS            # needs an explicit chunk size
     assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
     assert "chunk_tiles" in la.la_last_error()
+
+
+def test_binding_rejects_tensors_too_small_for_the_call():
+    """The library sees pointers only; the binding checks torch tensors against
+    the sizes the call implies (here on CPU tensors, before any device use)."""
+    import torch
+    q = torch.zeros(2, 8, 64, dtype=torch.float16)
+    kv = torch.zeros(2 * 300, 64, dtype=torch.float16)      # 2 K/V heads x 300 tokens
+    out = torch.zeros(2, 8, 64)
+    with pytest.raises(ValueError, match="k_cache"):
+        la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out)        # as if 8 K/V heads
+    with pytest.raises(ValueError, match="q "):
+        la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out, kv_heads=2, q_tokens=2)
+    with pytest.raises(ValueError, match="out"):
+        la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out.half(), kv_heads=2)
+    with pytest.raises(ValueError, match="device tensors"):        # sizes fine: then the device check
+        la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out, kv_heads=2)

@@ -85,7 +85,7 @@ def check_owner(owner, I, C, kind, grid=None):
             assert next(iter(vals)) < grid
 
 
-CASES = [([3000, 17, 60000, 129, 4096], 4, 128, "bf16"),
+CASES = [([3000, 17, 60000, 129, 4096, 2176], 4, 128, "bf16"),
          ([1, 700, 256, 2049], 8, 64, "f16"),
          ([20000], 32, 128, "f16")]
 
@@ -113,7 +113,7 @@ def test_pull_parity_and_tile_map(la, lens, H, d, dtype, grid, C):
     I = tiles(lens, H, L)
     owner = torch.full((I,), -1, dtype=torch.int32, device="cuda")
     check(run(la, inp, "pull", owner, grid=grid, chunk_tiles=C), ref, tag=f"pull grid={grid}")
-    Ceff = C if C > 0 else max(16, -(-I // (8 * grid)))
+    Ceff = C if C > 0 else max(min(32, -(-I // grid)), -(-I // (8 * grid)))
     check_owner(owner, I, Ceff, "pull", grid)
 
 
@@ -177,7 +177,7 @@ def test_grouped_and_several_tokens(la, H, Hk, Nq, d, dtype, kind, grid, C):
     check((out.cpu().numpy(), m.cpu().numpy().reshape(ref[1].shape),
            l.cpu().numpy().reshape(ref[2].shape)), ref, tag=f"grouped {kind}")
     G = grid if grid > 0 else la.la_default_grid(d, la.LA_BF16 if dtype == "bf16" else la.LA_F16)
-    Ceff = C if C > 0 else max(16, -(-I // (8 * G)))
+    Ceff = C if C > 0 else max(min(32, -(-I // G)), -(-I // (8 * G)))
     check_owner(owner, I, Ceff, kind, grid if kind == "pull" and grid > 0 else 1 << 30)
 
 
