@@ -681,6 +681,14 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
     std::lock_guard<std::mutex> lock(g_mu);
+    // The schedule tables are copied into a workspace that the next call on
+    // this stream reuses (and skipped when unchanged), so a captured call
+    // would replay whatever tables the workspace holds by then.
+    hipStreamCaptureStatus cap_status = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing((hipStream_t)stream, &cap_status));
+    if (cap_status != hipStreamCaptureStatusNone)
+        return fail(LA_EUNSUPPORTED, "stream capture is not supported (per-call schedule tables "
+                                     "live in a reused workspace)");
     if (o.kind == LA_KIND_AUTO) {
         int kind = 0, grid = 0;
         if ((st = select_on_device(ctx_lens, B, hd, d, o, &kind, &grid)) != LA_OK) return st;

@@ -192,6 +192,9 @@ typedef struct la_opts {
 
 void la_opts_init(la_opts* opts);
 
+/* Calls are asynchronous on `stream`; a stream that is being captured into a
+ * HIP graph is refused (LA_EUNSUPPORTED): each call copies its schedule tables
+ * into a per-stream workspace that later calls reuse. */
 la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* ctx_lens, int B, int H, int d, float scale,
                        float* out, void* stream, const la_opts* opts);

@@ -357,3 +357,35 @@ def test_timestamps(la, kind, blocks):
     assert np.all(a[:, 3] == 0)
     span_us = (a[:, 1].max() - a[:, 0].min()) / 100.0
     assert 0 < span_us < 1e6
+
+
+def test_stream_capture_is_refused(la):
+    """A stream being captured into a graph is refused before anything is
+    enqueued (the schedule tables live in a reused per-stream workspace)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    inp = W.make_custom([300, 40], H=2, d=64, dtype="f16", seed=61, device="cuda")
+    out = torch.empty((2, 2, 64), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    hip.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    hip.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipGraphDestroy.argtypes = [ctypes.c_void_p]
+    assert hip.hipStreamBeginCapture(ctypes.c_void_p(s.cuda_stream), 2) == 0   # relaxed mode
+    try:
+        with pytest.raises(la.LaError) as e:
+            la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, 2, 2, 64, inp.scale, out,
+                            stream=s.cuda_stream)
+    finally:
+        graph = ctypes.c_void_p()
+        assert hip.hipStreamEndCapture(ctypes.c_void_p(s.cuda_stream), ctypes.byref(graph)) == 0
+        if graph.value:
+            hip.hipGraphDestroy(graph)
+    assert e.value.status == 2 and "capture" in str(e.value)
+    # the stream works normally afterwards
+    la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, 2, 2, 64, inp.scale, out,
+                    stream=s.cuda_stream)
+    s.synchronize()
+    O = out.cpu().numpy()
+    Or = reference(inp)[0]
+    assert float(np.max(np.abs(O - Or))) <= 1e-3
