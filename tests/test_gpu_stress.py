@@ -74,3 +74,62 @@ def test_back_to_back_without_sync(la):
     la.la_sync_check()
     for o in outs:
         assert float(np.max(np.abs(o.cpu().numpy() - ref))) <= 1e-3
+
+
+def _random_case(rng):
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    H = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    Hk = int(rng.choice([h for h in (1, 2, 4, 8, 16, 32) if H % h == 0]))
+    Nq = int(rng.choice([1, 1, 1, 2, 3, 8]))
+    B = int(rng.integers(1, 9))
+    L = 2048 // d * 8
+    lens = []
+    for _ in range(B):
+        r = rng.random()
+        if r < 0.2:
+            n = int(rng.integers(1, 4)) * L + int(rng.integers(-1, 2))    # at a tile edge
+        else:
+            n = int(np.exp(rng.uniform(0, np.log(60000))))
+        lens.append(max(n, Nq, 1))
+    return d, dtype, H, Hk, Nq, lens
+
+
+def test_random_shapes_every_kind(la):
+    """Random ragged batches, grouped heads, several new tokens, head dims and
+    dtypes, under every kind with random grids, tiles and chunk sizes; each
+    launch against the oracle on all of its query rows."""
+    rng = np.random.default_rng(2024)
+    kinds = ["lean", "fixed_split", "per_head", "auto", "pull", "chunks"]
+    worst = 0.0
+    for i in range(60):
+        d, dtype, H, Hk, Nq, lens = _random_case(rng)
+        kind = kinds[i % len(kinds)]
+        grouped = H // Hk * Nq > 1
+        opts = {}
+        if kind == "lean":
+            dt = la.LA_BF16 if dtype == "bf16" else la.LA_F16
+            cap = min(la.la_max_grid(d, dt), 512 if grouped else 1 << 30)
+            opts = {"grid": int(rng.integers(1, cap + 1)),
+                    "tile_tokens": int(rng.choice([0, 16, 64, 300]))}
+        elif kind == "fixed_split":
+            opts = {"num_splits": int(rng.choice([0, 1, 3, 16, 64]))}
+        elif kind == "pull":
+            opts = {"grid": int(rng.choice([0, 1, 7, 256, 2000])),
+                    "chunk_tiles": int(rng.choice([0, 1, 2, 9]))}
+        elif kind == "chunks":
+            opts = {"chunk_tiles": int(rng.choice([0, 1, 5, 33]))}
+        print(f"[stress {i}] {kind} {opts} d={d} {dtype} H={H} Hk={Hk} Nq={Nq} lens={lens}",
+              file=sys.stderr, flush=True)
+        inp = W.make_custom(lens, H, d, dtype, seed=100 + i, device="cuda", kv_heads=Hk,
+                            q_tokens=Nq)
+        ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                                 inp.scale, dtype, workers=16, kv_heads=Hk)[0]
+        out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+        la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out, kind=kind,
+                        kv_heads=Hk, q_tokens=Nq, **opts)
+        la.la_sync_check()
+        err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+        assert err <= 1e-3, (i, kind, opts, err)
+        worst = max(worst, err)
+    print(f"60 random launches, worst max|dO| = {worst:.2e}", file=sys.stderr)
