@@ -302,7 +302,7 @@ def selector_sweep(steps=10, warmup=2, rounds=3):
         dt = la.LA_BF16 if s["dt"] == "bf16" else la.LA_F16
         pick, grid = la.la_select(inp.ctx_lens, inp.H, inp.d, dt, kv_heads=Hk, q_tokens=Nq)
         kinds = [("auto", "auto", {}), ("lean_1cu", "lean", {"grid": cus}),
-                 ("lean_2cu", "lean", {"grid": 2 * cus}),
+                 ("lean_2cu", "lean", {"grid": 2 * cus}), ("pull", "pull", {}),
                  ("per_head", "per_head", {}), ("fixed_split_heuristic", "fixed_split", {})]
         kinds += [(f"fixed_split_{K}", "fixed_split", {"num_splits": K}) for K in (2, 4, 8, 16, 32)]
         # rounds over all kinds, each round starting at another kind, so that
