@@ -7,16 +7,18 @@ reduction. The computation lives in the HIP library ``libla_decode.so``; this
 package only binds it (``binding``) and builds it (``build``).
 """
 from .binding import (LA_BF16, LA_F16, LA_KIND_AUTO, LA_KIND_CHUNKS, LA_KIND_FIXED_SPLIT,
-                      LA_KIND_LEAN, LA_KIND_PER_HEAD, LA_KIND_PULL, LaError, decode_attention, la_decode, la_decode_bf16,
-                      la_decode_ex, la_decode_f16, la_default_grid, la_default_tile,
-                      la_last_error, la_max_grid, la_schedule, la_schedule_dims, la_select,
-                      la_select_for, la_set_wait_limit_us, la_shutdown, la_sync_check, lib)
+                      LA_KIND_LEAN, LA_KIND_PER_HEAD, LA_KIND_PULL, LaError, decode_attention,
+                      la_decode, la_decode_bf16, la_decode_ex, la_decode_f16, la_default_grid,
+                      la_default_tile, la_last_error, la_max_grid, la_max_grid_grouped,
+                      la_schedule, la_schedule_dims, la_select, la_select_for,
+                      la_set_wait_limit_us, la_shutdown, la_sync_check, lib)
 
 __all__ = [
     "LA_BF16", "LA_F16", "LA_KIND_AUTO", "LA_KIND_CHUNKS", "LA_KIND_FIXED_SPLIT", "LA_KIND_LEAN",
     "LA_KIND_PER_HEAD", "LA_KIND_PULL",
     "LaError", "decode_attention", "la_decode", "la_decode_bf16", "la_decode_ex", "la_decode_f16",
-    "la_default_grid", "la_default_tile", "la_last_error", "la_max_grid", "la_schedule",
+    "la_default_grid", "la_default_tile", "la_last_error", "la_max_grid", "la_max_grid_grouped",
+    "la_schedule",
     "la_schedule_dims", "la_select", "la_select_for", "la_set_wait_limit_us", "la_shutdown",
     "la_sync_check", "lib",
 ]

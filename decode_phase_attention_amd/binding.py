@@ -20,7 +20,8 @@ __all__ = [
     "LaError", "LA_F16", "LA_BF16", "LA_KIND_LEAN", "LA_KIND_FIXED_SPLIT", "LA_KIND_PER_HEAD",
     "LA_KIND_AUTO", "LA_KIND_PULL", "LA_KIND_CHUNKS", "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex",
     "la_select", "la_select_for", "la_schedule",
-    "la_schedule_dims", "la_default_tile", "la_max_grid", "la_default_grid", "la_sync_check",
+    "la_schedule_dims", "la_default_tile", "la_max_grid", "la_max_grid_grouped", "la_default_grid",
+    "la_sync_check",
     "la_last_error",
     "la_shutdown", "la_set_wait_limit_us", "decode_attention", "LIB_PATH",
 ]
@@ -87,6 +88,7 @@ _SIG = {
                        ctypes.POINTER(_I)]),
     "la_default_tile": (_I, [_I]),
     "la_max_grid": (_I, [_I, _I]),
+    "la_max_grid_grouped": (_I, [_I, _I]),
     "la_default_grid": (_I, [_I, _I]),
     "la_sync_check": (_I, [_P]),
     "la_last_error": (ctypes.c_char_p, []),
@@ -325,6 +327,13 @@ def la_default_tile(d: int) -> int:
 
 def la_max_grid(d: int, dtype: int) -> int:
     g = int(lib().la_max_grid(int(d), int(dtype)))
+    if g <= 0:
+        raise LaError(LA_EHIP, la_last_error())
+    return g
+
+
+def la_max_grid_grouped(d: int, dtype: int) -> int:
+    g = int(lib().la_max_grid_grouped(int(d), int(dtype)))
     if g <= 0:
         raise LaError(LA_EHIP, la_last_error())
     return g

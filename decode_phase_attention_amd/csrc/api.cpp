@@ -1,9 +1,11 @@
 // C-ABI entry points of libla_decode (declared in include/la_decode.h).
 //
-// Per call: validate, run the host scheduler into a pinned staging slot, copy
-// the tables to the workspace's device buffer on the caller's stream, launch.
-// Workspaces are per (device, stream) so that concurrent streams never share a
-// partials buffer or flags.
+// Per call: validate, build the tables the kind needs (the stream-K schedule,
+// the chunk tables of the pull kinds, or only the per-request lengths and
+// offsets), copy them through a pinned staging slot to the workspace's device
+// buffer on the caller's stream -- unless the buffer already holds the same
+// bytes -- and launch. Workspaces are per (device, stream) so that concurrent
+// streams never share partials, flags or counters.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -800,6 +802,17 @@ int la_max_grid(int d, int dtype) {
     std::lock_guard<std::mutex> lock(g_mu);
     Capacity cap;
     if (capacity(dtype, d, false, &cap) != LA_OK) return -1;
+    return cap.coresident;
+}
+
+int la_max_grid_grouped(int d, int dtype) {
+    if ((d != 64 && d != 128) || (dtype != LA_F16 && dtype != LA_BF16)) {
+        fail(LA_EINVAL, "unsupported d/dtype");
+        return -1;
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    Capacity cap;
+    if (capacity(dtype, d, true, &cap) != LA_OK) return -1;
     return cap.coresident;
 }
 

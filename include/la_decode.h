@@ -256,8 +256,14 @@ int la_default_tile(int d);
 /*
  * Co-resident workgroup capacity of the lean kernel for (d, dtype) on the
  * current device: occupancy per CU times the CU count. Returns <= 0 on error.
+ * This is the bound on la_opts.grid for calls with one query column per K/V
+ * head; calls with kv_heads < H or q_tokens > 1 run the grouped kernel, whose
+ * bound is la_max_grid_grouped.
  */
 int la_max_grid(int d, int dtype);
+
+/* The same for the grouped (MFMA) lean kernel. */
+int la_max_grid_grouped(int d, int dtype);
 
 /*
  * Grid the lean kind uses when la_opts.grid is 0: one workgroup per CU on the

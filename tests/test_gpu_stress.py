@@ -109,7 +109,7 @@ def test_random_shapes_every_kind(la):
         opts = {}
         if kind == "lean":
             dt = la.LA_BF16 if dtype == "bf16" else la.LA_F16
-            cap = min(la.la_max_grid(d, dt), 512 if grouped else 1 << 30)
+            cap = la.la_max_grid_grouped(d, dt) if grouped else la.la_max_grid(d, dt)
             opts = {"grid": int(rng.integers(1, cap + 1)),
                     "tile_tokens": int(rng.choice([0, 16, 64, 300]))}
         elif kind == "fixed_split":
