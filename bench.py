@@ -421,6 +421,34 @@ def contention(workloads, steps=10, warmup=3):
                       "table": table}), flush=True)
 
 
+def tile_sweep(workloads, steps=20, warmup=3):
+    """The lean kernel at LeanTile sizes 32..2048 tokens on each workload (the
+    pages pick the tile per head dim and hardware); prints one JSON line."""
+    import torch
+
+    import decode_phase_attention_amd as la
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    la.lib()
+    evs = HipEvents()
+    table = {}
+    for name in workloads:
+        log(f"[tiles] {name}")
+        inp = W.make_inputs(name, seed=0, device="cuda")
+        row = {}
+        for L in (32, 64, 128, 256, 512, 1024, 2048):
+            r = time_kind(la, torch, evs, inp, "lean", steps, warmup, tile_tokens=L)
+            row[str(L)] = round(r["kernel_us_p50"], 1)
+        row["default"] = la.la_default_tile(inp.d)
+        table[name] = row
+        log(f"   {row}")
+        del inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "lean kernel p50 us by LeanTile size (tokens)",
+                      "device": torch.cuda.get_device_name(0), "table": table}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,6 +467,8 @@ def main():
     ap.add_argument("--selector-sweep", action="store_true",
                     help="instead of the workload: measure kind=auto against every kind "
                          "on a sweep of shapes")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="instead of the headline line: the lean kernel at tile sizes 32..2048")
     ap.add_argument("--contention", action="store_true",
                     help="instead of the headline line: every kind on streams confined to "
                          "part of the CUs (512k and ragged, or --workload)")
@@ -449,6 +479,9 @@ def main():
         sys.exit(2)
     if args.selector_sweep:
         selector_sweep()
+        return
+    if args.tile_sweep:
+        tile_sweep(["512k", "ragged", "65k", "many-heads", "gqa-512k", "gqa8-ragged"])
         return
     if args.contention:
         contention(["512k", "ragged"] if args.workload == "512k" else [args.workload])
