@@ -1,8 +1,12 @@
 // Decode-attention kernels for gfx950 (CDNA4).
 //
-// Three kernels share one streaming routine:
+// Four kernels share one streaming routine:
 //   lean_kernel      stream-K over a persistent grid with in-launch merging
 //                    (xllm-io paper review of arXiv 2405.10480, §3.3-§3.5, §4.4)
+//   pull_kernel      the same tile order in fixed chunks that workgroups pull
+//                    from a counter (or take one each), merged by the last
+//                    piece to arrive (siliconandsystems digest, "Exact softmax
+//                    can be reduced in pieces")
 //   split_kernel +   fixed split of every head into `splits` pieces and a
 //   combine_kernel   second launch that merges them (the FlashDecoding scheme the
 //                    same review describes in §2.3)

@@ -33,7 +33,10 @@
 // head dims [(t % 16) * D/16, +D/16), so a wave covers four whole records.
 // The exchange between workgroups is the same agent-scope, completion-ordered
 // protocol as the single-head kernels, with 16 records (one per query column)
-// per workgroup, moved in 16-byte device-coherent buffer accesses.
+// per workgroup, moved in 16-byte device-coherent buffer accesses. The same
+// four decompositions exist as for single heads: lean (static stream-K),
+// pull (chunks taken from a counter, merged by the last piece), fixed split +
+// combine, and per unit.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
