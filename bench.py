@@ -467,6 +467,8 @@ def main():
     ap.add_argument("--selector-sweep", action="store_true",
                     help="instead of the workload: measure kind=auto against every kind "
                          "on a sweep of shapes")
+    ap.add_argument("--jsonl", default=None,
+                    help="also append one JSON record per measured kernel kind to this file")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="instead of the headline line: the lean kernel at tile sizes 32..2048")
     ap.add_argument("--contention", action="store_true",
@@ -616,7 +618,36 @@ def main():
         "env": {"torch": torch.__version__, "python": platform.python_version(),
                 "device": torch.cuda.get_device_name(0)},
     }
+    if args.jsonl:
+        write_jsonl(args.jsonl, rec, lean, comparators, occ, splits, alg_bytes, cpu)
     print(json.dumps(rec), flush=True)
+
+
+def write_jsonl(path, rec, lean, comparators, occ, splits, alg_bytes, cpu):
+    """Append one record per (workload, kernel kind) measured in this run."""
+    kinds = {"lean": lean}
+    for k, v in (comparators or {}).items():
+        if isinstance(v, dict) and "kernel_us_mean" in v:
+            kinds[k] = v
+    with open(path, "a") as f:
+        for k, v in kinds.items():
+            us = v["kernel_us_p50"]
+            r = {"workload": rec["config"]["workload"], "kernel": k,
+                 "kernel_us_p10": round(v["kernel_us_p10"], 2), "kernel_us_p50": round(us, 2),
+                 "kernel_us_p90": round(v["kernel_us_p90"], 2),
+                 "us_per_step": round(v["us_per_step"], 2),
+                 "tbs": round(alg_bytes / (us * 1e-6) / 1e12, 3),
+                 "frac_of_8tbs": round(alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                 "num_splits": v.get("num_splits"),
+                 "busy_frac": ((occ or {}).get(k) or {}).get("busy_frac_mean_all_cus"),
+                 "grid": rec["config"]["grid"] if k == "lean" else None,
+                 "tile_tokens": rec["config"]["tile_tokens"],
+                 "lean_splits_per_head": splits if k == "lean" else None,
+                 "fetch_bytes": rec["roofline"]["traffic"] if k == "lean" else None,
+                 "seed": rec["config"]["seed"], "ctx_lens": rec["config"]["ctx_lens"],
+                 "oracle_us_per_step": (cpu or {}).get("value"),
+                 "oracle_cores": (cpu or {}).get("cores"), "env": rec["env"]}
+            f.write(json.dumps(r) + "\n")
 
 
 if __name__ == "__main__":
