@@ -618,21 +618,18 @@ la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int 
     return LA_OK;
 }
 
+// Best effort at shutdown: errors are ignored (there is no caller to report
+// them to, and freeing continues with the next buffer).
 void free_workspace(Workspace* w) {
-    hipSetDevice(w->device);
-    hipDeviceSynchronize();
-    hipFree(w->part);
-    hipFree(w->flags);
-    hipFree(w->err);
-    hipFree(w->split_part);
-    hipFree(w->pull_part);
-    hipFree(w->arrive);
-    hipFree(w->pull_ctr);
-    hipFree(w->gcount);
-    hipFree(w->tables);
+    (void)hipSetDevice(w->device);
+    (void)hipDeviceSynchronize();
+    for (void* p : {(void*)w->part, (void*)w->flags, (void*)w->err, (void*)w->split_part,
+                    (void*)w->pull_part, (void*)w->arrive, (void*)w->pull_ctr, (void*)w->gcount,
+                    w->tables})
+        if (p != nullptr) (void)hipFree(p);
     for (auto& s : w->ring) {
-        if (s.host != nullptr) hipHostFree(s.host);
-        if (s.ev != nullptr) hipEventDestroy(s.ev);
+        if (s.host != nullptr) (void)hipHostFree(s.host);
+        if (s.ev != nullptr) (void)hipEventDestroy(s.ev);
     }
     delete w;
 }

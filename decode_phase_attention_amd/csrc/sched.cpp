@@ -40,6 +40,7 @@ int schedule_dims(const int32_t* ctx_lens, int B, int H, int L, int grid, int64_
 int build_schedule(const int32_t* ctx_lens, int B, int H, int L, int G, int64_t I,
                    int32_t* cta_begin, int32_t* cta_seg, int32_t* rows6, int32_t* rows4,
                    int32_t* host_cta, int32_t* last_cta) {
+    (void)B;   // the head cursor stops at I, within the B * H heads
     const int64_t base = I / G;
     const int64_t extra = I % G;
     // head cursor: head u covers iterations [head_lo, head_lo + Tu)

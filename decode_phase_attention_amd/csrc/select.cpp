@@ -25,6 +25,8 @@
 //      ragged lengths its balance is better.
 #include "select.h"
 
+#include <stddef.h>
+
 #include <vector>
 
 #include "sched.h"
