@@ -10,7 +10,6 @@ import os
 import random
 import re
 
-import numpy as np
 import pytest
 
 import oracle

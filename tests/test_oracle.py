@@ -25,7 +25,6 @@ import pytest
 import torch
 
 import oracle
-from oracle import attention as att
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
