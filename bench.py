@@ -7,7 +7,8 @@ scheduler builds the stream-K tables, they are copied to the device, and the
 lean kernel runs. Inputs are seeded synthetic caches already resident in HBM.
 Prints one JSON line on stdout (the last line); progress goes to stderr.
 
-`value` is microseconds per step (host-observed, whole call). The `roofline`
+`value` is microseconds per step (host-observed, whole call, a loop of plain
+calls; the kernel times come from a second loop with HIP events). The `roofline`
 object prices the lean kernel alone: algorithmic bytes per launch (K and V
 once, q once, the fp32 output once) over the kernel's average duration,
 measured with HIP events recorded on the call's stream right around the
@@ -71,7 +72,10 @@ class HipEvents:
 
 
 def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
-    """Host-observed µs/step and mean kernel µs (HIP events around the kernels)."""
+    """Host-observed µs/step over `steps` plain calls (synchronised on both
+    sides), then kernel µs from HIP events around the kernels over another
+    `steps` calls (the events add their own gaps, so they stay out of the
+    first loop)."""
     B, H, d = inp.B, inp.H, inp.d
     out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device=inp.q.device)
 
@@ -82,13 +86,17 @@ def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
     for _ in range(warmup):
         call()
     la.la_sync_check()
-    pairs = evs.create(2 * steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    la.la_sync_check()
+    pairs = evs.create(2 * steps)
     for i in range(steps):
         call(pairs[2 * i], pairs[2 * i + 1])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     la.la_sync_check()
     kern = [evs.elapsed_ms(pairs[2 * i], pairs[2 * i + 1]) * 1e3 for i in range(steps)]
     evs.destroy(pairs)
