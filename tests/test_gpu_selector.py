@@ -69,3 +69,18 @@ def test_auto_parity(la, lens, H, Hk, Nq, d, dtype, want):
     assert np.all(np.abs(M - mr) <= 1e-5 * np.maximum(1.0, np.abs(mr)))
     assert float(np.max(np.abs(L * np.exp(M.astype(np.float64) - mr) - lr) / lr)) <= 1e-5
     say(f"[auto] picked {pick}@{grid}, max|dO|={err:.2e}")
+
+
+def test_decode_attention_wrapper(la):
+    """The convenience wrapper: shapes from the tensors, 4-D q for several new
+    tokens, grouped K/V heads, kind auto."""
+    lens = [900, 37]
+    inp = W.make_custom(lens, 8, 64, "f16", seed=5, device="cuda", kv_heads=2, q_tokens=3)
+    out = la.decode_attention(inp.q, inp.k, inp.v, lens, kind="auto", kv_heads=2)
+    la.la_sync_check()
+    assert tuple(out.shape) == (2, 3, 8, 64) and out.dtype == torch.float32
+    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                             inp.scale, "f16", workers=8, kv_heads=2)[0]
+    assert float(np.max(np.abs(out.cpu().numpy() - ref))) <= 1e-3
+    with pytest.raises(ValueError):       # K/V sized for 2 heads, called as 8
+        la.decode_attention(inp.q, inp.k, inp.v, lens)
