@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_phase_attention_amd", "csrc", f)
-                  for f in ("kernels.hip", "kernels_gqa.hip", "kernels.h", "device_common.h")]
+                  for f in ("kernels.hip", "kernels_gqa.hip", "kernels.h", "device_common.h",
+                            "seg_walk.h")]
 METRIC = "decode-attention µs/step + achieved HBM TB/s vs 8 TB/s peak (512k, ragged)"
 
 

@@ -62,6 +62,7 @@ class LaOpts(ctypes.Structure):
         ("kv_heads", ctypes.c_int),
         ("q_tokens", ctypes.c_int),
         ("chunk_tiles", ctypes.c_int),
+        ("host_tables", ctypes.c_int),
     ]
 
 
@@ -230,7 +231,7 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
 def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
-                 ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0):
+                 ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0, host_tables=False):
     o = LaOpts()              # ctypes zero-fills it: the same as la_opts_init
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
     o.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
@@ -261,6 +262,8 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
         o.q_tokens = int(q_tokens)
     if chunk_tiles:
         o.chunk_tiles = int(chunk_tiles)
+    if host_tables:
+        o.host_tables = 1
     arr, p = _lens(ctx_lens)
     _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, kv_heads, q_tokens, m_out, l_out)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),

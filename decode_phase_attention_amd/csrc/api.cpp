@@ -149,15 +149,24 @@ la_status get_workspace(hipStream_t stream, Workspace** out) {
 la_status capacity(int dtype, int d, bool grouped, Capacity* out) {
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
-    const void* fn = grouped ? la::lean_gqa_kernel_ptr(dtype, d) : la::lean_kernel_ptr(dtype, d);
-    auto key = std::make_pair(dev, fn);
+    // the smaller occupancy of the two instantiations (segments derived in
+    // the launch or read from tables): the same grid limits for both
+    const void* fn[2];
+    for (int il = 0; il < 2; ++il)
+        fn[il] = grouped ? la::lean_gqa_kernel_ptr(dtype, d, il != 0)
+                         : la::lean_kernel_ptr(dtype, d, il != 0);
+    auto key = std::make_pair(dev, fn[0]);
     auto it = g_capacity.find(key);
     if (it != g_capacity.end()) {
         *out = it->second;
         return LA_OK;
     }
-    int per_cu = 0, cus = 0;
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, la::kThreads, 0));
+    int per_cu = 1 << 30, cus = 0;
+    for (int il = 0; il < 2; ++il) {
+        int p = 0;
+        HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, fn[il], la::kThreads, 0));
+        per_cu = p < per_cu ? p : per_cu;
+    }
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     if (per_cu < 1 || cus < 1) return fail(LA_EHIP, "lean kernel does not fit on this device");
     Capacity c;
@@ -320,41 +329,56 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
                                      &G, &max_rows, &why);
     if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
 
-    // table layout in one buffer
-    const int BU = B * U;
-    const size_t off_seg = 0;
-    const size_t off_cta_seg = align16(off_seg + 16 * (size_t)max_rows);
-    const size_t off_cta_begin = align16(off_cta_seg + 4 * (size_t)(G + 1));
-    const size_t off_last = align16(off_cta_begin + 4 * (size_t)(G + 1));
-    const size_t off_host = align16(off_last + 4 * (size_t)BU);
-    const ReqLayout rl = req_layout(off_host + 4 * (size_t)BU, B);
-
-    g_build.assign(rl.bytes, 0);
-    char* hb = g_build.data();
-    la::build_schedule(ctx_lens, B, U, L, G, I, (int32_t*)(hb + off_cta_begin),
-                       (int32_t*)(hb + off_cta_seg), nullptr, (int32_t*)(hb + off_seg),
-                       (int32_t*)(hb + off_host), (int32_t*)(hb + off_last));
-    fill_req(hb, rl, ctx_lens, B);
-
     const size_t records = (size_t)G * (hd.grouped ? 16 : 1);
     if ((st = grow(w, (void**)&w.part, &w.part_cap, sizeof(float) * records * la::part_stride(d),
                    false)) != LA_OK)
         return st;
     if ((st = grow(w, (void**)&w.flags, &w.flags_cap, sizeof(uint32_t) * (size_t)G, true)) != LA_OK)
         return st;
-    if ((st = upload(w, hb, rl.bytes)) != LA_OK) return st;
 
-    char* db = (char*)w.tables;
+    // Where the workgroups find their segments. Up to kInlineB requests: the
+    // lengths travel in the kernel arguments and each workgroup derives its
+    // own segments (nothing is copied on the stream, which matters when the
+    // lengths change every decode step). Otherwise, or on request, the host
+    // builds the tables and uploads them.
+    la::SchedArgs sa{};
+    sa.B = B;
+    sa.U = U;
+    sa.L = L;
+    sa.G = G;
+    if (B <= la::kInlineB && o.host_tables == 0) {
+        sa.inline_lens = 1;
+        for (int b = 0; b < B; ++b) sa.lens[b] = ctx_lens[b];
+    } else {
+        const int BU = B * U;
+        const size_t off_seg = 0;
+        const size_t off_cta_seg = align16(off_seg + 16 * (size_t)max_rows);
+        const size_t off_cta_begin = align16(off_cta_seg + 4 * (size_t)(G + 1));
+        const size_t off_last = align16(off_cta_begin + 4 * (size_t)(G + 1));
+        const size_t off_host = align16(off_last + 4 * (size_t)BU);
+        const ReqLayout rl = req_layout(off_host + 4 * (size_t)BU, B);
+        g_build.assign(rl.bytes, 0);
+        char* hb = g_build.data();
+        la::build_schedule(ctx_lens, B, U, L, G, I, (int32_t*)(hb + off_cta_begin),
+                           (int32_t*)(hb + off_cta_seg), nullptr, (int32_t*)(hb + off_seg),
+                           (int32_t*)(hb + off_host), (int32_t*)(hb + off_last));
+        fill_req(hb, rl, ctx_lens, B);
+        if ((st = upload(w, hb, rl.bytes)) != LA_OK) return st;
+        const char* db = (const char*)w.tables;
+        sa.inline_lens = 0;
+        sa.seg = (const int4*)(db + off_seg);
+        sa.cta_seg = (const int32_t*)(db + off_cta_seg);
+        sa.cta_begin = (const int32_t*)(db + off_cta_begin);
+        sa.last_cta = (const int32_t*)(db + off_last);
+        sa.ctx = (const int32_t*)(db + rl.off_ctx);
+        sa.tok_off = (const int64_t*)(db + rl.off_tok);
+    }
+
     const bool coop = o.cooperative != 0;
     if (hd.grouped) {
         la::GqaArgs a{};
         fill_gqa(a, q, k, v, out, o, hd, L, scale);
-        a.ctx = (const int32_t*)(db + rl.off_ctx);
-        a.tok_off = (const int64_t*)(db + rl.off_tok);
-        a.seg = (const int4*)(db + off_seg);
-        a.cta_seg = (const int32_t*)(db + off_cta_seg);
-        a.cta_begin = (const int32_t*)(db + off_cta_begin);
-        a.last_cta = (const int32_t*)(db + off_last);
+        a.sched = sa;
         a.part = w.part;
         a.part_bytes = w.part_cap > (size_t)INT32_MAX ? (uint32_t)INT32_MAX : (uint32_t)w.part_cap;
         a.flags = w.flags;
@@ -371,12 +395,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     a.out = out;
     a.m_out = o.m_out;
     a.l_out = o.l_out;
-    a.ctx = (const int32_t*)(db + rl.off_ctx);
-    a.tok_off = (const int64_t*)(db + rl.off_tok);
-    a.seg = (const int4*)(db + off_seg);
-    a.cta_seg = (const int32_t*)(db + off_cta_seg);
-    a.cta_begin = (const int32_t*)(db + off_cta_begin);
-    a.last_cta = (const int32_t*)(db + off_last);
+    a.sched = sa;
     a.part = w.part;
     a.flags = w.flags;
     a.err = w.err;

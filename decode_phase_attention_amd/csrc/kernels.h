@@ -18,6 +18,27 @@ constexpr int chunk_rows(int d) { return (2048 / d) * kRows; }
 // Stride in floats of one partial record (Obar[d], m, l), padded to 16 bytes.
 constexpr int part_stride(int d) { return d + 4; }
 
+// Where a lean workgroup finds its segments: in tables built and uploaded by
+// the host, or -- for up to kInlineB requests -- derived by the workgroup
+// itself from the context lengths carried in the kernel arguments (no table
+// copy on the stream; the partition and head walk are the host scheduler's).
+constexpr int kInlineB = 256;
+
+struct SchedArgs {
+    const int4* seg;           // tables: [nseg] (u, t0, t1, host | finishing << 1)
+    const int32_t* cta_seg;    // tables: [G+1]
+    const int32_t* cta_begin;  // tables: [G+1]
+    const int32_t* last_cta;   // tables: [B*U]
+    const int32_t* ctx;        // tables: [B] n_b
+    const int64_t* tok_off;    // tables: [B] sum_{b'<b} n_b'
+    int inline_lens;           // 1: derive from `lens`; 0: read the tables
+    int B;                     // requests
+    int U;                     // schedule units per request
+    int L;                     // tile tokens
+    int G;                     // workgroups launched
+    int32_t lens[kInlineB];    // inline: n_b
+};
+
 struct LeanArgs {
     const uint16_t* q;         // [B*H, d]
     const uint16_t* k;         // packed rows [H * sum n_b, d]
@@ -25,12 +46,7 @@ struct LeanArgs {
     float* out;                // [B*H, d]
     float* m_out;              // optional [B*H]
     float* l_out;              // optional [B*H]
-    const int32_t* ctx;        // [B] n_b
-    const int64_t* tok_off;    // [B] sum_{b'<b} n_b'
-    const int4* seg;           // [nseg] (u, t0, t1, host | finishing << 1)
-    const int32_t* cta_seg;    // [G+1]
-    const int32_t* cta_begin;  // [G+1]
-    const int32_t* last_cta;   // [B*H]
+    SchedArgs sched;
     float* part;               // [G * part_stride(d)]
     uint32_t* flags;           // [G], zero at launch, zero again at exit
     uint32_t* err;             // device error word
@@ -79,12 +95,9 @@ struct GqaArgs {
     float* out;                // [B*Nq*H, d]
     float* m_out;              // optional [B*Nq*H]
     float* l_out;              // optional [B*Nq*H]
-    const int32_t* ctx;        // [B]
+    const int32_t* ctx;        // [B] (fixed split, per unit, pull)
     const int64_t* tok_off;    // [B]
-    const int4* seg;           // lean tables, as in LeanArgs (units instead of heads)
-    const int32_t* cta_seg;
-    const int32_t* cta_begin;
-    const int32_t* last_cta;
+    SchedArgs sched;           // lean (units instead of heads)
     float* part;               // lean: [G*16]; split: [units*splits*16] records
     uint32_t part_bytes;       // size of the lean exchange buffer (bounds its accesses)
     uint32_t* flags;
@@ -149,9 +162,9 @@ struct PullArgs {
     float sl2e;
 };
 
-const void* lean_kernel_ptr(int dtype, int d);
+const void* lean_kernel_ptr(int dtype, int d, bool inline_lens);
 hipError_t launch_pull(int dtype, int d, const PullArgs& a, int grid, hipStream_t s);
-const void* lean_gqa_kernel_ptr(int dtype, int d);
+const void* lean_gqa_kernel_ptr(int dtype, int d, bool inline_lens);
 hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,
                            bool cooperative);
 hipError_t launch_split_gqa(int dtype, int d, const GqaArgs& a, int blocks, hipStream_t s);

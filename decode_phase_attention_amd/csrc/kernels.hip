@@ -274,41 +274,38 @@ __device__ __forceinline__ void write_out(float* out, float* m_out, float* l_out
 
 // ------------------------------------------------------------------ lean
 
-template <int DT, int D>
+template <int DT, int D, bool IL>
 __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     using G = Geo<D>;
     constexpr int P = kDpl<D>;
     __shared__ Smem<D> sm;
+    __shared__ SchedLds sl;
     const int c = blockIdx.x;
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
     stamp_start(a.ts, c);
-    const int s0 = a.cta_seg[c], s1 = a.cta_seg[c + 1];
-    int iter = a.cta_begin[c];
-    for (int si = s0; si < s1; ++si) {
-        const int4 sg = a.seg[si];
-        const int u = sg.x;
-        const int b = u / a.H;
-        const int h = u - b * a.H;
-        const int n = a.ctx[b];
-        const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
-        const int tok0 = sg.y * a.L;
-        const int tok1 = (int)min((int64_t)sg.z * a.L, (int64_t)n);
+    SegCursor<IL> cur(a.sched, kernarg_lens<LeanArgs>(), sl, c);
+    LeanSeg sg;
+    while (cur.next(sg)) {
+        const int u = sg.u;
+        const int n = sg.n;
+        const int64_t row0 = (int64_t)a.H * sg.tok_off + (int64_t)sg.unit * n;
+        const int tok0 = sg.t0 * a.L;
+        const int tok1 = (int)min((int64_t)sg.t1 * a.L, (int64_t)n);
         Acc acc;
         acc_init(acc);
         stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, load_q(a.q, u, D, sub),
                             a.sl2e, grp, sub, acc);
         if (a.tile_owner != nullptr && t == 0)
-            for (int i = sg.y; i < sg.z; ++i) a.tile_owner[iter + i - sg.y] = c;
-        iter += sg.z - sg.y;
+            for (int i = sg.t0; i < sg.t1; ++i) a.tile_owner[sg.iter0 + i - sg.t0] = c;
 
         float M = kNegInf, Ls = 0.f, O[P];
         wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
         if (t >= 64) continue;   // the epilogue is wave 0's; the others go on streaming
 
-        if (!(sg.w & 1)) {
+        if (!sg.host) {
             // a peer: publish (Obar, m, l) for the head's host, then raise the flag
             float* p = a.part + (int64_t)c * part_stride(D);
 #pragma unroll
@@ -321,11 +318,11 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
             if (lane == 0) __hip_atomic_store(&a.flags[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
         }
-        if (!(sg.w & 2)) {
+        if (!sg.fin) {
             // The host. Its peers (c, last] each publish one partial: wait for
             // all of them at once (one flag per lane), then fold them in
             // ascending workgroup order with their loads issued in batches.
-            const int last = a.last_cta[u];
+            const int last = sg.last;
             const int np = last - c;
             for (int i = lane; i < np; i += 64) wait_flag(&a.flags[c + 1 + i], a.wait_ticks, a.err);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -616,14 +613,17 @@ const void* pick(int dtype, int d, F f16_64, F f16_128, F bf16_64, F bf16_128) {
 
 }  // namespace
 
-const void* lean_kernel_ptr(int dtype, int d) {
-    return pick(dtype, d, &lean_kernel<0, 64>, &lean_kernel<0, 128>, &lean_kernel<1, 64>,
-                &lean_kernel<1, 128>);
+const void* lean_kernel_ptr(int dtype, int d, bool inline_lens) {
+    if (inline_lens)
+        return pick(dtype, d, &lean_kernel<0, 64, true>, &lean_kernel<0, 128, true>,
+                    &lean_kernel<1, 64, true>, &lean_kernel<1, 128, true>);
+    return pick(dtype, d, &lean_kernel<0, 64, false>, &lean_kernel<0, 128, false>,
+                &lean_kernel<1, 64, false>, &lean_kernel<1, 128, false>);
 }
 
 hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_t s,
                        bool cooperative) {
-    const void* fn = lean_kernel_ptr(dtype, d);
+    const void* fn = lean_kernel_ptr(dtype, d, a.sched.inline_lens != 0);
     void* args[] = {const_cast<LeanArgs*>(&a)};
     if (cooperative)
         return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);

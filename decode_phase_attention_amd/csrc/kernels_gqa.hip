@@ -309,6 +309,19 @@ struct Unit {
     int n;
 };
 
+// A unit met through a lean segment: its request, length and token offset
+// come with the segment.
+__device__ __forceinline__ Unit decode_unit(const GqaArgs& a, const LeanSeg& s) {
+    Unit x;
+    x.b = s.b;
+    x.kvh = s.unit / a.QB;
+    x.qb = s.unit - x.kvh * a.QB;
+    x.geff = min(16, a.cols - 16 * x.qb);
+    x.n = s.n;
+    x.kvrow0 = (int64_t)a.Hk * s.tok_off + (int64_t)x.kvh * x.n;
+    return x;
+}
+
 __device__ __forceinline__ Unit decode_unit(const GqaArgs& a, int u) {
     Unit x;
     const int upr = a.Hk * a.QB;
@@ -363,10 +376,11 @@ __device__ __forceinline__ void write_out_gqa(const GqaArgs& a, const Unit& x, i
 
 // ------------------------------------------------------------------ lean
 
-template <int DT, int D>
+template <int DT, int D, bool IL>
 __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     using G = GGeo<D>;
     __shared__ GSmem<D> sm;
+    __shared__ SchedLds sl;
     const int cta = blockIdx.x;
     const int t = threadIdx.x;
     const int wave = t >> 6;
@@ -376,14 +390,13 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     const int dc = t & 15;
     const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
     stamp_start(a.ts, cta);
-    const int s0 = a.cta_seg[cta], s1 = a.cta_seg[cta + 1];
-    int iter = a.cta_begin[cta];
-    for (int si = s0; si < s1; ++si) {
-        const int4 sg = a.seg[si];
-        const int u = sg.x;
-        const Unit x = decode_unit(a, u);
-        const int tok0 = sg.y * a.L;
-        const int tok1 = (int)min((int64_t)sg.z * a.L, (int64_t)x.n);
+    SegCursor<IL> cur(a.sched, kernarg_lens<GqaArgs>(), sl, cta);
+    LeanSeg sg;
+    while (cur.next(sg)) {
+        const int u = sg.u;
+        const Unit x = decode_unit(a, sg);
+        const int tok0 = sg.t0 * a.L;
+        const int tok1 = (int)min((int64_t)sg.t1 * a.L, (int64_t)x.n);
         u32x4_t qt[G::KK];
         load_qt<D>(a.q, c < x.geff ? col_row(a, x, c) : 0, c < x.geff, w, qt);
         int full, lim;
@@ -393,13 +406,12 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
         gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, full, lim, wave, w,
                          c, qt, a.sl2e, st);
         if (a.tile_owner != nullptr && t == 0)
-            for (int i = sg.y; i < sg.z; ++i) a.tile_owner[iter + i - sg.y] = cta;
-        iter += sg.z - sg.y;
+            for (int i = sg.t0; i < sg.t1; ++i) a.tile_owner[sg.iter0 + i - sg.t0] = cta;
 
         float M, L, O[G::DPT];
         gqa_fold<D>(sm, st, wave, w, c, M, L, O);
 
-        if (!(sg.w & 1)) {
+        if (!sg.host) {
             // a peer: publish one record per query column, then raise the flag
             if (q < x.geff) {
                 const uint32_t rec = (uint32_t)(cta * 16 + q) * (uint32_t)(part_stride(D) * 4);
@@ -414,11 +426,11 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
             if (t == 0) __hip_atomic_store(&a.flags[cta], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
         }
-        if (!(sg.w & 2)) {
+        if (!sg.fin) {
             // the host: wait for every peer at once, then fold their records in
             // ascending workgroup order, a batch of peers' loads in flight at a
             // time (the streaming registers are free by now)
-            const int last = a.last_cta[u];
+            const int last = sg.last;
             const int np = last - cta;
             for (int i = t; i < np; i += kThreads) wait_flag(&a.flags[cta + 1 + i], a.wait_ticks, a.err);
             __syncthreads();
@@ -745,14 +757,17 @@ const void* pick_g(int dtype, int d, F f16_64, F f16_128, F bf16_64, F bf16_128)
 
 }  // namespace
 
-const void* lean_gqa_kernel_ptr(int dtype, int d) {
-    return pick_g(dtype, d, &lean_gqa_kernel<0, 64>, &lean_gqa_kernel<0, 128>,
-                  &lean_gqa_kernel<1, 64>, &lean_gqa_kernel<1, 128>);
+const void* lean_gqa_kernel_ptr(int dtype, int d, bool inline_lens) {
+    if (inline_lens)
+        return pick_g(dtype, d, &lean_gqa_kernel<0, 64, true>, &lean_gqa_kernel<0, 128, true>,
+                      &lean_gqa_kernel<1, 64, true>, &lean_gqa_kernel<1, 128, true>);
+    return pick_g(dtype, d, &lean_gqa_kernel<0, 64, false>, &lean_gqa_kernel<0, 128, false>,
+                  &lean_gqa_kernel<1, 64, false>, &lean_gqa_kernel<1, 128, false>);
 }
 
 hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,
                            bool cooperative) {
-    const void* fn = lean_gqa_kernel_ptr(dtype, d);
+    const void* fn = lean_gqa_kernel_ptr(dtype, d, a.sched.inline_lens != 0);
     void* args[] = {const_cast<GqaArgs*>(&a)};
     if (cooperative)
         return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);

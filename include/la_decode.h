@@ -171,6 +171,11 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  * LA_EUNSUPPORTED. tile_owner receives the workgroup that processed each
  * tile; cta_timestamps needs an explicit grid (pull: grid*4 entries) or
  * chunk_tiles (chunks: ceil(I / chunk_tiles)*4 entries).
+ *   host_tables lean kind: 1 = the host builds the schedule tables and copies
+ *               them to the device on `stream` before the kernel; 0 = with up
+ *               to 256 requests, the lengths travel in the kernel arguments and
+ *               every workgroup derives its own segments with the same rules
+ *               (no copy on the stream), else as 1.
  */
 typedef struct la_opts {
     int dtype;
@@ -188,6 +193,7 @@ typedef struct la_opts {
     int kv_heads;
     int q_tokens;
     int chunk_tiles;
+    int host_tables;
 } la_opts;
 
 void la_opts_init(la_opts* opts);

@@ -76,9 +76,10 @@ def test_groups_ragged(la, H, Hk, dtype, d):
         check(run(la, inp, kind), ref, tag=f"H={H}/Hk={Hk}/{dtype}/{d}/{kind}")
 
 
+@pytest.mark.parametrize("host_tables", [False, True])
 @pytest.mark.parametrize("grid", [1, 3, 37, 0])
 @pytest.mark.parametrize("tile", [0, 32, 200])
-def test_schedule_invariance_and_tile_map(la, grid, tile):
+def test_schedule_invariance_and_tile_map(la, grid, tile, host_tables):
     lens = [33, 1, 700, 2048, 5]
     H, Hk, d = 24, 2, 128            # g = 12: one query block per K/V head
     inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=62, device="cuda", kv_heads=Hk)
@@ -90,7 +91,8 @@ def test_schedule_invariance_and_tile_map(la, grid, tile):
     for (c, u, t0, t1, _h, _f) in s["seg"]:
         own[s["S"][u] + t0:s["S"][u] + t1] = c
     owner = torch.full((own.size,), -1, dtype=torch.int32, device="cuda")
-    got = run(la, inp, "lean", grid=grid, tile_tokens=tile, tile_owner=owner)
+    got = run(la, inp, "lean", grid=grid, tile_tokens=tile, tile_owner=owner,
+              host_tables=host_tables)
     check(got, reference(inp), tag=f"grid={grid} tile={tile}")
     assert np.array_equal(owner.cpu().numpy(), own)
 

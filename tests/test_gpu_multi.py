@@ -92,8 +92,9 @@ def test_tokens_ragged(la, Nq, H, Hk, dtype, d):
         check(run(la, inp, kind), ref, tag=f"{kind} Nq={Nq} H={H} Hk={Hk} {dtype} d={d}")
 
 
+@pytest.mark.parametrize("host_tables", [False, True])
 @pytest.mark.parametrize("grid,tile", [(1, 128), (7, 128), (64, 32), (300, 256), (512, 128)])
-def test_schedule_invariance_and_tile_map(la, grid, tile):
+def test_schedule_invariance_and_tile_map(la, grid, tile, host_tables):
     H, Hk, Nq, d = 8, 2, 4, 128
     lens = [515, 4, 1030, 129, 2000]
     say(f"[multi sched] grid={grid} tile={tile}")
@@ -102,7 +103,8 @@ def test_schedule_invariance_and_tile_map(la, grid, tile):
     U = units_per_req(H, Hk, Nq)
     sch = lean_schedule(lens, U, tile, grid)
     owner = torch.full((sch["I"],), -1, dtype=torch.int32, device="cuda")
-    got = run(la, inp, "lean", grid=grid, tile_tokens=tile, tile_owner=owner)
+    got = run(la, inp, "lean", grid=grid, tile_tokens=tile, tile_owner=owner,
+              host_tables=host_tables)
     check(got, ref, tag=f"grid={grid} tile={tile}")
     want = np.repeat(np.arange(sch["G"]), np.diff(sch["cta_begin"]))
     np.testing.assert_array_equal(owner.cpu().numpy(), want)

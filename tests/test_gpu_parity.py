@@ -120,12 +120,14 @@ def test_ragged_small(la, dtype, d, kind):
     check(run(la, inp, kind), ref, tag=f"{dtype}/{d}/{kind}")
 
 
+@pytest.mark.parametrize("host_tables", [False, True])
 @pytest.mark.parametrize("grid", [1, 2, 3, 7, 255, 0, -1])
 @pytest.mark.parametrize("tile", [0, 16, 100, 384])
-def test_lean_schedule_invariance(la, grid, tile):
+def test_lean_schedule_invariance(la, grid, tile, host_tables):
     """Any grid (0: the default, -1: the co-resident maximum) and LeanTile size
     gives the oracle's result, and the kernel executes exactly the oracle's
-    tile-to-workgroup map."""
+    tile-to-workgroup map, with the segments derived in the launch or read
+    from the host's tables."""
     lens = [33, 1, 700, 2048, 5]
     H, d = 4, 128
     inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=3, device="cuda")
@@ -135,8 +137,9 @@ def test_lean_schedule_invariance(la, grid, tile):
     G_req = grid if grid else la.la_default_grid(d, la.LA_BF16)
     own_ref, G = tile_owner_ref(lens, H, L, G_req)
     owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
-    say(f"[invariance grid={grid} tile={tile}]")
-    got = run(la, inp, "lean", grid=grid, tile_tokens=tile, tile_owner=owner)
+    say(f"[invariance grid={grid} tile={tile} host_tables={host_tables}]")
+    got = run(la, inp, "lean", grid=grid, tile_tokens=tile, tile_owner=owner,
+              host_tables=host_tables)
     check(got, reference(inp), tag=f"grid={grid} tile={tile}")
     assert np.array_equal(owner.cpu().numpy(), own_ref)
 
@@ -295,6 +298,30 @@ def test_many_small_requests(la, kind):
     lens = [int(x) for x in rng.integers(1, 301, size=512)]
     inp = W.make_custom(lens, H=2, d=128, dtype="bf16", seed=41, device="cuda")
     check(run(la, inp, kind), reference(inp), tag=f"many-small/{kind}")
+
+
+@pytest.mark.parametrize("B", [255, 256, 257, 600])
+def test_schedule_source_across_the_inline_limit(la, B):
+    """Up to 256 requests the workgroups derive their segments from the
+    lengths in the kernel arguments, above that they read the host's tables:
+    on both sides of the limit the tile map is the oracle's, and forcing the
+    tables gives the same bits."""
+    rng = np.random.default_rng(B)
+    lens = [int(x) for x in rng.integers(1, 700, size=B)]
+    H, d = 2, 64
+    inp = W.make_custom(lens, H=H, d=d, dtype="f16", seed=B, device="cuda")
+    L = la.la_default_tile(d)
+    for grid in (0, 97):
+        G_req = grid if grid else la.la_default_grid(d, la.LA_F16)
+        own_ref, _ = tile_owner_ref(lens, H, L, G_req)
+        say(f"[inline limit B={B} grid={grid}]")
+        owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
+        a = run(la, inp, "lean", grid=grid, tile_owner=owner)
+        assert np.array_equal(owner.cpu().numpy(), own_ref)
+        b = run(la, inp, "lean", grid=grid, host_tables=True)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+    check(a, reference(inp), tag=f"B={B}")
 
 
 def test_grid_larger_than_work(la):
