@@ -337,18 +337,29 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         return st;
 
     // Where the workgroups find their segments. Up to kInlineB requests: the
-    // lengths travel in the kernel arguments and each workgroup derives its
-    // own segments (nothing is copied on the stream, which matters when the
-    // lengths change every decode step). Otherwise, or on request, the host
-    // builds the tables and uploads them.
+    // prefix sums of tiles and tokens travel in the kernel arguments and each
+    // workgroup derives its own segments (nothing is copied on the stream,
+    // which matters when the lengths change every decode step). Otherwise,
+    // or on request, the host builds the tables and uploads them.
     la::SchedArgs sa{};
     sa.B = B;
     sa.U = U;
     sa.L = L;
     sa.G = G;
-    if (B <= la::kInlineB && o.host_tables == 0) {
+    int64_t total = 0;
+    for (int b = 0; b < B; ++b) total += ctx_lens[b];
+    if (B <= la::kInlineB && total <= (int64_t)UINT32_MAX && o.host_tables == 0) {
         sa.inline_lens = 1;
-        for (int b = 0; b < B; ++b) sa.lens[b] = ctx_lens[b];
+        int32_t tp = 0;
+        uint32_t tk = 0;
+        for (int b = 0; b < B; ++b) {
+            sa.tp[b] = tp;
+            sa.tok[b] = tk;
+            tp += (ctx_lens[b] + L - 1) / L;
+            tk += (uint32_t)ctx_lens[b];
+        }
+        sa.tp[B] = tp;
+        sa.tok[B] = tk;
     } else {
         const int BU = B * U;
         const size_t off_seg = 0;

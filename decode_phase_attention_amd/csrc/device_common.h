@@ -102,77 +102,36 @@ __device__ __forceinline__ void wait_flag(uint32_t* f, uint64_t limit, uint32_t*
     }
 }
 
-// The context lengths carried in the kernel arguments (Args::sched.lens),
-// read in place through the kernarg segment: indexing the by-value argument
-// with a lane-varying index would make the compiler copy the whole argument
-// to scratch. Args must be the kernel's only argument (offset 0).
-typedef const __attribute__((address_space(4))) int32_t* klens_t;
+// The schedule prefix sums carried in the kernel arguments (Args::sched.tp
+// and .tok), read in place through the kernarg segment with scalar loads.
+// Args must be the kernel's only argument (offset 0).
+typedef const __attribute__((address_space(4))) int32_t* ktp_t;
+typedef const __attribute__((address_space(4))) uint32_t* ktok_t;
+struct KSched {
+    ktp_t tp;
+    ktok_t tok;
+};
 template <class Args>
-__device__ __forceinline__ klens_t kernarg_lens() {
+__device__ __forceinline__ KSched kernarg_sched() {
     typedef const __attribute__((address_space(4))) char* kchar_t;
     const kchar_t base = (kchar_t)__builtin_amdgcn_kernarg_segment_ptr();
-    return (klens_t)(base + offsetof(Args, sched) + offsetof(SchedArgs, lens));
+    return {(ktp_t)(base + offsetof(Args, sched) + offsetof(SchedArgs, tp)),
+            (ktok_t)(base + offsetof(Args, sched) + offsetof(SchedArgs, tok))};
 }
 
-// LDS for deriving the schedule in the workgroup.
-struct SchedLds {
-    int32_t tp[kInlineB + 1];   // tiles of the earlier requests (exclusive prefix)
-    int64_t tok[kInlineB + 1];  // tokens of the earlier requests
-};
-
 // Walks a workgroup's segments in order. kInline: derived here (SegWalk over
-// prefix sums the first wave computes into LDS; the constructor holds a
-// barrier, so every thread of the workgroup constructs it); else read from the
-// host's tables. The tests compare both with the executed tile map. Two
-// separate types, one per kernel instantiation, keep the cursor state in
-// scalar registers.
+// the prefix sums in the kernel arguments); else read from the host's
+// tables. The tests compare both with the executed tile map. Two separate
+// types, one per kernel instantiation, keep the cursor state in scalar
+// registers.
 template <bool kInline>
 struct SegCursor;
 
 template <>
 struct SegCursor<true> {
-    SegWalk w;
+    SegWalk<ktp_t, ktok_t> w;
 
-    __device__ SegCursor(const SchedArgs& a, klens_t lens, SchedLds& l, int c) {
-        if (threadIdx.x < 64) {
-            // exclusive prefix sums of tiles and tokens per request: each lane
-            // of the first wave takes up to four consecutive requests, then a
-            // scan across the wave
-            const int lane = threadIdx.x;
-            const int per = (a.B + 63) >> 6;
-            const int x0 = min(lane * per, a.B), x1 = min(x0 + per, a.B);
-            int32_t tp = 0;
-            int64_t tk = 0;
-            for (int x = x0; x < x1; ++x) {
-                tp += (lens[x] + a.L - 1) / a.L;
-                tk += lens[x];
-            }
-            int32_t tpi = tp;
-            int64_t tki = tk;
-            for (int o = 1; o < 64; o <<= 1) {
-                const int32_t t2 = __shfl_up(tpi, o, 64);
-                const int64_t k2 = __shfl_up(tki, o, 64);
-                if (lane >= o) {
-                    tpi += t2;
-                    tki += k2;
-                }
-            }
-            tp = tpi - tp;
-            tk = tki - tk;
-            for (int x = x0; x < x1; ++x) {
-                l.tp[x] = tp;
-                l.tok[x] = tk;
-                tp += (lens[x] + a.L - 1) / a.L;
-                tk += lens[x];
-            }
-            if (lane == 63) {
-                l.tp[a.B] = tpi;
-                l.tok[a.B] = tki;
-            }
-        }
-        __syncthreads();
-        w.init(l.tp, l.tok, a.B, a.U, a.G, c);
-    }
+    __device__ SegCursor(const SchedArgs& a, KSched k, int c) { w.init(k.tp, k.tok, a.B, a.U, a.G, c); }
 
     __device__ bool next(LeanSeg& s) { return w.next(s); }
 };
@@ -183,7 +142,7 @@ struct SegCursor<false> {
     int si, s1;                 // next segment, end
     int iter;                   // linear iteration of the next segment
 
-    __device__ SegCursor(const SchedArgs& a_, klens_t, SchedLds&, int c)
+    __device__ SegCursor(const SchedArgs& a_, KSched, int c)
         : a(a_), si(a_.cta_seg[c]), s1(a_.cta_seg[c + 1]), iter(a_.cta_begin[c]) {}
 
     __device__ bool next(LeanSeg& s) {

@@ -19,9 +19,10 @@ constexpr int chunk_rows(int d) { return (2048 / d) * kRows; }
 constexpr int part_stride(int d) { return d + 4; }
 
 // Where a lean workgroup finds its segments: in tables built and uploaded by
-// the host, or -- for up to kInlineB requests -- derived by the workgroup
-// itself from the context lengths carried in the kernel arguments (no table
-// copy on the stream; the partition and head walk are the host scheduler's).
+// the host, or -- for up to kInlineB requests and 2^32 - 1 tokens in all --
+// derived by the workgroup itself from per-request prefix sums carried in the
+// kernel arguments (no table copy on the stream; the partition and unit walk
+// are the host scheduler's).
 constexpr int kInlineB = 256;
 
 struct SchedArgs {
@@ -31,12 +32,13 @@ struct SchedArgs {
     const int32_t* last_cta;   // tables: [B*U]
     const int32_t* ctx;        // tables: [B] n_b
     const int64_t* tok_off;    // tables: [B] sum_{b'<b} n_b'
-    int inline_lens;           // 1: derive from `lens`; 0: read the tables
+    int inline_lens;           // 1: derive from `tp` and `tok`; 0: read the tables
     int B;                     // requests
     int U;                     // schedule units per request
     int L;                     // tile tokens
     int G;                     // workgroups launched
-    int32_t lens[kInlineB];    // inline: n_b
+    int32_t tp[kInlineB + 1];  // inline: tiles of the requests before b (exclusive prefix)
+    uint32_t tok[kInlineB + 1];// inline: tokens of the requests before b
 };
 
 struct LeanArgs {

@@ -279,14 +279,13 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     using G = Geo<D>;
     constexpr int P = kDpl<D>;
     __shared__ Smem<D> sm;
-    __shared__ SchedLds sl;
     const int c = blockIdx.x;
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
     stamp_start(a.ts, c);
-    SegCursor<IL> cur(a.sched, kernarg_lens<LeanArgs>(), sl, c);
+    SegCursor<IL> cur(a.sched, kernarg_sched<LeanArgs>(), c);
     LeanSeg sg;
     while (cur.next(sg)) {
         const int u = sg.u;

@@ -380,7 +380,6 @@ template <int DT, int D, bool IL>
 __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     using G = GGeo<D>;
     __shared__ GSmem<D> sm;
-    __shared__ SchedLds sl;
     const int cta = blockIdx.x;
     const int t = threadIdx.x;
     const int wave = t >> 6;
@@ -390,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     const int dc = t & 15;
     const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
     stamp_start(a.ts, cta);
-    SegCursor<IL> cur(a.sched, kernarg_lens<GqaArgs>(), sl, cta);
+    SegCursor<IL> cur(a.sched, kernarg_sched<GqaArgs>(), cta);
     LeanSeg sg;
     while (cur.next(sg)) {
         const int u = sg.u;

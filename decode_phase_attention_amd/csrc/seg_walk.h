@@ -18,9 +18,8 @@
 
 namespace la {
 
-// The walk's values are the same in every lane. Read from LDS they would sit
-// in vector registers for the whole streaming loop; on the device they are
-// moved to scalar registers instead.
+// The walk's values are the same in every lane; on the device they are kept
+// in scalar registers.
 #if defined(__HIP_DEVICE_COMPILE__)
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ int64_t uniform(int64_t x) {
@@ -45,43 +44,45 @@ struct LeanSeg {
     int iter0;                 // linear iteration of tile t0
 };
 
+// TpPtr / TokPtr: pointers (or any indexable) to the [B+1] exclusive prefix
+// sums of tiles and tokens per request.
+template <class TpPtr, class TokPtr>
 struct SegWalk {
-    const int32_t* tp;         // [B+1] tiles of the earlier requests (exclusive prefix)
-    const int64_t* tok;        // [B+1] tokens of the earlier requests
+    TpPtr tp;
+    TokPtr tok;
     int U;
-    int64_t q, r;              // I = q*G + r
+    int q, r;                  // I = q*G + r (I < 2^31, G <= I)
     int i, i1, b;              // next iteration, end of the range, request of i
 
     // Workgroup c of G; every request has at least one tile.
-    LA_HD void init(const int32_t* tp_, const int64_t* tok_, int B, int U_, int G, int c) {
+    LA_HD void init(TpPtr tp_, TokPtr tok_, int B, int U_, int G, int c) {
         tp = tp_;
         tok = tok_;
         U = U_;
-        const int64_t I = (int64_t)U * uniform(tp[B]);
+        const int I = U * uniform((int)tp[B]);
         q = I / G;
         r = I - q * G;
-        const int64_t lo = (int64_t)c * q + (c < r ? c : r);
-        i = (int)lo;
-        i1 = (int)(lo + q + (c < r ? 1 : 0));
+        i = c * q + (c < r ? c : r);
+        i1 = i + q + (c < r ? 1 : 0);
         int x = 0, y = B;   // U * tp[x] <= i < U * tp[y]
         while (y - x > 1) {
             const int mid = (x + y) >> 1;
-            if ((int64_t)U * uniform(tp[mid]) <= i) x = mid; else y = mid;
+            if (U * uniform((int)tp[mid]) <= i) x = mid; else y = mid;
         }
         b = x;
     }
 
     // Workgroup whose range holds linear iteration it.
-    LA_HD int cta_of(int64_t it) const {
-        const int64_t big = r * (q + 1);
-        return (int)(it < big ? it / (q + 1) : r + (it - big) / q);
+    LA_HD int cta_of(int it) const {
+        const int big = r * (q + 1);
+        return it < big ? it / (q + 1) : r + (it - big) / q;
     }
 
     LA_HD bool next(LeanSeg& s) {
         if (i >= i1) return false;
-        int p1 = uniform(tp[b + 1]);
-        while ((int64_t)U * p1 <= i) p1 = uniform(tp[++b + 1]);
-        const int p0 = uniform(tp[b]);
+        int p1 = uniform((int)tp[b + 1]);
+        while (U * p1 <= i) p1 = uniform((int)tp[++b + 1]);
+        const int p0 = uniform((int)tp[b]);
         const int T = p1 - p0;
         const int j = i - U * p0;
         const int h = j / T;
@@ -92,9 +93,9 @@ struct SegWalk {
         s.u = b * U + h;
         s.host = s.t0 == 0;
         s.fin = s.t1 == T;
-        s.tok_off = uniform(tok[b]);
-        s.n = (int)(uniform(tok[b + 1]) - s.tok_off);
-        s.last = (s.host && !s.fin) ? cta_of((int64_t)i - s.t0 + T - 1) : 0;
+        s.tok_off = uniform((int64_t)tok[b]);
+        s.n = (int)(uniform((int64_t)tok[b + 1]) - s.tok_off);
+        s.last = (s.host && !s.fin) ? cta_of(i - s.t0 + T - 1) : 0;
         s.iter0 = i;
         i += s.t1 - s.t0;
         return true;

@@ -11,7 +11,7 @@ int main() {
     int B, U, L, G;
     if (std::scanf("%d %d %d %d", &B, &U, &L, &G) != 4) return 2;
     std::vector<int32_t> lens(B), tp(B + 1);
-    std::vector<int64_t> tok(B + 1);
+    std::vector<uint32_t> tok(B + 1);   // the kernels' width: up to 2^32 - 1 tokens in all
     for (int b = 0; b < B; ++b)
         if (std::scanf("%d", &lens[b]) != 1) return 2;
     tp[0] = 0;
@@ -21,7 +21,7 @@ int main() {
         tok[b + 1] = tok[b] + lens[b];
     }
     for (int c = 0; c < G; ++c) {
-        la::SegWalk w;
+        la::SegWalk<const int32_t*, const uint32_t*> w;
         w.init(tp.data(), tok.data(), B, U, G, c);
         la::LeanSeg s;
         while (w.next(s))

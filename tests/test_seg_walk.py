@@ -47,7 +47,11 @@ def expected(lens, U, L, G_req):
 
 
 CASES = [([1], 1, 256, 1), ([1, 1, 1], 4, 16, 64), ([37, 5, 200, 64], 3, 16, 7),
-         ([524288], 32, 256, 256), ([4096] * 16, 32, 256, 512), ([400] * 256, 8, 64, 512)]
+         ([524288], 32, 256, 256), ([4096] * 16, 32, 256, 512), ([400] * 256, 8, 64, 512),
+         # I = 2^31 - 128, just below the 32-bit limit the host enforces
+         ([(1 << 24) - 1] * 2, 64, 1, 1023),
+         # 255 * (2^24 - 1) tokens: offsets past 2^31 in the 32-bit unsigned prefix
+         ([(1 << 24) - 1] * 255, 1, 65536, 300)]
 
 
 @pytest.mark.parametrize("lens,U,L,G", CASES)
