@@ -173,9 +173,11 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  * chunk_tiles (chunks: ceil(I / chunk_tiles)*4 entries).
  *   host_tables lean kind: 1 = the host builds the schedule tables and copies
  *               them to the device on `stream` before the kernel; 0 = with up
- *               to 256 requests, the lengths travel in the kernel arguments and
- *               every workgroup derives its own segments with the same rules
- *               (no copy on the stream), else as 1.
+ *               to 256 requests and 2^32-1 tokens in all, the per-request
+ *               prefix sums of tiles and tokens travel in the kernel
+ *               arguments and every workgroup derives its own segments with
+ *               the same rules (no copy on the stream), else as 1. Both give
+ *               the same tile-to-workgroup map and the same output bits.
  */
 typedef struct la_opts {
     int dtype;
