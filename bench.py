@@ -111,6 +111,31 @@ def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
     }
 
 
+def host_cost(la, torch, inp, steps=20):
+    """Host µs of one lean call while the GPU is busy with earlier ones (the
+    call only enqueues), through the Python binding: with the context lengths
+    changing on every call, as in decoding, and with fixed lengths; for the
+    schedule derived in the launch (default) and for host tables."""
+    out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device=inp.q.device)
+    res = {}
+    for mode, ht in (("in_launch", False), ("host_tables", True)):
+        res[mode] = {}
+        for vary in (True, False):
+            lens = [[max(n - (i + 1 if vary else 0), inp.Nq) for n in inp.ctx_lens]
+                    for i in range(steps)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                la.la_decode_ex(inp.q, inp.k, inp.v, lens[i], inp.B, inp.H, inp.d, inp.scale, out,
+                                kv_heads=inp.Hk, q_tokens=inp.Nq, host_tables=ht)
+            t1 = time.perf_counter()
+            torch.cuda.synchronize()
+            la.la_sync_check()
+            res[mode]["lengths_changing" if vary else "lengths_fixed"] = round(
+                (t1 - t0) * 1e6 / steps, 1)
+    return res
+
+
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
@@ -564,6 +589,11 @@ def main():
                                                 num_splits=K)
         log(f"[bench] occupancy: {occ}")
 
+    host = None
+    if not args.kernel_only:
+        host = host_cost(la, torch, inp)
+        log(f"[bench] host us per call: {host}")
+
     cpu = None
     if not args.no_cpu_baseline and not args.kernel_only:
         log("[bench] cpu baseline (oracle)")
@@ -624,6 +654,7 @@ def main():
         "comparators": comparators,
         "occupancy": occ,
         "lean_splits_per_head": splits,
+        "host_us_per_call": host,
         "env": {"torch": torch.__version__, "python": platform.python_version(),
                 "device": torch.cuda.get_device_name(0)},
     }

@@ -119,26 +119,26 @@ __device__ __forceinline__ void gstate_init(GState<D>& st) {
     for (int nb = 0; nb < GGeo<D>::NB; ++nb) st.o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// One wave step over keys [kb, kb + 32) of a head (rows of kh/vh). With TAIL,
-// loads stay below e and this lane's query column masks keys >= lim (lim <= e).
-// qt[kk] is the B operand of Q^T for head-dim chunk kk.
-template <int DT, int D, bool TAIL>
-__device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char* __restrict__ vh,
-                                         int kb, int e, int lim, int w, int c,
-                                         const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
-                                         GState<D>& st) {
+// K/V registers of one wave step (32 keys).
+template <int D>
+struct GRegs {
+    u32x4_t kr[2][GGeo<D>::KK];         // lane (w, c): key c (+16 sb), 16-byte piece w + 4kk
+    uint32_t vr[8][GGeo<D>::VW];        // keys 4w + r + 16sb (j = r + 4sb), dims [NB*c, NB*c + NB)
+};
+
+// Issue the loads of one wave step over keys [kb, kb + 32) of a head (rows of
+// kh/vh). With TAIL, loads stay below e.
+template <int D, bool TAIL>
+__device__ __forceinline__ void gqa_load(const char* __restrict__ kh, const char* __restrict__ vh,
+                                         int kb, int e, int w, int c, GRegs<D>& g) {
     using G = GGeo<D>;
-    // K: lane (w, c) loads key c (+16 sb), 16-byte piece w + 4kk
-    u32x4_t kr[2][G::KK];
-    // V: lane (w, c) loads keys 4w + r + 16sb (j = r + 4sb), dims [NB*c, NB*c + NB)
-    uint32_t vr[8][G::VW];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
         int key = kb + c + 16 * sb;
         if constexpr (TAIL) key = min(key, e - 1);
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk)
-            kr[sb][kk] = load16(kh + (uint64_t)((uint32_t)key * G::RB + (uint32_t)(w + 4 * kk) * 16u));
+            g.kr[sb][kk] = load16(kh + (uint64_t)((uint32_t)key * G::RB + (uint32_t)(w + 4 * kk) * 16u));
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -147,15 +147,23 @@ __device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char
         const char* src = vh + (uint64_t)((uint32_t)key * G::RB + (uint32_t)c * (G::NB * 2));
         if constexpr (G::VW == 4) {
             const u32x4_t x = load16(src);
-            vr[j][0] = x.x; vr[j][1] = x.y; vr[j][2] = x.z; vr[j][3] = x.w;
+            g.vr[j][0] = x.x; g.vr[j][1] = x.y; g.vr[j][2] = x.z; g.vr[j][3] = x.w;
         } else {
             typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
             const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src));
-            vr[j][0] = x.x; vr[j][1] = x.y;
+            g.vr[j][0] = x.x; g.vr[j][1] = x.y;
         }
     }
-    __builtin_amdgcn_sched_barrier(0);   // all loads of the step in flight first
+}
 
+// The arithmetic of one wave step on loaded registers. With TAIL, this lane's
+// query column masks keys >= lim. qt[kk] is the B operand of Q^T for head-dim
+// chunk kk.
+template <int DT, int D, bool TAIL>
+__device__ __forceinline__ void gqa_compute(const GRegs<D>& g, int kb, int lim, int w,
+                                            const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
+                                            GState<D>& st) {
+    using G = GGeo<D>;
     // scores S^T: lane holds s[j] = S[q = c][key = kb + 4w + (j & 3) + 16 (j >> 2)]
     float s[8];
     {
@@ -164,7 +172,7 @@ __device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char
         for (int sb = 0; sb < 2; ++sb) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < G::KK; ++kk) acc = mfma<DT>(kr[sb][kk], qt[kk], acc);
+            for (int kk = 0; kk < G::KK; ++kk) acc = mfma<DT>(g.kr[sb][kk], qt[kk], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float x = acc[r] * sl2e;
@@ -198,15 +206,44 @@ __device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char
         const int wd = nb >> 1;
         const uint32_t sel = (nb & 1) ? 0x07060302u : 0x05040100u;
         u32x4_t a;
-        a.x = __builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel);
-        a.y = __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel);
-        a.z = __builtin_amdgcn_perm(vr[5][wd], vr[4][wd], sel);
-        a.w = __builtin_amdgcn_perm(vr[7][wd], vr[6][wd], sel);
+        a.x = __builtin_amdgcn_perm(g.vr[1][wd], g.vr[0][wd], sel);
+        a.y = __builtin_amdgcn_perm(g.vr[3][wd], g.vr[2][wd], sel);
+        a.z = __builtin_amdgcn_perm(g.vr[5][wd], g.vr[4][wd], sel);
+        a.w = __builtin_amdgcn_perm(g.vr[7][wd], g.vr[6][wd], sel);
         f32x4_t o = st.o[nb] * alpha;
         o = mfma<DT>(a, phi, o);
         o = mfma<DT>(a, plo, o);
         st.o[nb] = o;
     }
+}
+
+// One wave step over keys [kb, kb + 32): all loads in flight, then the
+// arithmetic.
+template <int DT, int D, bool TAIL>
+__device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char* __restrict__ vh,
+                                         int kb, int e, int lim, int w, int c,
+                                         const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
+                                         GState<D>& st) {
+    GRegs<D> g;
+    gqa_load<D, TAIL>(kh, vh, kb, e, w, c, g);
+    __builtin_amdgcn_sched_barrier(0);   // all loads of the step in flight first
+    gqa_compute<DT, D, TAIL>(g, kb, lim, w, qt, sl2e, st);
+}
+
+// Two full wave steps, keys [kb, kb + 32) and [kb + stride, +32): the loads of
+// both in flight before either's arithmetic (twice the bytes in flight; at
+// d = 128 this measured 8% slower than one step at a time).
+template <int DT, int D>
+__device__ __forceinline__ void gqa_step2(const char* __restrict__ kh, const char* __restrict__ vh,
+                                          int kb, int stride, int w, int c,
+                                          const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
+                                          GState<D>& st) {
+    GRegs<D> g0, g1;
+    gqa_load<D, false>(kh, vh, kb, 0, w, c, g0);
+    gqa_load<D, false>(kh, vh, kb + stride, 0, w, c, g1);
+    __builtin_amdgcn_sched_barrier(0);
+    gqa_compute<DT, D, false>(g0, kb, 0, w, qt, sl2e, st);
+    gqa_compute<DT, D, false>(g1, kb + stride, 0, w, qt, sl2e, st);
 }
 
 // Stream keys [a, e) of one K/V head for the 16 query columns of qt. Keys
@@ -221,6 +258,11 @@ __device__ __forceinline__ void gqa_range(const uint16_t* kh, const uint16_t* vh
     const char* kc = reinterpret_cast<const char*>(kh);
     const char* vc = reinterpret_cast<const char*>(vh);
     int base = a;
+    // d = 64: a step moves 8 KiB per wave; two steps' loads in flight at once
+    // keep 16 KiB per wave in flight, like one step at d = 128
+    if constexpr (D == 64)
+        for (; base + 2 * G::CH <= full; base += 2 * G::CH)
+            gqa_step2<DT, D>(kc, vc, base + G::KEYS * wave, G::CH, w, c, qt, sl2e, st);
     for (; base + G::CH <= full; base += G::CH)
         gqa_step<DT, D, false>(kc, vc, base + G::KEYS * wave, e, lim, w, c, qt, sl2e, st);
     for (; base < e; base += G::CH)
