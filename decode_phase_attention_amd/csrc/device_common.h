@@ -172,12 +172,25 @@ __device__ __forceinline__ uint64_t hwreg_ids() {
 }
 
 // Per-workgroup trace: realtime clock at entry and exit plus the hardware
-// ids of the CU it ran on (thread 0 only).
-__device__ __forceinline__ void stamp_start(uint64_t* ts, int blk) {
+// ids of the CU it ran on (thread 0 only). Returns the entry clock.
+__device__ __forceinline__ uint64_t stamp_start(uint64_t* ts, int blk) {
+    const uint64_t t = ts != nullptr ? __builtin_amdgcn_s_memrealtime() : 0;
     if (ts != nullptr && threadIdx.x == 0) {
-        ts[blk * 4 + 0] = __builtin_amdgcn_s_memrealtime();
+        ts[blk * 4 + 0] = t;
         ts[blk * 4 + 2] = hwreg_ids();
         ts[blk * 4 + 3] = 0;
+    }
+    return t;
+}
+__device__ __forceinline__ uint64_t stamp_now(const uint64_t* ts) {
+    return ts != nullptr ? __builtin_amdgcn_s_memrealtime() : 0;
+}
+// A lean host's wait for its peers began at w0 and ends now: the fourth word
+// holds both as clock ticks after entry t_in, (end << 32) | begin.
+__device__ __forceinline__ void stamp_wait(uint64_t* ts, int blk, uint64_t t_in, uint64_t w0) {
+    if (ts != nullptr && threadIdx.x == 0) {
+        const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+        ts[blk * 4 + 3] = ((w1 - t_in) << 32) | ((w0 - t_in) & 0xffffffffull);
     }
 }
 __device__ __forceinline__ void stamp_end(uint64_t* ts, int blk) {

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     const int lane = t & 63;
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
-    stamp_start(a.ts, c);
+    const uint64_t t_in = stamp_start(a.ts, c);
     SegCursor<IL> cur(a.sched, kernarg_sched<LeanArgs>(), c);
     LeanSeg sg;
     while (cur.next(sg)) {
@@ -323,7 +323,9 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
             // ascending workgroup order with their loads issued in batches.
             const int last = sg.last;
             const int np = last - c;
+            const uint64_t w0 = stamp_now(a.ts);
             for (int i = lane; i < np; i += 64) wait_flag(&a.flags[c + 1 + i], a.wait_ticks, a.err);
+            stamp_wait(a.ts, c, t_in, w0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             constexpr int kBatch = 16;
             for (int p0 = c + 1; p0 <= last; p0 += kBatch) {

@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     const int q = t >> 4;
     const int dc = t & 15;
     const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
-    stamp_start(a.ts, cta);
+    const uint64_t t_in = stamp_start(a.ts, cta);
     SegCursor<IL> cur(a.sched, kernarg_sched<GqaArgs>(), cta);
     LeanSeg sg;
     while (cur.next(sg)) {
@@ -473,17 +473,20 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
             // time (the streaming registers are free by now)
             const int last = sg.last;
             const int np = last - cta;
+            const uint64_t w0 = stamp_now(a.ts);
             for (int i = t; i < np; i += kThreads) wait_flag(&a.flags[cta + 1 + i], a.wait_ticks, a.err);
             __syncthreads();
+            stamp_wait(a.ts, cta, t_in, w0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            // The host's CU reads every peer's records, so the merge runs at one
+            // CU's load rate: threads of columns past the group read nothing.
             constexpr int kBatch = 128 / D * 8;   // 16 peers at d = 64, 8 at d = 128
-            const int qq = min(q, x.geff - 1);   // columns past the group read a valid record
-            for (int p0 = cta + 1; p0 <= last; p0 += kBatch) {
+            for (int p0 = cta + 1; q < x.geff && p0 <= last; p0 += kBatch) {
                 float pm[kBatch], pl[kBatch], po[kBatch][G::DPT];
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
                     const uint32_t rec =
-                        (uint32_t)(min(p0 + j, last) * 16 + qq) * (uint32_t)(part_stride(D) * 4);
+                        (uint32_t)(min(p0 + j, last) * 16 + q) * (uint32_t)(part_stride(D) * 4);
                     const float2 ml = load8_agent(xr, rec + (uint32_t)D * 4u);
                     pm[j] = ml.x;
                     pl[j] = ml.y;
@@ -551,7 +554,8 @@ __device__ __forceinline__ bool count_in_wg(uint32_t* ctr, int last, int& s_word
 }
 
 // Fold, in order, column qq's records of chunks ch0, ch0 + step, ... (n of
-// them) at slot level `lvl` into (M, L, O), replacing what they held.
+// them) at slot level `lvl` into (M, L, O), replacing what they held. Callers
+// skip columns past the group (their records were never written).
 template <int D>
 __device__ __forceinline__ void fold_slots_g(__amdgpu_buffer_rsrc_t xr, int lvl, int ch0, int n,
                                              int step, int Su, int C, int qq, int dc, float& M,
@@ -652,8 +656,8 @@ __global__ __launch_bounds__(kThreads) void pull_gqa_kernel(const GqaArgs a) {
                 if (g1 > g0) {
                     publish_rec_g<D>(xr, k * 2 + side, q, dc, x.geff, M, L, O);
                     if (!count_in_wg(&a.gcount[gslot], g1 - g0, s_arrived)) continue;
-                    fold_slots_g<D>(xr, 0, g0, g1 - g0 + 1, 1, Su, a.C, min(q, x.geff - 1), dc,
-                                    M, L, O);
+                    if (q < x.geff)
+                        fold_slots_g<D>(xr, 0, g0, g1 - g0 + 1, 1, Su, a.C, q, dc, M, L, O);
                     if (t == 0)
                         __hip_atomic_store(&a.gcount[gslot], 0u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
@@ -662,8 +666,9 @@ __global__ __launch_bounds__(kThreads) void pull_gqa_kernel(const GqaArgs a) {
                     const int l1 = 2 * a.nchunks;   // second-level slots follow the first
                     publish_rec_g<D>(xr, l1 + gslot, q, dc, x.geff, M, L, O);
                     if (!count_in_wg(&a.arrive[u], ngroups - 1, s_arrived)) continue;
-                    fold_slots_g<D>(xr, l1, kf, ngroups, kMergeFanIn, Su, a.C, min(q, x.geff - 1),
-                                    dc, M, L, O);
+                    if (q < x.geff)
+                        fold_slots_g<D>(xr, l1, kf, ngroups, kMergeFanIn, Su, a.C, q, dc, M, L,
+                                        O);
                     if (t == 0)
                         __hip_atomic_store(&a.arrive[u], 0u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);

@@ -121,7 +121,10 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               the call's first kernel (lean: min(grid, I); fixed split:
  *               B*H*num_splits, which must then be given; per head: B*H). Per
  *               workgroup: realtime clock (100 MHz) at entry and at exit, then
- *               XCC_ID << 32 | HW_ID of the CU it ran on, then 0
+ *               XCC_ID << 32 | HW_ID of the CU it ran on, then -- kind lean,
+ *               for a workgroup that hosts a split unit -- when its wait for
+ *               the peers began and ended, in ticks after entry, as
+ *               (end << 32) | begin; 0 for every other workgroup and kind
  *   ev_start, ev_stop optional hipEvent_t: recorded on `stream` right before
  *               the first and right after the last kernel of the call (the
  *               schedule table copy is outside this pair)

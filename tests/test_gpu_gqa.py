@@ -119,6 +119,33 @@ def test_adversarial_scores(la):
         check(run(la, inp, "lean", grid=29), reference(inp), tag=f"adversarial/{dtype}")
 
 
+@pytest.mark.parametrize("host_tables", [False, True])
+def test_host_wait_timestamps(la, host_tables):
+    """Per-workgroup timestamps of the grouped lean kernel: every workgroup
+    that hosts a split unit records when its wait for the peers began and
+    ended, within its own entry and exit; the others record 0."""
+    lens = [9000, 40, 3000]
+    H, Hk, d = 16, 4, 64
+    inp = W.make_custom(lens, H=H, d=d, dtype="f16", seed=64, device="cuda", kv_heads=Hk)
+    G_req = 37
+    s = oracle.lean_schedule(lens, Hk, la.la_default_tile(d), G_req)
+    G = s["G"]
+    hosts = {c for (c, u, t0, t1, h, f) in s["seg"] if h and not f}
+    assert hosts
+    ts = torch.zeros(G * 4, dtype=torch.int64, device="cuda")
+    check(run(la, inp, "lean", grid=G_req, cta_timestamps=ts, host_tables=host_tables),
+          reference(inp), tag="timestamps")
+    a = ts.view(G, 4).cpu().numpy()
+    w = a[:, 3].astype(np.uint64)
+    begin = (w & np.uint64(0xFFFFFFFF)).astype(np.int64)
+    end = (w >> np.uint64(32)).astype(np.int64)
+    for c in range(G):
+        if c in hosts:
+            assert 0 < begin[c] <= end[c] <= a[c, 1] - a[c, 0], (c, begin[c], end[c])
+        else:
+            assert a[c, 3] == 0, c
+
+
 def test_determinism(la):
     inp = W.make_custom([777, 31000, 1], H=32, d=128, dtype="bf16", seed=65, device="cuda",
                         kv_heads=8)

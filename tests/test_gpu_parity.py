@@ -381,9 +381,23 @@ def test_timestamps(la, kind, blocks):
     check(got, reference(inp), tag=f"timestamps/{kind}")
     a = ts.view(n, 4).cpu().numpy()
     assert np.all(a[:, 0] > 0) and np.all(a[:, 1] >= a[:, 0])
-    assert np.all(a[:, 3] == 0)
     span_us = (a[:, 1].max() - a[:, 0].min()) / 100.0
     assert 0 < span_us < 1e6
+    if kind != "lean":
+        assert np.all(a[:, 3] == 0)
+        return
+    # the fourth word: a split unit's host, when its wait for the peers began
+    # and ended (ticks after entry); 0 for the other workgroups
+    s = oracle.lean_schedule(lens, H, la.la_default_tile(d), la.la_default_grid(d, la.LA_BF16))
+    hosts = {c for (c, u, t0, t1, h, f) in s["seg"] if h and not f}
+    assert hosts
+    w = a[:, 3].astype(np.uint64)
+    begin, end = (w & np.uint64(0xFFFFFFFF)).astype(np.int64), (w >> np.uint64(32)).astype(np.int64)
+    for c in range(n):
+        if c in hosts:
+            assert 0 < begin[c] <= end[c] <= a[c, 1] - a[c, 0], (c, begin[c], end[c])
+        else:
+            assert a[c, 3] == 0, c
 
 
 def test_stream_capture_is_refused(la):
