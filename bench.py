@@ -111,29 +111,61 @@ def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
     }
 
 
-def host_cost(la, torch, inp, steps=20):
-    """Host µs of one lean call while the GPU is busy with earlier ones (the
-    call only enqueues), through the Python binding: with the context lengths
-    changing on every call, as in decoding, and with fixed lengths; for the
-    schedule derived in the launch (default) and for host tables."""
+def host_cost(la, torch, inp, batches=8, per_batch=3):
+    """Host µs of one lean call through the Python binding while the GPU is
+    still busy with the previous ones (the call only enqueues): median over
+    `batches` bursts of `per_batch` calls, synchronised between bursts, with
+    the context lengths changing on every call (as in decoding) and fixed;
+    for the schedule derived in the launch (default) and for host tables.
+    Bursts stay below the four pinned staging slots of the table path, whose
+    reuse waits for the copy four calls back (that wait throttles the host to
+    the GPU's pace in table mode, not the in-launch mode)."""
     out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device=inp.q.device)
     res = {}
     for mode, ht in (("in_launch", False), ("host_tables", True)):
         res[mode] = {}
         for vary in (True, False):
-            lens = [[max(n - (i + 1 if vary else 0), inp.Nq) for n in inp.ctx_lens]
-                    for i in range(steps)]
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(steps):
-                la.la_decode_ex(inp.q, inp.k, inp.v, lens[i], inp.B, inp.H, inp.d, inp.scale, out,
-                                kv_heads=inp.Hk, q_tokens=inp.Nq, host_tables=ht)
-            t1 = time.perf_counter()
+            per_call = []
+            for bt in range(batches):
+                lens = [[max(n - ((bt * per_batch + i + 1) if vary else 0), inp.Nq)
+                         for n in inp.ctx_lens] for i in range(per_batch)]
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(per_batch):
+                    la.la_decode_ex(inp.q, inp.k, inp.v, lens[i], inp.B, inp.H, inp.d, inp.scale,
+                                    out, kv_heads=inp.Hk, q_tokens=inp.Nq, host_tables=ht)
+                t1 = time.perf_counter()
+                per_call.append((t1 - t0) * 1e6 / per_batch)
             torch.cuda.synchronize()
             la.la_sync_check()
+            per_call.sort()
             res[mode]["lengths_changing" if vary else "lengths_fixed"] = round(
-                (t1 - t0) * 1e6 / steps, 1)
+                per_call[len(per_call) // 2], 1)
     return res
+
+
+def read_ceiling(la, torch, gib=4, reps=10):
+    """Achievable streaming-read bandwidth of this device in GB/s: the
+    library's plain read kernel (the attention kernels' access pattern, one
+    workgroup per CU, no arithmetic) over a `gib` GiB buffer, best of `reps`
+    launches timed with events on the launch stream (torch's current one)."""
+    buf = torch.zeros(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        la.la_stream_read(buf, sink)
+    best = float("inf")
+    n = 0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        n = la.la_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    la.la_sync_check()
+    del buf
+    torch.cuda.empty_cache()
+    return n / (best * 1e-3) / 1e9
 
 
 def kernel_source_hash() -> str:
@@ -536,9 +568,11 @@ def main():
     w = inp.meta["workload"]
     torch.cuda.synchronize()
     dt_code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
-    G = la.la_default_grid(w.d, dt_code)
-    L = la.la_default_tile(w.d)
     Hk, Nq = inp.Hk, inp.Nq
+    # the lean kernel on the grid the library's shape rule picks (one or two
+    # workgroups per CU), whichever kind that rule would run
+    _, G = la.la_select(inp.ctx_lens, inp.H, w.d, dt_code, kv_heads=Hk, q_tokens=Nq)
+    L = la.la_default_tile(w.d)
     cols = inp.H // Hk * Nq                                # query columns per K/V head
     grouped = cols > 1
     units = Hk * ((cols + 15) // 16) if grouped else inp.H  # schedule units per request
@@ -547,12 +581,17 @@ def main():
     log(f"[bench] lens={inp.ctx_lens} I={I} G={Gu} L={L} bytes={alg_bytes}")
 
     log("[bench] timing lean")
-    lean = time_kind(la, torch, evs, inp, "lean", args.steps, args.warmup)
+    lean = time_kind(la, torch, evs, inp, "lean", args.steps, args.warmup, grid=Gu)
     achieved = alg_bytes / (lean["kernel_us_mean"] * 1e-6) / 1e9
     log(f"[bench] lean: {lean}")
 
     if args.copy_calibration:
         copy_calibration(torch)
+
+    ceiling = None
+    if not args.kernel_only:
+        ceiling = read_ceiling(la, torch)
+        log(f"[bench] streaming-read ceiling: {ceiling:.1f} GB/s")
 
     comparators = None
     if not args.no_comparators and not args.kernel_only:
@@ -581,7 +620,7 @@ def main():
         sch = la.la_schedule(inp.ctx_lens, units, L, G)
         per_head = np.bincount(sch["seg"][:, 1], minlength=inp.B * units)
         splits = {"max": int(per_head.max()), "mean": round(float(per_head.mean()), 3)}
-        occ = {"lean": occupancy(la, torch, inp, "lean", Gu),
+        occ = {"lean": occupancy(la, torch, inp, "lean", Gu, grid=Gu),
                "per_head": occupancy(la, torch, inp, "per_head", inp.B * units)}
         if comparators is not None:
             K = comparators["fixed_split_best"]["num_splits"]
@@ -645,6 +684,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "read_ceiling_GBps": round(ceiling, 1) if ceiling else None,
+            "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
             "traffic": committed_traffic(args.workload),
             "kernel": "lean_gqa_kernel" if grouped else "lean_kernel",
             "bytes_per_launch": alg_bytes,

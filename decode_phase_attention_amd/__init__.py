@@ -6,19 +6,7 @@ in-launch merging of partial (m, l, Obar) results with the softmax-rescaling
 reduction. The computation lives in the HIP library ``libla_decode.so``; this
 package only binds it (``binding``) and builds it (``build``).
 """
-from .binding import (LA_BF16, LA_F16, LA_KIND_AUTO, LA_KIND_CHUNKS, LA_KIND_FIXED_SPLIT,
-                      LA_KIND_LEAN, LA_KIND_PER_HEAD, LA_KIND_PULL, LaError, decode_attention,
-                      la_decode, la_decode_bf16, la_decode_ex, la_decode_f16, la_default_grid,
-                      la_default_tile, la_last_error, la_max_grid, la_max_grid_grouped,
-                      la_schedule, la_schedule_dims, la_select, la_select_for,
-                      la_set_wait_limit_us, la_shutdown, la_sync_check, lib)
+from . import binding
+from .binding import *  # noqa: F401,F403 -- exactly the names in binding.__all__
 
-__all__ = [
-    "LA_BF16", "LA_F16", "LA_KIND_AUTO", "LA_KIND_CHUNKS", "LA_KIND_FIXED_SPLIT", "LA_KIND_LEAN",
-    "LA_KIND_PER_HEAD", "LA_KIND_PULL",
-    "LaError", "decode_attention", "la_decode", "la_decode_bf16", "la_decode_ex", "la_decode_f16",
-    "la_default_grid", "la_default_tile", "la_last_error", "la_max_grid", "la_max_grid_grouped",
-    "la_schedule",
-    "la_schedule_dims", "la_select", "la_select_for", "la_set_wait_limit_us", "la_shutdown",
-    "la_sync_check", "lib",
-]
+__all__ = list(binding.__all__)

@@ -23,7 +23,7 @@ __all__ = [
     "la_schedule_dims", "la_default_tile", "la_max_grid", "la_max_grid_grouped", "la_default_grid",
     "la_sync_check",
     "la_last_error",
-    "la_shutdown", "la_set_wait_limit_us", "decode_attention", "LIB_PATH",
+    "la_shutdown", "la_set_wait_limit_us", "la_stream_read", "decode_attention", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_decode.so")
@@ -95,6 +95,7 @@ _SIG = {
     "la_last_error": (ctypes.c_char_p, []),
     "la_shutdown": (None, []),
     "la_set_wait_limit_us": (None, [ctypes.c_uint32]),
+    "la_stream_read": (_I, [_P, ctypes.c_size_t, _I, _P, _P, ctypes.POINTER(ctypes.c_size_t)]),
 }
 
 
@@ -333,6 +334,18 @@ def la_max_grid(d: int, dtype: int) -> int:
     if g <= 0:
         raise LaError(LA_EHIP, la_last_error())
     return g
+
+
+def la_stream_read(src, sink, grid=0, stream=None) -> int:
+    """Read the device tensor `src` once with the attention kernels' access
+    pattern and nothing else (a bandwidth measurement aid); `sink` is a device
+    int32/uint32 tensor of at least one element. Returns the bytes read."""
+    if src.element_size() * src.numel() < 1 or sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("src must be non-empty and sink a 4-byte device tensor")
+    n = ctypes.c_size_t()
+    _check(lib().la_stream_read(_ptr(src), src.element_size() * src.numel(), int(grid),
+                                _ptr(sink), _stream(stream), ctypes.byref(n)))
+    return int(n.value)
 
 
 def la_max_grid_grouped(d: int, dtype: int) -> int:

@@ -872,6 +872,27 @@ la_status la_sync_check(void* stream) {
     return fail(LA_ETIMEOUT, "a device-side wait exceeded its bound (error word 0x%x)", err);
 }
 
+la_status la_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream,
+                         size_t* bytes_read) {
+    g_msg[0] = 0;
+    if (src == nullptr || sink == nullptr || bytes_read == nullptr)
+        return fail(LA_EINVAL, "null pointer");
+    if (((uintptr_t)src & 15u) != 0) return fail(LA_EINVAL, "src must be 16-byte aligned");
+    int dev = 0, cus = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    if (grid == 0) grid = cus;
+    if (grid < 1 || grid > 65535) return fail(LA_EINVAL, "grid %d outside [1, 65535]", grid);
+    const uint64_t unit = la::stream_read_unit();
+    const uint64_t chunk = (uint64_t)bytes / (uint64_t)grid / unit * unit;
+    if (chunk == 0)
+        return fail(LA_EINVAL, "%zu bytes is less than %llu per workgroup", bytes,
+                    (unsigned long long)unit);
+    HIP_TRY(la::launch_stream_read(src, chunk, grid, sink, (hipStream_t)stream));
+    *bytes_read = (size_t)(chunk * (uint64_t)grid);
+    return LA_OK;
+}
+
 const char* la_last_error(void) { return g_msg; }
 
 void la_shutdown(void) {

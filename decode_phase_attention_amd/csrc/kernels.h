@@ -165,6 +165,9 @@ struct PullArgs {
 };
 
 const void* lean_kernel_ptr(int dtype, int d, bool inline_lens);
+uint64_t stream_read_unit();   // bytes per workgroup per loop trip of stream_read_kernel
+hipError_t launch_stream_read(const void* src, uint64_t chunk, int grid, uint32_t* sink,
+                              hipStream_t s);
 hipError_t launch_pull(int dtype, int d, const PullArgs& a, int grid, hipStream_t s);
 const void* lean_gqa_kernel_ptr(int dtype, int d, bool inline_lens);
 hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,

@@ -606,6 +606,31 @@ __global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
     stamp_end(a.ts, blockIdx.x);
 }
 
+// The achievable streaming-read bandwidth of the device, for measurement: each
+// workgroup reads one contiguous chunk with kReadDepth non-temporal 16-byte
+// loads per lane in flight, the access pattern of the attention kernels
+// without their arithmetic. The data are folded into one word so the loads
+// stay; the word is stored only in the (practically impossible) case that it
+// equals a fixed pattern.
+constexpr int kReadDepth = 16;
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* src, uint64_t chunk,
+                                                                uint32_t* sink) {
+    const char* base = src + blockIdx.x * chunk;
+    constexpr uint64_t kStride = (uint64_t)kReadDepth * kThreads * 16;
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (uint64_t off = threadIdx.x * 16ull; off < chunk; off += kStride) {
+        u32x4_t v[kReadDepth];
+#pragma unroll
+        for (int k = 0; k < kReadDepth; ++k)
+            v[k] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(base + off + (uint64_t)k * kThreads * 16));
+        __builtin_amdgcn_sched_barrier(0);   // all loads of the trip in flight first
+#pragma unroll
+        for (int k = 0; k < kReadDepth; ++k) acc ^= v[k];
+    }
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) sink[0] = 1u;
+}
+
 template <typename F>
 const void* pick(int dtype, int d, F f16_64, F f16_128, F bf16_64, F bf16_128) {
     if (dtype == 0) return d == 64 ? (const void*)f16_64 : (const void*)f16_128;
@@ -629,6 +654,15 @@ hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_
     if (cooperative)
         return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
     return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+uint64_t stream_read_unit() { return (uint64_t)kReadDepth * kThreads * 16; }
+
+hipError_t launch_stream_read(const void* src, uint64_t chunk, int grid, uint32_t* sink,
+                              hipStream_t s) {
+    const char* p = static_cast<const char*>(src);
+    void* args[] = {&p, &chunk, &sink};
+    return hipLaunchKernel((const void*)&stream_read_kernel, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
 hipError_t launch_pull(int dtype, int d, const PullArgs& a, int grid, hipStream_t s) {

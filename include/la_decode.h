@@ -299,6 +299,22 @@ la_status la_sync_check(void* stream);
  */
 void la_set_wait_limit_us(uint32_t us);
 
+/*
+ * Measurement aid, not part of attention: reads the device buffer `src`
+ * (16-byte aligned, `bytes` long) once on `stream` with the access pattern
+ * of the attention kernels (each of `grid` workgroups streams one contiguous
+ * chunk with 16 non-temporal 16-byte loads per lane in flight) and nothing
+ * else, so that the achievable read bandwidth of the device can be set next
+ * to the attention kernels' (the peak of the data sheet is not reachable).
+ * grid 0 = one workgroup per CU. Reads the largest multiple of 64 KiB per
+ * workgroup that fits; that byte count is stored in *bytes_read. `sink` is a
+ * device word that the kernel may write (it only keeps the loads from being
+ * optimised away). LA_EINVAL for null or misaligned pointers, a grid outside
+ * [1, 65535], or fewer than 64 KiB per workgroup. Asynchronous on `stream`.
+ */
+la_status la_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream,
+                         size_t* bytes_read);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* la_last_error(void);
 

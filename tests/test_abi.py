@@ -185,3 +185,19 @@ def test_binding_rejects_tensors_too_small_for_the_call():
         la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out.half(), kv_heads=2)
     with pytest.raises(ValueError, match="device tensors"):        # sizes fine: then the device check
         la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out, kv_heads=2)
+
+
+def test_stream_read_validation_before_device_work():
+    L = la.lib()
+    n = ctypes.c_size_t()
+    sink = 1 << 20
+    assert L.la_stream_read(None, 1 << 20, 0, sink, None, ctypes.byref(n)) == 1
+    assert L.la_stream_read(1 << 20, 1 << 20, 0, None, None, ctypes.byref(n)) == 1
+    assert L.la_stream_read((1 << 20) + 8, 1 << 20, 0, sink, None, ctypes.byref(n)) == 1
+    assert "aligned" in la.la_last_error()
+    assert L.la_stream_read(1 << 20, 1 << 20, 0, sink, None, None) == 1
+
+
+def test_package_exports_the_binding():
+    assert set(la.binding.__all__) <= set(dir(la))
+    assert "la_stream_read" in la.__all__
