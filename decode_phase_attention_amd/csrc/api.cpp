@@ -344,7 +344,6 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     la::SchedArgs sa{};
     sa.B = B;
     sa.U = U;
-    sa.L = L;
     sa.G = G;
     int64_t total = 0;
     for (int b = 0; b < B; ++b) total += ctx_lens[b];

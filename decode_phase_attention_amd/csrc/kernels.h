@@ -35,7 +35,6 @@ struct SchedArgs {
     int inline_lens;           // 1: derive from `tp` and `tok`; 0: read the tables
     int B;                     // requests
     int U;                     // schedule units per request
-    int L;                     // tile tokens
     int G;                     // workgroups launched
     int32_t tp[kInlineB + 1];  // inline: tiles of the requests before b (exclusive prefix)
     uint32_t tok[kInlineB + 1];// inline: tokens of the requests before b
@@ -53,7 +52,7 @@ struct LeanArgs {
     uint32_t* flags;           // [G], zero at launch, zero again at exit
     uint32_t* err;             // device error word
     int32_t* tile_owner;       // optional [I]
-    uint64_t* ts;              // optional [G*4]: start, end, HW_ID/XCC_ID, 0
+    uint64_t* ts;              // optional [G*4]: start, end, XCC_ID/HW_ID, host wait
     int H;
     int L;                     // tile tokens
     float sl2e;                // scale * log2(e)
@@ -70,7 +69,7 @@ struct SplitArgs {
     const int32_t* ctx;
     const int64_t* tok_off;
     float* part;               // split kernel: [B*H*splits * part_stride(d)]
-    uint64_t* ts;              // optional [blocks*4]: start, end, HW_ID/XCC_ID, 0
+    uint64_t* ts;              // optional [blocks*4]: start, end, XCC_ID/HW_ID, 0
     int H;
     int L;
     int splits;
@@ -105,7 +104,7 @@ struct GqaArgs {
     uint32_t* flags;
     uint32_t* err;
     int32_t* tile_owner;
-    uint64_t* ts;
+    uint64_t* ts;              // optional [blocks*4], as in LeanArgs
     int H;                     // query heads per request
     int Hk;                    // K/V heads per request
     int g;                     // H / Hk

@@ -76,6 +76,36 @@ def test_back_to_back_without_sync(la):
         assert float(np.max(np.abs(o.cpu().numpy() - ref))) <= 1e-3
 
 
+@pytest.mark.parametrize("host_tables", [False, True])
+@pytest.mark.parametrize("Hk,Nq", [(4, 1), (1, 2)])
+def test_decode_steps_with_changing_lengths(la, host_tables, Hk, Nq):
+    """Decode steps queued back to back, the context lengths different on
+    every call (each launch carries its own schedule: prefix sums in its
+    arguments, or tables through the staging ring): every step's output
+    against the oracle on that step's lengths. Step i reads the first
+    H*sum(lens_i) rows of the same K/V buffers as its packed cache."""
+    H, d = 4, 128
+    base = [3000, 517, 12000, 64]
+    steps = 12
+    inp = W.make_custom(base, H, d, "bf16", seed=77, device="cuda", kv_heads=Hk, q_tokens=Nq)
+    kb, vb, qb = W.to_bits(inp.k), W.to_bits(inp.v), W.to_bits(inp.q)
+    outs, all_lens = [], []
+    for i in range(steps):
+        lens = [max(n - 37 * i - (i % 3), Nq) for n in base]
+        out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+        la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out,
+                        kv_heads=Hk, q_tokens=Nq, host_tables=host_tables)
+        outs.append(out)
+        all_lens.append(lens)
+    la.la_sync_check()
+    for i, (lens, out) in enumerate(zip(all_lens, outs)):
+        rows = Hk * sum(lens)
+        ref = oracle.attend_fp64(qb, kb[:rows], vb[:rows], lens, inp.scale, "bf16", workers=8,
+                                 kv_heads=Hk)[0]
+        err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+        assert err <= 1e-3, (i, lens, err)
+
+
 def _random_case(rng):
     d = int(rng.choice([64, 128]))
     dtype = str(rng.choice(["f16", "bf16"]))
