@@ -97,6 +97,9 @@ uint32_t g_wait_us = kDefaultWaitUs;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
+// LeanTiles of a context of n tokens (n >= 1, any L >= 1 without overflow).
+int tiles_of(int32_t n, int L) { return (int)(((int64_t)n + L - 1) / L); }
+
 // Grows a device buffer. The old one may still be read by work queued on the
 // stream, so the stream is drained before it is freed.
 la_status grow(Workspace& w, void** p, size_t* cap, size_t need_bytes, bool zero) {
@@ -354,7 +357,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         for (int b = 0; b < B; ++b) {
             sa.tp[b] = tp;
             sa.tok[b] = tk;
-            tp += (ctx_lens[b] + L - 1) / L;
+            tp += tiles_of(ctx_lens[b], L);
             tk += (uint32_t)ctx_lens[b];
         }
         sa.tp[B] = tp;
@@ -515,7 +518,7 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     const int U = hd.units_per_req();
     const int BU = B * U;
     int64_t I = 0;
-    for (int b = 0; b < B; ++b) I += (int64_t)U * ((ctx_lens[b] + L - 1) / L);
+    for (int b = 0; b < B; ++b) I += (int64_t)U * tiles_of(ctx_lens[b], L);
     if (I > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "%lld tile iterations do not fit", (long long)I);
     const bool dynamic = o.kind == LA_KIND_PULL;
     // Default chunk: about eight chunks per workgroup of a one-per-CU grid,
@@ -547,7 +550,7 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
         int64_t acc = 0;
         int u = 0;
         for (int b = 0; b < B; ++b) {
-            const int T = (ctx_lens[b] + L - 1) / L;
+            const int T = tiles_of(ctx_lens[b], L);
             for (int h = 0; h < U; ++h, ++u) {
                 S[u] = (int32_t)acc;
                 acc += T;

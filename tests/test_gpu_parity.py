@@ -324,6 +324,19 @@ def test_schedule_source_across_the_inline_limit(la, B):
     check(a, reference(inp), tag=f"B={B}")
 
 
+@pytest.mark.parametrize("tile", [(1 << 20), (1 << 31) - 1])
+@pytest.mark.parametrize("kind,opts", [("lean", {}), ("lean", {"host_tables": True}),
+                                       ("pull", {"grid": 3}), ("chunks", {}),
+                                       ("fixed_split", {"num_splits": 4})])
+def test_tile_larger_than_every_context(la, tile, kind, opts):
+    """A LeanTile longer than any context (up to the largest int): one tile
+    per head, no overflow in the tile counts or token offsets."""
+    lens = [700, 1, 5000]
+    inp = W.make_custom(lens, H=3, d=64, dtype="f16", seed=44, device="cuda")
+    say(f"[huge tile {tile} {kind} {opts}]")
+    check(run(la, inp, kind, tile_tokens=tile, **opts), reference(inp), tag=f"L={tile}/{kind}")
+
+
 def test_grid_larger_than_work(la):
     """Fewer tile iterations than the requested grid: G is cut to I."""
     lens = [3, 200]
