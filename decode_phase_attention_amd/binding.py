@@ -63,6 +63,7 @@ class LaOpts(ctypes.Structure):
         ("q_tokens", ctypes.c_int),
         ("chunk_tiles", ctypes.c_int),
         ("host_tables", ctypes.c_int),
+        ("kv_stride", ctypes.c_int),
     ]
 
 
@@ -178,14 +179,18 @@ def _stream(stream) -> int | None:
 
 
 def _check_sizes(q, k_cache, v_cache, out, ctx_lens, B, H, d, kv_heads=0, q_tokens=0,
-                 m_out=None, l_out=None):
+                 m_out=None, l_out=None, kv_stride=0):
     """For torch tensors, reject a call that would read or write past them (the
     library sees only pointers and cannot check)."""
     import torch
     if not any(isinstance(t, torch.Tensor) for t in (q, k_cache, v_cache, out)):
         return
     rows = int(B) * int(q_tokens or 1) * int(H)
-    kv = int(kv_heads or H) * int(sum(int(n) for n in ctx_lens)) * int(d)
+    Hk = int(kv_heads or H)
+    if kv_stride:
+        kv = int(B) * Hk * int(kv_stride) * int(d)
+    else:
+        kv = Hk * int(sum(int(n) for n in ctx_lens)) * int(d)
     for name, t, need, size in (("q", q, rows * int(d), 2), ("k_cache", k_cache, kv, 2),
                                 ("v_cache", v_cache, kv, 2), ("out", out, rows * int(d), 4),
                                 ("m_out", m_out, rows, 4), ("l_out", l_out, rows, 4)):
@@ -232,7 +237,8 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
 def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
-                 ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0, host_tables=False):
+                 ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0, host_tables=False,
+                 kv_stride=0):
     o = LaOpts()              # ctypes zero-fills it: the same as la_opts_init
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
     o.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
@@ -265,8 +271,11 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
         o.chunk_tiles = int(chunk_tiles)
     if host_tables:
         o.host_tables = 1
+    if kv_stride:
+        o.kv_stride = int(kv_stride)
     arr, p = _lens(ctx_lens)
-    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, kv_heads, q_tokens, m_out, l_out)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, kv_heads, q_tokens, m_out, l_out,
+                 kv_stride)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
 
@@ -378,7 +387,9 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, kind="lean", out
                      stream=None, **opts):
     """Convenience wrapper: shapes from the tensors, fp32 output allocated if
     not given. q is [B, H, d], or [B, Nq, H, d] for Nq new tokens per request;
-    k_cache/v_cache are packed [kv_heads * sum(n_b), d]."""
+    k_cache/v_cache are packed [kv_heads * sum(n_b), d], or a cache
+    [B, kv_heads, S, d] of S >= max(n_b) rows per head (kv_heads and kv_stride
+    then come from its shape)."""
     import torch
     if q.dim() == 4:
         B, Nq, H, d = q.shape
@@ -391,10 +402,19 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, kind="lean", out
         scale = 1.0 / math.sqrt(d)
     if len(ctx_lens) != B:
         raise ValueError("ctx_lens must have B entries")
-    total = int(np.sum(np.asarray(ctx_lens, dtype=np.int64)))
-    Hk = int(opts.get("kv_heads") or H)
-    for t in (k_cache, v_cache):
-        if tuple(t.shape) != (Hk * total, d) or t.dtype != q.dtype:
-            raise ValueError("k_cache/v_cache must be [kv_heads * sum(ctx_lens), d] in q's dtype")
+    if k_cache.dim() == 4:
+        Bk, Hk, S, dk = k_cache.shape
+        if Bk != B or dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise ValueError("a [B, kv_heads, S, d] cache must match q in B and d, and V must match K")
+        opts["kv_heads"], opts["kv_stride"] = Hk, S
+        for t in (k_cache, v_cache):
+            if t.dtype != q.dtype or not t.is_contiguous():
+                raise ValueError("k_cache/v_cache must be contiguous, in q's dtype")
+    else:
+        total = int(np.sum(np.asarray(ctx_lens, dtype=np.int64)))
+        Hk = int(opts.get("kv_heads") or H)
+        for t in (k_cache, v_cache):
+            if tuple(t.shape) != (Hk * total, d) or t.dtype != q.dtype:
+                raise ValueError("k_cache/v_cache must be [kv_heads * sum(ctx_lens), d] in q's dtype")
     la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream, kind=kind, **opts)
     return out

@@ -309,6 +309,7 @@ void fill_gqa(la::GqaArgs& a, const void* q, const void* k, const void* v, float
     a.cols = hd.cols;
     a.QB = hd.QB;
     a.L = L;
+    a.kv_stride = o.kv_stride;
     a.splits = 1;
     a.sl2e = scale * 1.4426950408889634f;
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
@@ -416,6 +417,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     a.ts = o.cta_timestamps;
     a.H = hd.H;
     a.L = L;
+    a.kv_stride = o.kv_stride;
     a.sl2e = scale * 1.4426950408889634f;
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
@@ -486,6 +488,7 @@ la_status run_split_or_head(Workspace& w, const void* q, const void* k, const vo
     a.ts = o.cta_timestamps;
     a.H = hd.H;
     a.L = L;
+    a.kv_stride = o.kv_stride;
     a.splits = splits;
     a.sl2e = scale * 1.4426950408889634f;
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
@@ -622,6 +625,7 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     a.ts = o.cta_timestamps;
     a.H = hd.H;
     a.L = L;
+    a.kv_stride = o.kv_stride;
     a.C = C;
     a.I = (int)I;
     a.nchunks = (int)nchunks;
@@ -703,6 +707,11 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
         return fail(LA_EINVAL, "cta_timestamps with chunks needs an explicit chunk_tiles");
     if (o.kv_heads < 0 || (o.kv_heads > 0 && H % o.kv_heads != 0))
         return fail(LA_EINVAL, "kv_heads %d must divide H = %d", o.kv_heads, H);
+    if (o.kv_stride < 0) return fail(LA_EINVAL, "kv_stride must be >= 0");
+    for (int b = 0; b < B && o.kv_stride > 0; ++b)
+        if (ctx_lens[b] > o.kv_stride)
+            return fail(LA_EINVAL, "ctx_lens[%d] = %d exceeds kv_stride = %d", b, ctx_lens[b],
+                        o.kv_stride);
     if (o.q_tokens < 0 || o.q_tokens > kMaxQTokens)
         return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", o.q_tokens, kMaxQTokens);
     for (int b = 0; b < B && o.q_tokens > 1; ++b)
@@ -712,14 +721,14 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
     std::lock_guard<std::mutex> lock(g_mu);
-    // The schedule tables are copied into a workspace that the next call on
-    // this stream reuses (and skipped when unchanged), so a captured call
-    // would replay whatever tables the workspace holds by then.
+    // A call's partials, flags and (in table mode) schedule tables live in a
+    // per-stream workspace that later calls overwrite or reallocate, so a
+    // captured call would replay stale addresses or another call's tables.
     hipStreamCaptureStatus cap_status = hipStreamCaptureStatusNone;
     HIP_TRY(hipStreamIsCapturing((hipStream_t)stream, &cap_status));
     if (cap_status != hipStreamCaptureStatusNone)
-        return fail(LA_EUNSUPPORTED, "stream capture is not supported (per-call schedule tables "
-                                     "live in a reused workspace)");
+        return fail(LA_EUNSUPPORTED, "stream capture is not supported (partials, flags and "
+                                     "schedule tables live in a reused per-stream workspace)");
     if (o.kind == LA_KIND_AUTO) {
         int kind = 0, grid = 0;
         if ((st = select_on_device(ctx_lens, B, hd, d, o, &kind, &grid)) != LA_OK) return st;
@@ -814,6 +823,11 @@ la_status la_select(const int32_t* ctx_lens, int B, int H, int d, const la_opts*
     if (o.dtype != LA_F16 && o.dtype != LA_BF16) return fail(LA_EINVAL, "unknown dtype %d", o.dtype);
     if (o.kv_heads < 0 || (o.kv_heads > 0 && H % o.kv_heads != 0))
         return fail(LA_EINVAL, "kv_heads %d must divide H = %d", o.kv_heads, H);
+    if (o.kv_stride < 0) return fail(LA_EINVAL, "kv_stride must be >= 0");
+    for (int b = 0; b < B && o.kv_stride > 0; ++b)
+        if (ctx_lens[b] > o.kv_stride)
+            return fail(LA_EINVAL, "ctx_lens[%d] = %d exceeds kv_stride = %d", b, ctx_lens[b],
+                        o.kv_stride);
     if (o.q_tokens < 0 || o.q_tokens > kMaxQTokens)
         return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", o.q_tokens, kMaxQTokens);
     if (o.tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");

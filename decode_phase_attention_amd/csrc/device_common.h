@@ -87,6 +87,15 @@ __device__ __forceinline__ void drain_stores() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Row of the first key of head h (of Hx per request) of request b in the K/V
+// cache: packed per request (stride 0: request b's block [Hx, n_b, d] starts
+// at row Hx * tok_off) or a cache of `stride` rows per head ([B, Hx, stride,
+// d]).
+__device__ __forceinline__ int64_t head_row0(int stride, int Hx, int b, int h, int64_t tok_off,
+                                             int n) {
+    return stride > 0 ? ((int64_t)b * Hx + h) * stride : (int64_t)Hx * tok_off + (int64_t)h * n;
+}
+
 // Wait until a peer's flag is raised. Gives up after `limit` ticks of the
 // 100 MHz realtime clock, or at once when any wait has already given up, and
 // raises the error word: a missing peer cannot hang the launch.

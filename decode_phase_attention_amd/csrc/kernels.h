@@ -55,6 +55,7 @@ struct LeanArgs {
     uint64_t* ts;              // optional [G*4]: start, end, XCC_ID/HW_ID, host wait
     int H;
     int L;                     // tile tokens
+    int kv_stride;             // 0: K/V packed per request; else rows per head of a [B, H, kv_stride, d] cache
     float sl2e;                // scale * log2(e)
     uint64_t wait_ticks;       // 100 MHz clock ticks before a wait gives up
 };
@@ -72,6 +73,7 @@ struct SplitArgs {
     uint64_t* ts;              // optional [blocks*4]: start, end, XCC_ID/HW_ID, 0
     int H;
     int L;
+    int kv_stride;             // as in LeanArgs
     int splits;
     float sl2e;
 };
@@ -112,6 +114,7 @@ struct GqaArgs {
     int cols;                  // query columns per K/V head: g * Nq
     int QB;                    // column blocks of 16 per K/V head: ceil(cols / 16)
     int L;
+    int kv_stride;             // 0: K/V packed per request; else rows per K/V head ([B, Hk, kv_stride, d])
     int splits;
     float sl2e;
     uint64_t wait_ticks;
@@ -156,6 +159,7 @@ struct PullArgs {
     uint64_t* ts;              // optional [grid*4]
     int H;
     int L;
+    int kv_stride;             // as in LeanArgs
     int C;                     // tiles per chunk
     int I;                     // tile iterations
     int nchunks;

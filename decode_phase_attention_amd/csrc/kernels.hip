@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     while (cur.next(sg)) {
         const int u = sg.u;
         const int n = sg.n;
-        const int64_t row0 = (int64_t)a.H * sg.tok_off + (int64_t)sg.unit * n;
+        const int64_t row0 = head_row0(a.kv_stride, a.H, sg.b, sg.unit, sg.tok_off, n);
         const int tok0 = sg.t0 * a.L;
         const int tok1 = (int)min((int64_t)sg.t1 * a.L, (int64_t)n);
         Acc acc;
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
             const int b = u / a.H;
             const int h = u - b * a.H;
             const int n = a.ctx[b];
-            const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
+            const int64_t row0 = head_row0(a.kv_stride, a.H, b, h, a.tok_off[b], n);
             const int tok0 = (it - Su) * a.L;
             const int tok1 = (int)min((int64_t)(t1 - Su) * a.L, (int64_t)n);
             Acc acc;
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     const int b = u / a.H;
     const int h = u - b * a.H;
     const int n = a.ctx[b];
-    const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
+    const int64_t row0 = head_row0(a.kv_stride, a.H, b, h, a.tok_off[b], n);
     const int64_t T = ((int64_t)n + a.L - 1) / a.L;
     const int64_t t0 = (int64_t)k * T / a.splits, t1 = (int64_t)(k + 1) * T / a.splits;
     const int tok0 = (int)(t0 * a.L);
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
     const int b = u / a.H;
     const int h = u - b * a.H;
     const int n = a.ctx[b];
-    const int64_t row0 = (int64_t)a.H * a.tok_off[b] + (int64_t)h * n;
+    const int64_t row0 = head_row0(a.kv_stride, a.H, b, h, a.tok_off[b], n);
     Acc acc;
     acc_init(acc);
     stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, 0, n, load_q(a.q, u, D, sub), a.sl2e,

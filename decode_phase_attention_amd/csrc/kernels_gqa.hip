@@ -360,7 +360,7 @@ __device__ __forceinline__ Unit decode_unit(const GqaArgs& a, const LeanSeg& s) 
     x.qb = s.unit - x.kvh * a.QB;
     x.geff = min(16, a.cols - 16 * x.qb);
     x.n = s.n;
-    x.kvrow0 = (int64_t)a.Hk * s.tok_off + (int64_t)x.kvh * x.n;
+    x.kvrow0 = head_row0(a.kv_stride, a.Hk, x.b, x.kvh, s.tok_off, x.n);
     return x;
 }
 
@@ -373,7 +373,7 @@ __device__ __forceinline__ Unit decode_unit(const GqaArgs& a, int u) {
     x.qb = rem - x.kvh * a.QB;
     x.geff = min(16, a.cols - 16 * x.qb);
     x.n = a.ctx[x.b];
-    x.kvrow0 = (int64_t)a.Hk * a.tok_off[x.b] + (int64_t)x.kvh * x.n;
+    x.kvrow0 = head_row0(a.kv_stride, a.Hk, x.b, x.kvh, a.tok_off[x.b], x.n);
     return x;
 }
 

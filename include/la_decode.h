@@ -181,6 +181,12 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               arguments and every workgroup derives its own segments with
  *               the same rules (no copy on the stream), else as 1. Both give
  *               the same tile-to-workgroup map and the same output bits.
+ *   kv_stride   K/V cache layout: 0 = packed per request (request b's block
+ *               [Hk, n_b, d] at row Hk * sum_{b' < b} n_b'); > 0 = a cache of
+ *               kv_stride rows per head, [B, Hk, kv_stride, d] (head h of
+ *               request b starts at row (b * Hk + h) * kv_stride; only its
+ *               first n_b rows are read, so a decode loop appends to it in
+ *               place). Every n_b must be <= kv_stride (else LA_EINVAL).
  */
 typedef struct la_opts {
     int dtype;
@@ -199,6 +205,7 @@ typedef struct la_opts {
     int q_tokens;
     int chunk_tiles;
     int host_tables;
+    int kv_stride;
 } la_opts;
 
 void la_opts_init(la_opts* opts);

@@ -201,3 +201,29 @@ def test_stream_read_validation_before_device_work():
 def test_package_exports_the_binding():
     assert set(la.binding.__all__) <= set(dir(la))
     assert "la_stream_read" in la.__all__
+
+
+def test_kv_stride_validation_and_sizes():
+    """A [B, Hk, kv_stride, d] cache: a negative stride or a context longer than
+    the stride fails in argument checking; the binding sizes the cache as
+    B * Hk * kv_stride rows."""
+    import torch
+    L = la.lib()
+    lens = (ctypes.c_int32 * 2)(16, 40)
+    fake = 1 << 20
+    o = la.binding.LaOpts()
+    L.la_opts_init(ctypes.byref(o))
+    o.kv_stride = -1
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "kv_stride" in la.la_last_error()
+    o.kv_stride = 32                   # the second context (40) does not fit
+    assert L.la_decode_ex(fake, fake, fake, lens, 2, 4, 128, 0.1, fake, None, ctypes.byref(o)) == 1
+    assert "exceeds kv_stride" in la.la_last_error()
+    q = torch.zeros(2, 8, 64, dtype=torch.float16)
+    out = torch.zeros(2, 8, 64)
+    kv = torch.zeros(2 * 2 * 64 - 1, 64, dtype=torch.float16)   # one row short of [2, 2, 64, 64]
+    with pytest.raises(ValueError, match="k_cache"):
+        la.la_decode_ex(q, kv, kv, [16, 40], 2, 8, 64, 0.125, out, kv_heads=2, kv_stride=64)
+    cache = torch.zeros(2, 2, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="cache"):
+        la.decode_attention(q, cache, cache[:1], [16, 40])
