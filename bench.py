@@ -19,7 +19,9 @@ in-house fixed-split and per-head kernels on the same inputs.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import ctypes
+import gc
 import json
 import math
 import os
@@ -72,6 +74,22 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+@contextlib.contextmanager
+def gc_paused():
+    """Python's garbage collector paused over a timed region, as timeit does:
+    a full collection in this process takes ~25 ms and would otherwise land
+    inside a timed loop now and then (measured: one 1.2-ms-per-step loop of
+    32 calls stretched by 25 ms)."""
+    gc.collect()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
+
+
 def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
     """Host-observed µs/step over `steps` plain calls (synchronised on both
     sides), then kernel µs from HIP events around the kernels over another
@@ -87,17 +105,18 @@ def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
     for _ in range(warmup):
         call()
     la.la_sync_check()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        call()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    la.la_sync_check()
     pairs = evs.create(2 * steps)
-    for i in range(steps):
-        call(pairs[2 * i], pairs[2 * i + 1])
-    torch.cuda.synchronize()
+    with gc_paused():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        la.la_sync_check()
+        for i in range(steps):
+            call(pairs[2 * i], pairs[2 * i + 1])
+        torch.cuda.synchronize()
     la.la_sync_check()
     kern = [evs.elapsed_ms(pairs[2 * i], pairs[2 * i + 1]) * 1e3 for i in range(steps)]
     evs.destroy(pairs)
@@ -126,16 +145,18 @@ def host_cost(la, torch, inp, batches=8, per_batch=3):
         res[mode] = {}
         for vary in (True, False):
             per_call = []
-            for bt in range(batches):
-                lens = [[max(n - ((bt * per_batch + i + 1) if vary else 0), inp.Nq)
-                         for n in inp.ctx_lens] for i in range(per_batch)]
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for i in range(per_batch):
-                    la.la_decode_ex(inp.q, inp.k, inp.v, lens[i], inp.B, inp.H, inp.d, inp.scale,
-                                    out, kv_heads=inp.Hk, q_tokens=inp.Nq, host_tables=ht)
-                t1 = time.perf_counter()
-                per_call.append((t1 - t0) * 1e6 / per_batch)
+            with gc_paused():
+                for bt in range(batches):
+                    lens = [[max(n - ((bt * per_batch + i + 1) if vary else 0), inp.Nq)
+                             for n in inp.ctx_lens] for i in range(per_batch)]
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    for i in range(per_batch):
+                        la.la_decode_ex(inp.q, inp.k, inp.v, lens[i], inp.B, inp.H, inp.d,
+                                        inp.scale, out, kv_heads=inp.Hk, q_tokens=inp.Nq,
+                                        host_tables=ht)
+                    t1 = time.perf_counter()
+                    per_call.append((t1 - t0) * 1e6 / per_batch)
             torch.cuda.synchronize()
             la.la_sync_check()
             per_call.sort()
@@ -515,6 +536,63 @@ def tile_sweep(workloads, steps=20, warmup=3):
                       "device": torch.cuda.get_device_name(0), "table": table}), flush=True)
 
 
+def decode_loop(workloads, steps=64, warmup=4):
+    """Decode steps on a [B, Hk, S, d] cache (kv_stride = S) whose contexts
+    grow by one token per request every step (the rows are already in the
+    cache: appending them belongs to the model's K/V projection, not to
+    attention): µs per step over `steps` steps queued back to back, for the
+    schedule derived in the launch and for host tables, next to the same
+    calls at fixed lengths. Prints one JSON line."""
+    import torch
+
+    import decode_phase_attention_amd as la
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    la.lib()
+    table = {}
+    for name in workloads:
+        log(f"[decode loop] {name}")
+        inp = W.make_inputs(name, seed=0, device="cuda")
+        B, H, Hk, d, Nq = inp.B, inp.H, inp.Hk, inp.d, inp.Nq
+        base = [n - steps - warmup for n in inp.ctx_lens]
+        S = max(inp.ctx_lens)
+        kc = torch.empty((B, Hk, S, d), dtype=inp.k.dtype, device="cuda")
+        vc = torch.empty_like(kc)
+        row = 0
+        for b, n in enumerate(inp.ctx_lens):
+            kc[b, :, :n] = inp.k[row:row + Hk * n].view(Hk, n, d)
+            vc[b, :, :n] = inp.v[row:row + Hk * n].view(Hk, n, d)
+            row += Hk * n
+        out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device="cuda")
+        lens_of = [[n + i + 1 for n in base] for i in range(warmup + steps)]
+        row_out = {}
+        for label, ht, grow in (("in_launch_lengths_growing", False, True),
+                                ("host_tables_lengths_growing", True, True),
+                                ("in_launch_lengths_fixed", False, False)):
+            def step(i):
+                la.la_decode_ex(inp.q, kc, vc, lens_of[i] if grow else base, B, H, d, inp.scale,
+                                out, kv_heads=Hk, q_tokens=Nq, kv_stride=S, host_tables=ht)
+            for i in range(warmup):
+                step(i)
+            with gc_paused():
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(steps):
+                    step(warmup + i)
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+            la.la_sync_check()
+            row_out[label] = round((t1 - t0) * 1e6 / steps, 1)
+        table[name] = row_out
+        log(f"   {row_out}")
+        del kc, vc, inp, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode steps us/step, contexts growing by one token per "
+                                "request per step", "steps": steps,
+                      "device": torch.cuda.get_device_name(0), "table": table}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -537,6 +615,9 @@ def main():
                     help="also append one JSON record per measured kernel kind to this file")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="instead of the headline line: the lean kernel at tile sizes 32..2048")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="instead of the headline line: decode steps on a [B, Hk, S, d] cache "
+                         "whose contexts grow by one token per step")
     ap.add_argument("--contention", action="store_true",
                     help="instead of the headline line: every kind on streams confined to "
                          "part of the CUs (512k and ragged, or --workload)")
@@ -550,6 +631,10 @@ def main():
         return
     if args.tile_sweep:
         tile_sweep(["512k", "ragged", "65k", "many-heads", "gqa-512k", "gqa8-ragged"])
+        return
+    if args.decode_loop:
+        decode_loop(["512k", "ragged", "gqa8-ragged", "mqa-32k", "spec4-ragged"]
+                    if args.workload == "512k" else [args.workload])
         return
     if args.contention:
         contention(["512k", "ragged"] if args.workload == "512k" else [args.workload])
