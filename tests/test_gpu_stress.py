@@ -106,6 +106,34 @@ def test_decode_steps_with_changing_lengths(la, host_tables, Hk, Nq):
         assert err <= 1e-3, (i, lens, err)
 
 
+def test_two_streams_concurrently(la):
+    """Two streams, each with its own workspace (partials, flags, tables),
+    running lean launches of different shapes and kernels side by side with no
+    synchronisation between them: every output against the oracle. Both grids
+    are one workgroup per CU, so the two launches fit on the device together
+    (two per CU, within either kernel's occupancy)."""
+    a = W.make_custom([5000, 300, 12000], 8, 128, "bf16", seed=6, device="cuda")
+    b = W.make_custom([700] * 9, 4, 64, "f16", seed=7, device="cuda", kv_heads=2)
+    refs = [oracle.attend_fp64(W.to_bits(x.q), W.to_bits(x.k), W.to_bits(x.v), x.ctx_lens,
+                               x.scale, x.dtype, workers=8, kv_heads=x.Hk)[0] for x in (a, b)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    torch.cuda.synchronize()
+    for i in range(16):
+        for j, (x, s) in enumerate(zip((a, b), streams)):
+            with torch.cuda.stream(s):
+                out = torch.empty(tuple(x.q.shape), dtype=torch.float32, device="cuda")
+                la.la_decode_ex(x.q, x.k, x.v, x.ctx_lens, x.B, x.H, x.d, x.scale, out,
+                                kv_heads=x.Hk, host_tables=bool(i % 2))
+                outs.append((j, out))
+    for s in streams:
+        la.la_sync_check(s.cuda_stream)
+    torch.cuda.synchronize()
+    for j, out in outs:
+        err = float(np.max(np.abs(out.cpu().numpy() - refs[j])))
+        assert err <= 1e-3, (j, err)
+
+
 def _random_case(rng):
     d = int(rng.choice([64, 128]))
     dtype = str(rng.choice(["f16", "bf16"]))
