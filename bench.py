@@ -165,12 +165,14 @@ def host_cost(la, torch, inp, batches=8, per_batch=3):
     return res
 
 
-def read_ceiling(la, torch, gib=4, reps=10):
+def read_ceiling(la, torch, nbytes, reps=10):
     """Achievable streaming-read bandwidth of this device in GB/s: the
     library's plain read kernel (the attention kernels' access pattern, one
-    workgroup per CU, no arithmetic) over a `gib` GiB buffer, best of `reps`
-    launches timed with events on the launch stream (torch's current one)."""
-    buf = torch.zeros(gib << 30, dtype=torch.uint8, device="cuda")
+    workgroup per CU, no arithmetic) over an `nbytes` buffer, best of `reps`
+    launches timed with events on the launch stream (torch's current one).
+    Short reads pay the same launch ramp and tail as a short attention
+    kernel, so the buffer is sized like the workload's K/V."""
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for _ in range(3):
         la.la_stream_read(buf, sink)
@@ -674,9 +676,10 @@ def main():
         copy_calibration(torch)
 
     ceiling = None
+    ceiling_bytes = min(max(alg_bytes, 256 << 20), 4 << 30)
     if not args.kernel_only:
-        ceiling = read_ceiling(la, torch)
-        log(f"[bench] streaming-read ceiling: {ceiling:.1f} GB/s")
+        ceiling = read_ceiling(la, torch, ceiling_bytes)
+        log(f"[bench] streaming-read ceiling over {ceiling_bytes} bytes: {ceiling:.1f} GB/s")
 
     comparators = None
     if not args.no_comparators and not args.kernel_only:
@@ -770,6 +773,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "read_ceiling_GBps": round(ceiling, 1) if ceiling else None,
+            "read_ceiling_bytes": ceiling_bytes if ceiling else None,
             "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
             "traffic": committed_traffic(args.workload),
             "kernel": "lean_gqa_kernel" if grouped else "lean_kernel",
