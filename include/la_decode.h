@@ -114,9 +114,10 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               work shares the device, at the cost of a slower launch.
  *   m_out, l_out     optional device [B*H] fp32: m (natural-log units, on
  *               scaled logits) and l of every head
- *   tile_owner  optional device int32 [I]: lean only; entry i receives the
- *               workgroup that processed tile iteration i of the linearised
- *               schedule (for checking the tables the kernel executed)
+ *   tile_owner  optional device int32 [I]: lean, pull and chunks kinds; entry
+ *               i receives the workgroup that processed tile iteration i of
+ *               the linearised schedule (for checking the schedule the kernel
+ *               executed)
  *   cta_timestamps optional device uint64 [blocks*4], blocks = the grid of
  *               the call's first kernel (lean: min(grid, I); fixed split:
  *               B*H*num_splits, which must then be given; per head: B*H). Per
