@@ -17,8 +17,10 @@
  * How it is computed (same pages, §3.3-§3.5): the context of every head is cut
  * into LeanTiles of `tile_tokens` tokens; the tile iterations of all heads are
  * laid end to end and split into equal contiguous ranges over a persistent grid
- * of co-resident workgroups (a host-side scheduler builds these tables on every
- * call); each workgroup streams its tiles with an online softmax, and partial
+ * of co-resident workgroups (each workgroup derives its own range from
+ * per-request prefix sums passed with the launch, or reads tables a host-side
+ * scheduler builds); each workgroup streams its tiles with an online softmax,
+ * and partial
  * (m, l, Obar) results of heads that span several workgroups are merged inside
  * the same launch with the associative rescaling reduction
  *     f(x, y): m = max(m_x, m_y), l = e^{m_x-m} l_x + e^{m_y-m} l_y,
@@ -34,8 +36,9 @@
  *  - Layouts: q is [B, H, d] (fp16 or bf16). K and V are packed per request:
  *    request b's block is [H, n_b, d] and starts at element
  *    H * d * sum_{b' < b} n_{b'}; for equal lengths this is [B, H, n, d]
- *    (the (batch, heads, seq_len, head_dim) layout of §7.4). out is
- *    [B, H, d] fp32.
+ *    (the (batch, heads, seq_len, head_dim) layout of §7.4); la_opts.kv_stride
+ *    selects a [B, H, S, d] cache with room for S >= n_b tokens per head
+ *    instead. out is [B, H, d] fp32.
  *  - d must be 64 or 128. scale must be finite. One head's K (or V) block,
  *    n_b * d * 2 bytes, must not exceed 4 GiB (LA_EUNSUPPORTED otherwise).
  *  - Calls are asynchronous on `stream` (a hipStream_t; 0 is the null
@@ -156,25 +159,6 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *   chunk_tiles pull kinds: tiles per chunk; 0 = ceil(I / (8 G)) with G the
  *               pull grid (or one workgroup per CU), and at least
  *               min(32, ceil(I / G)).
- *
- * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
- * pieces": workgroups pull the next piece of the global tile order instead of
- * holding a fixed split; "The hardware-aware part": persistent and
- * non-persistent scheduling). The tile sequence of the lean schedule is cut
- * into chunks of chunk_tiles tiles. LA_KIND_PULL: a persistent grid of `grid`
- * workgroups (0 = la_default_grid, at most 65536) takes chunks from an atomic
- * counter until none is left. LA_KIND_CHUNKS: one workgroup per chunk. A head
- * spread over several chunks leaves one partial record per chunk; its chunks
- * form groups of 16, the workgroup whose piece arrives last in a group folds
- * the group with f in chunk order, and the last group folds the groups in
- * order. The tree is fixed, so outputs are bitwise the same whichever
- * workgroup took which chunk. No
- * workgroup ever waits for another (any grid is safe, co-resident or not).
- * With kv_heads or q_tokens the chunks cut the grouped units' tiles, and the
- * grouped exchange (16 records per chunk side) must fit 2 GiB, else
- * LA_EUNSUPPORTED. tile_owner receives the workgroup that processed each
- * tile; cta_timestamps needs an explicit grid (pull: grid*4 entries) or
- * chunk_tiles (chunks: ceil(I / chunk_tiles)*4 entries).
  *   host_tables lean kind: 1 = the host builds the schedule tables and copies
  *               them to the device on `stream` before the kernel; 0 = with up
  *               to 256 requests and 2^32-1 tokens in all, the per-request
@@ -188,6 +172,25 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               request b starts at row (b * Hk + h) * kv_stride; only its
  *               first n_b rows are read, so a decode loop appends to it in
  *               place). Every n_b must be <= kv_stride (else LA_EINVAL).
+ *
+ * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
+ * pieces": workgroups pull the next piece of the global tile order instead of
+ * holding a fixed split; "The hardware-aware part": persistent and
+ * non-persistent scheduling). The tile sequence of the lean schedule is cut
+ * into chunks of chunk_tiles tiles. LA_KIND_PULL: a persistent grid of `grid`
+ * workgroups (0 = la_default_grid, at most 65536) takes chunks from an atomic
+ * counter until none is left. LA_KIND_CHUNKS: one workgroup per chunk. A head
+ * spread over several chunks leaves one partial record per chunk; its chunks
+ * form groups of 16, the workgroup whose piece arrives last in a group folds
+ * the group with f in chunk order, and the last group folds the groups in
+ * order. The tree is fixed, so outputs are bitwise the same whichever
+ * workgroup took which chunk. No workgroup ever waits for another (any grid
+ * is safe, co-resident or not).
+ * With kv_heads or q_tokens the chunks cut the grouped units' tiles, and the
+ * grouped exchange (16 records per chunk side) must fit 2 GiB, else
+ * LA_EUNSUPPORTED. tile_owner receives the workgroup that processed each
+ * tile; cta_timestamps needs an explicit grid (pull: grid*4 entries) or
+ * chunk_tiles (chunks: ceil(I / chunk_tiles)*4 entries).
  */
 typedef struct la_opts {
     int dtype;
@@ -212,8 +215,9 @@ typedef struct la_opts {
 void la_opts_init(la_opts* opts);
 
 /* Calls are asynchronous on `stream`; a stream that is being captured into a
- * HIP graph is refused (LA_EUNSUPPORTED): each call copies its schedule tables
- * into a per-stream workspace that later calls reuse. */
+ * HIP graph is refused (LA_EUNSUPPORTED): a call's partials, flags and (in
+ * table mode) schedule tables live in a per-stream workspace that later calls
+ * overwrite or reallocate. */
 la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* ctx_lens, int B, int H, int d, float scale,
                        float* out, void* stream, const la_opts* opts);
