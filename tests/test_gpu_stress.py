@@ -134,6 +134,15 @@ def test_two_streams_concurrently(la):
         assert err <= 1e-3, (j, err)
 
 
+def _strided(t, lens, Hk, d, S):
+    c = torch.full((len(lens), Hk, S, d), float("nan"), dtype=t.dtype, device=t.device)
+    row = 0
+    for b, n in enumerate(lens):
+        c[b, :, :n] = t[row:row + Hk * n].view(Hk, n, d)
+        row += Hk * n
+    return c
+
+
 def _random_case(rng):
     d = int(rng.choice([64, 128]))
     dtype = str(rng.choice(["f16", "bf16"]))
@@ -155,8 +164,9 @@ def _random_case(rng):
 
 def test_random_shapes_every_kind(la):
     """Random ragged batches, grouped heads, several new tokens, head dims and
-    dtypes, under every kind with random grids, tiles and chunk sizes; each
-    launch against the oracle on all of its query rows."""
+    dtypes, packed or capacity-strided caches, under every kind with random
+    grids, tiles and chunk sizes; each launch against the oracle on all of
+    its query rows."""
     rng = np.random.default_rng(2024)
     kinds = ["lean", "fixed_split", "per_head", "auto", "pull", "chunks"]
     worst = 0.0
@@ -177,14 +187,20 @@ def test_random_shapes_every_kind(la):
                     "chunk_tiles": int(rng.choice([0, 1, 2, 9]))}
         elif kind == "chunks":
             opts = {"chunk_tiles": int(rng.choice([0, 1, 5, 33]))}
+        if (i // 6) % 2 == 1:         # every kind, every other round of six
+            opts["kv_stride"] = max(lens) + int(rng.integers(0, 100))
         print(f"[stress {i}] {kind} {opts} d={d} {dtype} H={H} Hk={Hk} Nq={Nq} lens={lens}",
               file=sys.stderr, flush=True)
         inp = W.make_custom(lens, H, d, dtype, seed=100 + i, device="cuda", kv_heads=Hk,
                             q_tokens=Nq)
         ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
                                  inp.scale, dtype, workers=16, kv_heads=Hk)[0]
+        k, v = inp.k, inp.v
+        if "kv_stride" in opts:
+            # the same rows in a [B, Hk, S, d] cache whose unused rows hold NaN
+            k, v = (_strided(t, lens, Hk, d, opts["kv_stride"]) for t in (inp.k, inp.v))
         out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda")
-        la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out, kind=kind,
+        la.la_decode_ex(inp.q, k, v, lens, len(lens), H, d, inp.scale, out, kind=kind,
                         kv_heads=Hk, q_tokens=Nq, **opts)
         la.la_sync_check()
         err = float(np.max(np.abs(out.cpu().numpy() - ref)))
