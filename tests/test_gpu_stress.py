@@ -207,3 +207,48 @@ def test_random_shapes_every_kind(la):
         assert err <= 1e-3, (i, kind, opts, err)
         worst = max(worst, err)
     print(f"60 random launches, worst max|dO| = {worst:.2e}", file=sys.stderr)
+
+
+def test_host_threads_and_shutdown(la):
+    """Two host threads, each on its own stream, call the library at once (it
+    serialises them internally; error messages are per thread); then
+    la_shutdown frees every workspace and later calls build new ones."""
+    import threading
+    a = W.make_custom([3000, 40], 4, 128, "bf16", seed=31, device="cuda")
+    b = W.make_custom([900, 5000, 7], 8, 64, "f16", seed=32, device="cuda", kv_heads=2)
+    refs = [oracle.attend_fp64(W.to_bits(x.q), W.to_bits(x.k), W.to_bits(x.v), x.ctx_lens,
+                               x.scale, x.dtype, workers=8, kv_heads=x.Hk)[0] for x in (a, b)]
+    results, errors = {}, {}
+
+    def worker(j, x):
+        s = torch.cuda.Stream()
+        outs = []
+        with torch.cuda.stream(s):
+            for i in range(10):
+                out = torch.empty(tuple(x.q.shape), dtype=torch.float32, device="cuda")
+                la.la_decode_ex(x.q, x.k, x.v, x.ctx_lens, x.B, x.H, x.d, x.scale, out,
+                                kv_heads=x.Hk, kind=["lean", "pull", "fixed_split"][i % 3])
+                outs.append(out)
+            try:                             # a bad call: its message is this thread's
+                la.la_decode_ex(x.q, x.k, x.v, x.ctx_lens, x.B, x.H, x.d, x.scale, outs[0],
+                                kv_heads=x.Hk, tile_tokens=-j - 1)
+            except la.LaError as e:
+                errors[j] = (str(e), la.la_last_error())
+            la.la_sync_check(s.cuda_stream)
+        results[j] = outs
+
+    threads = [threading.Thread(target=worker, args=(j, x)) for j, x in enumerate((a, b))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for j in (0, 1):
+        for out in results[j]:
+            assert float(np.max(np.abs(out.cpu().numpy() - refs[j]))) <= 1e-3, j
+        assert "tile_tokens" in errors[j][0] and "tile_tokens" in errors[j][1]
+    la.la_shutdown()
+    out = torch.empty(tuple(a.q.shape), dtype=torch.float32, device="cuda")
+    la.la_decode_ex(a.q, a.k, a.v, a.ctx_lens, a.B, a.H, a.d, a.scale, out)
+    la.la_sync_check()
+    assert float(np.max(np.abs(out.cpu().numpy() - refs[0]))) <= 1e-3
