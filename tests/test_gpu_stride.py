@@ -119,3 +119,31 @@ def test_wrapper_takes_a_4d_cache(la):
     ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
                              inp.scale, "f16", workers=8, kv_heads=2)[0]
     assert float(np.max(np.abs(out.cpu().numpy() - ref))) <= 1e-3
+
+
+@pytest.mark.parametrize("name", ["512k", "gqa8-ragged"])
+def test_full_size_strided(la, name):
+    """Full-size workloads in a [B, Hk, S, d] cache with S = the longest
+    context (gqa8-ragged: heads up to 5.9 GB into the cache, past 32-bit
+    offsets), lean and pull, on sampled heads against the oracle."""
+    inp = W.make_inputs(name, seed=0, device="cuda")
+    S = max(inp.ctx_lens)
+    say(f"[stride full {name}] S={S}")
+    kc, vc = strided(inp, S)
+    rng = np.random.default_rng(5)
+    allh = [(b, h) for b in range(inp.B) for h in range(inp.H)]
+    heads = sorted({allh[0], allh[-1]} | {allh[int(i)] for i in rng.choice(len(allh), 20, replace=False)})
+    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), inp.ctx_lens,
+                             inp.scale, inp.dtype, heads=heads, workers=16, kv_heads=inp.Hk)[0]
+    del inp.k, inp.v
+    idx = tuple(np.array(heads).T)
+    for kind in ("lean", "pull"):
+        out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+        la.la_decode_ex(inp.q, kc, vc, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
+                        kind=kind, kv_heads=inp.Hk, kv_stride=S)
+        la.la_sync_check()
+        err = float(np.max(np.abs(out.cpu().numpy()[idx] - ref[idx])))
+        say(f"[stride full {name}] {kind} max|dO|={err:.2e}")
+        assert err <= 1e-3
+    del kc, vc, inp
+    torch.cuda.empty_cache()
