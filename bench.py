@@ -3,8 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 512k]
 
 One step is one decode-attention call over the whole workload: the host
-scheduler builds the stream-K tables, they are copied to the device, and the
-lean kernel runs. Inputs are seeded synthetic caches already resident in HBM.
+computes the per-request prefix sums of tiles and tokens, they travel in the
+kernel arguments, and the lean kernel derives its stream-K segments from them
+and runs (above 256 requests the host builds the schedule tables and copies
+them to the device instead). Inputs are seeded synthetic caches already
+resident in HBM.
 Prints one JSON line on stdout (the last line); progress goes to stderr.
 
 `value` is microseconds per step (host-observed, whole call, a loop of plain
@@ -543,8 +546,11 @@ def decode_loop(workloads, steps=64, warmup=4):
     grow by one token per request every step (the rows are already in the
     cache: appending them belongs to the model's K/V projection, not to
     attention): µs per step over `steps` steps queued back to back, for the
-    schedule derived in the launch and for host tables, next to the same
-    calls at fixed lengths. Prints one JSON line."""
+    schedule derived in the launch from host lengths, for host tables, for
+    lengths kept on the device (each step adds one to them with a small
+    device kernel, then calls the library), and for that step captured once
+    into a HIP graph and replayed; next to the in-launch calls at fixed
+    lengths. Prints one JSON line."""
     import torch
 
     import decode_phase_attention_amd as la
@@ -586,6 +592,44 @@ def decode_loop(workloads, steps=64, warmup=4):
                 t1 = time.perf_counter()
             la.la_sync_check()
             row_out[label] = round((t1 - t0) * 1e6 / steps, 1)
+        base_t = torch.tensor(base, dtype=torch.int32, device="cuda")
+        dl = base_t.clone()
+        s = torch.cuda.Stream()
+
+        def dstep():
+            dl.add_(1)
+            la.la_decode_ex(inp.q, kc, vc, None, B, H, d, inp.scale, out, kv_heads=Hk,
+                            q_tokens=Nq, kv_stride=S, ctx_lens_device=dl)
+        with torch.cuda.stream(s):
+            for i in range(warmup):
+                dstep()
+            with gc_paused():
+                s.synchronize()
+                t0 = time.perf_counter()
+                for i in range(steps):
+                    dstep()
+                s.synchronize()
+                t1 = time.perf_counter()
+        la.la_sync_check(s.cuda_stream)
+        row_out["device_lengths_growing"] = round((t1 - t0) * 1e6 / steps, 1)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            dstep()
+        with torch.cuda.stream(s):
+            dl.copy_(base_t)
+            for i in range(warmup):
+                g.replay()
+            with gc_paused():
+                s.synchronize()
+                t0 = time.perf_counter()
+                for i in range(steps):
+                    g.replay()
+                s.synchronize()
+                t1 = time.perf_counter()
+        la.la_sync_check(s.cuda_stream)
+        assert dl.cpu().tolist() == lens_of[-1]
+        row_out["graph_device_lengths_growing"] = round((t1 - t0) * 1e6 / steps, 1)
+        del g
         table[name] = row_out
         log(f"   {row_out}")
         del kc, vc, inp, out

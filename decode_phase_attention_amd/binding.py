@@ -64,6 +64,7 @@ class LaOpts(ctypes.Structure):
         ("chunk_tiles", ctypes.c_int),
         ("host_tables", ctypes.c_int),
         ("kv_stride", ctypes.c_int),
+        ("ctx_lens_device", ctypes.c_void_p),
     ]
 
 
@@ -238,7 +239,9 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
                  ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0, host_tables=False,
-                 kv_stride=0):
+                 kv_stride=0, ctx_lens_device=None):
+    """la_decode_ex with the options as keywords. With ctx_lens_device (a
+    device int32 tensor of B lengths), ctx_lens may be None."""
     o = LaOpts()              # ctypes zero-fills it: the same as la_opts_init
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
     o.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
@@ -273,7 +276,19 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
         o.host_tables = 1
     if kv_stride:
         o.kv_stride = int(kv_stride)
-    arr, p = _lens(ctx_lens)
+    if ctx_lens_device is not None:
+        import torch
+        if (isinstance(ctx_lens_device, torch.Tensor) and
+                (ctx_lens_device.dtype != torch.int32 or ctx_lens_device.numel() < int(B) or
+                 not ctx_lens_device.is_cuda or not ctx_lens_device.is_contiguous())):
+            raise ValueError("ctx_lens_device must be a contiguous int32 device tensor of at "
+                             "least B entries")
+        o.ctx_lens_device = _ptr(ctx_lens_device)
+        if not kv_stride:
+            raise ValueError("ctx_lens_device needs kv_stride (a [B, Hk, S, d] cache)")
+        arr, p = [], None
+    else:
+        arr, p = _lens(ctx_lens)
     _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, kv_heads, q_tokens, m_out, l_out,
                  kv_stride)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),

@@ -75,6 +75,9 @@ struct Workspace {
     std::vector<char> last_tables;  // host copy of what `tables` holds (valid while non-empty)
     Staging ring[kRing];
     int next = 0;
+    bool capturing = false;         // the current call is being captured: nothing may be allocated
+    bool captured = false;          // a graph may hold the buffers: growing keeps the old ones
+    std::vector<void*> retired;     // buffers replaced after a capture, freed at shutdown
 };
 
 std::mutex g_mu;
@@ -104,9 +107,17 @@ int tiles_of(int32_t n, int L) { return (int)(((int64_t)n + L - 1) / L); }
 // stream, so the stream is drained before it is freed.
 la_status grow(Workspace& w, void** p, size_t* cap, size_t need_bytes, bool zero) {
     if (need_bytes <= *cap) return LA_OK;
+    if (w.capturing)
+        return fail(LA_EUNSUPPORTED, "the stream's workspace must grow, which a captured call "
+                                     "cannot do: make a call of this size (grid, head dim) on the "
+                                     "stream before capturing");
     if (*p != nullptr) {
-        HIP_TRY(hipStreamSynchronize(w.stream));
-        HIP_TRY(hipFree(*p));
+        if (w.captured) {
+            w.retired.push_back(*p);   // a captured graph's replays may still use it
+        } else {
+            HIP_TRY(hipStreamSynchronize(w.stream));
+            HIP_TRY(hipFree(*p));
+        }
         *p = nullptr;
         *cap = 0;
     }
@@ -152,12 +163,11 @@ la_status get_workspace(hipStream_t stream, Workspace** out) {
 la_status capacity(int dtype, int d, bool grouped, Capacity* out) {
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
-    // the smaller occupancy of the two instantiations (segments derived in
-    // the launch or read from tables): the same grid limits for both
-    const void* fn[2];
-    for (int il = 0; il < 2; ++il)
-        fn[il] = grouped ? la::lean_gqa_kernel_ptr(dtype, d, il != 0)
-                         : la::lean_kernel_ptr(dtype, d, il != 0);
+    // the smallest occupancy of the three instantiations (schedule from the
+    // tables, the kernel arguments or device lengths): the same grid limits
+    const void* fn[3];
+    for (int src = 0; src < 3; ++src)
+        fn[src] = grouped ? la::lean_gqa_kernel_ptr(dtype, d, src) : la::lean_kernel_ptr(dtype, d, src);
     auto key = std::make_pair(dev, fn[0]);
     auto it = g_capacity.find(key);
     if (it != g_capacity.end()) {
@@ -165,9 +175,9 @@ la_status capacity(int dtype, int d, bool grouped, Capacity* out) {
         return LA_OK;
     }
     int per_cu = 1 << 30, cus = 0;
-    for (int il = 0; il < 2; ++il) {
+    for (int src = 0; src < 3; ++src) {
         int p = 0;
-        HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, fn[il], la::kThreads, 0));
+        HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, fn[src], la::kThreads, 0));
         per_cu = p < per_cu ? p : per_cu;
     }
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
@@ -202,9 +212,11 @@ la_status staging(Workspace& w, size_t bytes, Staging** out) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-la_status validate(const void* q, const void* k, const void* v, const int32_t* ctx_lens, int B,
-                   int H, int d, float scale, const float* out, int dtype) {
-    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || ctx_lens == nullptr)
+// ctx_lens may be null when the lengths are read on the device.
+la_status validate(const void* q, const void* k, const void* v, const int32_t* ctx_lens,
+                   bool host_lens, int B, int H, int d, float scale, const float* out, int dtype) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr ||
+        (host_lens && ctx_lens == nullptr))
         return fail(LA_EINVAL, "null pointer argument");
     if (B < 1 || H < 1) return fail(LA_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
     if (d != 64 && d != 128) return fail(LA_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
@@ -212,7 +224,7 @@ la_status validate(const void* q, const void* k, const void* v, const int32_t* c
     if (!isfinite(scale)) return fail(LA_EINVAL, "scale must be finite");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(LA_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B && host_lens; ++b) {
         if (ctx_lens[b] < 1) return fail(LA_EINVAL, "ctx_lens[%d] = %d; must be >= 1", b, ctx_lens[b]);
         // kernels address one head's rows with 32-bit byte offsets
         if ((int64_t)ctx_lens[b] * d * 2 > (int64_t)UINT32_MAX)
@@ -315,6 +327,15 @@ void fill_gqa(la::GqaArgs& a, const void* q, const void* k, const void* v, float
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
 }
 
+// Whether a lean call with host lengths derives its segments in the launch
+// (prefix sums in the kernel arguments) rather than from uploaded tables.
+bool in_launch_schedule(const int32_t* ctx_lens, int B, const la_opts& o) {
+    if (B > la::kInlineB || o.host_tables != 0) return false;
+    int64_t total = 0;
+    for (int b = 0; b < B; ++b) total += ctx_lens[b];
+    return total <= (int64_t)UINT32_MAX;
+}
+
 la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
                    const int32_t* ctx_lens, int B, const Heads& hd, int d, float scale,
                    float* out, const la_opts& o) {
@@ -328,10 +349,17 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     const int U = hd.units_per_req();
     int64_t I = 0;
     int G = 0, max_rows = 0;
-    const char* why = "";
-    const int rc = la::schedule_dims(ctx_lens, B, U, L, o.grid > 0 ? o.grid : cap.preferred, &I,
-                                     &G, &max_rows, &why);
-    if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+    const bool dev_lens = o.ctx_lens_device != nullptr;
+    if (dev_lens) {
+        // The lengths are known only in the launch: the grid is the requested
+        // (or default) one, and workgroups beyond the iterations stay empty.
+        G = o.grid > 0 ? o.grid : cap.preferred;
+    } else {
+        const char* why = "";
+        const int rc = la::schedule_dims(ctx_lens, B, U, L, o.grid > 0 ? o.grid : cap.preferred,
+                                         &I, &G, &max_rows, &why);
+        if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+    }
 
     const size_t records = (size_t)G * (hd.grouped ? 16 : 1);
     if ((st = grow(w, (void**)&w.part, &w.part_cap, sizeof(float) * records * la::part_stride(d),
@@ -349,10 +377,14 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     sa.B = B;
     sa.U = U;
     sa.G = G;
-    int64_t total = 0;
-    for (int b = 0; b < B; ++b) total += ctx_lens[b];
-    if (B <= la::kInlineB && total <= (int64_t)UINT32_MAX && o.host_tables == 0) {
-        sa.inline_lens = 1;
+    if (dev_lens) {
+        sa.src = la::kSrcDevice;
+        sa.dlens = o.ctx_lens_device;
+        sa.L = L;
+        sa.n_min = hd.Nq;
+        sa.n_max = o.kv_stride;
+    } else if (in_launch_schedule(ctx_lens, B, o)) {
+        sa.src = la::kSrcArgs;
         int32_t tp = 0;
         uint32_t tk = 0;
         for (int b = 0; b < B; ++b) {
@@ -379,7 +411,7 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         fill_req(hb, rl, ctx_lens, B);
         if ((st = upload(w, hb, rl.bytes)) != LA_OK) return st;
         const char* db = (const char*)w.tables;
-        sa.inline_lens = 0;
+        sa.src = la::kSrcTables;
         sa.seg = (const int4*)(db + off_seg);
         sa.cta_seg = (const int32_t*)(db + off_cta_seg);
         sa.cta_begin = (const int32_t*)(db + off_cta_begin);
@@ -663,6 +695,7 @@ void free_workspace(Workspace* w) {
                     (void*)w->pull_part, (void*)w->arrive, (void*)w->pull_ctr, (void*)w->gcount,
                     w->tables})
         if (p != nullptr) (void)hipFree(p);
+    for (void* p : w->retired) (void)hipFree(p);
     for (auto& s : w->ring) {
         if (s.host != nullptr) (void)hipHostFree(s.host);
         if (s.ev != nullptr) (void)hipEventDestroy(s.ev);
@@ -685,7 +718,8 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     la_opts o;
     la_opts_init(&o);
     if (opts != nullptr) o = *opts;
-    la_status st = validate(q, k, v, ctx_lens, B, H, d, scale, out, o.dtype);
+    const bool dev_lens = o.ctx_lens_device != nullptr;
+    la_status st = validate(q, k, v, ctx_lens, !dev_lens, B, H, d, scale, out, o.dtype);
     if (st != LA_OK) return st;
     if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_FIXED_SPLIT && o.kind != LA_KIND_PER_HEAD &&
         o.kind != LA_KIND_AUTO && o.kind != LA_KIND_PULL && o.kind != LA_KIND_CHUNKS)
@@ -708,27 +742,57 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     if (o.kv_heads < 0 || (o.kv_heads > 0 && H % o.kv_heads != 0))
         return fail(LA_EINVAL, "kv_heads %d must divide H = %d", o.kv_heads, H);
     if (o.kv_stride < 0) return fail(LA_EINVAL, "kv_stride must be >= 0");
-    for (int b = 0; b < B && o.kv_stride > 0; ++b)
+    if (o.q_tokens < 0 || o.q_tokens > kMaxQTokens)
+        return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", o.q_tokens, kMaxQTokens);
+    if (dev_lens) {
+        // lengths read in the launch: the lean kind on a [B, Hk, kv_stride, d]
+        // cache, whose size bounds every read; lengths outside
+        // [max(1, q_tokens), kv_stride] are reported by la_sync_check
+        if (o.kind != LA_KIND_LEAN)
+            return fail(LA_EINVAL, "ctx_lens_device needs kind lean");
+        if (o.kv_stride < 1)
+            return fail(LA_EINVAL, "ctx_lens_device needs a cache with kv_stride rows per head");
+        if ((int64_t)o.kv_stride * d * 2 > (int64_t)UINT32_MAX)
+            return fail(LA_EUNSUPPORTED, "kv_stride %d: one head's cache exceeds 4 GiB", o.kv_stride);
+        if (o.q_tokens > o.kv_stride)
+            return fail(LA_EINVAL, "q_tokens %d exceeds kv_stride %d", o.q_tokens, o.kv_stride);
+        if (B > la::kInlineB)
+            return fail(LA_EUNSUPPORTED, "ctx_lens_device takes up to %d requests", la::kInlineB);
+        if (o.host_tables != 0) return fail(LA_EINVAL, "host_tables needs host lengths");
+        if (o.tile_owner != nullptr)
+            return fail(LA_EINVAL, "tile_owner needs host lengths (its size is the tile count)");
+        if (((uintptr_t)o.ctx_lens_device & 3u) != 0)
+            return fail(LA_EINVAL, "ctx_lens_device must be 4-byte aligned");
+    }
+    for (int b = 0; b < B && o.kv_stride > 0 && !dev_lens; ++b)
         if (ctx_lens[b] > o.kv_stride)
             return fail(LA_EINVAL, "ctx_lens[%d] = %d exceeds kv_stride = %d", b, ctx_lens[b],
                         o.kv_stride);
-    if (o.q_tokens < 0 || o.q_tokens > kMaxQTokens)
-        return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", o.q_tokens, kMaxQTokens);
-    for (int b = 0; b < B && o.q_tokens > 1; ++b)
+    for (int b = 0; b < B && o.q_tokens > 1 && !dev_lens; ++b)
         if (ctx_lens[b] < o.q_tokens)
             return fail(LA_EINVAL, "ctx_lens[%d] = %d is shorter than the %d new tokens it must hold",
                         b, ctx_lens[b], o.q_tokens);
     const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
     std::lock_guard<std::mutex> lock(g_mu);
-    // A call's partials, flags and (in table mode) schedule tables live in a
-    // per-stream workspace that later calls overwrite or reallocate, so a
-    // captured call would replay stale addresses or another call's tables.
+    // Stream capture: only a lean launch whose schedule needs nothing copied
+    // (lengths on the device, or prefix sums in the kernel arguments), into a
+    // workspace that already exists and need not grow. Table uploads and the
+    // other kinds' tables go through staging buffers that later calls reuse,
+    // and growing would allocate and clear memory inside the graph.
     hipStreamCaptureStatus cap_status = hipStreamCaptureStatusNone;
     HIP_TRY(hipStreamIsCapturing((hipStream_t)stream, &cap_status));
-    if (cap_status != hipStreamCaptureStatusNone)
-        return fail(LA_EUNSUPPORTED, "stream capture is not supported (partials, flags and "
-                                     "schedule tables live in a reused per-stream workspace)");
+    const bool capturing = cap_status != hipStreamCaptureStatusNone;
+    if (capturing) {
+        if (o.kind != LA_KIND_LEAN || (!dev_lens && !in_launch_schedule(ctx_lens, B, o)))
+            return fail(LA_EUNSUPPORTED, "stream capture takes only the lean kind with the "
+                                         "schedule derived in the launch");
+        int dev = 0;
+        HIP_TRY(hipGetDevice(&dev));
+        if (g_ws.find(std::make_pair(dev, (hipStream_t)stream)) == g_ws.end())
+            return fail(LA_EUNSUPPORTED, "stream capture needs the stream's workspace: make a "
+                                         "call on the stream before capturing");
+    }
     if (o.kind == LA_KIND_AUTO) {
         int kind = 0, grid = 0;
         if ((st = select_on_device(ctx_lens, B, hd, d, o, &kind, &grid)) != LA_OK) return st;
@@ -737,7 +801,13 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     }
     Workspace* w = nullptr;
     if ((st = get_workspace((hipStream_t)stream, &w)) != LA_OK) return st;
-    if (o.kind == LA_KIND_LEAN) return run_lean(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
+    if (o.kind == LA_KIND_LEAN) {
+        w->capturing = capturing;
+        st = run_lean(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
+        w->capturing = false;
+        if (capturing && st == LA_OK) w->captured = true;
+        return st;
+    }
     if (o.kind == LA_KIND_PULL || o.kind == LA_KIND_CHUNKS)
         return run_pull(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
     return run_split_or_head(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
@@ -885,6 +955,10 @@ la_status la_sync_check(void* stream) {
     HIP_TRY(hipMemsetAsync(w.err, 0, sizeof(uint32_t), w.stream));
     if (w.flags != nullptr) HIP_TRY(hipMemsetAsync(w.flags, 0, w.flags_cap, w.stream));
     HIP_TRY(hipStreamSynchronize(w.stream));
+    if (err & la::kErrLengths)
+        return fail(LA_EINVAL, "context lengths read on the device were outside "
+                               "[max(1, q_tokens), kv_stride], or their tiles overflowed "
+                               "(error word 0x%x)", err);
     return fail(LA_ETIMEOUT, "a device-side wait exceeded its bound (error word 0x%x)", err);
 }
 

@@ -105,7 +105,7 @@ __device__ __forceinline__ void wait_flag(uint32_t* f, uint64_t limit, uint32_t*
     while (load_flag(f) == 0u) {
         __builtin_amdgcn_s_sleep(2);
         if (__builtin_amdgcn_s_memrealtime() - t0 > limit || load_flag(err) != 0u) {
-            atomicOr(err, 1u);
+            atomicOr(err, kErrTimeout);
             return;
         }
     }
@@ -128,31 +128,101 @@ __device__ __forceinline__ KSched kernarg_sched() {
             (ktok_t)(base + offsetof(Args, sched) + offsetof(SchedArgs, tok))};
 }
 
-// Walks a workgroup's segments in order. kInline: derived here (SegWalk over
-// the prefix sums in the kernel arguments); else read from the host's
-// tables. The tests compare both with the executed tile map. Two separate
-// types, one per kernel instantiation, keep the cursor state in scalar
-// registers.
-template <bool kInline>
+// LDS for the segment walk over lengths read from device memory.
+struct SchedLds {
+    int32_t tp[kInlineB + 1];   // tiles of the requests before b (exclusive prefix)
+    int64_t tok[kInlineB + 1];  // tokens of the requests before b
+    int bad;                    // a length was out of range, or the tiles overflow
+};
+
+// Walks a workgroup's segments in order: derived here (SegWalk over prefix
+// sums from the kernel arguments, or computed by the first wave from lengths
+// in device memory), or read from the host's tables. The tests compare every
+// source with the executed tile map. One type per source and kernel
+// instantiation keeps the cursor state in scalar registers.
+template <int kSrc>
 struct SegCursor;
 
 template <>
-struct SegCursor<true> {
+struct SegCursor<kSrcArgs> {
     SegWalk<ktp_t, ktok_t> w;
 
-    __device__ SegCursor(const SchedArgs& a, KSched k, int c) { w.init(k.tp, k.tok, a.B, a.U, a.G, c); }
-
+    __device__ SegCursor(const SchedArgs& a, KSched k, SchedLds&, int c) {
+        w.init(k.tp, k.tok, a.B, a.U, a.G, c);
+    }
+    __device__ bool bad() const { return false; }
     __device__ bool next(LeanSeg& s) { return w.next(s); }
 };
 
 template <>
-struct SegCursor<false> {
+struct SegCursor<kSrcDevice> {
+    SegWalk<const int32_t*, const int64_t*> w;
+    int bad_;
+
+    // Every thread constructs it (a barrier inside). The first wave reads the
+    // lengths (up to four consecutive requests per lane), checks them, and
+    // scans tiles and tokens across the wave into LDS.
+    __device__ SegCursor(const SchedArgs& a, KSched, SchedLds& l, int c) {
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            const int per = (a.B + 63) >> 6;
+            const int x0 = min(lane * per, a.B), x1 = min(x0 + per, a.B);
+            int32_t n[4];
+            int bad = 0;
+            int64_t tp = 0, tk = 0;
+            for (int j = 0; j < 4; ++j) {
+                const int x = x0 + j;
+                n[j] = x < x1 ? a.dlens[x] : 0;
+                if (x < x1) {
+                    bad |= n[j] < a.n_min || n[j] > a.n_max;
+                    tp += ((int64_t)n[j] + a.L - 1) / a.L;
+                    tk += n[j];
+                }
+            }
+            int64_t tpi = tp, tki = tk;
+            for (int o = 1; o < 64; o <<= 1) {
+                const int64_t t2 = __shfl_up(tpi, o, 64);
+                const int64_t k2 = __shfl_up(tki, o, 64);
+                if (lane >= o) {
+                    tpi += t2;
+                    tki += k2;
+                }
+            }
+            tp = tpi - tp;
+            tk = tki - tk;
+            for (int j = 0; j < 4 && x0 + j < x1; ++j) {
+                l.tp[x0 + j] = (int32_t)tp;
+                l.tok[x0 + j] = tk;
+                tp += ((int64_t)n[j] + a.L - 1) / a.L;
+                tk += n[j];
+            }
+            // the total must leave U * tiles < 2^31 (the schedule's 32-bit iterations)
+            const int64_t total = __shfl(tpi, 63, 64);
+            bad |= total * a.U > (int64_t)0x7fffffff;
+            bad = __any(bad);
+            if (lane == 63) {
+                l.tp[a.B] = (int32_t)total;
+                l.tok[a.B] = tki;
+            }
+            if (lane == 0) l.bad = bad;
+        }
+        __syncthreads();
+        bad_ = __builtin_amdgcn_readfirstlane(l.bad);
+        if (!bad_) w.init(l.tp, l.tok, a.B, a.U, a.G, c);
+    }
+    __device__ bool bad() const { return bad_ != 0; }
+    __device__ bool next(LeanSeg& s) { return bad_ ? false : w.next(s); }
+};
+
+template <>
+struct SegCursor<kSrcTables> {
     const SchedArgs& a;
     int si, s1;                 // next segment, end
     int iter;                   // linear iteration of the next segment
 
-    __device__ SegCursor(const SchedArgs& a_, KSched, int c)
+    __device__ SegCursor(const SchedArgs& a_, KSched, SchedLds&, int c)
         : a(a_), si(a_.cta_seg[c]), s1(a_.cta_seg[c + 1]), iter(a_.cta_begin[c]) {}
+    __device__ bool bad() const { return false; }
 
     __device__ bool next(LeanSeg& s) {
         if (si >= s1) return false;

@@ -19,11 +19,18 @@ constexpr int chunk_rows(int d) { return (2048 / d) * kRows; }
 constexpr int part_stride(int d) { return d + 4; }
 
 // Where a lean workgroup finds its segments: in tables built and uploaded by
-// the host, or -- for up to kInlineB requests and 2^32 - 1 tokens in all --
-// derived by the workgroup itself from per-request prefix sums carried in the
-// kernel arguments (no table copy on the stream; the partition and unit walk
-// are the host scheduler's).
+// the host (kSrcTables), or -- for up to kInlineB requests -- derived by the
+// workgroup itself with the host scheduler's partition and unit walk, from
+// per-request prefix sums carried in the kernel arguments (kSrcArgs, up to
+// 2^32 - 1 tokens in all) or from context lengths it reads from device memory
+// (kSrcDevice: nothing about the lengths passes through the host, so a
+// captured launch stays valid while they change).
 constexpr int kInlineB = 256;
+constexpr int kSrcTables = 0, kSrcArgs = 1, kSrcDevice = 2;
+
+// Device error word bits.
+constexpr uint32_t kErrTimeout = 1u;     // a wait gave up
+constexpr uint32_t kErrLengths = 2u;     // device context lengths out of range
 
 struct SchedArgs {
     const int4* seg;           // tables: [nseg] (u, t0, t1, host | finishing << 1)
@@ -32,10 +39,13 @@ struct SchedArgs {
     const int32_t* last_cta;   // tables: [B*U]
     const int32_t* ctx;        // tables: [B] n_b
     const int64_t* tok_off;    // tables: [B] sum_{b'<b} n_b'
-    int inline_lens;           // 1: derive from `tp` and `tok`; 0: read the tables
+    const int32_t* dlens;      // device: [B] n_b
+    int src;                   // kSrcTables, kSrcArgs or kSrcDevice
     int B;                     // requests
     int U;                     // schedule units per request
     int G;                     // workgroups launched
+    int L;                     // device: tile tokens
+    int n_min, n_max;          // device: valid n_b range (new tokens per request, cache rows per head)
     int32_t tp[kInlineB + 1];  // inline: tiles of the requests before b (exclusive prefix)
     uint32_t tok[kInlineB + 1];// inline: tokens of the requests before b
 };
@@ -167,12 +177,12 @@ struct PullArgs {
     float sl2e;
 };
 
-const void* lean_kernel_ptr(int dtype, int d, bool inline_lens);
+const void* lean_kernel_ptr(int dtype, int d, int src);
 uint64_t stream_read_unit();   // bytes per workgroup per loop trip of stream_read_kernel
 hipError_t launch_stream_read(const void* src, uint64_t chunk, int grid, uint32_t* sink,
                               hipStream_t s);
 hipError_t launch_pull(int dtype, int d, const PullArgs& a, int grid, hipStream_t s);
-const void* lean_gqa_kernel_ptr(int dtype, int d, bool inline_lens);
+const void* lean_gqa_kernel_ptr(int dtype, int d, int src);
 hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,
                            bool cooperative);
 hipError_t launch_split_gqa(int dtype, int d, const GqaArgs& a, int blocks, hipStream_t s);

@@ -274,7 +274,7 @@ __device__ __forceinline__ void write_out(float* out, float* m_out, float* l_out
 
 // ------------------------------------------------------------------ lean
 
-template <int DT, int D, bool IL>
+template <int DT, int D, int SRC>
 __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     using G = Geo<D>;
     constexpr int P = kDpl<D>;
@@ -285,7 +285,13 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
     const uint64_t t_in = stamp_start(a.ts, c);
-    SegCursor<IL> cur(a.sched, kernarg_sched<LeanArgs>(), c);
+    __shared__ SchedLds sl;
+    SegCursor<SRC> cur(a.sched, kernarg_sched<LeanArgs>(), sl, c);
+    if (cur.bad()) {   // lengths from device memory out of range: nothing is computed
+        if (c == 0 && t == 0) atomicOr(a.err, kErrLengths);
+        stamp_end(a.ts, c);
+        return;
+    }
     LeanSeg sg;
     while (cur.next(sg)) {
         const int u = sg.u;
@@ -639,17 +645,20 @@ const void* pick(int dtype, int d, F f16_64, F f16_128, F bf16_64, F bf16_128) {
 
 }  // namespace
 
-const void* lean_kernel_ptr(int dtype, int d, bool inline_lens) {
-    if (inline_lens)
-        return pick(dtype, d, &lean_kernel<0, 64, true>, &lean_kernel<0, 128, true>,
-                    &lean_kernel<1, 64, true>, &lean_kernel<1, 128, true>);
-    return pick(dtype, d, &lean_kernel<0, 64, false>, &lean_kernel<0, 128, false>,
-                &lean_kernel<1, 64, false>, &lean_kernel<1, 128, false>);
+const void* lean_kernel_ptr(int dtype, int d, int src) {
+    if (src == kSrcArgs)
+        return pick(dtype, d, &lean_kernel<0, 64, kSrcArgs>, &lean_kernel<0, 128, kSrcArgs>,
+                    &lean_kernel<1, 64, kSrcArgs>, &lean_kernel<1, 128, kSrcArgs>);
+    if (src == kSrcDevice)
+        return pick(dtype, d, &lean_kernel<0, 64, kSrcDevice>, &lean_kernel<0, 128, kSrcDevice>,
+                    &lean_kernel<1, 64, kSrcDevice>, &lean_kernel<1, 128, kSrcDevice>);
+    return pick(dtype, d, &lean_kernel<0, 64, kSrcTables>, &lean_kernel<0, 128, kSrcTables>,
+                &lean_kernel<1, 64, kSrcTables>, &lean_kernel<1, 128, kSrcTables>);
 }
 
 hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_t s,
                        bool cooperative) {
-    const void* fn = lean_kernel_ptr(dtype, d, a.sched.inline_lens != 0);
+    const void* fn = lean_kernel_ptr(dtype, d, a.sched.src);
     void* args[] = {const_cast<LeanArgs*>(&a)};
     if (cooperative)
         return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);

@@ -418,7 +418,7 @@ __device__ __forceinline__ void write_out_gqa(const GqaArgs& a, const Unit& x, i
 
 // ------------------------------------------------------------------ lean
 
-template <int DT, int D, bool IL>
+template <int DT, int D, int SRC>
 __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     using G = GGeo<D>;
     __shared__ GSmem<D> sm;
@@ -431,7 +431,13 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     const int dc = t & 15;
     const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
     const uint64_t t_in = stamp_start(a.ts, cta);
-    SegCursor<IL> cur(a.sched, kernarg_sched<GqaArgs>(), cta);
+    __shared__ SchedLds sl;
+    SegCursor<SRC> cur(a.sched, kernarg_sched<GqaArgs>(), sl, cta);
+    if (cur.bad()) {   // lengths from device memory out of range: nothing is computed
+        if (cta == 0 && t == 0) atomicOr(a.err, kErrLengths);
+        stamp_end(a.ts, cta);
+        return;
+    }
     LeanSeg sg;
     while (cur.next(sg)) {
         const int u = sg.u;
@@ -803,17 +809,23 @@ const void* pick_g(int dtype, int d, F f16_64, F f16_128, F bf16_64, F bf16_128)
 
 }  // namespace
 
-const void* lean_gqa_kernel_ptr(int dtype, int d, bool inline_lens) {
-    if (inline_lens)
-        return pick_g(dtype, d, &lean_gqa_kernel<0, 64, true>, &lean_gqa_kernel<0, 128, true>,
-                      &lean_gqa_kernel<1, 64, true>, &lean_gqa_kernel<1, 128, true>);
-    return pick_g(dtype, d, &lean_gqa_kernel<0, 64, false>, &lean_gqa_kernel<0, 128, false>,
-                  &lean_gqa_kernel<1, 64, false>, &lean_gqa_kernel<1, 128, false>);
+const void* lean_gqa_kernel_ptr(int dtype, int d, int src) {
+    if (src == kSrcArgs)
+        return pick_g(dtype, d, &lean_gqa_kernel<0, 64, kSrcArgs>,
+                      &lean_gqa_kernel<0, 128, kSrcArgs>, &lean_gqa_kernel<1, 64, kSrcArgs>,
+                      &lean_gqa_kernel<1, 128, kSrcArgs>);
+    if (src == kSrcDevice)
+        return pick_g(dtype, d, &lean_gqa_kernel<0, 64, kSrcDevice>,
+                      &lean_gqa_kernel<0, 128, kSrcDevice>, &lean_gqa_kernel<1, 64, kSrcDevice>,
+                      &lean_gqa_kernel<1, 128, kSrcDevice>);
+    return pick_g(dtype, d, &lean_gqa_kernel<0, 64, kSrcTables>,
+                  &lean_gqa_kernel<0, 128, kSrcTables>, &lean_gqa_kernel<1, 64, kSrcTables>,
+                  &lean_gqa_kernel<1, 128, kSrcTables>);
 }
 
 hipError_t launch_lean_gqa(int dtype, int d, const GqaArgs& a, int grid, hipStream_t s,
                            bool cooperative) {
-    const void* fn = lean_gqa_kernel_ptr(dtype, d, a.sched.inline_lens != 0);
+    const void* fn = lean_gqa_kernel_ptr(dtype, d, a.sched.src);
     void* args[] = {const_cast<GqaArgs*>(&a)};
     if (cooperative)
         return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);

@@ -54,14 +54,21 @@ struct SegWalk {
     int q, r;                  // I = q*G + r (I < 2^31, G <= I)
     int i, i1, b;              // next iteration, end of the range, request of i
 
-    // Workgroup c of G; every request has at least one tile.
+    // Workgroup c of a grid of G; every request has at least one tile. A grid
+    // larger than the I iterations splits them over its first I workgroups
+    // (one each) and leaves the others empty.
     LA_HD void init(TpPtr tp_, TokPtr tok_, int B, int U_, int G, int c) {
         tp = tp_;
         tok = tok_;
         U = U_;
         const int I = U * uniform((int)tp[B]);
-        q = I / G;
-        r = I - q * G;
+        const int Ge = G < I ? G : I;
+        q = I / Ge;
+        r = I - q * Ge;
+        if (c >= Ge) {
+            i = i1 = b = 0;
+            return;
+        }
         i = c * q + (c < r ? c : r);
         i1 = i + q + (c < r ? 1 : 0);
         int x = 0, y = B;   // U * tp[x] <= i < U * tp[y]

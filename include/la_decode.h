@@ -172,6 +172,18 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               request b starts at row (b * Hk + h) * kv_stride; only its
  *               first n_b rows are read, so a decode loop appends to it in
  *               place). Every n_b must be <= kv_stride (else LA_EINVAL).
+ *   ctx_lens_device optional device int32 [B]: the context lengths, read by
+ *               the kernel in the launch instead of from the host array
+ *               (ctx_lens may then be NULL and is ignored). Nothing about the
+ *               lengths passes through the host, so a launch captured into a
+ *               HIP graph stays valid while a decode loop grows them on the
+ *               device. Lean kind only, on a kv_stride cache (whose size
+ *               bounds every read), up to 256 requests, no tile_owner; the
+ *               grid is `grid` (or the default) and workgroups beyond the tile
+ *               iterations stay idle. Lengths outside [max(1, q_tokens),
+ *               kv_stride] make the kernel compute nothing and la_sync_check
+ *               return LA_EINVAL. Same tile map and output bits as the host
+ *               lengths on the same grid.
  *
  * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
  * pieces": workgroups pull the next piece of the global tile order instead of
@@ -210,14 +222,25 @@ typedef struct la_opts {
     int chunk_tiles;
     int host_tables;
     int kv_stride;
+    const int32_t* ctx_lens_device;
 } la_opts;
 
 void la_opts_init(la_opts* opts);
 
-/* Calls are asynchronous on `stream`; a stream that is being captured into a
- * HIP graph is refused (LA_EUNSUPPORTED): a call's partials, flags and (in
- * table mode) schedule tables live in a per-stream workspace that later calls
- * overwrite or reallocate. */
+/* Calls are asynchronous on `stream`. A stream that is being captured into a
+ * HIP graph takes only the lean kind with its schedule derived in the launch
+ * (ctx_lens_device, or host lengths within the in-launch limits and no
+ * host_tables), and only once an earlier call on the stream has sized its
+ * workspace for this grid and head dim: partials and flags live in a
+ * per-stream workspace that growing would reallocate, and table uploads go
+ * through staging buffers that later calls reuse. Anything else is refused
+ * with LA_EUNSUPPORTED before anything is enqueued. A captured launch with
+ * host lengths replays those lengths. The graph uses the capturing stream's
+ * workspace, which that stream's later calls share: replay it on that stream
+ * (or order it against the stream's other work). Once a launch has been
+ * captured on a stream, a later call there that needs a larger workspace
+ * allocates new buffers and keeps the old ones until la_shutdown, so the
+ * graph stays valid; la_shutdown ends every captured graph's validity. */
 la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* ctx_lens, int B, int H, int d, float scale,
                        float* out, void* stream, const la_opts* opts);

@@ -227,3 +227,47 @@ def test_kv_stride_validation_and_sizes():
     cache = torch.zeros(2, 2, 64, 64, dtype=torch.float16)
     with pytest.raises(ValueError, match="cache"):
         la.decode_attention(q, cache, cache[:1], [16, 40])
+
+
+def test_device_lengths_validation():
+    """ctx_lens_device: refused in argument checking (before any device call)
+    without a kv_stride cache, for any kind but lean, above 256 requests, with
+    host tables or a tile map, or misaligned; the binding wants an int32 tensor."""
+    import torch
+    L = la.lib()
+    fake = 1 << 20
+    o = la.binding.LaOpts()
+
+    def call(B=2, **kw):
+        L.la_opts_init(ctypes.byref(o))
+        o.ctx_lens_device = fake
+        o.kv_stride = 64
+        for k, v in kw.items():
+            setattr(o, k, v)
+        st = L.la_decode_ex(fake, fake, fake, None, B, 4, 128, 0.1, fake, None, ctypes.byref(o))
+        return st, la.la_last_error()
+
+    st, msg = call(kv_stride=0)
+    assert st == 1 and "kv_stride" in msg
+    for kind in (la.LA_KIND_FIXED_SPLIT, la.LA_KIND_PER_HEAD, la.LA_KIND_PULL, la.LA_KIND_AUTO,
+                 la.LA_KIND_CHUNKS):
+        st, msg = call(kind=kind)
+        assert st == 1 and "lean" in msg, kind
+    st, msg = call(B=257)
+    assert st == 2 and "256" in msg
+    st, msg = call(host_tables=1)
+    assert st == 1 and "host_tables" in msg
+    st, msg = call(tile_owner=fake)
+    assert st == 1 and "tile_owner" in msg
+    st, msg = call(q_tokens=65 - 1, kv_stride=8)
+    assert st == 1 and "q_tokens" in msg
+    st, msg = call(ctx_lens_device=fake + 2)
+    assert st == 1 and "aligned" in msg
+    st, msg = call(kv_stride=(1 << 24) + 1)
+    assert st == 2 and "4 GiB" in msg
+    q = torch.zeros(2, 4, 64, dtype=torch.float16)
+    out = torch.zeros(2, 4, 64)
+    kv = torch.zeros(2, 4, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="int32"):
+        la.la_decode_ex(q, kv, kv, None, 2, 4, 64, 0.125, out, kv_stride=64,
+                        ctx_lens_device=torch.zeros(2, dtype=torch.int64))

@@ -414,8 +414,8 @@ def test_timestamps(la, kind, blocks):
 
 
 def test_stream_capture_is_refused(la):
-    """A stream being captured into a graph is refused before anything is
-    enqueued (the schedule tables live in a reused per-stream workspace)."""
+    """A stream being captured into a graph before any call has sized its
+    workspace is refused before anything is enqueued."""
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so.7")
     inp = W.make_custom([300, 40], H=2, d=64, dtype="f16", seed=61, device="cuda")

@@ -71,3 +71,13 @@ def test_walk_random_shapes(walker, seed):
     G = int(rng.integers(1, 1100))
     Gu, rows = expected(lens, U, L, G)
     assert walk(walker, lens, U, L, Gu) == rows
+
+
+def test_grid_larger_than_the_work(walker):
+    """A grid of more workgroups than tile iterations: the first I take one
+    iteration each, as the oracle's G = min(G_req, I), and the rest are
+    empty."""
+    lens, U, L = [3, 40, 17], 2, 16
+    Gu, rows = expected(lens, U, L, 50)
+    assert Gu < 50
+    assert walk(walker, lens, U, L, 50) == rows
