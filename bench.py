@@ -548,9 +548,9 @@ def decode_loop(workloads, steps=64, warmup=4):
     attention): µs per step over `steps` steps queued back to back, for the
     schedule derived in the launch from host lengths, for host tables, for
     lengths kept on the device (each step adds one to them with a small
-    device kernel, then calls the library), and for that step captured once
-    into a HIP graph and replayed; next to the in-launch calls at fixed
-    lengths. Prints one JSON line."""
+    device kernel, then calls the library), for that step captured once into
+    a HIP graph and replayed, and for 16 such steps captured into one graph;
+    next to the in-launch calls at fixed lengths. Prints one JSON line."""
     import torch
 
     import decode_phase_attention_amd as la
@@ -629,6 +629,28 @@ def decode_loop(workloads, steps=64, warmup=4):
         la.la_sync_check(s.cuda_stream)
         assert dl.cpu().tolist() == lens_of[-1]
         row_out["graph_device_lengths_growing"] = round((t1 - t0) * 1e6 / steps, 1)
+        del g
+        # several steps in one graph: the graph launch's own cost shared by them
+        chain = 16
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(chain):
+                dstep()
+        with torch.cuda.stream(s):
+            dl.copy_(base_t)
+            g.replay()
+            dl.copy_(base_t)
+            with gc_paused():
+                s.synchronize()
+                t0 = time.perf_counter()
+                for i in range(steps // chain):
+                    g.replay()
+                s.synchronize()
+                t1 = time.perf_counter()
+        la.la_sync_check(s.cuda_stream)
+        assert dl.cpu().tolist() == lens_of[steps // chain * chain - 1]
+        row_out[f"graph_{chain}_steps_device_lengths_growing"] = round(
+            (t1 - t0) * 1e6 / (steps // chain * chain), 1)
         del g
         table[name] = row_out
         log(f"   {row_out}")
