@@ -51,7 +51,7 @@ struct SegWalk {
     TpPtr tp;
     TokPtr tok;
     int U;
-    int q, r;                  // I = q*G + r (I < 2^31, G <= I)
+    int q, r;                  // I = q*Ge + r, Ge = min(G, I) workgroups with work (I < 2^31)
     int i, i1, b;              // next iteration, end of the range, request of i
 
     // Workgroup c of a grid of G; every request has at least one tile. A grid

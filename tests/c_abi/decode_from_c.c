@@ -1,9 +1,12 @@
 /*
  * Calls libla_decode from plain C through include/la_decode.h: device buffers
  * from the HIP runtime, host context lengths, one la_decode_bf16 call and one
- * la_decode_ex call (kind auto, 4 K/V heads for 8 query heads), then writes
- * the inputs' bit patterns and both outputs to a file for the test to check
- * against the oracle. Test infrastructure (tests/test_c_abi.py).
+ * la_decode_ex call (kind auto, 4 K/V heads for 8 query heads); then a decode
+ * step on a [B, H, S, D] cache with the lengths in device memory, captured
+ * into a HIP graph on a stream of its own and replayed STEPS times, the
+ * lengths raised by one token between replays. Writes the inputs' bit
+ * patterns and all outputs to a file for the test to check against the
+ * oracle. Test infrastructure (tests/test_c_abi.py).
  *
  * Usage: decode_from_c OUTFILE. Exit status 0 on success.
  */
@@ -15,7 +18,7 @@
 
 #include "la_decode.h"
 
-enum { B = 2, H = 8, HK = 4, D = 128 };
+enum { B = 2, H = 8, HK = 4, D = 128, S = 1024, STEPS = 3 };
 static const int32_t kLens[B] = {300, 1000};
 
 /* xorshift64*, mapped to roughly N(0,1) by summing four uniforms */
@@ -84,6 +87,50 @@ int main(int argc, char** argv) {
     CHECK_LA(la_sync_check(NULL));
     CHECK_HIP(hipMemcpy(out2, dout, nq * 4, hipMemcpyDeviceToHost));
 
+    /* 3: lengths on the device, one decode step captured into a graph */
+    const size_t ncache = (size_t)B * H * S * D;
+    uint16_t* ks = malloc(ncache * 2);
+    uint16_t* vs = malloc(ncache * 2);
+    float* out3 = malloc(nq * 4 * STEPS);
+    if (!ks || !vs || !out3) return 1;
+    for (size_t i = 0; i < ncache; ++i) ks[i] = to_bf16(draw());
+    for (size_t i = 0; i < ncache; ++i) vs[i] = to_bf16(draw());
+    void *dks, *dvs;
+    int32_t* dlens;
+    CHECK_HIP(hipMalloc(&dks, ncache * 2));
+    CHECK_HIP(hipMalloc(&dvs, ncache * 2));
+    CHECK_HIP(hipMalloc((void**)&dlens, B * sizeof(int32_t)));
+    CHECK_HIP(hipMemcpy(dks, ks, ncache * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dvs, vs, ncache * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dlens, kLens, B * sizeof(int32_t), hipMemcpyHostToDevice));
+    hipStream_t st;
+    CHECK_HIP(hipStreamCreate(&st));
+    la_opts_init(&o);
+    o.dtype = LA_BF16;
+    o.kv_stride = S;
+    o.ctx_lens_device = dlens;
+    /* an eager call sizes the stream's workspace; capture needs it */
+    CHECK_LA(la_decode_ex(dq, dks, dvs, NULL, B, H, D, scale, dout, st, &o));
+    CHECK_LA(la_sync_check(st));
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    CHECK_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeGlobal));
+    const la_status cap = la_decode_ex(dq, dks, dvs, NULL, B, H, D, scale, dout, st, &o);
+    CHECK_HIP(hipStreamEndCapture(st, &graph));
+    CHECK_LA(cap);
+    CHECK_HIP(hipGraphInstantiateWithFlags(&exec, graph, 0));
+    for (int i = 0; i < STEPS; ++i) {
+        int32_t lens[B];
+        for (int b = 0; b < B; ++b) lens[b] = kLens[b] + i + 1;
+        CHECK_HIP(hipMemcpy(dlens, lens, sizeof(lens), hipMemcpyHostToDevice));
+        CHECK_HIP(hipGraphLaunch(exec, st));
+        CHECK_HIP(hipStreamSynchronize(st));
+        CHECK_LA(la_sync_check(st));
+        CHECK_HIP(hipMemcpy(out3 + (size_t)i * nq, dout, nq * 4, hipMemcpyDeviceToHost));
+    }
+    CHECK_HIP(hipGraphExecDestroy(exec));
+    CHECK_HIP(hipGraphDestroy(graph));
+
     FILE* f = fopen(argv[1], "wb");
     if (!f) return 1;
     const int32_t hdr[4] = {B, H, HK, D};
@@ -94,8 +141,12 @@ int main(int argc, char** argv) {
     fwrite(v, 2, nkv_mha, f);
     fwrite(out1, 4, nq, f);
     fwrite(out2, 4, nq, f);
+    fwrite(ks, 2, ncache, f);
+    fwrite(vs, 2, ncache, f);
+    fwrite(out3, 4, nq * STEPS, f);
     fclose(f);
     la_shutdown();
+    CHECK_HIP(hipStreamDestroy(st));
     (void)nkv;
     return 0;
 }

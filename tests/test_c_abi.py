@@ -1,8 +1,9 @@
 """The C ABI from a plain C program (tests/c_abi/decode_from_c.c): it builds
 against include/la_decode.h with a C compiler and links libla_decode.so (CPU
-test), and on the GPU its two calls -- la_decode_bf16 with the plain argument
-list, and la_decode_ex with kind auto over grouped K/V heads -- match the fp64
-oracle on the bits it wrote out."""
+test), and on the GPU its calls -- la_decode_bf16 with the plain argument
+list, la_decode_ex with kind auto over grouped K/V heads, and a decode step
+with the lengths in device memory captured into a HIP graph and replayed over
+growing lengths -- match the fp64 oracle on the bits it wrote out."""
 from __future__ import annotations
 
 import os
@@ -69,3 +70,17 @@ def test_c_program_matches_oracle(tmp_path):
                               kv_heads=int(HK))[0]
     assert float(np.max(np.abs(out1 - ref1))) <= 1e-3
     assert float(np.max(np.abs(out2 - ref2))) <= 1e-3
+    off += 4 * B * H * D
+    S, steps = 1024, 3
+    ks = np.frombuffer(raw, np.uint16, B * H * S * D, off).reshape(B, H, S, D)
+    off += 2 * B * H * S * D
+    vs = np.frombuffer(raw, np.uint16, B * H * S * D, off).reshape(B, H, S, D)
+    off += 2 * B * H * S * D
+    out3 = np.frombuffer(raw, np.float32, steps * B * H * D, off).reshape(steps, B, H, D)
+    assert off + 4 * steps * B * H * D == len(raw)
+    for i in range(steps):
+        ln = [x + i + 1 for x in lens]
+        kp = np.concatenate([ks[b, :, :x].reshape(-1, D) for b, x in enumerate(ln)])
+        vp = np.concatenate([vs[b, :, :x].reshape(-1, D) for b, x in enumerate(ln)])
+        ref3 = oracle.attend_fp64(q, kp, vp, ln, scale, "bf16", workers=8)[0]
+        assert float(np.max(np.abs(out3[i] - ref3))) <= 1e-3, i
