@@ -78,6 +78,7 @@ struct Workspace {
     bool capturing = false;         // the current call is being captured: nothing may be allocated
     bool captured = false;          // a graph may hold the buffers: growing keeps the old ones
     std::vector<void*> retired;     // buffers replaced after a capture, freed at shutdown
+    std::vector<std::pair<void*, size_t>> retired_zeroed;   // the same for zero-between-launch buffers
 };
 
 std::mutex g_mu;
@@ -113,7 +114,11 @@ la_status grow(Workspace& w, void** p, size_t* cap, size_t need_bytes, bool zero
                                      "stream before capturing");
     if (*p != nullptr) {
         if (w.captured) {
-            w.retired.push_back(*p);   // a captured graph's replays may still use it
+            // a captured graph's replays may still use it
+            if (zero)
+                w.retired_zeroed.emplace_back(*p, *cap);
+            else
+                w.retired.push_back(*p);
         } else {
             HIP_TRY(hipStreamSynchronize(w.stream));
             HIP_TRY(hipFree(*p));
@@ -696,6 +701,7 @@ void free_workspace(Workspace* w) {
                     w->tables})
         if (p != nullptr) (void)hipFree(p);
     for (void* p : w->retired) (void)hipFree(p);
+    for (auto& r : w->retired_zeroed) (void)hipFree(r.first);
     for (auto& s : w->ring) {
         if (s.host != nullptr) (void)hipHostFree(s.host);
         if (s.ev != nullptr) (void)hipEventDestroy(s.ev);
@@ -954,6 +960,8 @@ la_status la_sync_check(void* stream) {
     if (err == 0) return LA_OK;
     HIP_TRY(hipMemsetAsync(w.err, 0, sizeof(uint32_t), w.stream));
     if (w.flags != nullptr) HIP_TRY(hipMemsetAsync(w.flags, 0, w.flags_cap, w.stream));
+    // flags that graphs captured before a workspace growth still use
+    for (auto& r : w.retired_zeroed) HIP_TRY(hipMemsetAsync(r.first, 0, r.second, w.stream));
     HIP_TRY(hipStreamSynchronize(w.stream));
     if (err & la::kErrLengths)
         return fail(LA_EINVAL, "context lengths read on the device were outside "
