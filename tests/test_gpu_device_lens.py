@@ -226,3 +226,50 @@ def test_capture_refusals(la):
     ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
                              inp.scale, "f16", workers=8)[0]
     assert float(np.max(np.abs(out.cpu().numpy() - ref))) <= 1e-3
+
+
+def test_random_device_lengths(la):
+    """Random shapes (head dims, dtypes, grouped heads, new tokens, up to 256
+    requests, lengths at tile edges), random grids and tiles on capacity-strided
+    caches: device lengths give the host-length bits and meet the oracle."""
+    rng = np.random.default_rng(4242)
+    worst = 0.0
+    for i in range(30):
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["f16", "bf16"]))
+        H = int(rng.choice([1, 2, 4, 8, 16]))
+        Hk = int(rng.choice([h for h in (1, 2, 4, 8, 16) if H % h == 0]))
+        Nq = int(rng.choice([1, 1, 2, 5]))
+        B = int(rng.choice([1, 3, 8, 64, 256]))
+        L = 128 if d == 128 else 256
+        hi = 20000 if B <= 8 else 600
+        lens = []
+        for _ in range(B):
+            if rng.random() < 0.25:
+                n = int(rng.integers(1, 4)) * L + int(rng.integers(-1, 2))
+            else:
+                n = int(np.exp(rng.uniform(0, np.log(hi))))
+            lens.append(max(n, Nq))
+        grouped = H // Hk * Nq > 1
+        dt = la.LA_BF16 if dtype == "bf16" else la.LA_F16
+        cap = la.la_max_grid_grouped(d, dt) if grouped else la.la_max_grid(d, dt)
+        grid = int(rng.choice([0, 1, int(rng.integers(1, cap + 1)), cap]))
+        tile = int(rng.choice([0, 16, 64, 300]))
+        S = max(lens) + int(rng.integers(0, 50))
+        say(f"[random device lens {i}] d={d} {dtype} H={H} Hk={Hk} Nq={Nq} B={B} grid={grid} "
+            f"tile={tile} S={S} max_len={max(lens)}")
+        inp = W.make_custom(lens, H, d, dtype, seed=500 + i, device="cuda", kv_heads=Hk,
+                            q_tokens=Nq)
+        kc, vc = strided(inp, S)
+        host = run(la, inp, kc, vc, S, lens=lens, grid=grid, tile_tokens=tile)
+        dl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        dev = run(la, inp, kc, vc, S, dlens=dl, grid=grid, tile_tokens=tile)
+        for x, y in zip(host, dev):
+            np.testing.assert_array_equal(x, y)
+        ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                                 inp.scale, dtype, workers=16, kv_heads=Hk)[0]
+        err = float(np.max(np.abs(dev[0] - ref)))
+        assert err <= 1e-3, (i, err)
+        worst = max(worst, err)
+        del inp, kc, vc
+    say(f"30 random device-length launches, worst max|dO| = {worst:.2e}")
