@@ -793,6 +793,9 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
         if (o.kind != LA_KIND_LEAN || (!dev_lens && !in_launch_schedule(ctx_lens, B, o)))
             return fail(LA_EUNSUPPORTED, "stream capture takes only the lean kind with the "
                                          "schedule derived in the launch");
+        if (o.cooperative != 0)
+            return fail(LA_EUNSUPPORTED, "stream capture takes ordinary launches only "
+                                         "(cooperative = 0)");
         int dev = 0;
         HIP_TRY(hipGetDevice(&dev));
         if (g_ws.find(std::make_pair(dev, (hipStream_t)stream)) == g_ws.end())

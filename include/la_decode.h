@@ -230,7 +230,8 @@ void la_opts_init(la_opts* opts);
 /* Calls are asynchronous on `stream`. A stream that is being captured into a
  * HIP graph takes only the lean kind with its schedule derived in the launch
  * (ctx_lens_device, or host lengths within the in-launch limits and no
- * host_tables), and only once an earlier call on the stream has sized its
+ * host_tables) as an ordinary launch (cooperative = 0), and only once an
+ * earlier call on the stream has sized its
  * workspace for this grid and head dim: partials and flags live in a
  * per-stream workspace that growing would reallocate, and table uploads go
  * through staging buffers that later calls reuse. Anything else is refused

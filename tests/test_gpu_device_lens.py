@@ -183,7 +183,8 @@ def test_graph_captured_decode_loop(la, H, Hk, Nq, d, dtype):
 def test_capture_refusals(la):
     """Refused before anything is enqueued: capture on a stream with no
     workspace yet, capture that would have to grow the workspace, capture of
-    a kind that uploads tables. The stream works normally afterwards."""
+    a kind that uploads tables, a cooperative launch. The stream works
+    normally afterwards."""
     hip = ctypes.CDLL("libamdhip64.so.7")
     hip.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
     hip.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
@@ -219,6 +220,7 @@ def test_capture_refusals(la):
     assert "grow" in captured(ctx_lens_device=dl, grid=512)     # more workgroups than sized for
     assert "lean" in captured(lens=lens, kind="pull")           # tables through staging
     assert "lean" in captured(lens=lens, host_tables=True)
+    assert "cooperative" in captured(ctx_lens_device=dl, grid=16, cooperative=True)
     la.la_decode_ex(inp.q, kc, vc, lens, 2, 4, 64, inp.scale, out, stream=s.cuda_stream,
                     kv_stride=S)
     s.synchronize()
