@@ -762,8 +762,8 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
             return fail(LA_EUNSUPPORTED, "kv_stride %d: one head's cache exceeds 4 GiB", o.kv_stride);
         if (o.q_tokens > o.kv_stride)
             return fail(LA_EINVAL, "q_tokens %d exceeds kv_stride %d", o.q_tokens, o.kv_stride);
-        if (B > la::kInlineB)
-            return fail(LA_EUNSUPPORTED, "ctx_lens_device takes up to %d requests", la::kInlineB);
+        if (B > la::kMaxDeviceB)
+            return fail(LA_EUNSUPPORTED, "ctx_lens_device takes up to %d requests", la::kMaxDeviceB);
         if (o.host_tables != 0) return fail(LA_EINVAL, "host_tables needs host lengths");
         if (o.tile_owner != nullptr)
             return fail(LA_EINVAL, "tile_owner needs host lengths (its size is the tile count)");

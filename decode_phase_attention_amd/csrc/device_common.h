@@ -130,8 +130,8 @@ __device__ __forceinline__ KSched kernarg_sched() {
 
 // LDS for the segment walk over lengths read from device memory.
 struct SchedLds {
-    int32_t tp[kInlineB + 1];   // tiles of the requests before b (exclusive prefix)
-    int64_t tok[kInlineB + 1];  // tokens of the requests before b
+    int32_t tp[kMaxDeviceB + 1];   // tiles of the requests before b (exclusive prefix)
+    int64_t tok[kMaxDeviceB + 1];  // tokens of the requests before b
     int bad;                    // a length was out of range, or the tiles overflow
 };
 
@@ -160,24 +160,23 @@ struct SegCursor<kSrcDevice> {
     int bad_;
 
     // Every thread constructs it (a barrier inside). The first wave reads the
-    // lengths (up to four consecutive requests per lane), checks them, and
-    // scans tiles and tokens across the wave into LDS.
+    // lengths once (up to 16 consecutive requests per lane), checks them, and
+    // scans tiles and tokens across the wave into LDS. Each length is read
+    // from device memory once and kept in the lane's own LDS entries, so the
+    // checked values are the ones the walk uses.
     __device__ SegCursor(const SchedArgs& a, KSched, SchedLds& l, int c) {
         if (threadIdx.x < 64) {
             const int lane = threadIdx.x;
             const int per = (a.B + 63) >> 6;
             const int x0 = min(lane * per, a.B), x1 = min(x0 + per, a.B);
-            int32_t n[4];
             int bad = 0;
             int64_t tp = 0, tk = 0;
-            for (int j = 0; j < 4; ++j) {
-                const int x = x0 + j;
-                n[j] = x < x1 ? a.dlens[x] : 0;
-                if (x < x1) {
-                    bad |= n[j] < a.n_min || n[j] > a.n_max;
-                    tp += ((int64_t)n[j] + a.L - 1) / a.L;
-                    tk += n[j];
-                }
+            for (int x = x0; x < x1; ++x) {
+                const int32_t n = a.dlens[x];
+                l.tp[x] = n;
+                bad |= n < a.n_min || n > a.n_max;
+                tp += ((int64_t)n + a.L - 1) / a.L;
+                tk += n;
             }
             int64_t tpi = tp, tki = tk;
             for (int o = 1; o < 64; o <<= 1) {
@@ -190,11 +189,12 @@ struct SegCursor<kSrcDevice> {
             }
             tp = tpi - tp;
             tk = tki - tk;
-            for (int j = 0; j < 4 && x0 + j < x1; ++j) {
-                l.tp[x0 + j] = (int32_t)tp;
-                l.tok[x0 + j] = tk;
-                tp += ((int64_t)n[j] + a.L - 1) / a.L;
-                tk += n[j];
+            for (int x = x0; x < x1; ++x) {
+                const int32_t n = l.tp[x];
+                l.tp[x] = (int32_t)tp;
+                l.tok[x] = tk;
+                tp += ((int64_t)n + a.L - 1) / a.L;
+                tk += n;
             }
             // the total must leave U * tiles < 2^31 (the schedule's 32-bit iterations)
             const int64_t total = __shfl(tpi, 63, 64);

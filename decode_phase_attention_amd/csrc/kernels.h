@@ -26,6 +26,8 @@ constexpr int part_stride(int d) { return d + 4; }
 // (kSrcDevice: nothing about the lengths passes through the host, so a
 // captured launch stays valid while they change).
 constexpr int kInlineB = 256;
+// Most requests whose lengths the lean kernels read from device memory.
+constexpr int kMaxDeviceB = 1024;
 constexpr int kSrcTables = 0, kSrcArgs = 1, kSrcDevice = 2;
 
 // Device error word bits.

@@ -178,12 +178,14 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               lengths passes through the host, so a launch captured into a
  *               HIP graph stays valid while a decode loop grows them on the
  *               device. Lean kind only, on a kv_stride cache (whose size
- *               bounds every read), up to 256 requests, no tile_owner; the
+ *               bounds every read), up to 1024 requests, no tile_owner; the
  *               grid is `grid` (or the default) and workgroups beyond the tile
  *               iterations stay idle. Lengths outside [max(1, q_tokens),
  *               kv_stride] make the kernel compute nothing and la_sync_check
  *               return LA_EINVAL. Same tile map and output bits as the host
- *               lengths on the same grid.
+ *               lengths on the same grid. Each workgroup reads every length
+ *               once at its start: writes to them must be ordered before the
+ *               call (on its stream, or synchronised with it).
  *
  * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
  * pieces": workgroups pull the next piece of the global tile order instead of

@@ -231,7 +231,7 @@ def test_kv_stride_validation_and_sizes():
 
 def test_device_lengths_validation():
     """ctx_lens_device: refused in argument checking (before any device call)
-    without a kv_stride cache, for any kind but lean, above 256 requests, with
+    without a kv_stride cache, for any kind but lean, above 1024 requests, with
     host tables or a tile map, or misaligned; the binding wants an int32 tensor."""
     import torch
     L = la.lib()
@@ -253,8 +253,8 @@ def test_device_lengths_validation():
                  la.LA_KIND_CHUNKS):
         st, msg = call(kind=kind)
         assert st == 1 and "lean" in msg, kind
-    st, msg = call(B=257)
-    assert st == 2 and "256" in msg
+    st, msg = call(B=1025)
+    assert st == 2 and "1024" in msg
     st, msg = call(host_tables=1)
     assert st == 1 and "host_tables" in msg
     st, msg = call(tile_owner=fake)

@@ -62,7 +62,9 @@ def run(la, inp, kc, vc, S, lens=None, dlens=None, **opts):
 CASES = [([3000, 17, 60000, 129], 4, 4, 1, 128, "bf16"),
          ([1, 700, 256, 2049], 8, 2, 1, 64, "f16"),
          ([515, 4, 1030], 8, 2, 3, 128, "bf16"),
-         ([int(x) for x in np.random.default_rng(3).integers(1, 400, 256)], 2, 2, 1, 64, "f16")]
+         ([int(x) for x in np.random.default_rng(3).integers(1, 400, 256)], 2, 2, 1, 64, "f16"),
+         ([int(x) for x in np.random.default_rng(4).integers(1, 300, 600)], 4, 4, 1, 128, "bf16"),
+         ([int(x) for x in np.random.default_rng(5).integers(2, 300, 1024)], 2, 1, 2, 64, "f16")]
 
 
 @pytest.mark.parametrize("lens,H,Hk,Nq,d,dtype", CASES)
@@ -70,7 +72,9 @@ CASES = [([3000, 17, 60000, 129], 4, 4, 1, 128, "bf16"),
 def test_device_lengths_match_host_lengths(la, lens, H, Hk, Nq, d, dtype, grid):
     """Same grid, same partition: the device-length launch gives the host-length
     launch's output, m and l bit for bit, and both meet the oracle. A grid
-    larger than the tile iterations leaves the extra workgroups idle."""
+    larger than the tile iterations leaves the extra workgroups idle. Above 256
+    requests the host lengths go through the host-built tables, so those cases
+    also compare the tables with the partition computed in the launch."""
     inp = W.make_custom(lens, H, d, dtype, seed=len(lens) + H + Nq, device="cuda", kv_heads=Hk,
                         q_tokens=Nq)
     dt = la.LA_BF16 if dtype == "bf16" else la.LA_F16
@@ -231,7 +235,7 @@ def test_capture_refusals(la):
 
 
 def test_random_device_lengths(la):
-    """Random shapes (head dims, dtypes, grouped heads, new tokens, up to 256
+    """Random shapes (head dims, dtypes, grouped heads, new tokens, up to 1024
     requests, lengths at tile edges), random grids and tiles on capacity-strided
     caches: device lengths give the host-length bits and meet the oracle."""
     rng = np.random.default_rng(4242)
@@ -242,7 +246,7 @@ def test_random_device_lengths(la):
         H = int(rng.choice([1, 2, 4, 8, 16]))
         Hk = int(rng.choice([h for h in (1, 2, 4, 8, 16) if H % h == 0]))
         Nq = int(rng.choice([1, 1, 2, 5]))
-        B = int(rng.choice([1, 3, 8, 64, 256]))
+        B = int(rng.choice([1, 3, 8, 64, 256, 700, 1024]))
         L = 128 if d == 128 else 256
         hi = 20000 if B <= 8 else 600
         lens = []
