@@ -72,7 +72,7 @@ int main(int argc, char** argv) {
     CHECK_HIP(hipMemcpy(dv, v, nkv_mha * 2, hipMemcpyHostToDevice));
     const float scale = 0.08838834764831845f;   /* 1/sqrt(128) */
 
-    /* 1: plain multi-head decode, the spec argument list */
+    /* 1: plain multi-head decode with the plain argument list */
     CHECK_LA(la_decode_bf16(dq, dk, dv, kLens, B, H, D, scale, dout, NULL));
     CHECK_LA(la_sync_check(NULL));
     CHECK_HIP(hipMemcpy(out1, dout, nq * 4, hipMemcpyDeviceToHost));
