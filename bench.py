@@ -366,7 +366,16 @@ def selector_shapes():
           dict(lens=[32768] * 8, H=16, Hk=1, d=64, dt="f16"),
           dict(lens=loguni(16, 1024, 262144, 6), H=32, Hk=4, d=128, dt="bf16"),
           dict(lens=loguni(16, 1024, 65536, 7), H=32, Hk=8, Nq=4, d=128, dt="bf16"),
-          dict(lens=[8192] * 32, H=32, Nq=4, d=128, dt="bf16")]
+          dict(lens=[8192] * 32, H=32, Nq=4, d=128, dt="bf16"),
+          # latency-bound launches: a few short units, all at once
+          dict(lens=[1024], H=4, d=64, dt="f16"),
+          dict(lens=[512], H=8, d=128, dt="bf16"),
+          dict(lens=[256] * 2, H=32, d=128, dt="bf16"),
+          dict(lens=[512] * 8, H=32, d=128, dt="bf16"),
+          dict(lens=[1024] * 4, H=8, d=64, dt="f16"),
+          dict(lens=[512] * 8, H=32, Hk=8, d=128, dt="bf16"),
+          dict(lens=[1024], H=32, d=128, dt="bf16"),
+          dict(lens=[4096], H=1, d=128, dt="bf16")]
     return S
 
 

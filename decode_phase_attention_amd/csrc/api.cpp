@@ -685,8 +685,8 @@ la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int 
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
     const char* why = "";
-    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, cus, cap.coresident, kind,
-                                   grid, &why);
+    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, d, hd.grouped, cus,
+                                   cap.coresident, kind, grid, &why);
     if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
     return LA_OK;
 }
@@ -883,8 +883,8 @@ la_status la_select_for(const int32_t* ctx_lens, int B, int H, int d, int kv_hea
     const Heads hd = heads_of(H, kv_heads, q_tokens);
     const int L = tile_tokens > 0 ? tile_tokens : la::chunk_rows(d);
     const char* why = "";
-    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, cus, coresident, kind, grid,
-                                   &why);
+    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, d, hd.grouped, cus,
+                                   coresident, kind, grid, &why);
     if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
     return LA_OK;
 }

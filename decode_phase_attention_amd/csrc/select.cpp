@@ -23,6 +23,16 @@
 //      A fixed split is never chosen: on uniform lengths the lean schedule
 //      already is the best fixed split, in one launch instead of two, and on
 //      ragged lengths its balance is better.
+//   3. Short heads. When every head's K and V fit in kShortUnitBytes and all
+//      heads run at once on one workgroup per CU, the launch is bound by
+//      latency, not bandwidth: the few workgroups of the per-head kernel
+//      stream their head without contention, while the lean schedule would
+//      split the heads into one-tile pieces and add a merge. Per head is
+//      chosen (measured on 4 to 256 heads of 128-256 KiB: 12-19% faster than
+//      lean; heads of 512 KiB already favour lean). Single-head kernels
+//      only: the grouped per-head kernel, whose waves step through a short
+//      unit in few long-latency steps, measured 27% slower than lean on 64
+//      units of 256 KiB.
 #include "select.h"
 
 #include <stddef.h>
@@ -34,16 +44,30 @@
 namespace la {
 
 constexpr int64_t kMinTilesPerHead = 8;
+constexpr int64_t kShortUnitBytes = 256 * 1024;
 
-int select_kind(const int32_t* ctx_lens, int B, int units, int L, int cus, int coresident,
-                int* kind, int* grid, const char** why) {
-    if (cus < 1 || coresident < 1 || B < 1 || units < 1) {
-        *why = "select: cus, coresident, B and units must be >= 1";
+int select_kind(const int32_t* ctx_lens, int B, int units, int L, int d, bool grouped, int cus,
+                int coresident, int* kind, int* grid, const char** why) {
+    if (cus < 1 || coresident < 1 || B < 1 || units < 1 || d < 1) {
+        *why = "select: cus, coresident, B, units and d must be >= 1";
         return 1;
     }
     const int64_t U = (int64_t)B * units;
     int G = U >= 2 * (int64_t)cus ? 2 * cus : cus;
     if (G > coresident) G = coresident;
+    int32_t n_max = 0;
+    for (int b = 0; b < B; ++b) {
+        if (ctx_lens[b] < 1) {
+            *why = "select: every context length must be >= 1";
+            return 1;
+        }
+        n_max = ctx_lens[b] > n_max ? ctx_lens[b] : n_max;
+    }
+    if (!grouped && U <= cus && (int64_t)n_max * 4 * d <= kShortUnitBytes) {
+        *kind = 2;
+        *grid = G;
+        return 0;
+    }
     int64_t I = 0;
     int Gu = 0, rows = 0;
     const int rc = schedule_dims(ctx_lens, B, units, L, G, &I, &Gu, &rows, why);

@@ -1,7 +1,9 @@
 """The shape-driven kind selection (kind="auto"), host only: its grid rule and
 its per-head decision checked against the oracle's schedule, which must split
-no head exactly when the selection is per-head (xllm-io paper review §4.3: the
-stream-K schedule with whole heads per workgroup is the per-head one)."""
+no head when the selection is per-head for long heads (xllm-io paper review
+§4.3: the stream-K schedule with whole heads per workgroup is the per-head
+one); short single-head units that all run at once (K and V of each within
+256 KiB, no more heads than CUs) go per head whatever the schedule."""
 from __future__ import annotations
 
 import ctypes
@@ -24,6 +26,9 @@ def expected(lens, H, d, cus, cores, Hk=None, Nq=1, L=None):
     L = L or la.la_default_tile(d)
     G = 2 * cus if len(lens) * U >= 2 * cus else cus
     G = min(G, cores)
+    single = H // Hk * Nq == 1
+    if single and len(lens) * U <= cus and max(lens) * 4 * d <= 256 * 1024:
+        return "per_head", G            # short heads, all at once: latency-bound
     s = lean_schedule(lens, U, L, G)
     whole = all(h == l for h, l in zip(s["host_cta"], s["last_cta"]))
     long_heads = s["I"] >= 8 * len(lens) * U
@@ -61,8 +66,16 @@ def test_identities_of_the_pages():
     assert la.la_select_for([1000, 30000, 7, 90000] * 4, 32, 128, 256, 1024) == ("lean", 512)
     # the grid never exceeds the co-resident capacity
     assert la.la_select_for([1000, 30000, 7, 90000] * 4, 32, 128, 256, 384)[1] == 384
-    # explicit tile size: 64 heads of 4 tiles on 256 workgroups = one tile each -> split
-    assert la.la_select_for([512] * 2, 32, 128, 256, 1024, tile_tokens=128) == ("lean", 256)
+    # explicit tile size: 64 heads of 5 tiles on 256 workgroups -> split
+    assert la.la_select_for([600] * 2, 32, 128, 256, 1024, tile_tokens=128) == ("lean", 256)
+    # short heads that all run at once: per head (1024 tokens x 4 x 64 bytes = 256 KiB)
+    assert la.la_select_for([1024], 4, 64, 256, 1024) == ("per_head", 256)
+    assert la.la_select_for([1025], 4, 64, 256, 1024) == ("lean", 256)
+    assert la.la_select_for([512] * 8, 32, 128, 256, 1024) == ("per_head", 256)
+    # ... but not when there are more units than CUs
+    assert la.la_select_for([512] * 9, 32, 128, 256, 1024) == ("lean", 256)
+    # not for grouped heads, whose per-head kernel is slow on short units
+    assert la.la_select_for([512] * 8, 32, 128, 256, 1024, kv_heads=8) == ("lean", 256)
 
 
 def test_validation():
