@@ -404,8 +404,15 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, kind="lean", out
     not given. q is [B, H, d], or [B, Nq, H, d] for Nq new tokens per request;
     k_cache/v_cache are packed [kv_heads * sum(n_b), d], or a cache
     [B, kv_heads, S, d] of S >= max(n_b) rows per head (kv_heads and kv_stride
-    then come from its shape)."""
+    then come from its shape). ctx_lens is a host sequence, or -- with such a
+    cache -- an int32 device tensor that the kernel reads in the launch (lean
+    kind; the call can then be captured into a graph)."""
     import torch
+    dev_lens = isinstance(ctx_lens, torch.Tensor) and ctx_lens.is_cuda
+    if dev_lens:
+        if k_cache.dim() != 4:
+            raise ValueError("lengths on the device need a [B, kv_heads, S, d] cache")
+        opts["ctx_lens_device"] = ctx_lens
     if q.dim() == 4:
         B, Nq, H, d = q.shape
         opts["q_tokens"] = Nq
@@ -431,5 +438,6 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, kind="lean", out
         for t in (k_cache, v_cache):
             if tuple(t.shape) != (Hk * total, d) or t.dtype != q.dtype:
                 raise ValueError("k_cache/v_cache must be [kv_heads * sum(ctx_lens), d] in q's dtype")
-    la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream, kind=kind, **opts)
+    la_decode_ex(q, k_cache, v_cache, None if dev_lens else ctx_lens, B, H, d, scale, out, stream,
+                 kind=kind, **opts)
     return out

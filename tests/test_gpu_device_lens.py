@@ -279,3 +279,19 @@ def test_random_device_lengths(la):
         worst = max(worst, err)
         del inp, kc, vc
     say(f"30 random device-length launches, worst max|dO| = {worst:.2e}")
+
+
+def test_wrapper_takes_device_lengths(la):
+    """decode_attention with an int32 device tensor of lengths and a 4-D cache
+    gives the host-length call's bits; with a packed cache it is refused."""
+    lens = [700, 33, 2049]
+    inp = W.make_custom(lens, 8, 128, "bf16", seed=71, device="cuda", kv_heads=2)
+    S = 2100
+    kc, vc = strided(inp, S)
+    host = la.decode_attention(inp.q, kc, vc, lens)
+    dl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    dev = la.decode_attention(inp.q, kc, vc, dl)
+    la.la_sync_check()
+    np.testing.assert_array_equal(host.cpu().numpy(), dev.cpu().numpy())
+    with pytest.raises(ValueError, match="cache"):
+        la.decode_attention(inp.q, inp.k, inp.v, dl)
