@@ -32,7 +32,8 @@
  *    la_opts. They must be 16-byte aligned. The caller owns them.
  *  - Host pointers: ctx_lens (B entries, each >= 1) and the la_schedule
  *    tables. ctx_lens is read before the call returns, so the caller may reuse
- *    it immediately.
+ *    it immediately. With la_opts.ctx_lens_device the lengths are a device
+ *    array read by the kernel instead, and ctx_lens may be NULL.
  *  - Layouts: q is [B, H, d] (fp16 or bf16). K and V are packed per request:
  *    request b's block is [H, n_b, d] and starts at element
  *    H * d * sum_{b' < b} n_{b'}; for equal lengths this is [B, H, n, d]
@@ -122,7 +123,8 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               the linearised schedule (for checking the schedule the kernel
  *               executed)
  *   cta_timestamps optional device uint64 [blocks*4], blocks = the grid of
- *               the call's first kernel (lean: min(grid, I); fixed split:
+ *               the call's first kernel (lean: min(grid, I), or the grid
+ *               itself with ctx_lens_device; fixed split:
  *               B*H*num_splits, which must then be given; per head: B*H). Per
  *               workgroup: realtime clock (100 MHz) at entry and at exit, then
  *               XCC_ID << 32 | HW_ID of the CU it ran on, then -- kind lean,
