@@ -262,8 +262,11 @@ la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
  *           units (K/V head x block of 16 query columns).
  *   kind  = LA_KIND_PER_HEAD if the lean schedule on that grid splits no
  *           head (every workgroup holds whole heads) and heads average at
- *           least 8 tiles, else LA_KIND_LEAN. LA_KIND_FIXED_SPLIT is never
- *           chosen.
+ *           least 8 tiles; also LA_KIND_PER_HEAD, with one query column per
+ *           K/V head, when every head's K and V fit in 256 KiB
+ *           (max n_b * 4 * d bytes) and B * H <= cus (a latency-bound launch
+ *           that runs every head at once); else LA_KIND_LEAN.
+ *           LA_KIND_FIXED_SPLIT is never chosen.
  * tile_tokens 0 = la_default_tile(d). Returns LA_EINVAL on bad arguments
  * (as la_decode_ex validates kv_heads, q_tokens, d), LA_EUNSUPPORTED if the
  * iteration count does not fit in int32.
@@ -324,9 +327,10 @@ int la_default_grid(int d, int dtype);
 
 /*
  * Synchronises `stream` and reads the device error word of its workspace.
- * LA_ETIMEOUT if a device-side wait exceeded its bound since the last check
- * (the word and the flags are then reset); LA_EHIP if the stream reports an
- * error; LA_OK otherwise.
+ * LA_EINVAL if lengths read on the device (ctx_lens_device) were out of
+ * range, LA_ETIMEOUT if a device-side wait exceeded its bound, since the last
+ * check (the word and the flags are then reset); LA_EHIP if the stream
+ * reports an error; LA_OK otherwise.
  */
 la_status la_sync_check(void* stream);
 
