@@ -295,3 +295,35 @@ def test_wrapper_takes_device_lengths(la):
     np.testing.assert_array_equal(host.cpu().numpy(), dev.cpu().numpy())
     with pytest.raises(ValueError, match="cache"):
         la.decode_attention(inp.q, inp.k, inp.v, dl)
+
+
+def test_graph_captured_with_host_lengths(la):
+    """A lean launch with host lengths within the in-launch limits (prefix sums
+    in the kernel arguments) can be captured too: each replay repeats those
+    lengths and equals the eager call bit for bit, with eager work between
+    replays."""
+    lens = [900, 17, 3000]
+    inp = W.make_custom(lens, 8, 64, "f16", seed=91, device="cuda", kv_heads=2)
+    out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device="cuda")
+    eager = torch.empty_like(out)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        la.la_decode_ex(inp.q, inp.k, inp.v, lens, 3, 8, 64, inp.scale, out, kv_heads=2,
+                        stream=s.cuda_stream)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        la.la_decode_ex(inp.q, inp.k, inp.v, lens, 3, 8, 64, inp.scale, out, kv_heads=2,
+                        stream=s.cuda_stream)
+    la.la_decode_ex(inp.q, inp.k, inp.v, lens, 3, 8, 64, inp.scale, eager, kv_heads=2)
+    la.la_sync_check()
+    ref = eager.cpu().numpy()
+    for i in range(4):
+        out.fill_(float("nan"))                 # eager work between replays
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        la.la_sync_check(s.cuda_stream)
+        np.testing.assert_array_equal(out.cpu().numpy(), ref)
+    del g
