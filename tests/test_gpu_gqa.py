@@ -204,3 +204,62 @@ def test_full_size(la, name):
         say(f"[gqa full {name}] {k} max|dO|={err:.2e}")
     del inp
     torch.cuda.empty_cache()
+
+
+def _inputs(q, K, V, lens, H, Hk, d, dtype):
+    import math
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    return W.Inputs(q=q.to(tdt).cuda().contiguous(), k=K.to(tdt).cuda().contiguous(),
+                    v=V.to(tdt).cuda().contiguous(), ctx_lens=lens, H=H, d=d, dtype=dtype,
+                    scale=1.0 / math.sqrt(d), seed=0, meta={"kv_heads": Hk})
+
+
+@pytest.mark.parametrize("kind,opts", [("lean", {}), ("lean", {"grid": 64}), ("lean", {"grid": 5}),
+                                       ("fixed_split", {"num_splits": 7}), ("per_head", {}),
+                                       ("pull", {"grid": 9})])
+@pytest.mark.parametrize("H,Hk,d", [(4, 1, 128), (8, 4, 128), (16, 1, 64)])
+def test_closed_forms(la, kind, opts, H, Hk, d):
+    """Results the definition fixes exactly, on the grouped kernels with heads
+    split over many workgroups: constant V gives that constant; a one-token
+    request gives its V row and l = 1 for every query head of the group; q = 0
+    gives m = 0, l = n and the mean of V; one dominant logit of one query head
+    gives that V row for that head only."""
+    import math
+    g = torch.Generator().manual_seed(3)
+    lens = [1, 5000]
+    N = sum(lens)
+    q = torch.randn((2, H, d), generator=g)
+    K = torch.randn((Hk * N, d), generator=g)
+    c = torch.randn(d, generator=g).to(torch.bfloat16).float()
+    say(f"[closed forms] {kind} {opts} H={H} Hk={Hk} d={d}")
+    inp = _inputs(q, K, c.expand(Hk * N, d), lens, H, Hk, d, "bf16")
+    O, m, l = run(la, inp, kind, **opts)
+    assert np.max(np.abs(O - c.numpy())) <= 1e-4
+    V = torch.randn((Hk * N, d), generator=g)
+    inp = _inputs(q, K, V, lens, H, Hk, d, "bf16")
+    O, m, l = run(la, inp, kind, **opts)
+    grp = H // Hk
+    v = inp.v.float().cpu().numpy()
+    for h in range(H):
+        assert np.max(np.abs(O[0, h] - v[h // grp])) <= 1e-6 and l[0, h] == 1.0
+    inp = _inputs(torch.zeros_like(q), K, V, lens, H, Hk, d, "bf16")
+    O, m, l = run(la, inp, kind, **opts)
+    v = inp.v.float().cpu().numpy()
+    for h in range(H):
+        kv = h // grp
+        rows = v[Hk * 1 + kv * 5000:Hk * 1 + (kv + 1) * 5000]
+        assert np.max(np.abs(O[1, h] - rows.mean(axis=0))) <= 1e-4
+        assert abs(l[1, h] - 5000) <= 5000 * 1e-5
+    assert np.all(m == 0.0)
+    Kd = K.clone()
+    h0, j = H - 1, 4321
+    kv0 = h0 // grp
+    qn = q[1, h0].norm()
+    row = Hk * 1 + kv0 * 5000 + j
+    Kd[row] = (100.0 * math.sqrt(d) / qn) * (q[1, h0] / qn)     # s_j = 100 for head h0
+    inp = _inputs(q, Kd, V, lens, H, Hk, d, "bf16")
+    O, m, l = run(la, inp, kind, **opts)
+    assert np.max(np.abs(O[1, h0] - inp.v[row].float().cpu().numpy())) <= 1e-4
+    assert 1.0 <= float(l[1, h0]) <= 1.0 + 1e-4
+    ref = reference(inp)
+    check((O, m, l), ref, tag=f"dominant/{kind}")
