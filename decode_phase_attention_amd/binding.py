@@ -9,6 +9,7 @@ HIP runtime (torch's), which the library then shares.
 """
 from __future__ import annotations
 
+import array
 import ctypes
 import math
 import os
@@ -148,16 +149,30 @@ def _ptr(x) -> int | None:
 _I32_MIN, _I32_MAX = -(1 << 31), (1 << 31) - 1
 
 
+if array.array("i").itemsize != 4:      # the fast path below hands the buffer over as int32
+    raise ImportError("array typecode 'i' is not 32-bit on this platform")
+
+
 def _lens(ctx_lens):
-    if isinstance(ctx_lens, (list, tuple)):
-        # the common case, a list of integers: no numpy round trip
-        if ctx_lens and (min(ctx_lens) < _I32_MIN or max(ctx_lens) > _I32_MAX):
-            raise ValueError("ctx_lens entries must fit in int32")
+    """ctx_lens as a contiguous int32 array: (owner, pointer). The owner keeps
+    the memory alive and supports len() and sum()."""
+    if isinstance(ctx_lens, array.array) and ctx_lens.typecode == "i":
+        a = ctx_lens
+    elif isinstance(ctx_lens, (list, tuple)):
+        # the common case, a list of integers: array.array converts and range-
+        # checks in C (several times faster than a ctypes constructor)
         try:
-            arr = (ctypes.c_int32 * len(ctx_lens))(*ctx_lens)
-            return arr, ctypes.cast(arr, _I32P)
+            a = array.array("i", ctx_lens)
+        except OverflowError:
+            raise ValueError("ctx_lens entries must fit in int32") from None
         except TypeError:
-            pass                  # not integers: let numpy convert (or reject) them
+            a = None              # not integers: let numpy convert (or reject) them
+    else:
+        a = None
+    if a is not None:
+        if len(a) == 0:
+            return a, None
+        return a, ctypes.cast(a.buffer_info()[0], _I32P)
     arr = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int64))
     if arr.ndim != 1:
         raise ValueError("ctx_lens must be one-dimensional")
@@ -179,23 +194,32 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+_torch_mod = None
+
+
+def _torch():
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+        _torch_mod = torch
+    return _torch_mod
+
+
 def _check_sizes(q, k_cache, v_cache, out, ctx_lens, B, H, d, kv_heads=0, q_tokens=0,
                  m_out=None, l_out=None, kv_stride=0):
     """For torch tensors, reject a call that would read or write past them (the
     library sees only pointers and cannot check)."""
-    import torch
-    if not any(isinstance(t, torch.Tensor) for t in (q, k_cache, v_cache, out)):
-        return
+    Tensor = _torch().Tensor
     rows = int(B) * int(q_tokens or 1) * int(H)
     Hk = int(kv_heads or H)
     if kv_stride:
         kv = int(B) * Hk * int(kv_stride) * int(d)
     else:
-        kv = Hk * int(sum(int(n) for n in ctx_lens)) * int(d)
+        kv = Hk * int(sum(ctx_lens)) * int(d)
     for name, t, need, size in (("q", q, rows * int(d), 2), ("k_cache", k_cache, kv, 2),
                                 ("v_cache", v_cache, kv, 2), ("out", out, rows * int(d), 4),
                                 ("m_out", m_out, rows, 4), ("l_out", l_out, rows, 4)):
-        if isinstance(t, torch.Tensor):
+        if t is not None and isinstance(t, Tensor):
             if t.element_size() != size:
                 raise ValueError(f"{name}: {size}-byte elements expected, got {t.dtype}")
             if t.numel() < need:

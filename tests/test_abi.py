@@ -10,6 +10,7 @@ import os
 import random
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -271,3 +272,18 @@ def test_device_lengths_validation():
     with pytest.raises(ValueError, match="int32"):
         la.la_decode_ex(q, kv, kv, None, 2, 4, 64, 0.125, out, kv_stride=64,
                         ctx_lens_device=torch.zeros(2, dtype=torch.int64))
+
+
+def test_length_marshalling():
+    """Host lengths reach the library as int32 values, whatever the Python
+    container, and values outside int32 are refused rather than wrapped."""
+    import array
+    b = la.binding
+    for src in ([5, 7, 2**31 - 1], (5, 7, 2**31 - 1), array.array("i", [5, 7, 2**31 - 1]),
+                np.array([5, 7, 2**31 - 1], dtype=np.int64)):
+        owner, p = b._lens(src)
+        assert len(owner) == 3 and sum(owner) == 12 + 2**31 - 1
+        assert [p[i] for i in range(3)] == [5, 7, 2**31 - 1], type(src)
+    for bad in ([2**31], [-2**31 - 1], np.array([2**40])):
+        with pytest.raises(ValueError, match="int32"):
+            b._lens(bad)
