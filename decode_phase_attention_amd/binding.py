@@ -215,7 +215,9 @@ def _check_sizes(q, k_cache, v_cache, out, ctx_lens, B, H, d, kv_heads=0, q_toke
     if kv_stride:
         kv = int(B) * Hk * int(kv_stride) * int(d)
     else:
-        kv = Hk * int(sum(ctx_lens)) * int(d)
+        total = (int(ctx_lens.sum(dtype=np.int64)) if isinstance(ctx_lens, np.ndarray)
+                 else sum(ctx_lens))
+        kv = Hk * total * int(d)
     for name, t, need, size in (("q", q, rows * int(d), 2), ("k_cache", k_cache, kv, 2),
                                 ("v_cache", v_cache, kv, 2), ("out", out, rows * int(d), 4),
                                 ("m_out", m_out, rows, 4), ("l_out", l_out, rows, 4)):

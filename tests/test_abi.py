@@ -276,14 +276,22 @@ def test_device_lengths_validation():
 
 def test_length_marshalling():
     """Host lengths reach the library as int32 values, whatever the Python
-    container, and values outside int32 are refused rather than wrapped."""
+    container, and values outside int32 are refused rather than wrapped; the
+    binding's size check sums them without wrapping."""
     import array
     b = la.binding
     for src in ([5, 7, 2**31 - 1], (5, 7, 2**31 - 1), array.array("i", [5, 7, 2**31 - 1]),
                 np.array([5, 7, 2**31 - 1], dtype=np.int64)):
         owner, p = b._lens(src)
-        assert len(owner) == 3 and sum(owner) == 12 + 2**31 - 1
+        assert [int(x) for x in owner] == [5, 7, 2**31 - 1]
         assert [p[i] for i in range(3)] == [5, 7, 2**31 - 1], type(src)
     for bad in ([2**31], [-2**31 - 1], np.array([2**40])):
         with pytest.raises(ValueError, match="int32"):
             b._lens(bad)
+    import torch
+    q = torch.zeros(2, 1, 64, dtype=torch.float16)
+    out = torch.zeros(2, 1, 64)
+    kv = torch.zeros(64, 64, dtype=torch.float16)
+    owner, _ = b._lens(np.array([2**30, 2**30], dtype=np.int64))   # total 2^31: past int32
+    with pytest.raises(ValueError, match="k_cache"):
+        b._check_sizes(q, kv, kv, out, owner, 2, 1, 64)
