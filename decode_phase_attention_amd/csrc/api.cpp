@@ -376,8 +376,10 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     // Where the workgroups find their segments. Up to kInlineB requests: the
     // prefix sums of tiles and tokens travel in the kernel arguments and each
     // workgroup derives its own segments (nothing is copied on the stream,
-    // which matters when the lengths change every decode step). Otherwise,
-    // or on request, the host builds the tables and uploads them.
+    // which matters when the lengths change every decode step). Up to
+    // kMaxDeviceB: only the lengths are copied and the launch derives the
+    // same segments from them. Beyond that, or on request, the host builds
+    // the tables and uploads them.
     la::SchedArgs sa{};
     sa.B = B;
     sa.U = U;
@@ -400,6 +402,17 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         }
         sa.tp[B] = tp;
         sa.tok[B] = tk;
+    } else if (o.host_tables == 0 && B <= la::kMaxDeviceB) {
+        // More requests than the kernel arguments hold: copy the B lengths
+        // (4 B each) and let the launch derive the partition from them, as
+        // with lengths kept on the device; G is the host's min(grid, I), so
+        // the partition is the tables' one.
+        if ((st = upload(w, (const char*)ctx_lens, sizeof(int32_t) * (size_t)B)) != LA_OK) return st;
+        sa.src = la::kSrcDevice;
+        sa.dlens = (const int32_t*)w.tables;
+        sa.L = L;
+        sa.n_min = 1;
+        sa.n_max = o.kv_stride > 0 ? o.kv_stride : INT32_MAX;
     } else {
         const int BU = B * U;
         const size_t off_seg = 0;

@@ -166,8 +166,10 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               to 256 requests and 2^32-1 tokens in all, the per-request
  *               prefix sums of tiles and tokens travel in the kernel
  *               arguments and every workgroup derives its own segments with
- *               the same rules (no copy on the stream), else as 1. Both give
- *               the same tile-to-workgroup map and the same output bits.
+ *               the same rules (no copy on the stream); with up to 1024
+ *               requests only the lengths are copied and the launch derives
+ *               the segments from them; else as 1. All give the same
+ *               tile-to-workgroup map and the same output bits.
  *   kv_stride   K/V cache layout: 0 = packed per request (request b's block
  *               [Hk, n_b, d] at row Hk * sum_{b' < b} n_b'); > 0 = a cache of
  *               kv_stride rows per head, [B, Hk, kv_stride, d] (head h of

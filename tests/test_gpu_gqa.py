@@ -263,3 +263,30 @@ def test_closed_forms(la, kind, opts, H, Hk, d):
     assert 1.0 <= float(l[1, h0]) <= 1.0 + 1e-4
     ref = reference(inp)
     check((O, m, l), ref, tag=f"dominant/{kind}")
+
+
+@pytest.mark.parametrize("B", [300, 1024, 1025])
+def test_copied_lengths_and_tables_agree(la, B):
+    """Grouped heads with more requests than the kernel arguments hold: up to
+    1024 the launch derives the partition from lengths copied to the device,
+    above that from the host's tables. The tile map is the oracle's and
+    forcing the tables gives the same bits."""
+    rng = np.random.default_rng(B + 7)
+    lens = [int(x) for x in rng.integers(1, 400, size=B)]
+    H, Hk, d = 8, 2, 64
+    inp = W.make_custom(lens, H=H, d=d, dtype="f16", seed=B, device="cuda", kv_heads=Hk)
+    L = la.la_default_tile(d)
+    for grid in (0, 61):
+        G_req = grid if grid else la.la_default_grid(d, la.LA_F16)
+        s = oracle.lean_schedule(lens, Hk, L, G_req)
+        own = np.empty(s["I"], np.int32)
+        for (c, u, t0, t1, _h, _f) in s["seg"]:
+            own[s["S"][u] + t0:s["S"][u] + t1] = c
+        say(f"[copied lengths B={B} grid={grid}]")
+        owner = torch.full((own.size,), -1, dtype=torch.int32, device="cuda")
+        a = run(la, inp, "lean", grid=grid, tile_owner=owner)
+        assert np.array_equal(owner.cpu().numpy(), own)
+        b = run(la, inp, "lean", grid=grid, host_tables=True)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+    check(a, reference(inp), tag=f"B={B}")

@@ -300,12 +300,13 @@ def test_many_small_requests(la, kind):
     check(run(la, inp, kind), reference(inp), tag=f"many-small/{kind}")
 
 
-@pytest.mark.parametrize("B", [255, 256, 257, 600])
+@pytest.mark.parametrize("B", [255, 256, 257, 600, 1024, 1025])
 def test_schedule_source_across_the_inline_limit(la, B):
-    """Up to 256 requests the workgroups derive their segments from the
-    lengths in the kernel arguments, above that they read the host's tables:
-    on both sides of the limit the tile map is the oracle's, and forcing the
-    tables gives the same bits."""
+    """Up to 256 requests the workgroups derive their segments from prefix
+    sums in the kernel arguments, up to 1024 from the lengths copied to the
+    device, above that they read the host's tables: on every side of both
+    limits the tile map is the oracle's, and forcing the tables gives the
+    same bits."""
     rng = np.random.default_rng(B)
     lens = [int(x) for x in rng.integers(1, 700, size=B)]
     H, d = 2, 64
