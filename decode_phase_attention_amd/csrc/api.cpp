@@ -738,6 +738,9 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     la_opts_init(&o);
     if (opts != nullptr) o = *opts;
     const bool dev_lens = o.ctx_lens_device != nullptr;
+    // lengths on the device are known only in the launch: auto means lean,
+    // the one kind that reads them there
+    if (dev_lens && o.kind == LA_KIND_AUTO) o.kind = LA_KIND_LEAN;
     la_status st = validate(q, k, v, ctx_lens, !dev_lens, B, H, d, scale, out, o.dtype);
     if (st != LA_OK) return st;
     if (o.kind != LA_KIND_LEAN && o.kind != LA_KIND_FIXED_SPLIT && o.kind != LA_KIND_PER_HEAD &&

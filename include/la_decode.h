@@ -181,7 +181,8 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               (ctx_lens may then be NULL and is ignored). Nothing about the
  *               lengths passes through the host, so a launch captured into a
  *               HIP graph stays valid while a decode loop grows them on the
- *               device. Lean kind only, on a kv_stride cache (whose size
+ *               device. Lean kind only (LA_KIND_AUTO means lean here), on a
+ *               kv_stride cache (whose size
  *               bounds every read), up to 1024 requests, no tile_owner; the
  *               grid is `grid` (or the default) and workgroups beyond the tile
  *               iterations stay idle. Lengths outside [max(1, q_tokens),

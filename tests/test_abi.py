@@ -250,7 +250,7 @@ def test_device_lengths_validation():
 
     st, msg = call(kv_stride=0)
     assert st == 1 and "kv_stride" in msg
-    for kind in (la.LA_KIND_FIXED_SPLIT, la.LA_KIND_PER_HEAD, la.LA_KIND_PULL, la.LA_KIND_AUTO,
+    for kind in (la.LA_KIND_FIXED_SPLIT, la.LA_KIND_PER_HEAD, la.LA_KIND_PULL,
                  la.LA_KIND_CHUNKS):
         st, msg = call(kind=kind)
         assert st == 1 and "lean" in msg, kind

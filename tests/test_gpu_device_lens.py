@@ -291,8 +291,10 @@ def test_wrapper_takes_device_lengths(la):
     host = la.decode_attention(inp.q, kc, vc, lens)
     dl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     dev = la.decode_attention(inp.q, kc, vc, dl)
+    auto = la.decode_attention(inp.q, kc, vc, dl, kind="auto")   # lean: the one kind that reads them
     la.la_sync_check()
     np.testing.assert_array_equal(host.cpu().numpy(), dev.cpu().numpy())
+    np.testing.assert_array_equal(dev.cpu().numpy(), auto.cpu().numpy())
     with pytest.raises(ValueError, match="cache"):
         la.decode_attention(inp.q, inp.k, inp.v, dl)
 
