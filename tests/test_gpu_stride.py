@@ -125,7 +125,9 @@ def test_wrapper_takes_a_4d_cache(la):
 def test_full_size_strided(la, name):
     """Full-size workloads in a [B, Hk, S, d] cache with S = the longest
     context (gqa8-ragged: heads up to 5.9 GB into the cache, past 32-bit
-    offsets), lean and pull, on sampled heads against the oracle."""
+    offsets), lean and pull, and lean with the lengths read on the device
+    (the same bits as with host lengths), on sampled heads against the
+    oracle."""
     inp = W.make_inputs(name, seed=0, device="cuda")
     S = max(inp.ctx_lens)
     say(f"[stride full {name}] S={S}")
@@ -137,13 +139,21 @@ def test_full_size_strided(la, name):
                              inp.scale, inp.dtype, heads=heads, workers=16, kv_heads=inp.Hk)[0]
     del inp.k, inp.v
     idx = tuple(np.array(heads).T)
-    for kind in ("lean", "pull"):
+    outs = {}
+    dl = torch.tensor(inp.ctx_lens, dtype=torch.int32, device="cuda")
+    for kind in ("lean", "pull", "device"):
         out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda")
-        la.la_decode_ex(inp.q, kc, vc, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
-                        kind=kind, kv_heads=inp.Hk, kv_stride=S)
+        if kind == "device":
+            la.la_decode_ex(inp.q, kc, vc, None, inp.B, inp.H, inp.d, inp.scale, out,
+                            kv_heads=inp.Hk, kv_stride=S, ctx_lens_device=dl)
+        else:
+            la.la_decode_ex(inp.q, kc, vc, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
+                            kind=kind, kv_heads=inp.Hk, kv_stride=S)
         la.la_sync_check()
-        err = float(np.max(np.abs(out.cpu().numpy()[idx] - ref[idx])))
+        outs[kind] = out.cpu().numpy()
+        err = float(np.max(np.abs(outs[kind][idx] - ref[idx])))
         say(f"[stride full {name}] {kind} max|dO|={err:.2e}")
         assert err <= 1e-3
+    np.testing.assert_array_equal(outs["lean"], outs["device"])
     del kc, vc, inp
     torch.cuda.empty_cache()
