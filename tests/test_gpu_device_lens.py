@@ -64,7 +64,8 @@ CASES = [([3000, 17, 60000, 129], 4, 4, 1, 128, "bf16"),
          ([515, 4, 1030], 8, 2, 3, 128, "bf16"),
          ([int(x) for x in np.random.default_rng(3).integers(1, 400, 256)], 2, 2, 1, 64, "f16"),
          ([int(x) for x in np.random.default_rng(4).integers(1, 300, 600)], 4, 4, 1, 128, "bf16"),
-         ([int(x) for x in np.random.default_rng(5).integers(2, 300, 1024)], 2, 1, 2, 64, "f16")]
+         ([int(x) for x in np.random.default_rng(5).integers(2, 300, 1024)], 2, 1, 2, 64, "f16"),
+         ([300, 64, 1000], 2, 1, 64, 64, "f16")]      # 64 new tokens: 8 column blocks per K/V head
 
 
 @pytest.mark.parametrize("lens,H,Hk,Nq,d,dtype", CASES)
