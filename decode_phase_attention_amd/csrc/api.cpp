@@ -57,9 +57,9 @@ struct Workspace {
     hipStream_t stream = nullptr;
     float* part = nullptr;          // lean partial records
     size_t part_cap = 0;            // bytes
-    uint32_t* flags = nullptr;      // one per lean workgroup, zero between launches
+    uint32_t* flags = nullptr;      // one per lean workgroup (epochs; zero-filled when allocated)
     size_t flags_cap = 0;
-    uint32_t* err = nullptr;        // device error word
+    uint32_t* ctl = nullptr;        // lean control block: error word, epoch, exit count, abort
     float* split_part = nullptr;    // fixed-split partial records
     size_t split_cap = 0;
     float* pull_part = nullptr;     // dynamic-pull partial records, two per chunk
@@ -78,7 +78,6 @@ struct Workspace {
     bool capturing = false;         // the current call is being captured: nothing may be allocated
     bool captured = false;          // a graph may hold the buffers: growing keeps the old ones
     std::vector<void*> retired;     // buffers replaced after a capture, freed at shutdown
-    std::vector<std::pair<void*, size_t>> retired_zeroed;   // the same for zero-between-launch buffers
 };
 
 std::mutex g_mu;
@@ -114,11 +113,7 @@ la_status grow(Workspace& w, void** p, size_t* cap, size_t need_bytes, bool zero
                                      "stream before capturing");
     if (*p != nullptr) {
         if (w.captured) {
-            // a captured graph's replays may still use it
-            if (zero)
-                w.retired_zeroed.emplace_back(*p, *cap);
-            else
-                w.retired.push_back(*p);
+            w.retired.push_back(*p);   // a captured graph's replays may still use it
         } else {
             HIP_TRY(hipStreamSynchronize(w.stream));
             HIP_TRY(hipFree(*p));
@@ -149,7 +144,7 @@ la_status get_workspace(hipStream_t stream, Workspace** out) {
     w->device = dev;
     w->stream = stream;
     size_t cap = 0;
-    la_status st = grow(*w, (void**)&w->err, &cap, 256, true);
+    la_status st = grow(*w, (void**)&w->ctl, &cap, sizeof(uint32_t) * la::kCtlWords, true);
     if (st != LA_OK) {
         delete w;
         return st;
@@ -341,9 +336,23 @@ bool in_launch_schedule(const int32_t* ctx_lens, int B, const la_opts& o) {
     return total <= (int64_t)UINT32_MAX;
 }
 
-la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
-                   const int32_t* ctx_lens, int B, const Heads& hd, int d, float scale,
-                   float* out, const la_opts& o) {
+// The buffers of a lean exchange: a stream's workspace, or a device's fixed
+// scratch array (allocation-free entry point).
+struct Exchange {
+    float* part;
+    size_t part_bytes;
+    uint32_t* flags;
+    uint32_t* ctl;
+    int max_grid;     // workgroups the flags hold
+};
+
+// A lean call. With `fixed` the exchange is that fixed scratch and nothing is
+// allocated or copied: the schedule must be derived in the launch, and the
+// grid and records must fit the scratch. Otherwise `w` is the stream's
+// workspace, grown as needed.
+la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, const void* q,
+                   const void* k, const void* v, const int32_t* ctx_lens, int B, const Heads& hd,
+                   int d, float scale, float* out, const la_opts& o) {
     Capacity cap;
     la_status st = capacity(o.dtype, d, hd.grouped, &cap);
     if (st != LA_OK) return st;
@@ -367,11 +376,23 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     }
 
     const size_t records = (size_t)G * (hd.grouped ? 16 : 1);
-    if ((st = grow(w, (void**)&w.part, &w.part_cap, sizeof(float) * records * la::part_stride(d),
-                   false)) != LA_OK)
-        return st;
-    if ((st = grow(w, (void**)&w.flags, &w.flags_cap, sizeof(uint32_t) * (size_t)G, true)) != LA_OK)
-        return st;
+    const size_t rec_bytes = sizeof(float) * records * la::part_stride(d);
+    Exchange x;
+    if (fixed != nullptr) {
+        if (G > fixed->max_grid)
+            return fail(LA_EUNSUPPORTED, "grid %d exceeds the %d workgroups of the "
+                        "allocation-free scratch", G, fixed->max_grid);
+        if (rec_bytes > fixed->part_bytes)
+            return fail(LA_EUNSUPPORTED, "%zu bytes of partial records (grid %d) exceed the "
+                        "%zu bytes of the allocation-free scratch", rec_bytes, G, fixed->part_bytes);
+        x = *fixed;
+    } else {
+        if ((st = grow(*w, (void**)&w->part, &w->part_cap, rec_bytes, false)) != LA_OK) return st;
+        if ((st = grow(*w, (void**)&w->flags, &w->flags_cap, sizeof(uint32_t) * (size_t)G, true)) !=
+            LA_OK)
+            return st;
+        x = {w->part, w->part_cap, w->flags, w->ctl, (int)(w->flags_cap / sizeof(uint32_t))};
+    }
 
     // Where the workgroups find their segments. Up to kInlineB requests: the
     // prefix sums of tiles and tokens travel in the kernel arguments and each
@@ -402,14 +423,18 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         }
         sa.tp[B] = tp;
         sa.tok[B] = tk;
+    } else if (fixed != nullptr) {
+        return fail(LA_EUNSUPPORTED, "the allocation-free entry point derives the schedule in "
+                    "the launch: up to %d host-side requests and 2^32 - 1 tokens in all, no "
+                    "host_tables, or lengths on the device (ctx_lens_device)", la::kInlineB);
     } else if (o.host_tables == 0 && B <= la::kMaxDeviceB) {
         // More requests than the kernel arguments hold: copy the B lengths
         // (4 B each) and let the launch derive the partition from them, as
         // with lengths kept on the device; G is the host's min(grid, I), so
         // the partition is the tables' one.
-        if ((st = upload(w, (const char*)ctx_lens, sizeof(int32_t) * (size_t)B)) != LA_OK) return st;
+        if ((st = upload(*w, (const char*)ctx_lens, sizeof(int32_t) * (size_t)B)) != LA_OK) return st;
         sa.src = la::kSrcDevice;
-        sa.dlens = (const int32_t*)w.tables;
+        sa.dlens = (const int32_t*)w->tables;
         sa.L = L;
         sa.n_min = 1;
         sa.n_max = o.kv_stride > 0 ? o.kv_stride : INT32_MAX;
@@ -427,8 +452,8 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
                            (int32_t*)(hb + off_cta_seg), nullptr, (int32_t*)(hb + off_seg),
                            (int32_t*)(hb + off_host), (int32_t*)(hb + off_last));
         fill_req(hb, rl, ctx_lens, B);
-        if ((st = upload(w, hb, rl.bytes)) != LA_OK) return st;
-        const char* db = (const char*)w.tables;
+        if ((st = upload(*w, hb, rl.bytes)) != LA_OK) return st;
+        const char* db = (const char*)w->tables;
         sa.src = la::kSrcTables;
         sa.seg = (const int4*)(db + off_seg);
         sa.cta_seg = (const int32_t*)(db + off_cta_seg);
@@ -443,13 +468,13 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
         la::GqaArgs a{};
         fill_gqa(a, q, k, v, out, o, hd, L, scale);
         a.sched = sa;
-        a.part = w.part;
-        a.part_bytes = w.part_cap > (size_t)INT32_MAX ? (uint32_t)INT32_MAX : (uint32_t)w.part_cap;
-        a.flags = w.flags;
-        a.err = w.err;
-        if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
-        HIP_TRY(la::launch_lean_gqa(o.dtype, d, a, G, w.stream, coop));
-        if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+        a.part = x.part;
+        a.part_bytes = x.part_bytes > (size_t)INT32_MAX ? (uint32_t)INT32_MAX : (uint32_t)x.part_bytes;
+        a.flags = x.flags;
+        a.ctl = x.ctl;
+        if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
+        HIP_TRY(la::launch_lean_gqa(o.dtype, d, a, G, stream, coop));
+        if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));
         return LA_OK;
     }
     la::LeanArgs a{};
@@ -460,9 +485,9 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     a.m_out = o.m_out;
     a.l_out = o.l_out;
     a.sched = sa;
-    a.part = w.part;
-    a.flags = w.flags;
-    a.err = w.err;
+    a.part = x.part;
+    a.flags = x.flags;
+    a.ctl = x.ctl;
     a.tile_owner = o.tile_owner;
     a.ts = o.cta_timestamps;
     a.H = hd.H;
@@ -470,9 +495,9 @@ la_status run_lean(Workspace& w, const void* q, const void* k, const void* v,
     a.kv_stride = o.kv_stride;
     a.sl2e = scale * 1.4426950408889634f;
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
-    if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
-    HIP_TRY(la::launch_lean(o.dtype, d, a, G, w.stream, coop));
-    if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));
+    if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
+    HIP_TRY(la::launch_lean(o.dtype, d, a, G, stream, coop));
+    if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));
     return LA_OK;
 }
 
@@ -709,12 +734,11 @@ la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int 
 void free_workspace(Workspace* w) {
     (void)hipSetDevice(w->device);
     (void)hipDeviceSynchronize();
-    for (void* p : {(void*)w->part, (void*)w->flags, (void*)w->err, (void*)w->split_part,
+    for (void* p : {(void*)w->part, (void*)w->flags, (void*)w->ctl, (void*)w->split_part,
                     (void*)w->pull_part, (void*)w->arrive, (void*)w->pull_ctr, (void*)w->gcount,
                     w->tables})
         if (p != nullptr) (void)hipFree(p);
     for (void* p : w->retired) (void)hipFree(p);
-    for (auto& r : w->retired_zeroed) (void)hipFree(r.first);
     for (auto& s : w->ring) {
         if (s.host != nullptr) (void)hipHostFree(s.host);
         if (s.ev != nullptr) (void)hipEventDestroy(s.ev);
@@ -722,21 +746,11 @@ void free_workspace(Workspace* w) {
     delete w;
 }
 
-}  // namespace
-
-extern "C" {
-
-void la_opts_init(la_opts* o) {
-    if (o != nullptr) memset(o, 0, sizeof(*o));
-}
-
-la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_t* ctx_lens,
-                       int B, int H, int d, float scale, float* out, void* stream,
-                       const la_opts* opts) {
-    g_msg[0] = 0;
-    la_opts o;
-    la_opts_init(&o);
-    if (opts != nullptr) o = *opts;
+// Argument checks of la_decode_ex. `o` holds
+// the caller's options (kind auto already mapped to lean with device
+// lengths); `hd` receives the query columns of the call.
+la_status prepare(const void* q, const void* k, const void* v, const int32_t* ctx_lens, int B,
+                  int H, int d, float scale, const float* out, la_opts& o, Heads& hd) {
     const bool dev_lens = o.ctx_lens_device != nullptr;
     // lengths on the device are known only in the launch: auto means lean,
     // the one kind that reads them there
@@ -794,8 +808,30 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
         if (ctx_lens[b] < o.q_tokens)
             return fail(LA_EINVAL, "ctx_lens[%d] = %d is shorter than the %d new tokens it must hold",
                         b, ctx_lens[b], o.q_tokens);
-    const Heads hd = heads_of(H, o.kv_heads, o.q_tokens);
+    hd = heads_of(H, o.kv_heads, o.q_tokens);
     if ((int64_t)B * hd.units_per_req() > INT32_MAX / 32) return fail(LA_EUNSUPPORTED, "too many heads");
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void la_opts_init(la_opts* o) {
+    if (o != nullptr) memset(o, 0, sizeof(*o));
+}
+
+la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_t* ctx_lens,
+                       int B, int H, int d, float scale, float* out, void* stream,
+                       const la_opts* opts) {
+    g_msg[0] = 0;
+    la_opts o;
+    la_opts_init(&o);
+    if (opts != nullptr) o = *opts;
+    Heads hd;
+    la_status st = prepare(q, k, v, ctx_lens, B, H, d, scale, out, o, hd);
+    if (st != LA_OK) return st;
+    const bool dev_lens = o.ctx_lens_device != nullptr;
     std::lock_guard<std::mutex> lock(g_mu);
     // Stream capture: only a lean launch whose schedule needs nothing copied
     // (lengths on the device, or prefix sums in the kernel arguments), into a
@@ -828,7 +864,7 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     if ((st = get_workspace((hipStream_t)stream, &w)) != LA_OK) return st;
     if (o.kind == LA_KIND_LEAN) {
         w->capturing = capturing;
-        st = run_lean(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
+        st = run_lean(w, nullptr, w->stream, q, k, v, ctx_lens, B, hd, d, scale, out, o);
         w->capturing = false;
         if (capturing && st == LA_OK) w->captured = true;
         return st;
@@ -971,17 +1007,22 @@ la_status la_sync_check(void* stream) {
     HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
+    uint32_t* words[1] = {nullptr};
     auto it = g_ws.find(std::make_pair(dev, (hipStream_t)stream));
-    if (it == g_ws.end()) return LA_OK;
-    Workspace& w = *it->second;
+    if (it != g_ws.end()) words[0] = it->second->ctl + la::kCtlErr;
     uint32_t err = 0;
-    HIP_TRY(hipMemcpy(&err, w.err, sizeof(err), hipMemcpyDeviceToHost));
+    for (uint32_t* word : words) {
+        if (word == nullptr) continue;
+        uint32_t e = 0;
+        HIP_TRY(hipMemcpy(&e, word, sizeof(e), hipMemcpyDeviceToHost));
+        if (e == 0) continue;
+        // only the sticky report is cleared: a wait that gave up affected its
+        // own launch alone (flags carry epochs), so nothing else needs resetting
+        HIP_TRY(hipMemsetAsync(word, 0, sizeof(uint32_t), (hipStream_t)stream));
+        err |= e;
+    }
     if (err == 0) return LA_OK;
-    HIP_TRY(hipMemsetAsync(w.err, 0, sizeof(uint32_t), w.stream));
-    if (w.flags != nullptr) HIP_TRY(hipMemsetAsync(w.flags, 0, w.flags_cap, w.stream));
-    // flags that graphs captured before a workspace growth still use
-    for (auto& r : w.retired_zeroed) HIP_TRY(hipMemsetAsync(r.first, 0, r.second, w.stream));
-    HIP_TRY(hipStreamSynchronize(w.stream));
+    HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
     if (err & la::kErrLengths)
         return fail(LA_EINVAL, "context lengths read on the device were outside "
                                "[max(1, q_tokens), kv_stride], or their tiles overflowed "

@@ -96,16 +96,39 @@ __device__ __forceinline__ int64_t head_row0(int stride, int Hx, int b, int h, i
     return stride > 0 ? ((int64_t)b * Hx + h) * stride : (int64_t)Hx * tok_off + (int64_t)h * n;
 }
 
-// Wait until a peer's flag is raised. Gives up after `limit` ticks of the
-// 100 MHz realtime clock, or at once when any wait has already given up, and
-// raises the error word: a missing peer cannot hang the launch.
-__device__ __forceinline__ void wait_flag(uint32_t* f, uint64_t limit, uint32_t* err) {
-    if (load_flag(f) != 0u) return;
+// Epoch of this launch on a lean exchange: one more than the last completed
+// launch's, never 0 (zero-filled flags never match).
+__device__ __forceinline__ uint32_t launch_epoch(uint32_t* ctl) {
+    const uint32_t e = __builtin_amdgcn_readfirstlane(load_flag(&ctl[kCtlEpoch])) + 1u;
+    return e == 0u ? 1u : e;
+}
+
+// One thread per workgroup, after its last access to the exchange: the last
+// workgroup out resets the exit count and makes this launch's epoch the
+// completed one, which the next launch starts from.
+__device__ __forceinline__ void launch_exit(uint32_t* ctl, uint32_t epoch) {
+    const uint32_t n = __hip_atomic_fetch_add(&ctl[kCtlExit], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (n == gridDim.x - 1) {
+        __hip_atomic_store(&ctl[kCtlExit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctl[kCtlEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Wait until a peer's flag holds this launch's epoch. Gives up after `limit`
+// ticks of the 100 MHz realtime clock, or at once when a wait of the same
+// launch has given up; then it raises the sticky error bit and marks the
+// launch aborted. A missing peer cannot hang the launch, and a give-up does
+// not reach later launches.
+__device__ __forceinline__ void wait_flag(uint32_t* f, uint32_t epoch, uint64_t limit,
+                                          uint32_t* ctl) {
+    if (load_flag(f) == epoch) return;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (load_flag(f) == 0u) {
+    while (load_flag(f) != epoch) {
         __builtin_amdgcn_s_sleep(2);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > limit || load_flag(err) != 0u) {
-            atomicOr(err, kErrTimeout);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > limit || load_flag(&ctl[kCtlAbort]) == epoch) {
+            atomicOr(&ctl[kCtlErr], kErrTimeout);
+            __hip_atomic_store(&ctl[kCtlAbort], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
     }

@@ -34,6 +34,21 @@ constexpr int kSrcTables = 0, kSrcArgs = 1, kSrcDevice = 2;
 constexpr uint32_t kErrTimeout = 1u;     // a wait gave up
 constexpr uint32_t kErrLengths = 2u;     // device context lengths out of range
 
+// Control block of a lean exchange (partials and flags), 256 bytes of
+// uint32 words, each on its own 64-byte line:
+//   err    sticky error bits, cleared only by the host (la_sync_check)
+//   epoch  epoch of the last launch that completed on this exchange
+//   exit   workgroups of the current launch that have finished (zero between
+//          launches: the last one out resets it)
+//   abort  epoch of a launch in which a wait gave up
+// A launch's epoch is the completed epoch plus one (never 0). Peers raise
+// their flag to the launch's epoch and hosts wait for exactly that value, so
+// a flag left from an earlier launch -- a late peer whose host gave up --
+// never counts, and a give-up makes the other waits of the same launch give
+// up at once without touching later launches. Flags need no lowering.
+constexpr int kCtlErr = 0, kCtlEpoch = 16, kCtlExit = 32, kCtlAbort = 48;
+constexpr int kCtlWords = 64;
+
 struct SchedArgs {
     const int4* seg;           // tables: [nseg] (u, t0, t1, host | finishing << 1)
     const int32_t* cta_seg;    // tables: [G+1]
@@ -61,8 +76,8 @@ struct LeanArgs {
     float* l_out;              // optional [B*H]
     SchedArgs sched;
     float* part;               // [G * part_stride(d)]
-    uint32_t* flags;           // [G], zero at launch, zero again at exit
-    uint32_t* err;             // device error word
+    uint32_t* flags;           // [G]: epoch of the launch whose record each holds
+    uint32_t* ctl;             // control block (kCtl* words)
     int32_t* tile_owner;       // optional [I]
     uint64_t* ts;              // optional [G*4]: start, end, XCC_ID/HW_ID, host wait
     int H;
@@ -115,8 +130,8 @@ struct GqaArgs {
     SchedArgs sched;           // lean (units instead of heads)
     float* part;               // lean: [G*16]; split: [units*splits*16] records
     uint32_t part_bytes;       // size of the lean exchange buffer (bounds its accesses)
-    uint32_t* flags;
-    uint32_t* err;
+    uint32_t* flags;           // lean: [G], as in LeanArgs
+    uint32_t* ctl;             // lean: control block (kCtl* words)
     int32_t* tile_owner;
     uint64_t* ts;              // optional [blocks*4], as in LeanArgs
     int H;                     // query heads per request

@@ -285,10 +285,12 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
     const uint64_t t_in = stamp_start(a.ts, c);
+    const uint32_t ep = launch_epoch(a.ctl);
     __shared__ SchedLds sl;
     SegCursor<SRC> cur(a.sched, kernarg_sched<LeanArgs>(), sl, c);
     if (cur.bad()) {   // lengths from device memory out of range: nothing is computed
-        if (c == 0 && t == 0) atomicOr(a.err, kErrLengths);
+        if (c == 0 && t == 0) atomicOr(&a.ctl[kCtlErr], kErrLengths);
+        if (t == 0) launch_exit(a.ctl, ep);
         stamp_end(a.ts, c);
         return;
     }
@@ -311,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         if (t >= 64) continue;   // the epilogue is wave 0's; the others go on streaming
 
         if (!sg.host) {
-            // a peer: publish (Obar, m, l) for the head's host, then raise the flag
+            // a peer: publish (Obar, m, l) for the head's host, then raise the
+            // flag to this launch's epoch
             float* p = a.part + (int64_t)c * part_stride(D);
 #pragma unroll
             for (int k = 0; k < P; ++k) store_agent(p + lane + 64 * k, O[k]);
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
                 store_agent(p + D + 1, Ls);
             }
             drain_stores();
-            if (lane == 0) __hip_atomic_store(&a.flags[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_store(&a.flags[c], ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
         }
         if (!sg.fin) {
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
             const int last = sg.last;
             const int np = last - c;
             const uint64_t w0 = stamp_now(a.ts);
-            for (int i = lane; i < np; i += 64) wait_flag(&a.flags[c + 1 + i], a.wait_ticks, a.err);
+            for (int i = lane; i < np; i += 64) wait_flag(&a.flags[c + 1 + i], ep, a.wait_ticks, a.ctl);
             stamp_wait(a.ts, c, t_in, w0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             constexpr int kBatch = 16;
@@ -348,12 +351,10 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
                 for (int j = 0; j < kBatch; ++j)
                     if (p0 + j <= last) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
             }
-            // consumed: lower the flags for the next launch
-            for (int i = lane; i < np; i += 64)
-                __hip_atomic_store(&a.flags[c + 1 + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
     }
+    if (t == 0) launch_exit(a.ctl, ep);
     stamp_end(a.ts, c);
 }
 

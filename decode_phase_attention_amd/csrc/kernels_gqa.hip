@@ -535,10 +535,12 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
     const int dc = t & 15;
     const __amdgpu_buffer_rsrc_t xr = exchange_rsrc(a.part, a.part_bytes);
     const uint64_t t_in = stamp_start(a.ts, cta);
+    const uint32_t ep = launch_epoch(a.ctl);
     __shared__ SchedLds sl;
     SegCursor<SRC> cur(a.sched, kernarg_sched<GqaArgs>(), sl, cta);
     if (cur.bad()) {   // lengths from device memory out of range: nothing is computed
-        if (cta == 0 && t == 0) atomicOr(a.err, kErrLengths);
+        if (cta == 0 && t == 0) atomicOr(&a.ctl[kCtlErr], kErrLengths);
+        if (t == 0) launch_exit(a.ctl, ep);
         stamp_end(a.ts, cta);
         return;
     }
@@ -563,7 +565,8 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
         gqa_fold<D>(sm, st, wave, w, c, M, L, O);
 
         if (!sg.host) {
-            // a peer: publish one record per query column, then raise the flag
+            // a peer: publish one record per query column, then raise the
+            // flag to this launch's epoch
             if (q < x.geff) {
                 const uint32_t rec = (uint32_t)(cta * 16 + q) * (uint32_t)(part_stride(D) * 4);
 #pragma unroll
@@ -574,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
             }
             drain_stores();
             __syncthreads();
-            if (t == 0) __hip_atomic_store(&a.flags[cta], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t == 0) __hip_atomic_store(&a.flags[cta], ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
         }
         if (!sg.fin) {
@@ -582,7 +585,8 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
             const int last = sg.last;
             const int np = last - cta;
             const uint64_t w0 = stamp_now(a.ts);
-            for (int i = t; i < np; i += kThreads) wait_flag(&a.flags[cta + 1 + i], a.wait_ticks, a.err);
+            for (int i = t; i < np; i += kThreads)
+                wait_flag(&a.flags[cta + 1 + i], ep, a.wait_ticks, a.ctl);
             __syncthreads();
             stamp_wait(a.ts, cta, t_in, w0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -593,12 +597,10 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
                 fold_peers_spread<D>(sm, xr, cta, last, x.geff, q, dc, M, L, O);
             else
                 fold_peers<D>(xr, cta, last, x.geff, q, dc, M, L, O);
-            __syncthreads();
-            for (int i = t; i < np; i += kThreads)
-                __hip_atomic_store(&a.flags[cta + 1 + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         write_out_gqa<D>(a, x, q, dc, M, L, O);
     }
+    if (t == 0) launch_exit(a.ctl, ep);
     stamp_end(a.ts, cta);
 }
 

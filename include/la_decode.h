@@ -329,20 +329,24 @@ int la_max_grid_grouped(int d, int dtype);
 int la_default_grid(int d, int dtype);
 
 /*
- * Synchronises `stream` and reads the device error word of its workspace.
- * LA_EINVAL if lengths read on the device (ctx_lens_device) were out of
- * range, LA_ETIMEOUT if a device-side wait exceeded its bound, since the last
- * check (the word and the flags are then reset); LA_EHIP if the stream
- * reports an error; LA_OK otherwise.
+ * Synchronises `stream` and reads the sticky device error word of its
+ * workspace. LA_EINVAL if lengths read on the device (ctx_lens_device) were
+ * out of range, LA_ETIMEOUT if a device-side wait exceeded its bound, since
+ * the last check (the word is then cleared); LA_EHIP if the stream reports an
+ * error; LA_OK otherwise. An error affects only the launch that raised it:
+ * later launches are computed normally whether or not this is called.
  */
 la_status la_sync_check(void* stream);
 
 /*
  * Bound, in microseconds, on one device-side wait of a host workgroup for a
  * peer's partial, for calls enqueued after this one (0 restores the default,
- * 2 s). A wait that runs out -- or any wait after one has run out -- gives up
- * and raises the error word reported by la_sync_check(); the output of that
- * launch is then undefined. Small bounds force this path in tests.
+ * 2 s). A wait that runs out -- and every other wait of the same launch after
+ * it -- gives up and raises the error word reported by la_sync_check(); the
+ * output of that launch is then undefined. Later launches are not affected:
+ * flags hold the epoch of the launch that raised them, so a late peer's flag
+ * never satisfies a later launch's wait. Small bounds force this path in
+ * tests.
  */
 void la_set_wait_limit_us(uint32_t us);
 

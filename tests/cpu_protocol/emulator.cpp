@@ -4,10 +4,13 @@
 //
 //   lean  the static stream-K schedule (xllm-io paper review of arXiv
 //         2405.10480, §3.5): the real tables from the library's host
-//         scheduler; a peer publishes its partial (m, l, Obar) and raises a
-//         flag; a head's host waits for its peers' flags (bounded, like the
-//         kernel's watchdog), folds their partials in workgroup order with f
-//         (§3.2), normalises, and lowers the flags.
+//         scheduler; a peer publishes its partial (m, l, Obar) and raises its
+//         flag to the launch's epoch; a head's host waits for its peers'
+//         flags to hold that epoch (bounded, like the kernel's watchdog),
+//         folds their partials in workgroup order with f (§3.2) and
+//         normalises. Several launches run back to back on one exchange
+//         (flags, partials, control words), as on one stream: the last
+//         workgroup out of a launch makes its epoch the completed one.
 //   pull  chunks of the same tile order pulled from a counter by a pool of
 //         threads (siliconandsystems digest, "Exact softmax can be reduced in
 //         pieces"); a head spread over chunks is merged by the two-level tree
@@ -20,10 +23,14 @@
 // read. Test infrastructure: built and run by tests/test_cpu_protocol.py.
 //
 // Input file (little endian): int32 mode (0 lean, 1 pull), B, H, d, L, G
-// (lean grid, or pull threads), C (pull chunk tiles), drop (lean: workgroup
-// whose flag is never raised, -1 none), wait_ms, seed; int32 ctx[B]; float64
-// scale, q[B*H*d], k[H*sum(n)*d], v[same]. Output file: int32 status (0 ok,
-// 4 a wait gave up), then float64 out[B*H*d], m[B*H], l[B*H].
+// (lean grid, or pull threads), C (pull chunk tiles), drop (lean: a peer
+// workgroup that raises its flag only after twice the wait bound in the
+// first launch, and after a quarter of it in later ones; -1 none), wait_ms,
+// seed, launches (lean: launches in a row); int32 ctx[B]; float64 scale,
+// q[B*H*d], k[H*sum(n)*d], v[same]. Output file: int32 status (0 ok, 4 a
+// wait gave up in some launch, 5 the control words were left inconsistent),
+// then float64 out[B*H*d], m[B*H], l[B*H] of the last launch (NaN for a head
+// whose host gave up).
 
 #include <atomic>
 #include <chrono>
@@ -49,6 +56,12 @@ constexpr std::memory_order kRelease = std::memory_order_release;
 constexpr std::memory_order kAcquire = std::memory_order_acquire;
 constexpr std::memory_order kAcqRel = std::memory_order_acq_rel;
 #endif
+
+// Built with -DEMU_UNEPOCHED, the lean exchange is the earlier protocol that
+// the epochs replaced: flags hold 1 and hosts lower them after merging, and
+// once any wait has given up every later wait gives up at once. A late peer
+// then leaves its flag raised into the next launch: a planted mistake that
+// the tests must catch.
 
 struct Rec {
     double m = -INFINITY, l = 0.0;
@@ -113,8 +126,8 @@ void nap(std::mt19937& rng) {
     std::this_thread::sleep_for(std::chrono::microseconds(rng() % 200));
 }
 
-int run_lean(const Problem& P, int grid, int drop, int wait_ms, unsigned seed, double* out,
-             double* mo, double* lo) {
+int run_lean(const Problem& P, int grid, int drop, int wait_ms, int launches, unsigned seed,
+             double* out, double* mo, double* lo) {
     const int BH = P.B * P.H;
     int64_t I = 0;
     int G = 0, rows = 0;
@@ -123,45 +136,77 @@ int run_lean(const Problem& P, int grid, int drop, int wait_ms, unsigned seed, d
     std::vector<int32_t> cta_begin(G + 1), cta_seg(G + 1), seg((size_t)rows * 6), host(BH), last(BH);
     la::build_schedule(P.ctx.data(), P.B, P.H, P.L, G, I, cta_begin.data(), cta_seg.data(),
                        seg.data(), nullptr, host.data(), last.data());
+    // the exchange, kept across launches
     std::vector<Rec> part(G);
     std::vector<std::atomic<uint32_t>> flag(G);
     for (auto& f : flag) f.store(0);
-    std::atomic<uint32_t> err{0};
-    auto cta = [&](int c) {
-        std::mt19937 rng(seed * 7919u + c);
-        for (int si = cta_seg[c]; si < cta_seg[c + 1]; ++si) {
-            const int32_t* r = &seg[(size_t)si * 6];
-            const int u = r[1], t0 = r[2], t1 = r[3], is_host = r[4];
-            nap(rng);
-            Rec acc = partial(P, u, t0, t1);
-            if (!is_host) {
-                part[c] = acc;
-                nap(rng);
-                if (c != drop) flag[c].store(1, kRelease);
-                continue;
-            }
-            const auto t_end = std::chrono::steady_clock::now() + std::chrono::milliseconds(wait_ms);
-            for (int p = c + 1; p <= last[u]; ++p) {
-                while (flag[p].load(kAcquire) == 0) {
-                    if (err.load() != 0 || std::chrono::steady_clock::now() > t_end) {
-                        err.store(1);
-                        return;
-                    }
-                    std::this_thread::yield();
-                }
-            }
-            for (int p = c + 1; p <= last[u]; ++p) merge(acc, part[p]);
-            for (int p = c + 1; p <= last[u]; ++p) flag[p].store(0, std::memory_order_relaxed);
-            finish(P, u, acc, out, mo, lo);
+    std::atomic<uint32_t> err{0}, epoch{0}, exited{0}, aborted{0};
+    for (int launch = 0; launch < launches; ++launch) {
+        for (int u = 0; u < BH; ++u) {
+            for (int i = 0; i < P.d; ++i) out[(size_t)u * P.d + i] = NAN;
+            mo[u] = lo[u] = NAN;
         }
-    };
-    std::vector<std::thread> th;
-    for (int c = 0; c < G; ++c) th.emplace_back(cta, c);
-    for (auto& t : th) t.join();
-    if (err.load() != 0) return 4;
-    for (auto& f : flag)
-        if (f.load() != 0) return 5;    // every flag lowered again: ready for the next launch
-    return 0;
+        auto cta = [&](int c) {
+            std::mt19937 rng(seed * 7919u + c + 104729u * (unsigned)launch);
+            uint32_t e = epoch.load(std::memory_order_relaxed) + 1u;
+            if (e == 0u) e = 1u;
+            for (int si = cta_seg[c]; si < cta_seg[c + 1]; ++si) {
+                const int32_t* r = &seg[(size_t)si * 6];
+                const int u = r[1], t0 = r[2], t1 = r[3], is_host = r[4], is_fin = r[5];
+                nap(rng);
+                Rec acc = partial(P, u, t0, t1);
+                if (!is_host) {
+                    part[c] = acc;
+                    nap(rng);
+                    if (c == drop)
+                        std::this_thread::sleep_for(
+                            std::chrono::milliseconds(launch == 0 ? 2 * wait_ms : wait_ms / 4));
+#ifdef EMU_UNEPOCHED
+                    flag[c].store(1, kRelease);
+#else
+                    flag[c].store(e, kRelease);
+#endif
+                    continue;
+                }
+                bool gave_up = false;
+                if (!is_fin) {
+                    const auto t_end =
+                        std::chrono::steady_clock::now() + std::chrono::milliseconds(wait_ms);
+                    for (int p = c + 1; p <= last[u] && !gave_up; ++p) {
+#ifdef EMU_UNEPOCHED
+                        while (flag[p].load(kAcquire) == 0) {
+                            if (err.load() != 0 || std::chrono::steady_clock::now() > t_end) {
+#else
+                        while (flag[p].load(kAcquire) != e) {
+                            if (aborted.load() == e || std::chrono::steady_clock::now() > t_end) {
+                                aborted.store(e);
+#endif
+                                err.fetch_or(1u);
+                                gave_up = true;
+                                break;
+                            }
+                            std::this_thread::yield();
+                        }
+                    }
+                    if (!gave_up)
+                        for (int p = c + 1; p <= last[u]; ++p) merge(acc, part[p]);
+#ifdef EMU_UNEPOCHED
+                    for (int p = c + 1; p <= last[u]; ++p) flag[p].store(0, std::memory_order_relaxed);
+#endif
+                }
+                if (!gave_up) finish(P, u, acc, out, mo, lo);
+            }
+            if (exited.fetch_add(1, std::memory_order_relaxed) == (uint32_t)G - 1) {
+                exited.store(0, std::memory_order_relaxed);
+                epoch.store(e, std::memory_order_relaxed);
+            }
+        };
+        std::vector<std::thread> th;
+        for (int c = 0; c < G; ++c) th.emplace_back(cta, c);
+        for (auto& t : th) t.join();
+    }
+    if (exited.load() != 0 || epoch.load() != (uint32_t)launches) return 5;
+    return err.load() != 0 ? 4 : 0;
 }
 
 int run_pull(const Problem& P, int threads, int C, unsigned seed, double* out, double* mo,
@@ -252,9 +297,9 @@ int main(int argc, char** argv) {
     }
     FILE* f = fopen(argv[1], "rb");
     if (!f) return 2;
-    int32_t h[10];
+    int32_t h[11];
     Problem P;
-    if (!rd(f, h, 10)) return 2;
+    if (!rd(f, h, 11)) return 2;
     const int mode = h[0];
     P.B = h[1];
     P.H = h[2];
@@ -262,6 +307,7 @@ int main(int argc, char** argv) {
     P.L = h[4];
     const int G = h[5], C = h[6], drop = h[7], wait_ms = h[8];
     const unsigned seed = (unsigned)h[9];
+    const int launches = h[10] > 0 ? h[10] : 1;
     P.ctx.resize(P.B);
     if (!rd(f, P.ctx.data(), P.B)) return 2;
     int64_t N = 0;
@@ -279,7 +325,7 @@ int main(int argc, char** argv) {
     fclose(f);
     const size_t BH = (size_t)P.B * P.H;
     std::vector<double> out(BH * P.d, NAN), mo(BH, NAN), lo(BH, NAN);
-    const int st = mode == 0 ? run_lean(P, G, drop, wait_ms, seed, out.data(), mo.data(), lo.data())
+    const int st = mode == 0 ? run_lean(P, G, drop, wait_ms, launches, seed, out.data(), mo.data(), lo.data())
                              : run_pull(P, G, C, seed, out.data(), mo.data(), lo.data());
     FILE* g = fopen(argv[2], "wb");
     if (!g) return 2;

@@ -4,8 +4,11 @@ One thread per workgroup runs the real stream-K tables from the library's host
 scheduler (lean) or pulls chunks from a counter (pull), in fp64 with random
 delays, under ThreadSanitizer. The merged outputs must equal the fp64 oracle,
 the pull results must be bitwise the same for any thread count and timing, no
-flag or counter may be left raised, TSan must report nothing, and a peer that
-never raises its flag must end in an error, not a hang (the watchdog path)."""
+counter may be left raised, TSan must report nothing, and a peer that never
+raises its flag must end in an error, not a hang (the watchdog path). Lean
+launches run back to back on one exchange: a peer that raises its flag late
+in one launch (after its host gave up) must not disturb the next ones, and
+the earlier protocol without epochs must be caught doing exactly that."""
 from __future__ import annotations
 
 import os
@@ -47,9 +50,9 @@ def problem(lens, H, d, seed):
 
 
 def run(emulator, tmp_path, inp, q, k, v, mode, G, C=0, drop=-1, wait_ms=5000, seed=1, L=8,
-        expect_race=False):
+        launches=1, expect_race=False):
     B, H, d = inp.B, inp.H, inp.d
-    hdr = np.array([mode, B, H, d, L, G, C, drop, wait_ms, seed], np.int32)
+    hdr = np.array([mode, B, H, d, L, G, C, drop, wait_ms, seed, launches], np.int32)
     fin, fout = tmp_path / f"in_{mode}_{G}_{C}_{seed}", tmp_path / f"out_{mode}_{G}_{C}_{seed}"
     with open(fin, "wb") as f:
         f.write(hdr.tobytes())
@@ -126,6 +129,37 @@ def test_missing_peer_ends_in_error_not_hang(emulator, tmp_path):
     inp, q, k, v = problem([400], 2, 8, seed=6)
     st, O, _, _ = run(emulator, tmp_path, inp, q, k, v, mode=0, G=8, drop=3, wait_ms=200)
     assert st == 4
+
+
+def test_late_peer_stays_in_its_launch(emulator, tmp_path):
+    """Workgroup 3 (a peer of head 0) raises its flag only after its host gave
+    up in the first launch, then on time in the next two, with nothing reset
+    in between: the sticky error is reported, and the last launch equals the
+    oracle on every head."""
+    inp, q, k, v = problem([400], 2, 8, seed=6)
+    st, O, m, l = run(emulator, tmp_path, inp, q, k, v, mode=0, G=8, drop=3, wait_ms=200,
+                      launches=3)
+    assert st == 4
+    close((O, m, l), reference(inp))
+
+
+@pytest.mark.parametrize("G", [5, 64])
+def test_launches_in_a_row_advance_the_epoch(emulator, tmp_path, G):
+    inp, q, k, v = problem([37, 5, 200, 64], 3, 16, seed=G)
+    st, O, m, l = run(emulator, tmp_path, inp, q, k, v, mode=0, G=G, seed=G, launches=4)
+    assert st == 0      # also: exit count back at zero, epoch == launches
+    close((O, m, l), reference(inp))
+
+
+def test_protocol_without_epochs_is_caught(tmp_path_factory, tmp_path):
+    """Plant the earlier protocol (flags 1/0, sticky give-up): the late peer of
+    the first launch leaves its flag raised, so in the next launch its host
+    reads the record while the peer is still writing it -- TSan reports it."""
+    bad = build(tmp_path_factory, "emu_unepoched", "-DEMU_UNEPOCHED")
+    inp, q, k, v = problem([400], 2, 8, seed=6)
+    r = run(bad, tmp_path, inp, q, k, v, mode=0, G=8, drop=3, wait_ms=200, launches=3,
+            expect_race=True)
+    assert r.returncode == 66 and "data race" in r.stderr, (r.returncode, r.stderr[-2000:])
 
 
 @pytest.mark.parametrize("mode,G,C", [(0, 6, 0), (1, 6, 1)])

@@ -56,6 +56,12 @@ def reference(inp, heads=None):
                               inp.scale, inp.dtype, heads=heads, workers=WORKERS)
 
 
+def reference_kv(inp):
+    """The oracle with the inputs' own K/V head count (grouped or not)."""
+    return oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), inp.ctx_lens,
+                              inp.scale, inp.dtype, workers=WORKERS, kv_heads=inp.Hk)
+
+
 def sampled_reference(inp, heads):
     """Oracle on a subset of heads, copying only those heads' rows to the host."""
     B, H, d = inp.B, inp.H, inp.d
@@ -240,6 +246,51 @@ def test_timeout_path_recovers(la):
     finally:
         la.la_set_wait_limit_us(0)
     check(run(la, inp, "lean"), reference(inp), tag="after-timeout")
+
+
+def _late_peer_case():
+    """Tiles of 8192 tokens, grid 3. Request 0 has one token per head (one
+    tile each), request 1 five full tiles per schedule unit. Workgroup 0's
+    range starts with request 0's tiny tiles and ends with the first tiles of
+    request 1's first unit, which it hosts; its first peer streams one full
+    tile more than it before publishing (2 against 1 with one unit per
+    request, 3 against 2 with two). The host so reaches its wait tens of
+    microseconds early, and a 1 us bound always gives up."""
+    return [1, 8192 * 5], dict(tile_tokens=8192, grid=3)
+
+
+@pytest.mark.parametrize("H,Hk", [(2, 2), (4, 1)])
+def test_timeout_stays_in_its_launch(la, H, Hk):
+    """Hosts give up waiting in three launches (1 us bound, forced from the
+    host); with the bound restored and no la_sync_check in between, the next
+    launches are exact on every head: a give-up reaches no later launch.
+    la_sync_check then reports the timeout once."""
+    lens, opts = _late_peer_case()
+    d = 128
+    inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=12, device="cuda", kv_heads=Hk)
+    ref = reference_kv(inp)
+    la.la_sync_check()
+    out = torch.empty((inp.B, H, d), dtype=torch.float32, device="cuda")
+    try:
+        la.la_set_wait_limit_us(1)
+        for _ in range(3):
+            la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, H, d, inp.scale, out,
+                            kv_heads=Hk, **opts)
+    finally:
+        la.la_set_wait_limit_us(0)
+    for i in range(2):
+        out = torch.full((inp.B, H, d), float("nan"), dtype=torch.float32, device="cuda")
+        m = torch.full((inp.B * H,), float("nan"), dtype=torch.float32, device="cuda")
+        l = torch.full((inp.B * H,), float("nan"), dtype=torch.float32, device="cuda")
+        la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, H, d, inp.scale, out,
+                        kv_heads=Hk, m_out=m, l_out=l, **opts)
+        torch.cuda.synchronize()
+        check((out.cpu().numpy(), m.view(inp.B, H).cpu().numpy(), l.view(inp.B, H).cpu().numpy()),
+              ref, tag=f"after-timeout launch {i}")
+    with pytest.raises(la.LaError) as e:
+        la.la_sync_check()
+    assert e.value.status == 4
+    la.la_sync_check()      # reported once, then clear
 
 
 # ------------------------------------------------------------------ full-size workloads
