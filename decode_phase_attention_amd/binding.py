@@ -20,6 +20,7 @@ import numpy as np
 __all__ = [
     "LaError", "LA_F16", "LA_BF16", "LA_KIND_LEAN", "LA_KIND_FIXED_SPLIT", "LA_KIND_PER_HEAD",
     "LA_KIND_AUTO", "LA_KIND_PULL", "LA_KIND_CHUNKS", "lib", "la_decode", "la_decode_bf16", "la_decode_f16", "la_decode_ex",
+    "la_decode_noalloc",
     "la_select", "la_select_for", "la_schedule",
     "la_schedule_dims", "la_default_tile", "la_max_grid", "la_max_grid_grouped", "la_default_grid",
     "la_sync_check",
@@ -82,6 +83,8 @@ _SIG = {
     "la_opts_init": (None, [ctypes.POINTER(LaOpts)]),
     "la_decode_ex": (_I, [_P, _P, _P, _I32P, _I, _I, _I, ctypes.c_float, _P, _P,
                           ctypes.POINTER(LaOpts)]),
+    "la_decode_noalloc": (_I, [_P, _P, _P, _I32P, _I, _I, _I, ctypes.c_float, _P, _P,
+                               ctypes.POINTER(LaOpts)]),
     "la_schedule_dims": (_I, [_I32P, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_int64),
                               ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "la_schedule": (_I, [_I32P, _I, _I, _I, _I, _I32P, _I32P, _I32P, _I, ctypes.POINTER(_I),
@@ -261,13 +264,10 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
                                float(scale), _ptr(out), _stream(stream)))
 
 
-def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
-                 kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
-                 m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
-                 ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0, host_tables=False,
-                 kv_stride=0, ctx_lens_device=None):
-    """la_decode_ex with the options as keywords. With ctx_lens_device (a
-    device int32 tensor of B lengths), ctx_lens may be None."""
+def _marshal(q, k_cache, v_cache, ctx_lens, B, H, d, out, *, dtype, kind, tile_tokens, grid,
+             num_splits, cooperative, m_out, l_out, tile_owner, cta_timestamps, ev_start, ev_stop,
+             kv_heads, q_tokens, chunk_tiles, host_tables, kv_stride, ctx_lens_device):
+    """The la_opts of a call and its lengths pointer, after the size checks."""
     o = LaOpts()              # ctypes zero-fills it: the same as la_opts_init
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
     o.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
@@ -317,8 +317,44 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
         arr, p = _lens(ctx_lens)
     _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, kv_heads, q_tokens, m_out, l_out,
                  kv_stride)
+    # keep the lengths array alive with the options until the call returns
+    return o, arr, p
+
+
+def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *, dtype=None,
+                 kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
+                 m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
+                 ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0, host_tables=False,
+                 kv_stride=0, ctx_lens_device=None):
+    """la_decode_ex with the options as keywords. With ctx_lens_device (a
+    device int32 tensor of B lengths), ctx_lens may be None."""
+    o, arr, p = _marshal(q, k_cache, v_cache, ctx_lens, B, H, d, out, dtype=dtype, kind=kind,
+                         tile_tokens=tile_tokens, grid=grid, num_splits=num_splits,
+                         cooperative=cooperative, m_out=m_out, l_out=l_out, tile_owner=tile_owner,
+                         cta_timestamps=cta_timestamps, ev_start=ev_start, ev_stop=ev_stop,
+                         kv_heads=kv_heads, q_tokens=q_tokens, chunk_tiles=chunk_tiles,
+                         host_tables=host_tables, kv_stride=kv_stride,
+                         ctx_lens_device=ctx_lens_device)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
+
+
+def la_decode_noalloc(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, *,
+                      dtype=None, kind="lean", tile_tokens=0, grid=0, cooperative=False,
+                      m_out=None, l_out=None, tile_owner=None, cta_timestamps=None,
+                      ev_start=None, ev_stop=None, kv_heads=0, q_tokens=0, kv_stride=0,
+                      ctx_lens_device=None):
+    """la_decode_noalloc (the lean kind without any allocation) with the
+    options as keywords, as la_decode_ex."""
+    o, arr, p = _marshal(q, k_cache, v_cache, ctx_lens, B, H, d, out, dtype=dtype, kind=kind,
+                         tile_tokens=tile_tokens, grid=grid, num_splits=0,
+                         cooperative=cooperative, m_out=m_out, l_out=l_out, tile_owner=tile_owner,
+                         cta_timestamps=cta_timestamps, ev_start=ev_start, ev_stop=ev_stop,
+                         kv_heads=kv_heads, q_tokens=q_tokens, chunk_tiles=0, host_tables=False,
+                         kv_stride=kv_stride, ctx_lens_device=ctx_lens_device)
+    _check(lib().la_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H),
+                                   int(d), float(scale), _ptr(out), _stream(stream),
+                                   ctypes.byref(o)))
 
 
 def la_schedule_dims(ctx_lens, H, tile_tokens, grid):

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libla_decode.so")
-SOURCES = ["kernels.hip", "kernels_gqa.hip", "api.cpp", "sched.cpp", "select.cpp"]
+SOURCES = ["kernels.hip", "kernels_gqa.hip", "noalloc.hip", "api.cpp", "sched.cpp", "select.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -22,6 +22,7 @@
 #include "la_decode.h"
 #include "kernels.h"
 #include "sched.h"
+#include "noalloc.h"
 #include "select.h"
 
 namespace {
@@ -746,7 +747,35 @@ void free_workspace(Workspace* w) {
     delete w;
 }
 
-// Argument checks of la_decode_ex. `o` holds
+// The exchange of the allocation-free entry point on the current device:
+// its fixed scratch array. The first call on a device looks the array up and
+// clears its control words (la::scratch_setup), and caches the co-resident
+// capacity of both lean kernels at every head dim and dtype, so that later
+// calls only read cached values.
+la_status noalloc_exchange(hipStream_t stream, Exchange* x) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    void* base = la::scratch_base(dev);
+    if (base == nullptr) {
+        Capacity c;
+        for (int dt = 0; dt < 2; ++dt)
+            for (int d : {64, 128})
+                for (bool grouped : {false, true}) {
+                    la_status st = capacity(dt, d, grouped, &c);
+                    if (st != LA_OK) return st;
+                }
+        HIP_TRY(la::scratch_setup(dev, stream, &base));
+    }
+    char* p = static_cast<char*>(base);
+    x->ctl = reinterpret_cast<uint32_t*>(p);
+    x->flags = reinterpret_cast<uint32_t*>(p + la::kScratchFlagsOff);
+    x->part = reinterpret_cast<float*>(p + la::kScratchPartOff);
+    x->part_bytes = la::kScratchPartBytes;
+    x->max_grid = la::kScratchMaxGrid;
+    return LA_OK;
+}
+
+// Argument checks shared by la_decode_ex and la_decode_noalloc. `o` holds
 // the caller's options (kind auto already mapped to lean with device
 // lengths); `hd` receives the query columns of the call.
 la_status prepare(const void* q, const void* k, const void* v, const int32_t* ctx_lens, int B,
@@ -872,6 +901,41 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     if (o.kind == LA_KIND_PULL || o.kind == LA_KIND_CHUNKS)
         return run_pull(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
     return run_split_or_head(*w, q, k, v, ctx_lens, B, hd, d, scale, out, o);
+}
+
+la_status la_decode_noalloc(const void* q, const void* k, const void* v,
+                            const int32_t* ctx_lens, int B, int H, int d, float scale, float* out,
+                            void* stream, const la_opts* opts) {
+    g_msg[0] = 0;
+    la_opts o;
+    la_opts_init(&o);
+    if (opts != nullptr) o = *opts;
+    if (o.kind != LA_KIND_LEAN)
+        return fail(LA_EINVAL, "the allocation-free entry point runs the lean kind only (kind %d)",
+                    o.kind);
+    Heads hd;
+    la_status st = prepare(q, k, v, ctx_lens, B, H, d, scale, out, o, hd);
+    if (st != LA_OK) return st;
+    if (o.ctx_lens_device == nullptr && !in_launch_schedule(ctx_lens, B, o))
+        return fail(LA_EUNSUPPORTED, "the allocation-free entry point derives the schedule in "
+                    "the launch: up to %d host-side requests and 2^32 - 1 tokens in all, no "
+                    "host_tables, or lengths on the device (ctx_lens_device)", la::kInlineB);
+    std::lock_guard<std::mutex> lock(g_mu);
+    hipStreamCaptureStatus cap_status = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing((hipStream_t)stream, &cap_status));
+    if (cap_status != hipStreamCaptureStatusNone) {
+        if (o.cooperative != 0)
+            return fail(LA_EUNSUPPORTED, "stream capture takes ordinary launches only "
+                                         "(cooperative = 0)");
+        int dev = 0;
+        HIP_TRY(hipGetDevice(&dev));
+        if (la::scratch_base(dev) == nullptr)
+            return fail(LA_EUNSUPPORTED, "the first allocation-free call on a device sets up its "
+                                         "scratch array and must not be captured");
+    }
+    Exchange x;
+    if ((st = noalloc_exchange((hipStream_t)stream, &x)) != LA_OK) return st;
+    return run_lean(nullptr, &x, (hipStream_t)stream, q, k, v, ctx_lens, B, hd, d, scale, out, o);
 }
 
 la_status la_decode(const void* q, const void* k, const void* v, const int32_t* ctx_lens, int B,
@@ -1007,9 +1071,11 @@ la_status la_sync_check(void* stream) {
     HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
-    uint32_t* words[1] = {nullptr};
+    // the stream's workspace, and the device's allocation-free scratch
+    uint32_t* words[2] = {nullptr, nullptr};
     auto it = g_ws.find(std::make_pair(dev, (hipStream_t)stream));
     if (it != g_ws.end()) words[0] = it->second->ctl + la::kCtlErr;
+    if (void* base = la::scratch_base(dev)) words[1] = static_cast<uint32_t*>(base) + la::kCtlErr;
     uint32_t err = 0;
     for (uint32_t* word : words) {
         if (word == nullptr) continue;

@@ -254,6 +254,43 @@ la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
                        float* out, void* stream, const la_opts* opts);
 
 /*
+ * la_decode_noalloc: la_decode_ex for callers that cannot allocate -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It calls no hipMalloc, hipFree or other allocating routine and
+ * uses no per-stream workspace: the lean exchange (partial records, flags and
+ * control words) lives in a fixed array of device memory, one per GPU, that
+ * the library holds until the process ends: 8 MiB of partial records plus
+ * 8448 bytes of flags and control words.
+ *
+ * Arguments and options are those of la_decode_ex, restricted to:
+ *   - kind LA_KIND_LEAN (LA_EINVAL otherwise);
+ *   - a schedule derived in the launch: host lengths for at most 256 requests
+ *     and 2^32 - 1 tokens in all with host_tables = 0, or ctx_lens_device
+ *     (LA_EUNSUPPORTED otherwise);
+ *   - a grid of at most 2048 workgroups whose partial records fit the 8 MiB:
+ *     grid * (d + 4) * 4 bytes with one query column per K/V head, 16 times
+ *     that with kv_heads < H or q_tokens > 1 -- at d = 128 that allows 992
+ *     grouped workgroups (LA_EUNSUPPORTED otherwise);
+ *   - while `stream` is being captured: cooperative = 0, and an earlier
+ *     call of this entry point on the device (the first one sets up the
+ *     array and is refused under capture).
+ * Every rejection happens before anything is enqueued. For the same options
+ * the outputs are bitwise those of la_decode_ex (same kernels, same schedule).
+ *
+ * The first call on a device (the current one) looks up the array's address
+ * and enqueues one small kernel on `stream` that clears its control words
+ * and flags; every later call enqueues only the attention kernel. All calls
+ * on a GPU share that GPU's array, which keeps the last call's contents:
+ * calls that overlap on one GPU -- on streams not ordered with each other,
+ * graph replays included -- race and give undefined results, so order them.
+ * A wait that gives up is reported, and the array's error word cleared, by
+ * la_sync_check on any stream of the device.
+ */
+la_status la_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* ctx_lens, int B, int H, int d, float scale,
+                            float* out, void* stream, const la_opts* opts);
+
+/*
  * la_select_for: the kind and lean grid that LA_KIND_AUTO uses, for a device
  * with `cus` compute units whose lean kernel fits `coresident` workgroups at
  * once. Host only: reads nothing from a device. A shape-driven control policy
@@ -330,7 +367,7 @@ int la_default_grid(int d, int dtype);
 
 /*
  * Synchronises `stream` and reads the sticky device error word of its
- * workspace. LA_EINVAL if lengths read on the device (ctx_lens_device) were
+ * workspace, and that of the device's la_decode_noalloc array. LA_EINVAL if lengths read on the device (ctx_lens_device) were
  * out of range, LA_ETIMEOUT if a device-side wait exceeded its bound, since
  * the last check (the word is then cleared); LA_EHIP if the stream reports an
  * error; LA_OK otherwise. An error affects only the launch that raised it:
