@@ -18,6 +18,10 @@ measured with HIP events recorded on the call's stream right around the
 launch. `cpu_baseline` times the fp64 oracle on a bounded sample of heads of
 the same workload and scales it to a whole step. `comparators` times the
 in-house fixed-split and per-head kernels on the same inputs.
+
+With the default workload (512k) the line also carries a `ragged` object: the
+same measurements on the ragged batch (B=16, H=32, d=128, lengths log-uniform
+in [1024, 262144]), the metric's second headline workload.
 """
 from __future__ import annotations
 
@@ -170,28 +174,33 @@ def host_cost(la, torch, inp, batches=8, per_batch=3):
 
 def read_ceiling(la, torch, nbytes, reps=10):
     """Achievable streaming-read bandwidth of this device in GB/s: the
-    library's plain read kernel (the attention kernels' access pattern, one
-    workgroup per CU, no arithmetic) over an `nbytes` buffer, best of `reps`
-    launches timed with events on the launch stream (torch's current one).
-    Short reads pay the same launch ramp and tail as a short attention
-    kernel, so the buffer is sized like the workload's K/V."""
-    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    library's plain read kernel (the attention kernels' access pattern, no
+    arithmetic) over an `nbytes` buffer, best of `reps` launches timed with
+    events on the launch stream (torch's current one). Short reads pay the same
+    launch ramp and tail as a short attention kernel, so the buffer is the
+    workload's own size: one workgroup per CU, or fewer when the buffer holds
+    less than the read kernel's 64 KiB per workgroup."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    unit = 64 << 10
+    grid = max(1, min(cus, nbytes // unit))
+    buf = torch.zeros(max(nbytes, unit), dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for _ in range(3):
-        la.la_stream_read(buf, sink)
+        la.la_stream_read(buf, sink, grid=grid)
     best = float("inf")
     n = 0
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        n = la.la_stream_read(buf, sink)
+        n = la.la_stream_read(buf, sink, grid=grid)
         e1.record()
         torch.cuda.synchronize()
         best = min(best, e0.elapsed_time(e1))
     la.la_sync_check()
+    # freed to torch's cache only: returning it to the driver and allocating
+    # again slows every kernel for about a second afterwards
     del buf
-    torch.cuda.empty_cache()
-    return n / (best * 1e-3) / 1e9
+    return n / (best * 1e-3) / 1e9, n, grid
 
 
 def kernel_source_hash() -> str:
@@ -274,6 +283,24 @@ def occupancy(la, torch, inp, kind, blocks, **opts):
     }
 
 
+def host_cpu():
+    """CPU model name and the number of cores this process may run on."""
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cpu, len(os.sched_getaffinity(0))
+
+
+# Worker threads of the CPU baseline: the GPU box allots 16 host CPUs to its
+# one GPU, whatever the affinity mask shows, so pools are sized to that share.
+CPU_SHARE = 16
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """fp64 oracle on whole query rows of the workload until ~budget_s of wall
     time, scaled by (all head-tokens / head-tokens done) to microseconds per
@@ -284,7 +311,8 @@ def cpu_baseline(inp, budget_s=12.0):
     import oracle
     import workloads as W
 
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    cpu, visible = host_cpu()
+    workers = max(1, min(CPU_SHARE, visible))
     B, H, Hk, Nq = inp.B, inp.H, inp.Hk, inp.Nq
     g = H // Hk
     starts = np.concatenate([[0], np.cumsum(inp.ctx_lens)]) * Hk
@@ -317,23 +345,20 @@ def cpu_baseline(inp, budget_s=12.0):
         del ks, vs, kcat, vcat
     total_tokens = H * sum(Nq * n - Nq * (Nq - 1) // 2 for n in inp.ctx_lens)
     value = spent * 1e6 * total_tokens / tokens_done
-    cpu = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
+    kv_bytes = 2 * tokens_done * inp.d * 2        # the 16-bit K and V rows the oracle read
     return {
         "value": round(value, 1),
         "unit": "us/step",
         "cores": workers,
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} query rows ({tokens_done} of {total_tokens} "
-                  f"head-tokens), "
-                  f"fp64 two-pass numpy oracle, {spent:.1f} s wall, scaled by head-tokens; "
-                  f"host {cpu}",
+                  f"head-tokens), fp64 two-pass numpy oracle, {spent:.1f} s wall, scaled by "
+                  f"head-tokens; {workers} worker threads (the box's CPU share) of "
+                  f"{visible} cores visible; host {cpu}",
+        "wall_s": round(spent, 2),
+        "kv_GBps": round(kv_bytes / spent / 1e9, 3) if spent > 0 else None,
+        "host_cores_visible": visible,
+        "cpu_model": cpu,
     }
 
 
@@ -681,6 +706,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="with the default 512k workload, skip the ragged workload that the "
+                         "line otherwise also carries")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only the lean kernel on the workload (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -720,103 +748,31 @@ def main():
     import torch
 
     import decode_phase_attention_amd as la
-    import workloads as W
 
     torch.cuda.set_device(0)
     la.lib()
     evs = HipEvents()
-    log(f"[bench] generating {args.workload} (seed {args.seed})")
-    inp = W.make_inputs(args.workload, seed=args.seed, device="cuda")
-    w = inp.meta["workload"]
+    import workloads as W
+
+    # Every workload's inputs are drawn first and stay resident until the end:
+    # after a large buffer is freed and another allocated, every kernel runs
+    # several percent slower for about a second (measured on ragged right after
+    # freeing 512k's caches: 2130 against 2037 us for lean, 2166 against 2094
+    # for the best fixed split), so nothing is freed between measurements.
+    names = [args.workload]
+    if args.workload == "512k" and not args.kernel_only and not args.no_ragged:
+        names.append("ragged")      # the metric's second headline workload, in the same line
+    inputs = {}
+    for n in names:
+        log(f"[bench] generating {n} (seed {args.seed})")
+        inputs[n] = W.make_inputs(n, seed=args.seed, device="cuda")
     torch.cuda.synchronize()
-    dt_code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
-    Hk, Nq = inp.Hk, inp.Nq
-    # the lean kernel on the grid the library's shape rule picks (one or two
-    # workgroups per CU), whichever kind that rule would run
-    _, G = la.la_select(inp.ctx_lens, inp.H, w.d, dt_code, kv_heads=Hk, q_tokens=Nq)
-    L = la.la_default_tile(w.d)
-    cols = inp.H // Hk * Nq                                # query columns per K/V head
-    grouped = cols > 1
-    units = Hk * ((cols + 15) // 16) if grouped else inp.H  # schedule units per request
-    I, Gu, _ = la.la_schedule_dims(inp.ctx_lens, units, L, G)
-    alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d, kv_heads=Hk, q_tokens=Nq)
-    log(f"[bench] lens={inp.ctx_lens} I={I} G={Gu} L={L} bytes={alg_bytes}")
-
-    log("[bench] timing lean")
-    lean = time_kind(la, torch, evs, inp, "lean", args.steps, args.warmup, grid=Gu)
-    achieved = alg_bytes / (lean["kernel_us_mean"] * 1e-6) / 1e9
-    log(f"[bench] lean: {lean}")
-
-    if args.copy_calibration:
-        copy_calibration(torch)
-
-    ceiling = None
-    ceiling_bytes = min(max(alg_bytes, 256 << 20), 4 << 30)
-    if not args.kernel_only:
-        ceiling = read_ceiling(la, torch, ceiling_bytes)
-        log(f"[bench] streaming-read ceiling over {ceiling_bytes} bytes: {ceiling:.1f} GB/s")
-
-    comparators = None
-    if not args.no_comparators and not args.kernel_only:
-        comparators = {}
-        comparators["per_head"] = time_kind(la, torch, evs, inp, "per_head", 10, 2)
-        log(f"[bench] per_head: {comparators['per_head']}")
-        comparators["fixed_split_heuristic"] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2)
-        comparators["pull"] = time_kind(la, torch, evs, inp, "pull", 10, 2)
-        log(f"[bench] pull: {comparators['pull']}")
-        sweep = {}
-        for K in (1, 2, 4, 8, 16, 32, 64):
-            sweep[K] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2, num_splits=K)
-        bestK = min(sweep, key=lambda k: sweep[k]["kernel_us_mean"])
-        comparators["fixed_split_best"] = dict(sweep[bestK], num_splits=bestK)
-        comparators["fixed_split_sweep_kernel_us"] = {str(k): round(v["kernel_us_mean"], 2)
-                                                      for k, v in sweep.items()}
-        log(f"[bench] fixed_split best K={bestK}: {comparators['fixed_split_best']}")
-        for v in comparators.values():
-            if isinstance(v, dict) and "kernel_us_mean" in v:
-                v["tbs"] = round(alg_bytes / (v["kernel_us_mean"] * 1e-6) / 1e12, 3)
-
-    occ = None
-    splits = None
-    if not args.kernel_only:
-        import numpy as np
-        sch = la.la_schedule(inp.ctx_lens, units, L, G)
-        per_head = np.bincount(sch["seg"][:, 1], minlength=inp.B * units)
-        splits = {"max": int(per_head.max()), "mean": round(float(per_head.mean()), 3)}
-        occ = {"lean": occupancy(la, torch, inp, "lean", Gu, grid=Gu),
-               "per_head": occupancy(la, torch, inp, "per_head", inp.B * units)}
-        if comparators is not None:
-            K = comparators["fixed_split_best"]["num_splits"]
-            occ["fixed_split_best"] = occupancy(la, torch, inp, "fixed_split", inp.B * units * K,
-                                                num_splits=K)
-        log(f"[bench] occupancy: {occ}")
-
-    host = None
-    if not args.kernel_only:
-        host = host_cost(la, torch, inp)
-        log(f"[bench] host us per call: {host}")
-
-    cpu = None
-    if not args.no_cpu_baseline and not args.kernel_only:
-        log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(inp)
-        log(f"[bench] cpu: {cpu}")
-
-    desc = {
-        "tiny": "tiny: B=1, H=4, d=64, n=1024, fp16",
-        "65k": "65k: B=1, H=32, d=128, n=65536, bf16",
-        "512k": "512k: B=1, H=32, d=128, n=524288, bf16",
-        "ragged": "ragged: B=16, H=32, d=128, n_b log-uniform in [1024, 262144], bf16",
-        "many-heads": "many-heads: B=8, H=128, d=64, n=16384, fp16",
-        "gqa-512k": "gqa-512k: B=1, H=32 over 8 K/V heads, d=128, n=524288, bf16",
-        "gqa8-ragged": "gqa8-ragged: B=16, H=64 over 8 K/V heads, d=128, n_b log-uniform "
-                       "in [1024, 262144], bf16",
-        "mqa-32k": "mqa-32k: B=8, H=16 over 1 K/V head, d=64, n=32768, fp16",
-        "spec4-ragged": "spec4-ragged: B=16, 4 new tokens each, H=32 over 8 K/V heads, d=128, "
-                        "n_b log-uniform in [1024, 262144], causal among the new tokens, bf16",
-        "spec8-64k": "spec8-64k: B=4, 8 new tokens each, H=32, d=128, n=65536, causal among "
-                     "the new tokens, bf16",
-    }[args.workload]
+    head = measure(la, torch, evs, args.workload, inputs[args.workload], args,
+                   cpu=not args.no_cpu_baseline)
+    extra = {}
+    for n in names[1:]:
+        extra[n] = measure(la, torch, evs, n, inputs[n], args, cpu=not args.no_cpu_baseline)
+    lean = head.pop("_lean")
     rec = {
         "metric": METRIC,
         "value": round(lean["us_per_step"], 2),
@@ -828,10 +784,160 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": head["config"]["inputs"],
         "data": "synthetic",
+        "config": head.pop("config"),
+        "achieved_tbs": head.pop("achieved_tbs"),
+        "kernel_us": head.pop("kernel_us"),
+        "roofline": head.pop("roofline"),
+        "cpu_baseline": head.pop("cpu_baseline"),
+    }
+    rec.update(head)
+    for name, m in extra.items():
+        m.pop("_lean")
+        rec[name] = m
+    rec["env"] = {"torch": torch.__version__, "python": platform.python_version(),
+                  "device": torch.cuda.get_device_name(0)}
+    if args.jsonl:
+        write_jsonl(args.jsonl, rec, lean, rec.get("comparators"), rec.get("occupancy"),
+                    rec.get("lean_splits_per_head"), rec["roofline"]["bytes_per_launch"],
+                    rec["cpu_baseline"])
+    print(json.dumps(rec), flush=True)
+
+
+WORKLOAD_DESC = {
+    "tiny": "tiny: B=1, H=4, d=64, n=1024, fp16",
+    "65k": "65k: B=1, H=32, d=128, n=65536, bf16",
+    "512k": "512k: B=1, H=32, d=128, n=524288, bf16",
+    "ragged": "ragged: B=16, H=32, d=128, n_b log-uniform in [1024, 262144], bf16",
+    "many-heads": "many-heads: B=8, H=128, d=64, n=16384, fp16",
+    "gqa-512k": "gqa-512k: B=1, H=32 over 8 K/V heads, d=128, n=524288, bf16",
+    "gqa8-ragged": "gqa8-ragged: B=16, H=64 over 8 K/V heads, d=128, n_b log-uniform "
+                   "in [1024, 262144], bf16",
+    "mqa-32k": "mqa-32k: B=8, H=16 over 1 K/V head, d=64, n=32768, fp16",
+    "spec4-ragged": "spec4-ragged: B=16, 4 new tokens each, H=32 over 8 K/V heads, d=128, "
+                    "n_b log-uniform in [1024, 262144], causal among the new tokens, bf16",
+    "spec8-64k": "spec8-64k: B=4, 8 new tokens each, H=32, d=128, n=65536, causal among "
+                 "the new tokens, bf16",
+}
+
+
+def method_overhead(la, inp, units, L, G, d, cols, alg_bytes):
+    """Bytes the lean launch moves beyond the algorithmic ones: one partial
+    record (Obar[d], m, l padded to d + 4 floats) per live query column of
+    every peer segment, written by the peer and read by the host, plus the
+    flags. From the schedule tables of the launch."""
+    import numpy as np
+    sch = la.la_schedule(inp.ctx_lens, units, L, G)
+    seg = sch["seg"]
+    peers = seg[seg[:, 4] == 0]
+    if cols > 1:
+        QB = (cols + 15) // 16
+        qb = (peers[:, 1] % units) % QB
+        live = np.minimum(16, cols - 16 * qb)
+    else:
+        live = np.ones(len(peers), np.int64)
+    records = int(live.sum())
+    rec_bytes = (d + 4) * 4
+    part = 2 * records * rec_bytes
+    flags = 2 * 4 * len(peers)
+    per_head = np.bincount(seg[:, 1], minlength=inp.B * units)
+    return {
+        "splits_per_unit": {"max": int(per_head.max()), "mean": round(float(per_head.mean()), 3)},
+        "peer_segments": int(len(peers)),
+        "partial_records": records,
+        "partial_record_bytes": rec_bytes,
+        "partial_bytes_written_and_read": part,
+        "flag_bytes": flags,
+        "overhead_over_algorithmic": round((part + flags) / alg_bytes, 6),
+    }
+
+
+def measure(la, torch, evs, name, inp, args, cpu=True):
+    """Every measurement of one workload: the lean kernel (host-observed µs per
+    step and kernel µs from events), its roofline against 8 TB/s and against
+    the device's streaming-read rate at the same size, the committed HBM
+    traffic, the in-house comparators (per head, pull, fixed split with the
+    fill-one-wave K and every K in 1..64), per-CU busy balance, the method's
+    own overhead, the host's cost per call and the fp64 oracle on the host."""
+    import workloads as W
+
+    w = inp.meta["workload"]
+    dt_code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
+    Hk, Nq = inp.Hk, inp.Nq
+    # the lean kernel on the grid the library's shape rule picks (one or two
+    # workgroups per CU), whichever kind that rule would run
+    _, G = la.la_select(inp.ctx_lens, inp.H, w.d, dt_code, kv_heads=Hk, q_tokens=Nq)
+    L = la.la_default_tile(w.d)
+    cols = inp.H // Hk * Nq                                # query columns per K/V head
+    grouped = cols > 1
+    units = Hk * ((cols + 15) // 16) if grouped else inp.H  # schedule units per request
+    I, Gu, _ = la.la_schedule_dims(inp.ctx_lens, units, L, G)
+    alg_bytes = W.algorithmic_bytes(inp.ctx_lens, inp.H, w.d, kv_heads=Hk, q_tokens=Nq)
+    log(f"[bench] {name}: lens={inp.ctx_lens} I={I} G={Gu} L={L} bytes={alg_bytes}")
+
+    log(f"[bench] {name}: timing lean")
+    lean = time_kind(la, torch, evs, inp, "lean", args.steps, args.warmup, grid=Gu)
+    achieved = alg_bytes / (lean["kernel_us_mean"] * 1e-6) / 1e9
+    log(f"[bench] {name}: lean: {lean}")
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+
+    ceiling = ceiling_bytes = ceiling_grid = None
+    if not args.kernel_only:
+        ceiling, ceiling_bytes, ceiling_grid = read_ceiling(la, torch, min(alg_bytes, 4 << 30))
+        log(f"[bench] {name}: streaming-read ceiling over {ceiling_bytes} bytes "
+            f"({ceiling_grid} workgroups): {ceiling:.1f} GB/s")
+
+    comparators = None
+    if not args.no_comparators and not args.kernel_only:
+        comparators = {}
+        comparators["per_head"] = time_kind(la, torch, evs, inp, "per_head", 10, 2)
+        comparators["fixed_split_heuristic"] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2)
+        comparators["pull"] = time_kind(la, torch, evs, inp, "pull", 10, 2)
+        sweep = {}
+        for K in (1, 2, 4, 8, 16, 32, 64):
+            sweep[K] = time_kind(la, torch, evs, inp, "fixed_split", 10, 2, num_splits=K)
+        bestK = min(sweep, key=lambda k: sweep[k]["kernel_us_mean"])
+        comparators["fixed_split_best"] = dict(sweep[bestK], num_splits=bestK)
+        comparators["fixed_split_sweep_kernel_us"] = {str(k): round(v["kernel_us_mean"], 2)
+                                                      for k, v in sweep.items()}
+        log(f"[bench] {name}: fixed_split best K={bestK}: {comparators['fixed_split_best']}")
+        for v in comparators.values():
+            if isinstance(v, dict) and "kernel_us_mean" in v:
+                v["tbs"] = round(alg_bytes / (v["kernel_us_mean"] * 1e-6) / 1e12, 3)
+        best = comparators["fixed_split_best"]["kernel_us_mean"]
+        comparators["lean_over_fixed_split_best"] = round(lean["kernel_us_mean"] / best, 4)
+        comparators["lean_over_fixed_split_heuristic"] = round(
+            lean["kernel_us_mean"] / comparators["fixed_split_heuristic"]["kernel_us_mean"], 4)
+
+    occ = overhead = None
+    if not args.kernel_only:
+        overhead = method_overhead(la, inp, units, L, G, w.d, cols, alg_bytes)
+        occ = {"lean": occupancy(la, torch, inp, "lean", Gu, grid=Gu),
+               "per_head": occupancy(la, torch, inp, "per_head", inp.B * units)}
+        if comparators is not None:
+            K = comparators["fixed_split_best"]["num_splits"]
+            occ["fixed_split_best"] = occupancy(la, torch, inp, "fixed_split", inp.B * units * K,
+                                                num_splits=K)
+        log(f"[bench] {name}: occupancy: {occ}")
+
+    host = None
+    if not args.kernel_only:
+        host = host_cost(la, torch, inp)
+        log(f"[bench] {name}: host us per call: {host}")
+
+    cpu_res = None
+    if cpu and not args.kernel_only:
+        log(f"[bench] {name}: cpu baseline (oracle)")
+        cpu_res = cpu_baseline(inp)
+        log(f"[bench] {name}: cpu: {cpu_res}")
+
+    res = {
+        "_lean": lean,
         "config": {
-            "workload": desc,
+            "workload": WORKLOAD_DESC[name],
             "B": inp.B, "H": inp.H, "kv_heads": Hk, "q_tokens": Nq, "d": w.d,
             "ctx_lens": inp.ctx_lens,
             "seed": args.seed,
@@ -839,6 +945,7 @@ def main():
             "kind": "lean", "grid": Gu, "tile_tokens": L, "iterations": I,
             "parallelism": "single GPU",
         },
+        "us_per_step": round(lean["us_per_step"], 2),
         "achieved_tbs": round(achieved / 1e3, 3),
         "kernel_us": {k: round(v, 2) for k, v in lean.items() if k.startswith("kernel")},
         "roofline": {
@@ -848,24 +955,22 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "read_ceiling_GBps": round(ceiling, 1) if ceiling else None,
-            "read_ceiling_bytes": ceiling_bytes if ceiling else None,
+            "read_ceiling_bytes": ceiling_bytes,
+            "read_ceiling_workgroups": ceiling_grid,
             "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
-            "traffic": committed_traffic(args.workload),
+            "traffic": committed_traffic(name),
             "kernel": "lean_gqa_kernel" if grouped else "lean_kernel",
             "bytes_per_launch": alg_bytes,
             "kernel_source_sha256_16": kernel_source_hash(),
         },
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_res,
         "comparators": comparators,
         "occupancy": occ,
-        "lean_splits_per_head": splits,
+        "lean_splits_per_head": overhead["splits_per_unit"] if overhead else None,
+        "method_overhead": overhead,
         "host_us_per_call": host,
-        "env": {"torch": torch.__version__, "python": platform.python_version(),
-                "device": torch.cuda.get_device_name(0)},
     }
-    if args.jsonl:
-        write_jsonl(args.jsonl, rec, lean, comparators, occ, splits, alg_bytes, cpu)
-    print(json.dumps(rec), flush=True)
+    return res
 
 
 def write_jsonl(path, rec, lean, comparators, occ, splits, alg_bytes, cpu):

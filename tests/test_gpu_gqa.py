@@ -12,6 +12,7 @@ import torch
 
 import oracle
 import workloads as W
+from fullsize_ref import full_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -172,35 +173,16 @@ def test_random_grids_stress(la):
         assert err <= O_TOL, (i, g, err)
 
 
-def _sampled_reference(inp, heads):
-    B, H, d, Hk = inp.B, inp.H, inp.d, inp.Hk
-    g = H // Hk
-    starts = np.concatenate([[0], np.cumsum(inp.ctx_lens)]) * Hk
-    qb = W.to_bits(inp.q)
-    O = np.full((B, H, d), np.nan)
-    M = np.full((B, H), np.nan)
-    L = np.full((B, H), np.nan)
-    for (b, h) in heads:
-        n = inp.ctx_lens[b]
-        r0 = int(starts[b]) + (h // g) * n
-        o, m, l = oracle.attend_fp64(qb[b:b + 1, h:h + 1], W.to_bits(inp.k[r0:r0 + n]),
-                                     W.to_bits(inp.v[r0:r0 + n]), [n], inp.scale, inp.dtype,
-                                     workers=1)
-        O[b, h], M[b, h], L[b, h] = o[0, 0], m[0, 0], l[0, 0]
-    return O, M, L
-
-
 @pytest.mark.parametrize("name", ["gqa-512k", "gqa8-ragged", "mqa-32k"])
 def test_full_size(la, name):
+    """Every kind on the full workload, every (request, query head) against
+    the oracle."""
     say(f"[gqa full {name}]")
     inp = W.make_inputs(name, seed=0, device="cuda")
-    rng = np.random.default_rng(3)
-    allh = [(b, h) for b in range(inp.B) for h in range(inp.H)]
-    heads = sorted({allh[0], allh[-1]} | {allh[int(i)] for i in rng.choice(len(allh), 24, replace=False)})
     res = {k: run(la, inp, k) for k in KINDS}
-    ref = _sampled_reference(inp, heads)
+    ref = full_reference(name, 0, inp)
     for k in KINDS:
-        err = check(res[k], ref, heads=heads, tag=f"{name}/{k}")
+        err = check(res[k], ref, tag=f"{name}/{k}")
         say(f"[gqa full {name}] {k} max|dO|={err:.2e}")
     del inp
     torch.cuda.empty_cache()

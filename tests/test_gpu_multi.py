@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads as W
+from fullsize_ref import full_reference
 from oracle.schedule import lean_schedule
 
 pytestmark = pytest.mark.gpu
@@ -178,23 +179,15 @@ def test_determinism(la):
             np.testing.assert_array_equal(x, y)
 
 
-def _sample(inp, count, seed):
-    rng = np.random.default_rng(seed)
-    allt = [(b, t, h) for b in range(inp.B) for t in range(inp.Nq) for h in range(inp.H)]
-    pick = {allt[0], allt[-1]} | {allt[int(i)] for i in rng.choice(len(allt), count, replace=False)}
-    # the last token of every request (sees the whole cache) and the first
-    pick |= {(b, inp.Nq - 1, 0) for b in range(inp.B)} | {(b, 0, inp.H - 1) for b in range(inp.B)}
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name", ["spec4-ragged", "spec8-64k"])
 def test_full_size(la, name):
+    """Every kind on the full workload, every (request, new token, query
+    head) against the oracle."""
     say(f"[multi full {name}]")
     inp = W.make_inputs(name, seed=0, device="cuda")
-    heads = _sample(inp, 24, 5)
-    ref = reference(inp, heads)
+    ref = full_reference(name, 0, inp)
     for k in KINDS:
-        err = check(run(la, inp, k), ref, heads=heads, tag=f"{name}/{k}")
+        err = check(run(la, inp, k), ref, tag=f"{name}/{k}")
         say(f"[multi full {name}] {k} max|dO|={err:.2e}")
     del inp
     torch.cuda.empty_cache()

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads as W
+from fullsize_ref import full_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -185,14 +186,8 @@ def test_grouped_and_several_tokens(la, H, Hk, Nq, d, dtype, kind, grid, C):
 def test_full_size(la, name):
     say(f"[pull full {name}]")
     inp = W.make_inputs(name, seed=0, device="cuda")
-    rng = np.random.default_rng(9)
     Nq = inp.Nq
-    allh = [(b, t, h) for b in range(inp.B) for t in range(Nq) for h in range(inp.H)]
-    heads = sorted({allh[0], allh[-1]} | {allh[int(i)] for i in rng.choice(len(allh), 24, replace=False)})
-    if Nq == 1:
-        heads = [(b, h) for b, _, h in heads]
-    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), inp.ctx_lens,
-                             inp.scale, inp.dtype, heads=heads, workers=16, kv_heads=inp.Hk)
+    ref = full_reference(name, 0, inp)      # every query row
     shape = tuple(inp.q.shape)
     rows = int(np.prod(shape[:-1]))
     for kind in ("pull", "chunks"):
@@ -204,7 +199,7 @@ def test_full_size(la, name):
         la.la_sync_check()
         got = (out.cpu().numpy(), m.cpu().numpy().reshape(ref[1].shape),
                l.cpu().numpy().reshape(ref[2].shape))
-        err = check(got, ref, heads=heads, tag=f"{name}/{kind}")
+        err = check(got, ref, tag=f"{name}/{kind}")
         say(f"[pull full {name}] {kind} max|dO|={err:.2e}")
     del inp
     torch.cuda.empty_cache()

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads as W
+from fullsize_ref import full_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -126,19 +127,14 @@ def test_full_size_strided(la, name):
     """Full-size workloads in a [B, Hk, S, d] cache with S = the longest
     context (gqa8-ragged: heads up to 5.9 GB into the cache, past 32-bit
     offsets), lean and pull, and lean with the lengths read on the device
-    (the same bits as with host lengths), on sampled heads against the
+    (the same bits as with host lengths), on every head against the
     oracle."""
     inp = W.make_inputs(name, seed=0, device="cuda")
     S = max(inp.ctx_lens)
     say(f"[stride full {name}] S={S}")
     kc, vc = strided(inp, S)
-    rng = np.random.default_rng(5)
-    allh = [(b, h) for b in range(inp.B) for h in range(inp.H)]
-    heads = sorted({allh[0], allh[-1]} | {allh[int(i)] for i in rng.choice(len(allh), 20, replace=False)})
-    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), inp.ctx_lens,
-                             inp.scale, inp.dtype, heads=heads, workers=16, kv_heads=inp.Hk)[0]
+    ref = full_reference(name, 0, inp)[0]      # every query row
     del inp.k, inp.v
-    idx = tuple(np.array(heads).T)
     outs = {}
     dl = torch.tensor(inp.ctx_lens, dtype=torch.int32, device="cuda")
     for kind in ("lean", "pull", "device"):
@@ -151,7 +147,7 @@ def test_full_size_strided(la, name):
                             kind=kind, kv_heads=inp.Hk, kv_stride=S)
         la.la_sync_check()
         outs[kind] = out.cpu().numpy()
-        err = float(np.max(np.abs(outs[kind][idx] - ref[idx])))
+        err = float(np.max(np.abs(outs[kind] - ref)))
         say(f"[stride full {name}] {kind} max|dO|={err:.2e}")
         assert err <= 1e-3
     np.testing.assert_array_equal(outs["lean"], outs["device"])
