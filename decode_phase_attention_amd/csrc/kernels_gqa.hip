@@ -522,8 +522,59 @@ __device__ __forceinline__ void fold_peers_spread(GSmem<D>& sm, __amdgpu_buffer_
 
 // ------------------------------------------------------------------ lean
 
+// A lean segment whose streaming has begun: its unit, key range and bounds,
+// the lane's query operands, and whether its first step is a tail step. The
+// first step's K/V loads sit in a GRegs issued with it.
+template <int D>
+struct GSeg {
+    Unit x;
+    int tok0, tok1, full, lim;
+    bool tail0;
+    u32x4_t qt[GGeo<D>::KK];
+};
+
+// Set up segment `sg` and issue the loads of its first wave step into `g`.
+template <int D>
+__device__ __forceinline__ void gseg_start(const GqaArgs& a, const LeanSeg& sg, int wave, int w,
+                                           int c, GSeg<D>& s, GRegs<D>& g) {
+    using G = GGeo<D>;
+    s.x = decode_unit(a, sg);
+    s.tok0 = sg.t0 * a.L;
+    s.tok1 = (int)min((int64_t)sg.t1 * a.L, (int64_t)s.x.n);
+    col_bounds(a, s.x, c, s.tok1, s.full, s.lim);
+    s.tail0 = s.tok0 + G::CH > s.full;   // uniform: full depends on the unit only
+    load_qt<D>(a.q, c < s.x.geff ? col_row(a, s.x, c) : 0, c < s.x.geff, w, s.qt);
+    const char* kc = reinterpret_cast<const char*>(a.k + s.x.kvrow0 * D);
+    const char* vc = reinterpret_cast<const char*>(a.v + s.x.kvrow0 * D);
+    const int kb = s.tok0 + G::KEYS * wave;
+    if (!s.tail0)
+        gqa_load<D, false>(kc, vc, kb, s.tok1, w, c, g);
+    else
+        gqa_load<D, true>(kc, vc, kb, s.tok1, w, c, g);
+}
+
+// Stream a started segment: its first step from the loaded `g`, then the rest.
+template <int DT, int D>
+__device__ __forceinline__ void gseg_stream(const GqaArgs& a, const GSeg<D>& s, const GRegs<D>& g,
+                                            int wave, int w, int c, GState<D>& st) {
+    using G = GGeo<D>;
+    const int kb = s.tok0 + G::KEYS * wave;
+    if (!s.tail0)
+        gqa_compute<DT, D, false>(g, kb, s.lim, w, s.qt, a.sl2e, st);
+    else
+        gqa_compute<DT, D, true>(g, kb, s.lim, w, s.qt, a.sl2e, st);
+    gqa_range<DT, D>(a.k + s.x.kvrow0 * D, a.v + s.x.kvrow0 * D, s.tok0 + G::CH, s.tok1, s.full,
+                     s.lim, wave, w, c, s.qt, a.sl2e, st);
+}
+
+// Segments of a workgroup are streamed back to back: when one ends, the next
+// one's query operands and first K/V step are loaded before the cross-wave
+// fold and the epilogue of the one that ended, so that their latency overlaps
+// that work instead of stalling every wave at the start of the next segment.
+// A host that merges its peers' records loads the next segment after the
+// merge, whose batched record loads need those registers.
 template <int DT, int D, int SRC>
-__global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void lean_gqa_kernel(const GqaArgs a) {
     using G = GGeo<D>;
     __shared__ GSmem<D> sm;
     const int cta = blockIdx.x;
@@ -545,21 +596,22 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
         return;
     }
     LeanSeg sg;
-    while (cur.next(sg)) {
-        const int u = sg.u;
-        const Unit x = decode_unit(a, sg);
-        const int tok0 = sg.t0 * a.L;
-        const int tok1 = (int)min((int64_t)sg.t1 * a.L, (int64_t)x.n);
-        u32x4_t qt[G::KK];
-        load_qt<D>(a.q, c < x.geff ? col_row(a, x, c) : 0, c < x.geff, w, qt);
-        int full, lim;
-        col_bounds(a, x, c, tok1, full, lim);
+    bool have = cur.next(sg);
+    GSeg<D> cs;
+    GRegs<D> pre;
+    if (have) gseg_start<D>(a, sg, wave, w, c, cs, pre);
+    while (have) {
         GState<D> st;
         gstate_init<D>(st);
-        gqa_range<DT, D>(a.k + x.kvrow0 * D, a.v + x.kvrow0 * D, tok0, tok1, full, lim, wave, w,
-                         c, qt, a.sl2e, st);
+        gseg_stream<DT, D>(a, cs, pre, wave, w, c, st);
         if (a.tile_owner != nullptr && t == 0)
             for (int i = sg.t0; i < sg.t1; ++i) a.tile_owner[sg.iter0 + i - sg.t0] = cta;
+
+        LeanSeg nsg;
+        const bool nhave = cur.next(nsg);
+        const bool merging = sg.host && !sg.fin;
+        GSeg<D> ns;
+        if (nhave && !merging) gseg_start<D>(a, nsg, wave, w, c, ns, pre);
 
         float M, L, O[G::DPT];
         gqa_fold<D>(sm, st, wave, w, c, M, L, O);
@@ -567,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
         if (!sg.host) {
             // a peer: publish one record per query column, then raise the
             // flag to this launch's epoch
-            if (q < x.geff) {
+            if (q < cs.x.geff) {
                 const uint32_t rec = (uint32_t)(cta * 16 + q) * (uint32_t)(part_stride(D) * 4);
 #pragma unroll
                 for (int i = 0; i < G::DPT; i += 4)
@@ -578,27 +630,31 @@ __global__ __launch_bounds__(kThreads) void lean_gqa_kernel(const GqaArgs a) {
             drain_stores();
             __syncthreads();
             if (t == 0) __hip_atomic_store(&a.flags[cta], ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            continue;
+        } else {
+            if (merging) {
+                // the host: wait for every peer at once, then fold their records
+                const int last = sg.last;
+                const int np = last - cta;
+                const uint64_t w0 = stamp_now(a.ts);
+                for (int i = t; i < np; i += kThreads)
+                    wait_flag(&a.flags[cta + 1 + i], ep, a.wait_ticks, a.ctl);
+                __syncthreads();
+                stamp_wait(a.ts, cta, t_in, w0);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                // The host's CU reads every peer's records, so the merge runs
+                // at one CU's load rate; with at most 4 live columns the idle
+                // column groups share the loads.
+                if (D == 128 && cs.x.geff <= 4)
+                    fold_peers_spread<D>(sm, xr, cta, last, cs.x.geff, q, dc, M, L, O);
+                else
+                    fold_peers<D>(xr, cta, last, cs.x.geff, q, dc, M, L, O);
+            }
+            write_out_gqa<D>(a, cs.x, q, dc, M, L, O);
+            if (nhave && merging) gseg_start<D>(a, nsg, wave, w, c, ns, pre);
         }
-        if (!sg.fin) {
-            // the host: wait for every peer at once, then fold their records
-            const int last = sg.last;
-            const int np = last - cta;
-            const uint64_t w0 = stamp_now(a.ts);
-            for (int i = t; i < np; i += kThreads)
-                wait_flag(&a.flags[cta + 1 + i], ep, a.wait_ticks, a.ctl);
-            __syncthreads();
-            stamp_wait(a.ts, cta, t_in, w0);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            // The host's CU reads every peer's records, so the merge runs at one
-            // CU's load rate; with at most 4 live columns the idle column
-            // groups share the loads.
-            if (D == 128 && x.geff <= 4)
-                fold_peers_spread<D>(sm, xr, cta, last, x.geff, q, dc, M, L, O);
-            else
-                fold_peers<D>(xr, cta, last, x.geff, q, dc, M, L, O);
-        }
-        write_out_gqa<D>(a, x, q, dc, M, L, O);
+        sg = nsg;
+        cs = ns;
+        have = nhave;
     }
     if (t == 0) launch_exit(a.ctl, ep);
     stamp_end(a.ts, cta);
