@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "la_decode.h"
+#include "budget.h"
 #include "kernels.h"
 #include "sched.h"
 #include "noalloc.h"
@@ -79,10 +80,52 @@ struct Workspace {
     bool capturing = false;         // the current call is being captured: nothing may be allocated
     bool captured = false;          // a graph may hold the buffers: growing keeps the old ones
     std::vector<void*> retired;     // buffers replaced after a capture, freed at shutdown
+    int last_lean_grid = 0;         // the last lean launch on the stream (for the budget)
+    int last_lean_cap = 1;
 };
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
+
+// Completion events for the lean launch budget (budget.h), from a per-device
+// pool of timing-free events. An error of the runtime counts as done, so that
+// no wait can block on an event that will never complete.
+struct HipEventOps {
+    using event = hipEvent_t;
+    std::vector<hipEvent_t>* pool;
+    hipEvent_t record(void* stream) {
+        hipEvent_t e = nullptr;
+        if (!pool->empty()) {
+            e = pool->back();
+            pool->pop_back();
+        } else if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            return nullptr;
+        }
+        if (hipEventRecord(e, (hipStream_t)stream) != hipSuccess) {
+            pool->push_back(e);
+            return nullptr;
+        }
+        return e;
+    }
+    bool done(hipEvent_t e) { return e == nullptr || hipEventQuery(e) != hipErrorNotReady; }
+    void wait(hipEvent_t e) {
+        if (e != nullptr) (void)hipEventSynchronize(e);
+    }
+    void release(hipEvent_t e) {
+        if (e != nullptr) pool->push_back(e);
+    }
+};
+
+// Per device: how many streams have a workspace, and -- once there are two
+// or more -- the budget that keeps their unfinished lean launches within the
+// co-resident capacity. With one stream every lean launch is ordered after the
+// previous one and nothing is tracked.
+struct DeviceState {
+    int streams = 0;
+    std::vector<hipEvent_t> pool;
+    la::LaunchBudget<HipEventOps>* budget = nullptr;
+};
+std::map<int, DeviceState> g_dev;
 struct Capacity {
     int coresident;   // occupancy per CU x CUs: the largest grid a launch may use
     int preferred;    // default grid: kWgPerCu workgroups on every CU
@@ -157,6 +200,16 @@ la_status get_workspace(hipStream_t stream, Workspace** out) {
         }
     }
     g_ws[key] = w;
+    DeviceState& ds = g_dev[dev];
+    if (++ds.streams == 2) {
+        // from now on lean launches are tracked; the other stream's last lean
+        // launch may still run, so it is counted from here on
+        ds.budget = new la::LaunchBudget<HipEventOps>(HipEventOps{&ds.pool});
+        for (auto& kv : g_ws)
+            if (kv.first.first == dev && kv.second != w && kv.second->last_lean_grid > 0)
+                ds.budget->record(kv.second->stream, kv.second->last_lean_grid,
+                                  kv.second->last_lean_cap);
+    }
     *out = w;
     return LA_OK;
 }
@@ -347,6 +400,15 @@ struct Exchange {
     int max_grid;     // workgroups the flags hold
 };
 
+// After a lean launch through a workspace: remember it on the stream, and
+// count it in the device's budget when one is kept.
+void lean_launched(Workspace* w, la::LaunchBudget<HipEventOps>* budget, int G, int cap) {
+    if (w == nullptr || w->capturing) return;
+    w->last_lean_grid = G;
+    w->last_lean_cap = cap;
+    if (budget != nullptr) budget->record(w->stream, G, cap);
+}
+
 // A lean call. With `fixed` the exchange is that fixed scratch and nothing is
 // allocated or copied: the schedule must be derived in the launch, and the
 // grid and records must fit the scratch. Otherwise `w` is the stream's
@@ -374,6 +436,27 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
         const int rc = la::schedule_dims(ctx_lens, B, U, L, o.grid > 0 ? o.grid : cap.preferred,
                                          &I, &G, &max_rows, &why);
         if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+    }
+
+    // With lean launches on several streams of the device, their unfinished
+    // grids together stay within the co-resident capacity (budget.h): this
+    // launch may get a smaller grid, or wait for another stream's launch.
+    la::LaunchBudget<HipEventOps>* budget = nullptr;
+    if (fixed == nullptr && !w->capturing) {
+        auto it = g_dev.find(w->device);
+        if (it != g_dev.end()) budget = it->second.budget;
+    }
+    if (budget != nullptr) {
+        const int g = budget->admit(w->stream, G, cap.coresident);
+        if (g < G) {
+            if (dev_lens) {
+                G = g;
+            } else {
+                const char* why = "";
+                const int rc = la::schedule_dims(ctx_lens, B, U, L, g, &I, &G, &max_rows, &why);
+                if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+            }
+        }
     }
 
     const size_t records = (size_t)G * (hd.grouped ? 16 : 1);
@@ -476,6 +559,7 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
         if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
         HIP_TRY(la::launch_lean_gqa(o.dtype, d, a, G, stream, coop));
         if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));
+        lean_launched(w, budget, G, cap.coresident);
         return LA_OK;
     }
     la::LeanArgs a{};
@@ -499,6 +583,7 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
     HIP_TRY(la::launch_lean(o.dtype, d, a, G, stream, coop));
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));
+    lean_launched(w, budget, G, cap.coresident);
     return LA_OK;
 }
 
@@ -1123,6 +1208,14 @@ void la_shutdown(void) {
     std::lock_guard<std::mutex> lock(g_mu);
     for (auto& kv : g_ws) free_workspace(kv.second);
     g_ws.clear();
+    for (auto& kv : g_dev) {
+        if (kv.second.budget != nullptr) {
+            kv.second.budget->clear();
+            delete kv.second.budget;
+        }
+        for (hipEvent_t e : kv.second.pool) (void)hipEventDestroy(e);
+    }
+    g_dev.clear();
     g_capacity.clear();
 }
 

@@ -116,6 +116,15 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               grid at la_max_grid, so every workgroup a host waits for can be
  *               resident; the cooperative form also guarantees it while other
  *               work shares the device, at the cost of a slower launch.
+ *               Once lean calls have run on two or more streams of a device,
+ *               the library also keeps the unfinished lean launches of all
+ *               those streams within the co-resident capacity together (each
+ *               counted as grid / capacity of its kernel): a call whose grid
+ *               does not fit beside the other streams' unfinished launches
+ *               runs on the largest grid that does, or waits on the host for
+ *               the oldest of them when none fits. Its outputs then follow the
+ *               smaller grid's schedule (equal within tolerance, not bitwise).
+ *               Graph replays and la_decode_noalloc calls are not counted.
  *   m_out, l_out     optional device [B*H] fp32: m (natural-log units, on
  *               scaled logits) and l of every head
  *   tile_owner  optional device int32 [I]: lean, pull and chunks kinds; entry

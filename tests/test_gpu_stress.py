@@ -20,6 +20,10 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
 @pytest.fixture(scope="module")
 def la():
     if not torch.cuda.is_available():
@@ -132,6 +136,42 @@ def test_two_streams_concurrently(la):
     for j, out in outs:
         err = float(np.max(np.abs(out.cpu().numpy() - refs[j])))
         assert err <= 1e-3, (j, err)
+
+
+def test_three_streams_past_capacity(la):
+    """Three streams, each issuing kind=auto lean launches that pick two
+    workgroups per CU: together they ask for more workgroups than the device
+    holds at once. The library's budget keeps the unfinished lean launches
+    within the co-resident capacity (shrinking a grid, or waiting for another
+    stream's launch), so no host waits on a peer that cannot be resident:
+    every output meets the oracle and no wait runs out."""
+    H, d = 32, 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    lens = [int(x) for x in np.random.default_rng(77).integers(2000, 9000, size=16)]
+    inp = W.make_custom(lens, H, d, "bf16", seed=77, device="cuda")
+    kind, grid = la.la_select(inp.ctx_lens, H, d, la.LA_BF16)
+    cap = la.la_max_grid(d, la.LA_BF16)
+    say(f"[three streams] auto picks {kind} on {grid} workgroups; capacity {cap}")
+    assert kind == "lean" and grid == 2 * cus and 3 * grid > cap
+    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                             inp.scale, "bf16", workers=8)[0]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    outs = []
+    torch.cuda.synchronize()
+    for i in range(6):
+        for s in streams:
+            with torch.cuda.stream(s):
+                out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32,
+                                 device="cuda")
+                la.la_decode_ex(inp.q, inp.k, inp.v, lens, inp.B, H, d, inp.scale, out,
+                                kind="auto")
+                outs.append(out)
+    for s in streams:
+        la.la_sync_check(s.cuda_stream)
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+        assert err <= 1e-3, (i, err)
 
 
 def _strided(t, lens, Hk, d, S):
