@@ -52,6 +52,13 @@
  *    owned by the library, one per (device, stream), allocated on first use and
  *    freed by la_shutdown(). Calls on the same stream are ordered; calls from
  *    several host threads are serialised inside the library.
+ *  - Types across the boundary are plain C: streams and events are passed as
+ *    void* (a hipStream_t / hipEvent_t converts unchanged), and the dtype and
+ *    kind travel as int holding an la_dtype / la_kind value, so that no HIP
+ *    header and no enum size enters the ABI. The argument list of
+ *    la_decode_bf16 / la_decode_f16 is exactly (q, k_cache, v_cache,
+ *    ctx_lens, B, H, d, scale, out, stream); la_decode adds the dtype as a
+ *    trailing argument, since a void* cannot carry the element type.
  */
 #ifndef LA_DECODE_H
 #define LA_DECODE_H
