@@ -385,10 +385,11 @@ def test_grid_larger_than_work(la):
     """Fewer tile iterations than the requested grid: G is cut to I."""
     lens = [3, 200]
     inp = W.make_custom(lens, H=2, d=128, dtype="bf16", seed=43, device="cuda")
-    own_ref, G = tile_owner_ref(lens, 2, 16, 999)
-    assert G == own_ref.size
+    grid = la.la_max_grid(128, la.LA_BF16)     # the largest grid a launch may ask for
+    own_ref, G = tile_owner_ref(lens, 2, 16, grid)
+    assert G == own_ref.size < grid
     owner = torch.full((own_ref.size,), -1, dtype=torch.int32, device="cuda")
-    check(run(la, inp, "lean", grid=999, tile_tokens=16, tile_owner=owner), reference(inp),
+    check(run(la, inp, "lean", grid=grid, tile_tokens=16, tile_owner=owner), reference(inp),
           tag="G>I")
     assert np.array_equal(owner.cpu().numpy(), own_ref)
 
