@@ -137,7 +137,7 @@ def time_kind(la, torch, evs, inp, kind, steps, warmup, **opts):
     }
 
 
-def host_cost(la, torch, inp, batches=8, per_batch=3):
+def host_cost(la, torch, inp, batches=8, per_batch=3, grid=0):
     """Host µs of one lean call through the Python binding while the GPU is
     still busy with the previous ones (the call only enqueues): median over
     `batches` bursts of `per_batch` calls, synchronised between bursts, with
@@ -161,7 +161,7 @@ def host_cost(la, torch, inp, batches=8, per_batch=3):
                     for i in range(per_batch):
                         la.la_decode_ex(inp.q, inp.k, inp.v, lens[i], inp.B, inp.H, inp.d,
                                         inp.scale, out, kv_heads=inp.Hk, q_tokens=inp.Nq,
-                                        host_tables=ht)
+                                        host_tables=ht, grid=grid)
                     t1 = time.perf_counter()
                     per_call.append((t1 - t0) * 1e6 / per_batch)
             torch.cuda.synchronize()
@@ -925,7 +925,7 @@ def measure(la, torch, evs, name, inp, args, cpu=True):
 
     host = None
     if not args.kernel_only:
-        host = host_cost(la, torch, inp)
+        host = host_cost(la, torch, inp, grid=Gu)
         log(f"[bench] {name}: host us per call: {host}")
 
     cpu_res = None
