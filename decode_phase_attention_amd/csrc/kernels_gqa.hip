@@ -126,16 +126,22 @@ struct GRegs {
     uint32_t vr[8][GGeo<D>::VW];        // keys 4w + r + 16sb (j = r + 4sb), dims [NB*c, NB*c + NB)
 };
 
+// Kinds of wave step: every key valid; keys from a lane's limit masked (the
+// last steps of a range); and keys before the range start masked too (the
+// first step of a range whose step grid starts before it, see gseg_start).
+constexpr int kStepFull = 0, kStepTail = 1, kStepEdge = 2;
+
 // Issue the loads of one wave step over keys [kb, kb + 32) of a head (rows of
-// kh/vh). With TAIL, loads stay below e.
-template <int D, bool TAIL>
+// kh/vh). A tail step keeps loads below e; an edge step keeps them in [lo, e).
+template <int D, int MODE>
 __device__ __forceinline__ void gqa_load(const char* __restrict__ kh, const char* __restrict__ vh,
-                                         int kb, int e, int w, int c, GRegs<D>& g) {
+                                         int kb, int lo, int e, int w, int c, GRegs<D>& g) {
     using G = GGeo<D>;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
         int key = kb + c + 16 * sb;
-        if constexpr (TAIL) key = min(key, e - 1);
+        if constexpr (MODE == kStepTail) key = min(key, e - 1);
+        if constexpr (MODE == kStepEdge) key = min(max(key, lo), e - 1);
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk)
             g.kr[sb][kk] = load16(kh + (uint64_t)((uint32_t)key * G::RB + (uint32_t)(w + 4 * kk) * 16u));
@@ -143,7 +149,8 @@ __device__ __forceinline__ void gqa_load(const char* __restrict__ kh, const char
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         int key = kb + 4 * w + (j & 3) + 16 * (j >> 2);
-        if constexpr (TAIL) key = min(key, e - 1);
+        if constexpr (MODE == kStepTail) key = min(key, e - 1);
+        if constexpr (MODE == kStepEdge) key = min(max(key, lo), e - 1);
         const char* src = vh + (uint64_t)((uint32_t)key * G::RB + (uint32_t)c * (G::NB * 2));
         if constexpr (G::VW == 4) {
             const u32x4_t x = load16(src);
@@ -156,11 +163,11 @@ __device__ __forceinline__ void gqa_load(const char* __restrict__ kh, const char
     }
 }
 
-// The arithmetic of one wave step on loaded registers. With TAIL, this lane's
-// query column masks keys >= lim. qt[kk] is the B operand of Q^T for head-dim
-// chunk kk.
-template <int DT, int D, bool TAIL>
-__device__ __forceinline__ void gqa_compute(const GRegs<D>& g, int kb, int lim, int w,
+// The arithmetic of one wave step on loaded registers. In a tail step this
+// lane's query column masks keys >= lim; an edge step also masks keys < lo.
+// qt[kk] is the B operand of Q^T for head-dim chunk kk.
+template <int DT, int D, int MODE>
+__device__ __forceinline__ void gqa_compute(const GRegs<D>& g, int kb, int lo, int lim, int w,
                                             const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
                                             GState<D>& st) {
     using G = GGeo<D>;
@@ -176,7 +183,11 @@ __device__ __forceinline__ void gqa_compute(const GRegs<D>& g, int kb, int lim, 
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float x = acc[r] * sl2e;
-                s[r + 4 * sb] = (!TAIL || kb + 4 * w + r + 16 * sb < lim) ? x : kNegInf;
+                const int key = kb + 4 * w + r + 16 * sb;
+                const bool ok = MODE == kStepFull ? true
+                              : MODE == kStepTail ? key < lim
+                                                  : (key >= lo && key < lim);
+                s[r + 4 * sb] = ok ? x : kNegInf;
             }
         }
     }
@@ -224,10 +235,11 @@ __device__ __forceinline__ void gqa_step(const char* __restrict__ kh, const char
                                          int kb, int e, int lim, int w, int c,
                                          const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
                                          GState<D>& st) {
+    constexpr int kMode = TAIL ? kStepTail : kStepFull;
     GRegs<D> g;
-    gqa_load<D, TAIL>(kh, vh, kb, e, w, c, g);
+    gqa_load<D, kMode>(kh, vh, kb, 0, e, w, c, g);
     __builtin_amdgcn_sched_barrier(0);   // all loads of the step in flight first
-    gqa_compute<DT, D, TAIL>(g, kb, lim, w, qt, sl2e, st);
+    gqa_compute<DT, D, kMode>(g, kb, 0, lim, w, qt, sl2e, st);
 }
 
 // Two full wave steps, keys [kb, kb + 32) and [kb + stride, +32): the loads of
@@ -239,11 +251,11 @@ __device__ __forceinline__ void gqa_step2(const char* __restrict__ kh, const cha
                                           const u32x4_t (&qt)[GGeo<D>::KK], float sl2e,
                                           GState<D>& st) {
     GRegs<D> g0, g1;
-    gqa_load<D, false>(kh, vh, kb, 0, w, c, g0);
-    gqa_load<D, false>(kh, vh, kb + stride, 0, w, c, g1);
+    gqa_load<D, kStepFull>(kh, vh, kb, 0, 0, w, c, g0);
+    gqa_load<D, kStepFull>(kh, vh, kb + stride, 0, 0, w, c, g1);
     __builtin_amdgcn_sched_barrier(0);
-    gqa_compute<DT, D, false>(g0, kb, 0, w, qt, sl2e, st);
-    gqa_compute<DT, D, false>(g1, kb + stride, 0, w, qt, sl2e, st);
+    gqa_compute<DT, D, kStepFull>(g0, kb, 0, 0, w, qt, sl2e, st);
+    gqa_compute<DT, D, kStepFull>(g1, kb + stride, 0, 0, w, qt, sl2e, st);
 }
 
 // Stream keys [a, e) of one K/V head for the 16 query columns of qt. Keys
@@ -523,34 +535,50 @@ __device__ __forceinline__ void fold_peers_spread(GSmem<D>& sm, __amdgpu_buffer_
 // ------------------------------------------------------------------ lean
 
 // A lean segment whose streaming has begun: its unit, key range and bounds,
-// the lane's query operands, and whether its first step is a tail step. The
-// first step's K/V loads sit in a GRegs issued with it.
+// the lane's query operands, where its step grid starts, and the kind of its
+// first step. The first step's K/V loads sit in a GRegs issued with it.
 template <int D>
 struct GSeg {
     Unit x;
     int tok0, tok1, full, lim;
-    bool tail0;
+    int base0;      // first step's key: tok0, or up to one 4 KiB block of K before it
+    int mode0;      // kStepFull, kStepTail or kStepEdge
     u32x4_t qt[GGeo<D>::KK];
 };
 
 // Set up segment `sg` and issue the loads of its first wave step into `g`.
+// The step grid starts where the K rows cross a 4 KiB address boundary: each
+// 16-key block of a wave's K loads (64 bytes of each of 16 rows per
+// instruction) then covers whole 4 KiB blocks. Measured with a plain read of
+// this load pattern at 4 GiB per K and V on MI355X, the rate depends on where
+// a block starts: 7.22 TB/s aligned, down to 6.94 TB/s at 5-11 rows past a
+// boundary. Packed caches put heads at arbitrary rows, so the grid is aligned
+// here; the keys of the first step before tok0 are masked and their loads
+// clamped into the segment.
 template <int D>
 __device__ __forceinline__ void gseg_start(const GqaArgs& a, const LeanSeg& sg, int wave, int w,
                                            int c, GSeg<D>& s, GRegs<D>& g) {
     using G = GGeo<D>;
+    constexpr int kAlignRows = 4096 / G::RB;     // 16 at d = 128, 32 at d = 64
     s.x = decode_unit(a, sg);
     s.tok0 = sg.t0 * a.L;
     s.tok1 = (int)min((int64_t)sg.t1 * a.L, (int64_t)s.x.n);
     col_bounds(a, s.x, c, s.tok1, s.full, s.lim);
-    s.tail0 = s.tok0 + G::CH > s.full;   // uniform: full depends on the unit only
-    load_qt<D>(a.q, c < s.x.geff ? col_row(a, s.x, c) : 0, c < s.x.geff, w, s.qt);
     const char* kc = reinterpret_cast<const char*>(a.k + s.x.kvrow0 * D);
     const char* vc = reinterpret_cast<const char*>(a.v + s.x.kvrow0 * D);
-    const int kb = s.tok0 + G::KEYS * wave;
-    if (!s.tail0)
-        gqa_load<D, false>(kc, vc, kb, s.tok1, w, c, g);
+    const uint32_t phase =
+        (uint32_t)(((uintptr_t)kc + (uint64_t)s.tok0 * G::RB) & 4095u) / G::RB;
+    s.base0 = s.tok0 - (int)min(phase, (uint32_t)(kAlignRows - 1));
+    // uniform: full depends on the unit only
+    s.mode0 = s.base0 < s.tok0 ? kStepEdge : (s.tok0 + G::CH > s.full ? kStepTail : kStepFull);
+    load_qt<D>(a.q, c < s.x.geff ? col_row(a, s.x, c) : 0, c < s.x.geff, w, s.qt);
+    const int kb = s.base0 + G::KEYS * wave;
+    if (s.mode0 == kStepFull)
+        gqa_load<D, kStepFull>(kc, vc, kb, s.tok0, s.tok1, w, c, g);
+    else if (s.mode0 == kStepTail)
+        gqa_load<D, kStepTail>(kc, vc, kb, s.tok0, s.tok1, w, c, g);
     else
-        gqa_load<D, true>(kc, vc, kb, s.tok1, w, c, g);
+        gqa_load<D, kStepEdge>(kc, vc, kb, s.tok0, s.tok1, w, c, g);
 }
 
 // Stream a started segment: its first step from the loaded `g`, then the rest.
@@ -558,12 +586,14 @@ template <int DT, int D>
 __device__ __forceinline__ void gseg_stream(const GqaArgs& a, const GSeg<D>& s, const GRegs<D>& g,
                                             int wave, int w, int c, GState<D>& st) {
     using G = GGeo<D>;
-    const int kb = s.tok0 + G::KEYS * wave;
-    if (!s.tail0)
-        gqa_compute<DT, D, false>(g, kb, s.lim, w, s.qt, a.sl2e, st);
+    const int kb = s.base0 + G::KEYS * wave;
+    if (s.mode0 == kStepFull)
+        gqa_compute<DT, D, kStepFull>(g, kb, s.tok0, s.lim, w, s.qt, a.sl2e, st);
+    else if (s.mode0 == kStepTail)
+        gqa_compute<DT, D, kStepTail>(g, kb, s.tok0, s.lim, w, s.qt, a.sl2e, st);
     else
-        gqa_compute<DT, D, true>(g, kb, s.lim, w, s.qt, a.sl2e, st);
-    gqa_range<DT, D>(a.k + s.x.kvrow0 * D, a.v + s.x.kvrow0 * D, s.tok0 + G::CH, s.tok1, s.full,
+        gqa_compute<DT, D, kStepEdge>(g, kb, s.tok0, s.lim, w, s.qt, a.sl2e, st);
+    gqa_range<DT, D>(a.k + s.x.kvrow0 * D, a.v + s.x.kvrow0 * D, s.base0 + G::CH, s.tok1, s.full,
                      s.lim, wave, w, c, s.qt, a.sl2e, st);
 }
 

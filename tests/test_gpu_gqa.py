@@ -272,3 +272,30 @@ def test_copied_lengths_and_tables_agree(la, B):
         for x, y in zip(a, b):
             np.testing.assert_array_equal(x, y)
     check(a, reference(inp), tag=f"B={B}")
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f16")])
+def test_step_grid_phase(la, d, dtype):
+    """The grouped lean kernel starts each segment's step grid at the 4 KiB
+    boundary of the K rows at or before the segment start, masking the keys of
+    the first step that precede it. Caches placed at every row offset within
+    4 KiB, with tiles and grids that start segments at many rows, must give the
+    oracle's result: a key counted twice or dropped at a segment start shows in
+    l and O."""
+    lens = [3, 130, 1000, 77, 515]
+    H, Hk = 8, 2
+    inp = W.make_custom(lens, H=H, d=d, dtype=dtype, seed=88, device="cuda", kv_heads=Hk)
+    ref = reference(inp)
+    rows = 4096 // (2 * d)
+    for r in range(rows):
+        kb = torch.zeros((inp.k.shape[0] + r, d), dtype=inp.k.dtype, device="cuda")
+        vb = torch.zeros_like(kb)
+        kb[r:].copy_(inp.k)
+        vb[r:].copy_(inp.v)
+        k, v = kb[r:], vb[r:]
+        assert k.is_contiguous() and (k.data_ptr() - kb.data_ptr()) == r * 2 * d
+        view = W.Inputs(q=inp.q, k=k, v=v, ctx_lens=lens, H=H, d=d, dtype=dtype,
+                        scale=inp.scale, seed=88, meta={"kv_heads": Hk})
+        for opts in ({"tile_tokens": 48, "grid": 37}, {"tile_tokens": 32, "grid": 5}, {}):
+            say(f"[gqa phase d={d} offset={r} rows {opts}]")
+            check(run(la, view, "lean", **opts), ref, tag=f"d={d}/offset={r}/{opts}")
