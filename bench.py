@@ -172,18 +172,33 @@ def host_cost(la, torch, inp, batches=8, per_batch=3, grid=0):
     return res
 
 
-def read_ceiling(la, torch, nbytes, reps=10):
+CEILING_MAX_BYTES = 16 << 30
+
+
+def ceiling_bytes_for(alg_bytes: int) -> int:
+    """Size of the streaming read set next to a workload of `alg_bytes`."""
+    return max(64 << 10, min(alg_bytes, CEILING_MAX_BYTES))
+
+
+def read_ceiling(la, torch, nbytes, reps=10, buf=None):
     """Achievable streaming-read bandwidth of this device in GB/s: the
-    library's plain read kernel (the attention kernels' access pattern, no
-    arithmetic) over an `nbytes` buffer, best of `reps` launches timed with
-    events on the launch stream (torch's current one). Short reads pay the same
-    launch ramp and tail as a short attention kernel, so the buffer is the
-    workload's own size: one workgroup per CU, or fewer when the buffer holds
-    less than the read kernel's 64 KiB per workgroup."""
+    library's plain read kernel (the attention kernels' loads, K-like and
+    V-like halves side by side, no arithmetic) over `nbytes` bytes, best of
+    `reps` launches timed with events on the launch stream (torch's current
+    one). Short reads pay the same launch ramp and tail as a short attention
+    kernel, and a long one amortises them as a long kernel does, so the read
+    is the workload's own size: one workgroup per CU, or fewer when the
+    buffer holds less than the read kernel's 64 KiB per workgroup. `buf`, a
+    uint8 device buffer of at least `nbytes` allocated beforehand, keeps the
+    allocation out of the timed phase."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     unit = 64 << 10
+    nbytes = max(nbytes, unit)
     grid = max(1, min(cus, nbytes // unit))
-    buf = torch.zeros(max(nbytes, unit), dtype=torch.uint8, device="cuda")
+    if buf is None:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    else:
+        buf = buf[:nbytes]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for _ in range(3):
         la.la_stream_read(buf, sink, grid=grid)
@@ -766,12 +781,20 @@ def main():
     for n in names:
         log(f"[bench] generating {n} (seed {args.seed})")
         inputs[n] = W.make_inputs(n, seed=args.seed, device="cuda")
+    # the streaming-read ceiling's buffer too, sized for the largest workload
+    read_buf = None
+    if not args.kernel_only:
+        need = max(ceiling_bytes_for(W.algorithmic_bytes(inp.ctx_lens, inp.H, inp.d,
+                                                         kv_heads=inp.Hk, q_tokens=inp.Nq))
+                   for inp in inputs.values())
+        read_buf = torch.zeros(need, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     head = measure(la, torch, evs, args.workload, inputs[args.workload], args,
-                   cpu=not args.no_cpu_baseline)
+                   cpu=not args.no_cpu_baseline, read_buf=read_buf)
     extra = {}
     for n in names[1:]:
-        extra[n] = measure(la, torch, evs, n, inputs[n], args, cpu=not args.no_cpu_baseline)
+        extra[n] = measure(la, torch, evs, n, inputs[n], args, cpu=not args.no_cpu_baseline,
+                           read_buf=read_buf)
     lean = head.pop("_lean")
     rec = {
         "metric": METRIC,
@@ -853,7 +876,7 @@ def method_overhead(la, inp, units, L, G, d, cols, alg_bytes):
     }
 
 
-def measure(la, torch, evs, name, inp, args, cpu=True):
+def measure(la, torch, evs, name, inp, args, cpu=True, read_buf=None):
     """Every measurement of one workload: the lean kernel (host-observed µs per
     step and kernel µs from events), its roofline against 8 TB/s and against
     the device's streaming-read rate at the same size, the committed HBM
@@ -886,7 +909,8 @@ def measure(la, torch, evs, name, inp, args, cpu=True):
 
     ceiling = ceiling_bytes = ceiling_grid = None
     if not args.kernel_only:
-        ceiling, ceiling_bytes, ceiling_grid = read_ceiling(la, torch, min(alg_bytes, 4 << 30))
+        ceiling, ceiling_bytes, ceiling_grid = read_ceiling(la, torch, ceiling_bytes_for(alg_bytes),
+                                                            buf=read_buf)
         log(f"[bench] {name}: streaming-read ceiling over {ceiling_bytes} bytes "
             f"({ceiling_grid} workgroups): {ceiling:.1f} GB/s")
 

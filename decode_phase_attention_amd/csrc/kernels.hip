@@ -13,15 +13,18 @@
 //   per_head_kernel  one workgroup per (request, head) over its whole context
 //                    (the FlashAttention-2 decode mapping, §2.2)
 //
-// Streaming routine. A K or V row of d halves is d/8 lanes x 16 bytes, so
-// d/8 consecutive lanes form a "lane group" that owns one row per load. Each
-// group keeps its own online-softmax state (m, l, Obar slice of 8 dims) over
-// the rows it sees (§3.3: update the statistics per tile, then
-// O_acc = P V + diag(rescale) O_acc). Scores are reduced across the group's
-// lanes with DPP; no barrier or LDS traffic happens inside a range. Decode
-// attention has a single query row, so K and V elements are each used by one
-// lane exactly once: they go straight from HBM to registers with 16-byte
-// loads and are never staged in LDS. Only at the end of a range do the
+// Streaming routine. A K or V row of d halves is d/8 pieces of 16 bytes. V
+// rows are read whole by "lane groups" of d/8 consecutive lanes, each lane one
+// piece, and each group keeps its own online-softmax state (m, l, Obar slice
+// of 8 dims) over the rows it accumulates (§3.3: update the statistics per
+// tile, then O_acc = P V + diag(rescale) O_acc). K rows are read with another
+// pattern -- 64 bytes of each of 16 rows per instruction, four lanes per row
+// -- because K and V streamed side by side in the same pattern read slower
+// (see stream_step); the four lanes of a K row add their partial dot products
+// across the wave, and each wave hands its scores to its V lane groups
+// through a small slice of LDS. Decode attention has a single query row, so K
+// and V elements are each used once: they go straight from HBM to registers
+// with 16-byte loads and are not staged in LDS. At the end of a range the
 // groups meet in LDS, where the reduction f (§3.2) folds them into one
 // (m, l, Obar[d]).
 //
@@ -109,63 +112,119 @@ __device__ __forceinline__ void acc_init(Acc& a) {
 
 template <int D>
 struct Geo {
-    static constexpr int LPR = D / 8;                 // lanes per row
+    static constexpr int LPR = D / 8;                 // lanes per row (16-byte pieces of a row)
     static constexpr int GPW = 64 / LPR;              // groups per wave
     static constexpr int NG = GPW * kWaves;           // groups per workgroup
-    static constexpr int CH = NG * kRows;             // rows per step
+    static constexpr int CH = NG * kRows;             // rows per step (workgroup)
+    static constexpr int RW = GPW * kRows;            // rows per step (wave): 32 or 64
+    static constexpr int SB = RW / 16;                // K: blocks of 16 rows per wave step
+    static constexpr int KK = LPR / 4;                // K: 16-byte pieces of a row per lane
+    static constexpr uint32_t RB = D * 2;             // bytes per row
 };
 
-// One step of the streaming loop: kRows rows per lane group, K and V loads
-// issued back to back, then scores, one rescale, and the V accumulation.
-// Row r of group g in a step starting at `base` is base + r*NG + g, so one
-// load instruction of a wave reads GPW consecutive rows (1 KiB contiguous).
-// Full steps address rows as (uniform base) + (fixed 32-bit lane offset); the
-// last, partial step clamps rows at or past e to e-1 (never reading outside
-// the head) and masks their scores to -inf.
-template <int DT, int D, bool TAIL>
+// One step of the streaming loop over the RW rows [kb, kb + RW) of this wave
+// (a workgroup step covers CH = 4 RW rows, wave w taking the w-th block).
+// K and V are read with different patterns, because they are read side by
+// side and their patterns interact: measured with a plain read of 512k's K
+// and V on MI355X, K read as 64 bytes of each of 16 rows per instruction next
+// to V read as contiguous 1 KiB streams at 7.27 TB/s with all XCDs equally
+// fast, where both read contiguously stream at 7.0 TB/s with the odd XCDs
+// ~8% slower, and both read as 64-byte pieces at 6.15 TB/s.
+//   K: lane (w, c) = (lane / 16, lane % 16) loads 16-byte pieces w + 4 kk
+//      (kk < KK) of rows kb + c + 16 sb (sb < SB) and dots them with the same
+//      pieces of q; the four lanes w of a row add their parts (two exchanges
+//      across 16-lane rows), so every lane ends with the full scores of its
+//      rows c + 16 sb.
+//   V: lane group g = lane / LPR takes rows kb + GPW i + g (i < kRows), each
+//      lane a 16-byte piece `sub` of the row, so one instruction reads GPW
+//      whole rows (1 KiB contiguous). The group's scores come from the
+//      wave's slice of LDS, where the K lanes leave them.
+// Each lane group keeps its own online-softmax state (m, l, Obar of its 8
+// dims) over the rows it accumulates. A tail step (the last, partial one)
+// clamps rows at or past e to e-1, never reading outside the head, and masks
+// their scores to -inf; an edge step (the first one of a range whose step
+// grid starts before it, see stream_range) also clamps rows before lo to lo
+// and masks them.
+constexpr int kStepFull = 0, kStepTail = 1, kStepEdge = 2;
+constexpr int kAlignMinSteps = 4;
+
+template <int DT, int D, int MODE>
 __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const char* __restrict__ vh,
-                                            int base, int e, uint32_t lane_off, const uint4 qv,
-                                            float sl2e, int grp, Acc& acc) {
+                                            int kb, int lo, int e, const uint4 (&qk)[Geo<D>::KK],
+                                            float sl2e, float* sx, Acc& acc) {
     using G = Geo<D>;
-    constexpr uint32_t kRowBytes = D * 2;
-    constexpr uint32_t kStepRowBytes = G::NG * kRowBytes;
-    uint4 kr[kRows], vr[kRows];
-    if constexpr (!TAIL) {
-        const uint32_t off = (uint32_t)base * kRowBytes + lane_off;
+    const int lane = threadIdx.x & 63;
+    const int w = lane >> 4, c = lane & 15;
+    const int gw = lane / G::LPR, sub = lane % G::LPR;
+    uint4 kr[G::SB][G::KK], vr[kRows];
+    if constexpr (MODE == kStepFull) {
+        const uint32_t koff = (uint32_t)kb * G::RB + (uint32_t)c * G::RB + (uint32_t)w * 16u;
+        const uint32_t voff = (uint32_t)kb * G::RB + (uint32_t)lane * 16u;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) kr[r] = load_nt(kh + (uint64_t)(off + r * kStepRowBytes));
+        for (int sb = 0; sb < G::SB; ++sb)
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) vr[r] = load_nt(vh + (uint64_t)(off + r * kStepRowBytes));
+            for (int kk = 0; kk < G::KK; ++kk)
+                kr[sb][kk] = load_nt(kh + (uint64_t)(koff + (uint32_t)sb * 16u * G::RB + kk * 64u));
+#pragma unroll
+        for (int i = 0; i < kRows; ++i)
+            vr[i] = load_nt(vh + (uint64_t)(voff + (uint32_t)i * G::GPW * G::RB));
     } else {
-        const uint32_t col_off = lane_off - (uint32_t)grp * kRowBytes;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
-            kr[r] = load_nt(kh + (uint64_t)(j * kRowBytes + col_off));
+        for (int sb = 0; sb < G::SB; ++sb) {
+            int r = min(kb + c + 16 * sb, e - 1);
+            if constexpr (MODE == kStepEdge) r = max(r, lo);
+            const uint32_t j = (uint32_t)r;
+#pragma unroll
+            for (int kk = 0; kk < G::KK; ++kk)
+                kr[sb][kk] = load_nt(kh + (uint64_t)(j * G::RB + (uint32_t)(w + 4 * kk) * 16u));
         }
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
-            vr[r] = load_nt(vh + (uint64_t)(j * kRowBytes + col_off));
+        for (int i = 0; i < kRows; ++i) {
+            int r = min(kb + G::GPW * i + gw, e - 1);
+            if constexpr (MODE == kStepEdge) r = max(r, lo);
+            const uint32_t j = (uint32_t)r;
+            vr[i] = load_nt(vh + (uint64_t)(j * G::RB + (uint32_t)sub * 16u));
         }
     }
-    // Keep all 2*kRows loads of the step in flight before any of them is
+    // Keep all the loads of the step in flight before any of them is
     // consumed; without this the scheduler interleaves loads with the math
     // and fewer bytes are outstanding per wave.
     __builtin_amdgcn_sched_barrier(0);
-    float s[kRows];
-    float mx = kNegInf;
     {
         // The scaled score is rounded once and that same value feeds both the
         // max and exp2(s - m): no contraction of the product into the
-        // subtraction, so the maximal row gets weight exactly 1.
+        // subtraction, so the maximal row gets weight exactly 1. The four
+        // parts of a row are added as (w + w^1) + (w^2 + w^3) in every lane,
+        // so all four lanes hold the same bits.
 #pragma clang fp contract(off)
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const float x = group_sum<G::LPR>(dot8<DT>(kr[r], qv)) * sl2e;
-            s[r] = (!TAIL || base + r * G::NG + grp < e) ? x : kNegInf;
-            mx = fmaxf(mx, s[r]);
+        for (int sb = 0; sb < G::SB; ++sb) {
+            float x = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < G::KK; ++kk) x += dot8<DT>(kr[sb][kk], qk[kk]);
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            // row r = c + 16 sb goes to slot (r % GPW) kRows + r / GPW, where
+            // group r % GPW finds its rows in order
+            const int r = c + 16 * sb;
+            if (w == 0) sx[(r % G::GPW) * kRows + r / G::GPW] = x * sl2e;
         }
+    }
+    __builtin_amdgcn_wave_barrier();
+    float s[kRows];
+    {
+        const float4* src = reinterpret_cast<const float4*>(sx + gw * kRows);
+        const float4 s0 = src[0], s1 = src[1];
+        s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
+        s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int r = kb + G::GPW * i + gw;
+        if (MODE != kStepFull && (r >= e || (MODE == kStepEdge && r < lo))) s[i] = kNegInf;
+        mx = fmaxf(mx, s[i]);
     }
     const float mn = fmaxf(acc.m, mx);
     const float mu = (mn == kNegInf) ? 0.f : mn;   // no -inf - -inf
@@ -188,20 +247,44 @@ __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const c
     acc.m = mn;
 }
 
-// Stream rows [a, e) of one head (kh/vh point at its row 0) through the lane
-// group's online softmax. A head spans less than 4 GiB, so every offset
-// inside it fits in 32 bits.
+// Stream rows [a, e) of one head (kh/vh point at its row 0, qh at its query
+// row) through the lane groups' online softmax; sx is the wave's slice of
+// the score exchange in LDS (Geo<D>::RW floats). A head spans less than
+// 4 GiB, so every offset inside it fits in 32 bits.
+// The step grid starts at the 4 KiB boundary of the K rows at or before row
+// a, so that every 16-row block of K loads covers whole 4 KiB blocks: the K
+// pattern reads fastest so (measured with a plain read of this pattern on
+// MI355X: 7.2-7.3 TB/s aligned, about 3% less at 5-11 rows past a boundary),
+// and packed ragged caches put heads at arbitrary rows. The first step then
+// masks the rows before a. Where that adds a step to a range shorter than
+// kAlignMinSteps steps, the grid starts at a instead: a short range is bound
+// by the latency of its steps, not by the rate of its reads (tiny, 1024
+// tokens a head: 9.7 us unaligned against 11.0 us aligned).
 template <int DT, int D>
 __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t* vh, int a, int e,
-                                             const uint4 qv, float sl2e, int grp, int sub, Acc& acc) {
+                                             const uint16_t* qh, float sl2e, float* sx, Acc& acc) {
     using G = Geo<D>;
-    const uint32_t lane_off = (uint32_t)(grp * D + sub * 8) * 2u;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint4 qk[G::KK];
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk)
+        qk[kk] = *reinterpret_cast<const uint4*>(qh + ((lane >> 4) + 4 * kk) * 8);
     const char* kc = reinterpret_cast<const char*>(kh);
     const char* vc = reinterpret_cast<const char*>(vh);
-    int base = a;
+    constexpr uint32_t kAlignRows = 4096 / G::RB;   // 16 at d = 128, 32 at d = 64
+    const uint32_t phase = (uint32_t)(((uintptr_t)kc + (uint64_t)(uint32_t)a * G::RB) & 4095u) / G::RB;
+    int base = a - (int)min(phase, kAlignRows - 1);
+    if (base < a && e - a < kAlignMinSteps * G::CH &&
+        (e - base + G::CH - 1) / G::CH > (e - a + G::CH - 1) / G::CH)
+        base = a;
+    if (base < a && a < e) {
+        stream_step<DT, D, kStepEdge>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
+        base += G::CH;
+    }
     for (; base + G::CH <= e; base += G::CH)
-        stream_step<DT, D, false>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
-    if (base < e) stream_step<DT, D, true>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
+        stream_step<DT, D, kStepFull>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
+    if (base < e) stream_step<DT, D, kStepTail>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
 }
 
 template <int D>
@@ -209,6 +292,7 @@ struct alignas(16) Smem {
     float o[Geo<D>::NG][D];
     float m[Geo<D>::NG];
     float l[Geo<D>::NG];
+    float sx[kWaves][Geo<D>::RW];   // per wave: the scores of its step, for its V lanes
 };
 
 // Dims of the output each lane of wave 0 holds after a fold: lane i holds
@@ -255,9 +339,6 @@ __device__ __forceinline__ void wg_fold(Smem<D>& sm, const Acc& a, int grp, int 
     __syncthreads();
 }
 
-__device__ __forceinline__ uint4 load_q(const uint16_t* q, int u, int D, int sub) {
-    return *reinterpret_cast<const uint4*>(q + (int64_t)u * D + sub * 8);
-}
 
 // Wave 0 writes out = Obar / l (and m in natural-log units, l) for head u.
 template <int D>
@@ -303,8 +384,8 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         const int tok1 = (int)min((int64_t)sg.t1 * a.L, (int64_t)n);
         Acc acc;
         acc_init(acc);
-        stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, load_q(a.q, u, D, sub),
-                            a.sl2e, grp, sub, acc);
+        stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, a.q + (int64_t)u * D,
+                            a.sl2e, sm.sx[t >> 6], acc);
         if (a.tile_owner != nullptr && t == 0)
             for (int i = sg.t0; i < sg.t1; ++i) a.tile_owner[sg.iter0 + i - sg.t0] = c;
 
@@ -467,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
             Acc acc;
             acc_init(acc);
             stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1,
-                                load_q(a.q, u, D, sub), a.sl2e, grp, sub, acc);
+                                a.q + (int64_t)u * D, a.sl2e, sm.sx[t >> 6], acc);
             if (a.tile_owner != nullptr)
                 for (int i = it + t; i < t1; i += kThreads) a.tile_owner[i] = blockIdx.x;
             float M = kNegInf, Ls = 0.f, O[P];
@@ -553,8 +634,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     Acc acc;
     acc_init(acc);
     if (tok0 < tok1)
-        stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, load_q(a.q, u, D, sub),
-                            a.sl2e, grp, sub, acc);
+        stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, a.q + (int64_t)u * D,
+                            a.sl2e, sm.sx[t >> 6], acc);
     float M = kNegInf, Ls = 0.f, O[P];
     wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
     if (t >= 64) return;
@@ -605,35 +686,49 @@ __global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
     const int64_t row0 = head_row0(a.kv_stride, a.H, b, h, a.tok_off[b], n);
     Acc acc;
     acc_init(acc);
-    stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, 0, n, load_q(a.q, u, D, sub), a.sl2e,
-                        grp, sub, acc);
+    stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, 0, n, a.q + (int64_t)u * D, a.sl2e,
+                        sm.sx[t >> 6], acc);
     float M = kNegInf, Ls = 0.f, O[kDpl<D>];
     wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
     if (t < 64) write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
     stamp_end(a.ts, blockIdx.x);
 }
 
-// The achievable streaming-read bandwidth of the device, for measurement: each
-// workgroup reads one contiguous chunk with kReadDepth non-temporal 16-byte
-// loads per lane in flight, the access pattern of the attention kernels
-// without their arithmetic. The data are folded into one word so the loads
-// stay; the word is stored only in the (practically impossible) case that it
-// equals a fixed pattern.
-constexpr int kReadDepth = 16;
+// The achievable streaming-read bandwidth of the device, for measurement: the
+// loads of the attention kernels without their arithmetic. Each workgroup
+// reads one contiguous chunk as two halves side by side, a "K" half and a
+// "V" half, in trips of 32 KiB per half (8 KiB per wave): K as 64 bytes of
+// each of 16 rows of 256 bytes per instruction, V as contiguous 1 KiB per
+// instruction, 16 non-temporal 16-byte loads per lane in flight -- the load
+// pattern of a d = 128 streaming step. The data are folded into one word so
+// the loads stay; the word is stored only in the (practically impossible)
+// case that it equals a fixed pattern.
+constexpr int kReadTrip = 64 << 10;   // bytes per workgroup trip, both halves
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* src, uint64_t chunk,
                                                                 uint32_t* sink) {
-    const char* base = src + blockIdx.x * chunk;
-    constexpr uint64_t kStride = (uint64_t)kReadDepth * kThreads * 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int w = lane >> 4, c = lane & 15;
+    const uint64_t half = chunk / 2;
+    const char* kb = src + blockIdx.x * chunk + (uint64_t)wave * 8192u;
+    const char* vb = kb + half;
+    const uint32_t koff = (uint32_t)c * 256u + (uint32_t)w * 16u;
+    const uint32_t voff = (uint32_t)lane * 16u;
     u32x4_t acc = {0u, 0u, 0u, 0u};
-    for (uint64_t off = threadIdx.x * 16ull; off < chunk; off += kStride) {
-        u32x4_t v[kReadDepth];
+    for (uint64_t off = 0; off < half; off += kReadTrip / 2) {
+        u32x4_t v[16];
 #pragma unroll
-        for (int k = 0; k < kReadDepth; ++k)
-            v[k] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t*>(base + off + (uint64_t)k * kThreads * 16));
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                v[4 * sb + kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                    kb + off + koff + (uint32_t)sb * 4096u + (uint32_t)kk * 64u));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[8 + i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(vb + off + voff + (uint32_t)i * 1024u));
         __builtin_amdgcn_sched_barrier(0);   // all loads of the trip in flight first
 #pragma unroll
-        for (int k = 0; k < kReadDepth; ++k) acc ^= v[k];
+        for (int k = 0; k < 16; ++k) acc ^= v[k];
     }
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) sink[0] = 1u;
 }
@@ -666,7 +761,7 @@ hipError_t launch_lean(int dtype, int d, const LeanArgs& a, int grid, hipStream_
     return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
-uint64_t stream_read_unit() { return (uint64_t)kReadDepth * kThreads * 16; }
+uint64_t stream_read_unit() { return (uint64_t)kReadTrip; }
 
 hipError_t launch_stream_read(const void* src, uint64_t chunk, int grid, uint32_t* sink,
                               hipStream_t s) {

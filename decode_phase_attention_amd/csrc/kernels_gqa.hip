@@ -130,6 +130,7 @@ struct GRegs {
 // last steps of a range); and keys before the range start masked too (the
 // first step of a range whose step grid starts before it, see gseg_start).
 constexpr int kStepFull = 0, kStepTail = 1, kStepEdge = 2;
+constexpr int kAlignMinSteps = 4;
 
 // Issue the loads of one wave step over keys [kb, kb + 32) of a head (rows of
 // kh/vh). A tail step keeps loads below e; an edge step keeps them in [lo, e).
@@ -554,7 +555,9 @@ struct GSeg {
 // a block starts: 7.22 TB/s aligned, down to 6.94 TB/s at 5-11 rows past a
 // boundary. Packed caches put heads at arbitrary rows, so the grid is aligned
 // here; the keys of the first step before tok0 are masked and their loads
-// clamped into the segment.
+// clamped into the segment. A segment shorter than kAlignMinSteps steps
+// keeps its grid at tok0 where aligning would add a step: its time is the
+// latency of its steps, not the rate of its reads.
 template <int D>
 __device__ __forceinline__ void gseg_start(const GqaArgs& a, const LeanSeg& sg, int wave, int w,
                                            int c, GSeg<D>& s, GRegs<D>& g) {
@@ -569,6 +572,9 @@ __device__ __forceinline__ void gseg_start(const GqaArgs& a, const LeanSeg& sg, 
     const uint32_t phase =
         (uint32_t)(((uintptr_t)kc + (uint64_t)s.tok0 * G::RB) & 4095u) / G::RB;
     s.base0 = s.tok0 - (int)min(phase, (uint32_t)(kAlignRows - 1));
+    if (s.tok1 - s.tok0 < kAlignMinSteps * G::CH &&
+        (s.tok1 - s.base0 + G::CH - 1) / G::CH > (s.tok1 - s.tok0 + G::CH - 1) / G::CH)
+        s.base0 = s.tok0;
     // uniform: full depends on the unit only
     s.mode0 = s.base0 < s.tok0 ? kStepEdge : (s.tok0 + G::CH > s.full ? kStepTail : kStepFull);
     load_qt<D>(a.q, c < s.x.geff ? col_row(a, s.x, c) : 0, c < s.x.geff, w, s.qt);

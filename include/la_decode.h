@@ -405,11 +405,14 @@ void la_set_wait_limit_us(uint32_t us);
 
 /*
  * Measurement aid, not part of attention: reads the device buffer `src`
- * (16-byte aligned, `bytes` long) once on `stream` with the access pattern
- * of the attention kernels (each of `grid` workgroups streams one contiguous
- * chunk with 16 non-temporal 16-byte loads per lane in flight) and nothing
- * else, so that the achievable read bandwidth of the device can be set next
- * to the attention kernels' (the peak of the data sheet is not reachable).
+ * (16-byte aligned, `bytes` long) once on `stream` with the load pattern of
+ * the attention kernels and nothing else, so that the achievable read
+ * bandwidth of the device can be set next to the attention kernels' (the
+ * peak of the data sheet is not reachable). Each of `grid` workgroups reads
+ * one contiguous chunk as two halves side by side, like a K and a V cache:
+ * the first half as 64 bytes of each of 16 rows of 256 bytes per wave
+ * instruction, the second as contiguous 1 KiB per wave instruction, with 16
+ * non-temporal 16-byte loads per lane in flight.
  * grid 0 = one workgroup per CU. Reads the largest multiple of 64 KiB per
  * workgroup that fits; that byte count is stored in *bytes_read. `sink` is a
  * device word that the kernel may write (it only keeps the loads from being
