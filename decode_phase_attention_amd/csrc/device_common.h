@@ -24,6 +24,34 @@ __device__ __forceinline__ uint4 load_nt(const char* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Butterflies across the 16-lane rows of a wave on gfx950's row-swap
+// instructions, without the LDS round trip of a lane shuffle. A swap of x with
+// itself leaves both lanes of every pair (l, l ^ 16), or (l, l ^ 32), with the
+// lower lane's value first and the upper lane's second (checked on MI355X), so
+// combining the two gives the same bits in both lanes.
+__device__ __forceinline__ float2 pair16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return make_float2(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float2 pair32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return make_float2(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+// x summed over lanes (l, l ^ 16, l ^ 32, l ^ 48) as (x_l + x_l^16) + (...),
+// and the maximum over the same four lanes; every one of them gets the same bits.
+__device__ __forceinline__ float sum_xor16_32(float x) {
+    float2 p = pair16(x);
+    p = pair32(p.x + p.y);
+    return p.x + p.y;
+}
+__device__ __forceinline__ float max_xor16_32(float x) {
+    float2 p = pair16(x);
+    p = pair32(fmaxf(p.x, p.y));
+    return fmaxf(p.x, p.y);
+}
+
 // f applied to a running (M, Ls, O) and one more record (pm, pl, po).
 template <int N>
 __device__ __forceinline__ void merge_into(float& M, float& Ls, float (&O)[N], float pm, float pl,

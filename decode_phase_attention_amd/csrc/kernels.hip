@@ -17,12 +17,14 @@
 // rows are read whole by "lane groups" of d/8 consecutive lanes, each lane one
 // piece, and each group keeps its own online-softmax state (m, l, Obar slice
 // of 8 dims) over the rows it accumulates (§3.3: update the statistics per
-// tile, then O_acc = P V + diag(rescale) O_acc). K rows are read with another
-// pattern -- 64 bytes of each of 16 rows per instruction, four lanes per row
-// -- because K and V streamed side by side in the same pattern read slower
-// (see stream_step); the four lanes of a K row add their partial dot products
-// across the wave, and each wave hands its scores to its V lane groups
-// through a small slice of LDS. Decode attention has a single query row, so K
+// tile, then O_acc = P V + diag(rescale) O_acc). In long ranges K rows are
+// read with another pattern -- 64 bytes of each of 16 rows per instruction,
+// four lanes per row -- because K and V streamed side by side in the same
+// pattern read slower (see stream_step); the four lanes of a K row add their
+// partial dot products across the wave, and each wave hands its scores to its
+// V lane groups through a small slice of LDS. Short ranges read K like V, by
+// lane groups, for the lower latency of each step (see stream_range and
+// stream_step_rows). Decode attention has a single query row, so K
 // and V elements are each used once: they go straight from HBM to registers
 // with 16-byte loads and are not staged in LDS. At the end of a range the
 // groups meet in LDS, where the reduction f (§3.2) folds them into one
@@ -122,6 +124,78 @@ struct Geo {
     static constexpr uint32_t RB = D * 2;             // bytes per row
 };
 
+// One step over rows in the contiguous pattern, for short ranges: kRows rows
+// per lane group, K and V loads issued back to back, then scores, one
+// rescale, and the V accumulation. Row r of group g (of the workgroup's NG)
+// in a step starting at `base` is base + r*NG + g, so one load instruction of
+// a wave reads GPW consecutive rows (1 KiB contiguous) of K and of V. Full
+// steps address rows as (uniform base) + (fixed 32-bit lane offset); the
+// last, partial step clamps rows at or past e to e-1 (never reading outside
+// the head) and masks their scores to -inf. Scores are summed within the lane
+// group by DPP, with no LDS traffic, which keeps a step's latency low.
+template <int DT, int D, bool TAIL>
+__device__ __forceinline__ void stream_step_rows(const char* __restrict__ kh,
+                                                 const char* __restrict__ vh, int base, int e,
+                                                 uint32_t lane_off, const uint4 qv, float sl2e,
+                                                 int grp, Acc& acc) {
+    using G = Geo<D>;
+    constexpr uint32_t kStepRowBytes = G::NG * G::RB;
+    uint4 kr[kRows], vr[kRows];
+    if constexpr (!TAIL) {
+        const uint32_t off = (uint32_t)base * G::RB + lane_off;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) kr[r] = load_nt(kh + (uint64_t)(off + r * kStepRowBytes));
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) vr[r] = load_nt(vh + (uint64_t)(off + r * kStepRowBytes));
+    } else {
+        const uint32_t col_off = lane_off - (uint32_t)grp * G::RB;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
+            kr[r] = load_nt(kh + (uint64_t)(j * G::RB + col_off));
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
+            vr[r] = load_nt(vh + (uint64_t)(j * G::RB + col_off));
+        }
+    }
+    // all 2*kRows loads of the step in flight before any is consumed
+    __builtin_amdgcn_sched_barrier(0);
+    float s[kRows];
+    float mx = kNegInf;
+    {
+        // one rounding of the scaled score feeds both the max and exp2(s - m),
+        // so the maximal row gets weight exactly 1
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const float x = group_sum<G::LPR>(dot8<DT>(kr[r], qv)) * sl2e;
+            s[r] = (!TAIL || base + r * G::NG + grp < e) ? x : kNegInf;
+            mx = fmaxf(mx, s[r]);
+        }
+    }
+    const float mn = fmaxf(acc.m, mx);
+    const float mu = (mn == kNegInf) ? 0.f : mn;   // no -inf - -inf
+    const float alpha = fexp2(acc.m - mu);
+    acc.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc.o[i] *= alpha;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const float p = fexp2(s[r] - mu);
+        acc.l += p;
+        float f[8];
+        widen2<DT>(vr[r].x, f[0], f[1]);
+        widen2<DT>(vr[r].y, f[2], f[3]);
+        widen2<DT>(vr[r].z, f[4], f[5]);
+        widen2<DT>(vr[r].w, f[6], f[7]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc.o[i] = fmaf(p, f[i], acc.o[i]);
+    }
+    acc.m = mn;
+}
+
 // One step of the streaming loop over the RW rows [kb, kb + RW) of this wave
 // (a workgroup step covers CH = 4 RW rows, wave w taking the w-th block).
 // K and V are read with different patterns, because they are read side by
@@ -146,7 +220,7 @@ struct Geo {
 // grid starts before it, see stream_range) also clamps rows before lo to lo
 // and masks them.
 constexpr int kStepFull = 0, kStepTail = 1, kStepEdge = 2;
-constexpr int kAlignMinSteps = 4;
+constexpr int kBlockMinSteps = 8;
 
 template <int DT, int D, int MODE>
 __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const char* __restrict__ vh,
@@ -202,8 +276,7 @@ __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const c
             float x = 0.f;
 #pragma unroll
             for (int kk = 0; kk < G::KK; ++kk) x += dot8<DT>(kr[sb][kk], qk[kk]);
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
+            x = sum_xor16_32(x);
             // row r = c + 16 sb goes to slot (r % GPW) kRows + r / GPW, where
             // group r % GPW finds its rows in order
             const int r = c + 16 * sb;
@@ -251,34 +324,48 @@ __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const c
 // row) through the lane groups' online softmax; sx is the wave's slice of
 // the score exchange in LDS (Geo<D>::RW floats). A head spans less than
 // 4 GiB, so every offset inside it fits in 32 bits.
-// The step grid starts at the 4 KiB boundary of the K rows at or before row
-// a, so that every 16-row block of K loads covers whole 4 KiB blocks: the K
-// pattern reads fastest so (measured with a plain read of this pattern on
-// MI355X: 7.2-7.3 TB/s aligned, about 3% less at 5-11 rows past a boundary),
-// and packed ragged caches put heads at arbitrary rows. The first step then
-// masks the rows before a. Where that adds a step to a range shorter than
-// kAlignMinSteps steps, the grid starts at a instead: a short range is bound
-// by the latency of its steps, not by the rate of its reads (tiny, 1024
-// tokens a head: 9.7 us unaligned against 11.0 us aligned).
+//
+// The two step routines suit different ranges. A long range is bound by the
+// rate of its reads, and reads K fastest in 16-row blocks (stream_step);
+// a short one is bound by the latency of its few steps, which is lower with
+// contiguous rows and DPP sums (stream_step_rows). Measured on MI355X: 512k
+// (ranges of 1024 steps) 1211 us contiguous against 1182 us in 16-row blocks;
+// 4096 heads of 2 steps 84 us against 94 us; one uncontended workgroup
+// streams 55 GB/s contiguous against 39 GB/s in 16-row blocks. Ranges of at
+// least kBlockMinSteps steps take the 16-row blocks.
+//
+// In 16-row blocks, the step grid starts at the 4 KiB boundary of the K rows
+// at or before row a, so that every 16-row block of K loads covers whole 4 KiB
+// blocks: the pattern reads fastest so (measured with a plain read of this
+// pattern on MI355X: 7.2-7.3 TB/s aligned, about 3% less at 5-11 rows past a
+// boundary), and packed ragged caches put heads at arbitrary rows. The first
+// step then masks the rows before a.
 template <int DT, int D>
 __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t* vh, int a, int e,
                                              const uint16_t* qh, float sl2e, float* sx, Acc& acc) {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const char* kc = reinterpret_cast<const char*>(kh);
+    const char* vc = reinterpret_cast<const char*>(vh);
+    if (e - a < kBlockMinSteps * G::CH) {
+        const int grp = wave * G::GPW + lane / G::LPR, sub = lane % G::LPR;
+        const uint4 qv = *reinterpret_cast<const uint4*>(qh + sub * 8);
+        const uint32_t lane_off = (uint32_t)(grp * D + sub * 8) * 2u;
+        int base = a;
+        for (; base + G::CH <= e; base += G::CH)
+            stream_step_rows<DT, D, false>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
+        if (base < e) stream_step_rows<DT, D, true>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
+        return;
+    }
     uint4 qk[G::KK];
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk)
         qk[kk] = *reinterpret_cast<const uint4*>(qh + ((lane >> 4) + 4 * kk) * 8);
-    const char* kc = reinterpret_cast<const char*>(kh);
-    const char* vc = reinterpret_cast<const char*>(vh);
     constexpr uint32_t kAlignRows = 4096 / G::RB;   // 16 at d = 128, 32 at d = 64
     const uint32_t phase = (uint32_t)(((uintptr_t)kc + (uint64_t)(uint32_t)a * G::RB) & 4095u) / G::RB;
     int base = a - (int)min(phase, kAlignRows - 1);
-    if (base < a && e - a < kAlignMinSteps * G::CH &&
-        (e - base + G::CH - 1) / G::CH > (e - a + G::CH - 1) / G::CH)
-        base = a;
-    if (base < a && a < e) {
+    if (base < a) {
         stream_step<DT, D, kStepEdge>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
         base += G::CH;
     }

@@ -196,8 +196,7 @@ __device__ __forceinline__ void gqa_compute(const GRegs<D>& g, int kb, int lo, i
     float mx = s[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mx = fmaxf(mx, s[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor16_32(mx);
     const float mn = fmaxf(st.m, mx);
     const float mu = (mn == kNegInf) ? 0.f : mn;
     const float alpha = fexp2(st.m - mu);
@@ -313,8 +312,7 @@ __device__ __forceinline__ void gqa_fold(GSmem<D>& sm, GState<D>& st, int wave, 
     using G = GGeo<D>;
     // the lanes of query c split its keys over w = 0..3: add their partial sums
     float l = st.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum_xor16_32(l);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll

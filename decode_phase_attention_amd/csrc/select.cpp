@@ -15,14 +15,17 @@
 //   2. Kind. If the lean schedule on that grid splits no head, every
 //      workgroup holds whole heads: the per-head decomposition (review §4.3's
 //      FlashAttention-2 case) does the same work with no tables, partials or
-//      flags, and the hardware dispatcher balances it, so per head is chosen
-//      -- provided heads average at least kMinTilesPerHead tiles. Shorter
-//      heads make per-head workgroups spend a large share of their life in
-//      their prologue and epilogue, which the persistent grid amortises over
-//      many heads (measured: 2-tile heads 6% faster on lean). Otherwise lean.
-//      A fixed split is never chosen: on uniform lengths the lean schedule
-//      already is the best fixed split, in one launch instead of two, and on
-//      ragged lengths its balance is better.
+//      flags, and the hardware dispatcher balances it, so per head is chosen.
+//      Single-head kernels take it for any head length (measured on 4096
+//      to 65536 whole heads of 1-8 tiles: per head 20% faster at one tile, 9%
+//      at two, 2% at four, 1.5% at eight: several per-head workgroups on a CU
+//      hide the latency of a short head's few steps, which a lean workgroup
+//      walking its heads one after the other does not). Grouped units take it
+//      from kMinTilesPerUnitGrouped tiles on average (measured: 2-tile units
+//      4% faster on lean, 4- and 8-tile units 3% faster per head). Otherwise
+//      lean. A fixed split is never chosen: on uniform
+//      lengths the lean schedule already is the best fixed split, in one
+//      launch instead of two, and on ragged lengths its balance is better.
 //   3. Short heads. When every head's K and V fit in kShortUnitBytes and all
 //      heads run at once on one workgroup per CU, the launch is bound by
 //      latency, not bandwidth: the few workgroups of the per-head kernel
@@ -43,7 +46,7 @@
 
 namespace la {
 
-constexpr int64_t kMinTilesPerHead = 8;
+constexpr int64_t kMinTilesPerUnitGrouped = 4;
 constexpr int64_t kShortUnitBytes = 256 * 1024;
 
 int select_kind(const int32_t* ctx_lens, int B, int units, int L, int d, bool grouped, int cus,
@@ -81,7 +84,7 @@ int select_kind(const int32_t* ctx_lens, int B, int units, int L, int d, bool gr
                    host.data(), last.data());
     bool split = false;
     for (int64_t u = 0; u < U && !split; ++u) split = host[u] != last[u];
-    *kind = (split || I < kMinTilesPerHead * U) ? 0 : 2;
+    *kind = (split || (grouped && I < kMinTilesPerUnitGrouped * U)) ? 0 : 2;
     *grid = G;
     return 0;
 }

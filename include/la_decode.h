@@ -317,8 +317,8 @@ la_status la_decode_noalloc(const void* q, const void* k_cache, const void* v_ca
  *           coresident. units = H, or with kv_heads / q_tokens the grouped
  *           units (K/V head x block of 16 query columns).
  *   kind  = LA_KIND_PER_HEAD if the lean schedule on that grid splits no
- *           head (every workgroup holds whole heads) and heads average at
- *           least 8 tiles; also LA_KIND_PER_HEAD, with one query column per
+ *           head (every workgroup holds whole heads) and, for grouped units,
+ *           they average at least 4 tiles; also LA_KIND_PER_HEAD, with one query column per
  *           K/V head, when every head's K and V fit in 256 KiB
  *           (max n_b * 4 * d bytes) and B * H <= cus (a latency-bound launch
  *           that runs every head at once); else LA_KIND_LEAN.

@@ -33,7 +33,8 @@ CASES = [
     # (lens, H, Hk, Nq, d, dtype, expected pick on a 256-CU device)
     ([3000, 17, 60000], 8, 8, 1, 128, "bf16", "lean"),
     ([1024] * 64, 8, 8, 1, 128, "bf16", "per_head"),     # 512 whole heads on 512 workgroups
-    ([256] * 128, 32, 32, 1, 64, "f16", "lean"),           # whole heads, but one tile each
+    ([256] * 128, 32, 32, 1, 64, "f16", "per_head"),       # whole heads of one tile each
+    ([256] * 256, 32, 8, 1, 128, "bf16", "lean"),          # whole grouped units of 2 tiles
     ([2048] * 128, 32, 32, 1, 64, "f16", "per_head"),
     ([5000, 900, 33], 32, 8, 1, 128, "bf16", "lean"),
     ([2048] * 64, 64, 8, 1, 128, "bf16", "per_head"),    # grouped units: 512 whole units

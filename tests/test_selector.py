@@ -1,9 +1,10 @@
 """The shape-driven kind selection (kind="auto"), host only: its grid rule and
 its per-head decision checked against the oracle's schedule, which must split
-no head when the selection is per-head for long heads (xllm-io paper review
-§4.3: the stream-K schedule with whole heads per workgroup is the per-head
-one); short single-head units that all run at once (K and V of each within
-256 KiB, no more heads than CUs) go per head whatever the schedule."""
+no head when the selection is per-head (xllm-io paper review §4.3: the
+stream-K schedule with whole heads per workgroup is the per-head one); grouped
+units go per head only when they average at least 4 tiles; short single-head
+units that all run at once (K and V of each within 256 KiB, no more heads than
+CUs) go per head whatever the schedule."""
 from __future__ import annotations
 
 import ctypes
@@ -31,8 +32,8 @@ def expected(lens, H, d, cus, cores, Hk=None, Nq=1, L=None):
         return "per_head", G            # short heads, all at once: latency-bound
     s = lean_schedule(lens, U, L, G)
     whole = all(h == l for h, l in zip(s["host_cta"], s["last_cta"]))
-    long_heads = s["I"] >= 8 * len(lens) * U
-    return ("per_head" if whole and long_heads else "lean"), G
+    long_units = single or s["I"] >= 4 * len(lens) * U
+    return ("per_head" if whole and long_units else "lean"), G
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -57,9 +58,13 @@ def test_identities_of_the_pages():
     assert la.la_select_for([524288], 32, 128, 256, 1024) == ("lean", 256)
     # uniform lengths, whole heads per workgroup (B*H = 512 on 512 workgroups): per head
     assert la.la_select_for([4096] * 16, 32, 128, 256, 1024) == ("per_head", 512)
-    # ... unless the heads are short (2 tiles each): lean amortises the head switches
-    assert la.la_select_for([256] * 512, 8, 128, 256, 1024) == ("lean", 512)
+    # ... also when the heads are short (2 tiles each): several per-head
+    # workgroups per CU hide the latency of a short head's few steps
+    assert la.la_select_for([256] * 512, 8, 128, 256, 1024) == ("per_head", 512)
     assert la.la_select_for([1024] * 512, 8, 128, 256, 1024) == ("per_head", 512)
+    # grouped units of 2 tiles stay on lean, of 4 tiles go per head
+    assert la.la_select_for([256] * 256, 32, 128, 256, 1024, kv_heads=8) == ("lean", 512)
+    assert la.la_select_for([512] * 128, 64, 128, 256, 1024, kv_heads=8) == ("per_head", 512)
     # uniform lengths that do not divide evenly: heads get split -> lean
     assert la.la_select_for([4096] * 9, 32, 128, 256, 1024) == ("lean", 256)
     # ragged batch of many heads: lean on two workgroups per CU
