@@ -129,6 +129,7 @@ std::map<int, DeviceState> g_dev;
 struct Capacity {
     int coresident;   // occupancy per CU x CUs: the largest grid a launch may use
     int preferred;    // default grid: kWgPerCu workgroups on every CU
+    int cus;          // compute units of the device
 };
 std::map<std::pair<int, const void*>, Capacity> g_capacity;
 
@@ -239,6 +240,7 @@ la_status capacity(int dtype, int d, bool grouped, Capacity* out) {
     Capacity c;
     c.coresident = per_cu * cus;
     c.preferred = (per_cu < kWgPerCu ? per_cu : kWgPerCu) * cus;
+    c.cus = cus;
     g_capacity[key] = c;
     *out = c;
     return LA_OK;
@@ -379,6 +381,16 @@ void fill_gqa(la::GqaArgs& a, const void* q, const void* k, const void* v, float
     a.splits = 1;
     a.sl2e = scale * 1.4426950408889634f;
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
+}
+
+// Whether a single-head launch whose workgroups take at most ceil(I / G)
+// tiles of L tokens each (at d) can stream a range long enough for the
+// 16-row K blocks, and so for the per-CU crowding watch: shorter ranges read
+// by whole rows anyway, and the watch's two counter atomics per workgroup
+// would be its only effect (tiny: 0.4 us of 9 us).
+bool watch_cus(int64_t I, int64_t G, int L, int d) {
+    const int64_t tiles = (I + G - 1) / G;
+    return tiles * (int64_t)L >= (int64_t)la::kBlockMinSteps * la::chunk_rows(d);
 }
 
 // Whether a lean call with host lengths derives its segments in the launch
@@ -580,6 +592,8 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
     a.kv_stride = o.kv_stride;
     a.sl2e = scale * 1.4426950408889634f;
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
+    // lengths on the device: the ranges are known only in the launch
+    a.cu_fair = dev_lens || watch_cus(I, G, L, d) ? (G + cap.cus - 1) / cap.cus : 0;
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
     HIP_TRY(la::launch_lean(o.dtype, d, a, G, stream, coop));
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));
@@ -792,6 +806,10 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     a.nchunks = (int)nchunks;
     a.dynamic = dynamic ? 1 : 0;
     a.sl2e = scale * 1.4426950408889634f;
+    // the stream's lean control block: launches on one stream never overlap,
+    // so its per-CU counters are free while a pull launch runs
+    a.ctl = w.ctl;
+    a.cu_fair = dynamic && watch_cus(C, 1, L, d) ? (grid + cap.cus - 1) / cap.cus : 0;
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, w.stream));
     HIP_TRY(la::launch_pull(o.dtype, d, a, grid, w.stream));
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, w.stream));

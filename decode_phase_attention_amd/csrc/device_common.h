@@ -294,6 +294,20 @@ struct SegCursor<kSrcTables> {
     }
 };
 
+// This workgroup's CU slot in the control block's per-CU counters.
+__device__ __forceinline__ uint32_t cu_slot() {
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+    return ((xcc & 15u) << 8) | ((hw >> 8) & 0xFFu);
+}
+__device__ __forceinline__ void cu_add(uint32_t* ctl, uint32_t slot, int delta) {
+    __hip_atomic_fetch_add(ctl + kCtlCu + slot, (uint32_t)delta, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t cu_count(const uint32_t* ctl, uint32_t slot) {
+    return __hip_atomic_load(ctl + kCtlCu + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint64_t hwreg_ids() {
     // HW_ID (register 4) and XCC_ID (register 20), all 32 bits of each
     const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);

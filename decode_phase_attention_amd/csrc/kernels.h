@@ -14,6 +14,9 @@ constexpr int kRows = 8;                  // K/V rows each lane group loads per 
 // a row of d halves is d/8 lanes of 16 bytes, so a wave holds 512/d rows per
 // load and the workgroup 2048/d; each lane group takes kRows of them.
 constexpr int chunk_rows(int d) { return (2048 / d) * kRows; }
+// Single-head ranges of at least this many steps (of chunk_rows(d) rows) read
+// K in 16-row blocks, shorter ones by whole rows.
+constexpr int kBlockMinSteps = 8;
 
 // Stride in floats of one partial record (Obar[d], m, l), padded to 16 bytes.
 constexpr int part_stride(int d) { return d + 4; }
@@ -47,7 +50,12 @@ constexpr uint32_t kErrLengths = 2u;     // device context lengths out of range
 // never counts, and a give-up makes the other waits of the same launch give
 // up at once without touching later launches. Flags need no lowering.
 constexpr int kCtlErr = 0, kCtlEpoch = 16, kCtlExit = 32, kCtlAbort = 48;
-constexpr int kCtlWords = 64;
+// After those words: how many workgroups of the running lean launch each CU
+// holds, one word per CU slot (XCC_ID & 15) * 256 + HW_ID bits 15:8 (CU, SH
+// and SE ids). Every workgroup adds one at entry and takes it back at exit,
+// so the words are zero between launches.
+constexpr int kCtlCu = 64, kCuSlots = 4096;
+constexpr int kCtlWords = kCtlCu + kCuSlots;
 
 struct SchedArgs {
     const int4* seg;           // tables: [nseg] (u, t0, t1, host | finishing << 1)
@@ -85,6 +93,7 @@ struct LeanArgs {
     int kv_stride;             // 0: K/V packed per request; else rows per head of a [B, H, kv_stride, d] cache
     float sl2e;                // scale * log2(e)
     uint64_t wait_ticks;       // 100 MHz clock ticks before a wait gives up
+    int cu_fair;               // ceil(grid / CUs): a CU holding more of the launch's workgroups is crowded
 };
 
 struct SplitArgs {
@@ -192,6 +201,8 @@ struct PullArgs {
     int nchunks;
     int dynamic;               // 1: pull chunks from the counter; 0: chunk = blockIdx.x
     float sl2e;
+    uint32_t* ctl;             // dynamic pull: the stream's lean control block (its per-CU counters)
+    int cu_fair;               // > 0: as in LeanArgs
 };
 
 const void* lean_kernel_ptr(int dtype, int d, int src);

@@ -124,40 +124,61 @@ struct Geo {
     static constexpr uint32_t RB = D * 2;             // bytes per row
 };
 
-// One step over rows in the contiguous pattern, for short ranges: kRows rows
-// per lane group, K and V loads issued back to back, then scores, one
-// rescale, and the V accumulation. Row r of group g (of the workgroup's NG)
-// in a step starting at `base` is base + r*NG + g, so one load instruction of
-// a wave reads GPW consecutive rows (1 KiB contiguous) of K and of V. Full
-// steps address rows as (uniform base) + (fixed 32-bit lane offset); the
-// last, partial step clamps rows at or past e to e-1 (never reading outside
-// the head) and masks their scores to -inf. Scores are summed within the lane
-// group by DPP, with no LDS traffic, which keeps a step's latency low.
-template <int DT, int D, bool TAIL>
+// Kinds of step: every row valid; rows from the range end masked (the last
+// step); rows before the range start masked too (the first step of a range
+// whose step grid starts before it, see stream_range).
+constexpr int kStepFull = 0, kStepTail = 1, kStepEdge = 2;
+// Steps between two looks at how crowded the workgroup's CU is (stream_range).
+constexpr int kCheckSteps = 16;
+
+// One step reading K like V, by whole rows: each lane group (d/8 lanes) takes
+// kRows rows, each lane a 16-byte piece `sub` of K and V, so one instruction
+// of a wave reads GPW consecutive rows (1 KiB contiguous). Scores are summed
+// within the lane group by DPP, with no LDS traffic, which keeps a step's
+// latency low, and every CU request moves a whole 128-byte line.
+//   WAVE_BLOCK: the step covers this wave's RW rows [kb, kb + RW); lane group
+//     g = lane / LPR of the wave takes rows kb + GPW i + g -- the rows of each
+//     wave and lane group are those of stream_step, so a wave may take either
+//     routine for any step of a range.
+//   otherwise: kb is the workgroup step's first row and lane group g of the
+//     workgroup (of NG) takes rows kb + NG i + g, so the four waves read one
+//     contiguous 4 KiB block per instruction (short ranges: measured 0.5 us
+//     faster than per-wave blocks on 1024-token heads).
+// Full steps address rows as (uniform base) + (fixed 32-bit lane offset); a
+// tail step clamps rows at or past e to e-1 (never reading outside the head)
+// and masks their scores to -inf; an edge step also clamps rows before lo to
+// lo and masks them.
+template <int DT, int D, int MODE, bool WAVE_BLOCK>
 __device__ __forceinline__ void stream_step_rows(const char* __restrict__ kh,
-                                                 const char* __restrict__ vh, int base, int e,
-                                                 uint32_t lane_off, const uint4 qv, float sl2e,
-                                                 int grp, Acc& acc) {
+                                                 const char* __restrict__ vh, int kb, int lo,
+                                                 int e, const uint4 qv, float sl2e, Acc& acc) {
     using G = Geo<D>;
-    constexpr uint32_t kStepRowBytes = G::NG * G::RB;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % G::LPR;
+    // first row of this lane group and the stride between its rows
+    const int g0 = WAVE_BLOCK ? lane / G::LPR : (threadIdx.x >> 6) * G::GPW + lane / G::LPR;
+    constexpr int kStride = WAVE_BLOCK ? G::GPW : G::NG;
     uint4 kr[kRows], vr[kRows];
-    if constexpr (!TAIL) {
-        const uint32_t off = (uint32_t)base * G::RB + lane_off;
+    if constexpr (MODE == kStepFull) {
+        const uint32_t off = (uint32_t)(kb + g0) * G::RB + (uint32_t)sub * 16u;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) kr[r] = load_nt(kh + (uint64_t)(off + r * kStepRowBytes));
+        for (int i = 0; i < kRows; ++i)
+            kr[i] = load_nt(kh + (uint64_t)(off + (uint32_t)i * kStride * G::RB));
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) vr[r] = load_nt(vh + (uint64_t)(off + r * kStepRowBytes));
+        for (int i = 0; i < kRows; ++i)
+            vr[i] = load_nt(vh + (uint64_t)(off + (uint32_t)i * kStride * G::RB));
     } else {
-        const uint32_t col_off = lane_off - (uint32_t)grp * G::RB;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
-            kr[r] = load_nt(kh + (uint64_t)(j * G::RB + col_off));
+        for (int i = 0; i < kRows; ++i) {
+            int row = min(kb + kStride * i + g0, e - 1);
+            if constexpr (MODE == kStepEdge) row = max(row, lo);
+            kr[i] = load_nt(kh + (uint64_t)((uint32_t)row * G::RB + (uint32_t)sub * 16u));
         }
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const uint32_t j = (uint32_t)min(base + r * G::NG + grp, e - 1);
-            vr[r] = load_nt(vh + (uint64_t)(j * G::RB + col_off));
+        for (int i = 0; i < kRows; ++i) {
+            int row = min(kb + kStride * i + g0, e - 1);
+            if constexpr (MODE == kStepEdge) row = max(row, lo);
+            vr[i] = load_nt(vh + (uint64_t)((uint32_t)row * G::RB + (uint32_t)sub * 16u));
         }
     }
     // all 2*kRows loads of the step in flight before any is consumed
@@ -169,10 +190,11 @@ __device__ __forceinline__ void stream_step_rows(const char* __restrict__ kh,
         // so the maximal row gets weight exactly 1
 #pragma clang fp contract(off)
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const float x = group_sum<G::LPR>(dot8<DT>(kr[r], qv)) * sl2e;
-            s[r] = (!TAIL || base + r * G::NG + grp < e) ? x : kNegInf;
-            mx = fmaxf(mx, s[r]);
+        for (int i = 0; i < kRows; ++i) {
+            const float x = group_sum<G::LPR>(dot8<DT>(kr[i], qv)) * sl2e;
+            const int row = kb + kStride * i + g0;
+            s[i] = (MODE == kStepFull || (row < e && (MODE != kStepEdge || row >= lo))) ? x : kNegInf;
+            mx = fmaxf(mx, s[i]);
         }
     }
     const float mn = fmaxf(acc.m, mx);
@@ -219,8 +241,6 @@ __device__ __forceinline__ void stream_step_rows(const char* __restrict__ kh,
 // their scores to -inf; an edge step (the first one of a range whose step
 // grid starts before it, see stream_range) also clamps rows before lo to lo
 // and masks them.
-constexpr int kStepFull = 0, kStepTail = 1, kStepEdge = 2;
-constexpr int kBlockMinSteps = 8;
 
 template <int DT, int D, int MODE>
 __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const char* __restrict__ vh,
@@ -320,58 +340,98 @@ __device__ __forceinline__ void stream_step(const char* __restrict__ kh, const c
     acc.m = mn;
 }
 
+// How crowded a workgroup's CU is, for the lean kernel (ctl == nullptr: not
+// watched). The 16-row K pattern moves half a cache line per request for K,
+// and one CU then reads at most ~34.6 GB/s, against ~48 GB/s for whole-line
+// patterns (measured on MI355X with a plain read of each pattern, K and V of
+// 4 GiB each, on 128 CUs: 4.43 against 6.18 TB/s). On a whole, uncontended
+// device a CU needs ~28 GB/s, so the 16-row blocks win there; when other work
+// holds CUs and the launch's workgroups double up on the rest, those CUs need
+// more than that ceiling. A wave whose CU holds more than `fair` of the
+// launch's workgroups (the per-CU counters of the control block) is crowded
+// and reads K by whole rows until it is not. `rows` is this wave's current
+// choice.
+struct CuWatch {
+    const uint32_t* ctl;
+    uint32_t slot;
+    uint32_t fair;
+    bool rows;
+};
+
 // Stream rows [a, e) of one head (kh/vh point at its row 0, qh at its query
 // row) through the lane groups' online softmax; sx is the wave's slice of
 // the score exchange in LDS (Geo<D>::RW floats). A head spans less than
-// 4 GiB, so every offset inside it fits in 32 bits.
+// 4 GiB, so every offset inside it fits in 32 bits. A workgroup step covers
+// CH rows, wave w its w-th block of RW rows, in either routine.
 //
 // The two step routines suit different ranges. A long range is bound by the
-// rate of its reads, and reads K fastest in 16-row blocks (stream_step);
-// a short one is bound by the latency of its few steps, which is lower with
-// contiguous rows and DPP sums (stream_step_rows). Measured on MI355X: 512k
+// rate of its reads, and reads K fastest in 16-row blocks (stream_step); a
+// short one is bound by the latency of its few steps, which is lower by
+// whole rows with DPP sums (stream_step_rows). Measured on MI355X: 512k
 // (ranges of 1024 steps) 1211 us contiguous against 1182 us in 16-row blocks;
 // 4096 heads of 2 steps 84 us against 94 us; one uncontended workgroup
 // streams 55 GB/s contiguous against 39 GB/s in 16-row blocks. Ranges of at
-// least kBlockMinSteps steps take the 16-row blocks.
+// least kBlockMinSteps steps take the 16-row blocks, unless `cw` finds the
+// CU crowded: every kCheckSteps steps a wave loads its CU's counter with the
+// loads of a step and picks the routine of the next steps from it once they
+// have arrived, so the look costs no wait.
 //
-// In 16-row blocks, the step grid starts at the 4 KiB boundary of the K rows
+// Long ranges step on a grid that starts at the 4 KiB boundary of the K rows
 // at or before row a, so that every 16-row block of K loads covers whole 4 KiB
 // blocks: the pattern reads fastest so (measured with a plain read of this
 // pattern on MI355X: 7.2-7.3 TB/s aligned, about 3% less at 5-11 rows past a
 // boundary), and packed ragged caches put heads at arbitrary rows. The first
-// step then masks the rows before a.
+// step then masks the rows before a, in either routine.
 template <int DT, int D>
 __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t* vh, int a, int e,
-                                             const uint16_t* qh, float sl2e, float* sx, Acc& acc) {
+                                             const uint16_t* qh, float sl2e, float* sx, Acc& acc,
+                                             CuWatch* cw = nullptr) {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const char* kc = reinterpret_cast<const char*>(kh);
     const char* vc = reinterpret_cast<const char*>(vh);
+    const uint4 qv = *reinterpret_cast<const uint4*>(qh + (lane % G::LPR) * 8);
     if (e - a < kBlockMinSteps * G::CH) {
-        const int grp = wave * G::GPW + lane / G::LPR, sub = lane % G::LPR;
-        const uint4 qv = *reinterpret_cast<const uint4*>(qh + sub * 8);
-        const uint32_t lane_off = (uint32_t)(grp * D + sub * 8) * 2u;
         int base = a;
         for (; base + G::CH <= e; base += G::CH)
-            stream_step_rows<DT, D, false>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
-        if (base < e) stream_step_rows<DT, D, true>(kc, vc, base, e, lane_off, qv, sl2e, grp, acc);
+            stream_step_rows<DT, D, kStepFull, false>(kc, vc, base, a, e, qv, sl2e, acc);
+        if (base < e) stream_step_rows<DT, D, kStepTail, false>(kc, vc, base, a, e, qv, sl2e, acc);
         return;
     }
     uint4 qk[G::KK];
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk)
         qk[kk] = *reinterpret_cast<const uint4*>(qh + ((lane >> 4) + 4 * kk) * 8);
+    const bool watch = cw != nullptr && cw->ctl != nullptr;
+    bool rows = watch && cw->rows;
     constexpr uint32_t kAlignRows = 4096 / G::RB;   // 16 at d = 128, 32 at d = 64
     const uint32_t phase = (uint32_t)(((uintptr_t)kc + (uint64_t)(uint32_t)a * G::RB) & 4095u) / G::RB;
     int base = a - (int)min(phase, kAlignRows - 1);
     if (base < a) {
-        stream_step<DT, D, kStepEdge>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
+        if (rows)
+            stream_step_rows<DT, D, kStepEdge, true>(kc, vc, base + G::RW * wave, a, e, qv, sl2e, acc);
+        else
+            stream_step<DT, D, kStepEdge>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
         base += G::CH;
     }
-    for (; base + G::CH <= e; base += G::CH)
-        stream_step<DT, D, kStepFull>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
-    if (base < e) stream_step<DT, D, kStepTail>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
+    for (int j = 1; base + G::CH <= e; base += G::CH, ++j) {
+        const bool look = watch && (j % kCheckSteps) == 0;
+        uint32_t count = 0;
+        if (look) count = cu_count(cw->ctl, cw->slot);   // arrives with the step's loads
+        if (rows)
+            stream_step_rows<DT, D, kStepFull, true>(kc, vc, base + G::RW * wave, a, e, qv, sl2e, acc);
+        else
+            stream_step<DT, D, kStepFull>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
+        if (look) rows = __builtin_amdgcn_readfirstlane(count) > cw->fair;
+    }
+    if (base < e) {
+        if (rows)
+            stream_step_rows<DT, D, kStepTail, true>(kc, vc, base + G::RW * wave, a, e, qv, sl2e, acc);
+        else
+            stream_step<DT, D, kStepTail>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
+    }
+    if (watch) cw->rows = rows;
 }
 
 template <int D>
@@ -462,6 +522,8 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         stamp_end(a.ts, c);
         return;
     }
+    CuWatch cw{a.cu_fair > 0 ? a.ctl : nullptr, cu_slot(), (uint32_t)a.cu_fair, false};
+    if (cw.ctl != nullptr && t == 0) cu_add(a.ctl, cw.slot, 1);
     LeanSeg sg;
     while (cur.next(sg)) {
         const int u = sg.u;
@@ -472,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         Acc acc;
         acc_init(acc);
         stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, a.q + (int64_t)u * D,
-                            a.sl2e, sm.sx[t >> 6], acc);
+                            a.sl2e, sm.sx[t >> 6], acc, &cw);
         if (a.tile_owner != nullptr && t == 0)
             for (int i = sg.t0; i < sg.t1; ++i) a.tile_owner[sg.iter0 + i - sg.t0] = c;
 
@@ -522,6 +584,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         }
         write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
     }
+    if (cw.ctl != nullptr && t == 0) cu_add(a.ctl, cw.slot, -1);
     if (t == 0) launch_exit(a.ctl, ep);
     stamp_end(a.ts, c);
 }
@@ -605,6 +668,8 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
     const int grp = (t >> 6) * G::GPW + lane / G::LPR;
     const int sub = lane % G::LPR;
     stamp_start(a.ts, blockIdx.x);
+    CuWatch cw{a.cu_fair > 0 ? a.ctl : nullptr, cu_slot(), (uint32_t)a.cu_fair, false};
+    if (cw.ctl != nullptr && t == 0) cu_add(a.ctl, cw.slot, 1);
     // A workgroup takes its next chunk only when it has finished the last one
     // (taking it earlier hands chunks to workgroups that are still busy while
     // others, started later, find none).
@@ -635,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
             Acc acc;
             acc_init(acc);
             stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1,
-                                a.q + (int64_t)u * D, a.sl2e, sm.sx[t >> 6], acc);
+                                a.q + (int64_t)u * D, a.sl2e, sm.sx[t >> 6], acc, &cw);
             if (a.tile_owner != nullptr)
                 for (int i = it + t; i < t1; i += kThreads) a.tile_owner[i] = blockIdx.x;
             float M = kNegInf, Ls = 0.f, O[P];
@@ -684,6 +749,7 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
             next = a.nchunks;
         }
     }
+    if (cw.ctl != nullptr && t == 0) cu_add(a.ctl, cw.slot, -1);
     if (a.dynamic && t == 0) {
         // the last workgroup out re-arms the counters for the next launch
         const uint32_t done = __hip_atomic_fetch_add(&a.pull[1], 1u, __ATOMIC_RELAXED,

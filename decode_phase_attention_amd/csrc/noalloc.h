@@ -12,8 +12,8 @@
 namespace la {
 
 // Layout of the scratch array, in bytes from its start:
-//   [0, 256)              control block (kCtl* words)
-//   [256, 256 + 4 G_max)  flags, one per workgroup
+//   [0, 4 kCtlWords)      control block (kCtl* words, per-CU counters included)
+//   [kScratchFlagsOff, + 4 G_max)  flags, one per workgroup
 //   [kScratchPartOff, +kScratchPartBytes)  partial records
 constexpr int kScratchMaxGrid = 2048;
 constexpr size_t kScratchFlagsOff = sizeof(uint32_t) * kCtlWords;

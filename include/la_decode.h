@@ -276,7 +276,7 @@ la_status la_decode_ex(const void* q, const void* k_cache, const void* v_cache,
  * uses no per-stream workspace: the lean exchange (partial records, flags and
  * control words) lives in a fixed array of device memory, one per GPU, that
  * the library holds until the process ends: 8 MiB of partial records plus
- * 8448 bytes of flags and control words.
+ * 24832 bytes of flags, control words and per-CU workgroup counters.
  *
  * Arguments and options are those of la_decode_ex, restricted to:
  *   - kind LA_KIND_LEAN (LA_EINVAL otherwise);

@@ -292,3 +292,59 @@ def test_host_threads_and_shutdown(la):
     la.la_decode_ex(a.q, a.k, a.v, a.ctx_lens, a.B, a.H, a.d, a.scale, out)
     la.la_sync_check()
     assert float(np.max(np.abs(out.cpu().numpy() - refs[0]))) <= 1e-3
+
+
+def _masked_stream(n_cus):
+    """A stream whose kernels may use only the first n_cus CUs (default priority)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    total = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (total + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for i in range(n_cus):
+        mask[i // 32] |= 1 << (i % 32)
+    s = ctypes.c_void_p()
+    assert hip.hipExtStreamCreateWithCUMask(ctypes.byref(s), words, mask) == 0
+    return torch.cuda.ExternalStream(s.value)
+
+
+@pytest.mark.parametrize("dtype,d,lens,H", [("bf16", 128, [65536, 65536], 8),
+                                            ("f16", 64, [70001, 33333, 9000, 129], 4)])
+@pytest.mark.parametrize("n_cus", [100, 200])
+def test_crowded_cus(la, dtype, d, lens, H, n_cus):
+    """The single-head lean and dynamic pull kernels on a stream confined to
+    part of the CUs, so that several of their workgroups share a CU: a wave
+    on such a CU finds it crowded (per-CU counters in the control block) and
+    switches from K in 16-row blocks to whole rows within a range, on the same
+    step grid. Every output meets the oracle, in launches back to back, and a
+    launch on the whole device afterwards (counters back at zero) too. Lean
+    grids stay within what the masked CUs hold at once, as a lean launch
+    needs."""
+    inp = W.make_custom(lens, H, d, dtype, seed=d + n_cus, device="cuda")
+    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                             inp.scale, dtype, workers=8)[0]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_cus = min(n_cus, cus)
+    per_cu = la.la_max_grid(d, la.LA_BF16 if dtype == "bf16" else la.LA_F16) // cus
+    grids = [g for g in (cus, 2 * cus) if g <= per_cu * n_cus]
+    assert grids
+    st = _masked_stream(n_cus)
+    outs = []
+    with torch.cuda.stream(st):
+        for kind, grid in [("lean", g) for g in grids] + [("pull", 0), ("pull", 2 * cus)]:
+            say(f"[crowded] {kind} {dtype} d={d} lens={lens} H={H} cus={n_cus} grid={grid}")
+            out = torch.full((len(lens), H, d), float("nan"), dtype=torch.float32, device="cuda")
+            la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out,
+                            kind=kind, grid=grid)
+            outs.append(out)
+    st.synchronize()
+    la.la_sync_check(st.cuda_stream)
+    out = torch.full((len(lens), H, d), float("nan"), dtype=torch.float32, device="cuda")
+    la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out, kind="lean")
+    la.la_sync_check()
+    outs.append(out)
+    for o in outs:
+        err = float(np.max(np.abs(o.cpu().numpy() - ref)))
+        assert err <= 1e-3, err
