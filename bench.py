@@ -807,6 +807,12 @@ def main():
                    for inp in inputs.values())
         read_buf = torch.zeros(need, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
+    # a second of untimed launches: right after large allocations every
+    # kernel runs slower for about a second (a short workload's whole timing
+    # would fall inside it)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        time_kind(la, torch, evs, inputs[args.workload], "lean", 5, 1)
     head = measure(la, torch, evs, args.workload, inputs[args.workload], args,
                    cpu=not args.no_cpu_baseline, read_buf=read_buf)
     extra = {}
