@@ -735,7 +735,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="512k",
                     choices=["tiny", "65k", "512k", "ragged", "many-heads", "gqa-512k",
-                             "gqa8-ragged", "mqa-32k", "spec4-ragged", "spec8-64k"])
+                             "gqa8-ragged", "mqa-32k", "spec4-ragged", "spec8-64k", "512k-h4"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
@@ -866,6 +866,8 @@ WORKLOAD_DESC = {
                     "n_b log-uniform in [1024, 262144], causal among the new tokens, bf16",
     "spec8-64k": "spec8-64k: B=4, 8 new tokens each, H=32, d=128, n=65536, causal among "
                  "the new tokens, bf16",
+    "512k-h4": "512k-h4: B=1, H=4, d=128, n=524288, bf16 (one GPU's share of 512k under "
+               "8-way head sharding)",
 }
 
 

@@ -325,7 +325,7 @@ def test_timeout_stays_in_its_launch(la, H, Hk):
 
 # ------------------------------------------------------------------ full-size workloads
 
-@pytest.mark.parametrize("name", ["65k", "512k", "ragged", "many-heads"])
+@pytest.mark.parametrize("name", ["65k", "512k", "ragged", "many-heads", "512k-h4"])
 def test_full_size(la, name):
     """Every kind on the full workload, every (request, head) against the
     oracle; the lean kernel's executed tile map against the schedule oracle."""

@@ -88,6 +88,9 @@ CONFIGS: dict[str, Workload] = {
                              note="4 new tokens per request, 32 query heads over 8 K/V heads"),
     "spec8-64k": Workload("spec8-64k", B=4, H=32, d=128, dtype="bf16", ctx=65536, q_tokens=8,
                           note="8 new tokens per request, plain multi-head"),
+    # one GPU's share of 512k when its 32 heads are sharded over 8 GPUs
+    "512k-h4": Workload("512k-h4", B=1, H=4, d=128, dtype="bf16", ctx=524288,
+                        note="4 of 512k's 32 heads: one GPU's share under 8-way head sharding"),
 }
 
 
