@@ -130,6 +130,8 @@ struct Geo {
 constexpr int kStepFull = 0, kStepTail = 1, kStepEdge = 2;
 // Steps between two looks at how crowded the workgroup's CU is (stream_range).
 constexpr int kCheckSteps = 16;
+// Peer records whose loads a host wave keeps in flight at once.
+constexpr int kMergeBatch = 16;
 
 // One step reading K like V, by whole rows: each lane group (d/8 lanes) takes
 // kRows rows, each lane a 16-byte piece `sub` of K and V, so one instruction
@@ -539,8 +541,15 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
             for (int i = sg.t0; i < sg.t1; ++i) a.tile_owner[sg.iter0 + i - sg.t0] = c;
 
         float M = kNegInf, Ls = 0.f, O[P];
+#pragma unroll
+        for (int k = 0; k < P; ++k) O[k] = 0.f;   // waves 1-3 start a wide merge from zero
         wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
-        if (t >= 64) continue;   // the epilogue is wave 0's; the others go on streaming
+        // A host's segment is the last of its workgroup's range. With more
+        // than kMergeBatch peers, all four waves wait for and fold a quarter
+        // of them each; otherwise the epilogue is wave 0's and the others go
+        // on streaming.
+        const bool wide = sg.host && !sg.fin && sg.last - c > kMergeBatch;
+        if (t >= 64 && !wide) continue;
 
         if (!sg.host) {
             // a peer: publish (Obar, m, l) for the head's host, then raise the
@@ -560,26 +569,51 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
             // The host. Its peers (c, last] each publish one partial: wait for
             // all of them at once (one flag per lane), then fold them in
             // ascending workgroup order with their loads issued in batches.
-            const int last = sg.last;
-            const int np = last - c;
+            // With many peers, wave w takes the w-th quarter of them (wave 0
+            // on top of the host's own state) and wave 0 then folds the other
+            // waves' states in wave order: a fixed order, so the bits do not
+            // depend on timing.
+            const int wave = t >> 6;
+            const int np = sg.last - c;
+            const int q = wide ? (np + kWaves - 1) / kWaves : np;
+            const int p_first = c + 1 + wave * q;
+            const int p_last = min(p_first + q - 1, sg.last);
             const uint64_t w0 = stamp_now(a.ts);
-            for (int i = lane; i < np; i += 64) wait_flag(&a.flags[c + 1 + i], ep, a.wait_ticks, a.ctl);
-            stamp_wait(a.ts, c, t_in, w0);
+            for (int i = lane; i <= p_last - p_first; i += 64)
+                wait_flag(&a.flags[p_first + i], ep, a.wait_ticks, a.ctl);
+            if (wave == 0) stamp_wait(a.ts, c, t_in, w0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            constexpr int kBatch = 16;
-            for (int p0 = c + 1; p0 <= last; p0 += kBatch) {
-                float pm[kBatch], pl[kBatch], po[kBatch][P];
+            for (int p0 = p_first; p0 <= p_last; p0 += kMergeBatch) {
+                float pm[kMergeBatch], pl[kMergeBatch], po[kMergeBatch][P];
 #pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    const float* p = a.part + (int64_t)min(p0 + j, last) * part_stride(D);
+                for (int j = 0; j < kMergeBatch; ++j) {
+                    const float* p = a.part + (int64_t)min(p0 + j, p_last) * part_stride(D);
                     pm[j] = load_agent(p + D);
                     pl[j] = load_agent(p + D + 1);
 #pragma unroll
                     for (int k = 0; k < P; ++k) po[j][k] = load_agent(p + lane + 64 * k);
                 }
 #pragma unroll
-                for (int j = 0; j < kBatch; ++j)
-                    if (p0 + j <= last) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
+                for (int j = 0; j < kMergeBatch; ++j)
+                    if (p0 + j <= p_last) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
+            }
+            if (wide) {
+                if (wave > 0) {
+#pragma unroll
+                    for (int k = 0; k < P; ++k) sm.o[wave][lane + 64 * k] = O[k];
+                    if (lane == 0) {
+                        sm.m[wave] = M;
+                        sm.l[wave] = Ls;
+                    }
+                }
+                __syncthreads();
+                if (wave > 0) continue;
+                for (int v = 1; v < kWaves; ++v) {
+                    float ov[P];
+#pragma unroll
+                    for (int k = 0; k < P; ++k) ov[k] = sm.o[v][lane + 64 * k];
+                    merge_into<P>(M, Ls, O, sm.m[v], sm.l[v], ov);
+                }
             }
         }
         write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
