@@ -23,18 +23,22 @@
 // pattern read slower (see stream_step); the four lanes of a K row add their
 // partial dot products across the wave, and each wave hands its scores to its
 // V lane groups through a small slice of LDS. Short ranges read K like V, by
-// lane groups, for the lower latency of each step (see stream_range and
-// stream_step_rows). Decode attention has a single query row, so K
+// lane groups, for the lower latency of each step, and so do the long ranges
+// of a lean or pull workgroup whose CU holds more of the launch's workgroups
+// than its share (see stream_range, stream_step_rows and CuWatch). Decode
+// attention has a single query row, so K
 // and V elements are each used once: they go straight from HBM to registers
 // with 16-byte loads and are not staged in LDS. At the end of a range the
 // groups meet in LDS, where the reduction f (§3.2) folds them into one
 // (m, l, Obar[d]).
 //
-// Epilogues run in wave 0 only. In the lean kernel a peer (a workgroup that
-// holds a head's tiles but not its first one) publishes its (Obar, m, l)
-// record and raises a flag; the head's host polls all its peers' flags at
-// once and folds their records in ascending workgroup order (§3.5). The other
-// waves meanwhile go on to the workgroup's next segment.
+// Epilogues run in wave 0. In the lean kernel a peer (a workgroup that holds
+// a head's tiles but not its first one) publishes its (Obar, m, l) record and
+// raises a flag; the head's host polls all its peers' flags at once and folds
+// their records in ascending workgroup order (§3.5). The other waves meanwhile
+// go on to the workgroup's next segment -- except at a host with more than
+// kMergeBatch peers, whose segment is its workgroup's last: there all four
+// waves share the merge.
 //
 // Exponentials are taken base 2 with log2(e) folded into the scale; m is kept
 // in log2 units inside the kernels and converted back to natural-log units

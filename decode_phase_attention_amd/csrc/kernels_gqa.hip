@@ -29,7 +29,8 @@
 //
 // Each wave streams 32 keys per step with its own online softmax (per query
 // column: m, a per-lane partial l, O^T); waves meet in LDS only at the end of
-// a range. The epilogue uses all 256 threads: thread t owns query t / 16 and
+// a range. A lean segment steps on a grid that starts at the 4 KiB boundary
+// of its K rows (see gseg_start). The epilogue uses all 256 threads: thread t owns query t / 16 and
 // head dims [(t % 16) * D/16, +D/16), so a wave covers four whole records.
 // The exchange between workgroups is the same agent-scope, completion-ordered
 // protocol as the single-head kernels, with 16 records (one per query column)

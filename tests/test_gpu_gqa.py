@@ -282,7 +282,7 @@ def test_step_grid_phase(la, d, dtype):
     4 KiB, with tiles and grids that start segments at many rows, must give the
     oracle's result: a key counted twice or dropped at a segment start shows in
     l and O."""
-    lens = [3, 130, 1000, 77, 515]
+    lens = [3, 130, 5000, 77, 2100]
     H, Hk = 8, 2
     inp = W.make_custom(lens, H=H, d=d, dtype=dtype, seed=88, device="cuda", kv_heads=Hk)
     ref = reference(inp)
@@ -296,6 +296,7 @@ def test_step_grid_phase(la, d, dtype):
         assert k.is_contiguous() and (k.data_ptr() - kb.data_ptr()) == r * 2 * d
         view = W.Inputs(q=inp.q, k=k, v=v, ctx_lens=lens, H=H, d=d, dtype=dtype,
                         scale=inp.scale, seed=88, meta={"kv_heads": Hk})
-        for opts in ({"tile_tokens": 48, "grid": 37}, {"tile_tokens": 32, "grid": 5}, {}):
+        for opts in ({"tile_tokens": 48, "grid": 37}, {"tile_tokens": 32, "grid": 5},
+                     {"grid": 3}, {}):
             say(f"[gqa phase d={d} offset={r} rows {opts}]")
             check(run(la, view, "lean", **opts), ref, tag=f"d={d}/offset={r}/{opts}")

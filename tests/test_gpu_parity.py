@@ -129,12 +129,13 @@ def test_ragged_small(la, dtype, d, kind):
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
 def test_step_grid_phase(la, dtype, d):
-    """Every range starts its step grid at the 4 KiB boundary of the K rows at
-    or before its first row and masks the rows of the first step that precede
-    it. Caches placed at every row offset within 4 KiB, with tiles and grids
-    that start ranges at many rows, must give the oracle's result on every
-    kind: a row counted twice or dropped at a range start shows in l and O."""
-    lens = [3, 130, 1000, 77, 515]
+    """Every range of 8 steps or more starts its step grid at the 4 KiB
+    boundary of the K rows at or before its first row and masks the rows of
+    the first step that precede it. Caches placed at every row offset within
+    4 KiB, with tiles and grids that start long and short ranges at many
+    rows, must give the oracle's result on every kind: a row counted twice or
+    dropped at a range start shows in l and O."""
+    lens = [3, 130, 5000, 77, 2100]
     H = 3
     inp = W.make_custom(lens, H=H, d=d, dtype=dtype, seed=89, device="cuda")
     ref = reference(inp)
@@ -148,10 +149,13 @@ def test_step_grid_phase(la, dtype, d):
         assert k.is_contiguous() and (k.data_ptr() - kb.data_ptr()) == r * 2 * d
         view = W.Inputs(q=inp.q, k=k, v=v, ctx_lens=lens, H=H, d=d, dtype=dtype,
                         scale=inp.scale, seed=89)
+        # ranges of 8 and more steps (16-row K blocks, edge steps at every
+        # phase) and shorter ones (whole rows)
         for kind, opts in (("lean", {"tile_tokens": 48, "grid": 37}),
+                           ("lean", {"tile_tokens": 48, "grid": 3}), ("lean", {"grid": 5}),
                            ("lean", {"tile_tokens": 16, "grid": 5}), ("lean", {}),
-                           ("fixed_split", {"num_splits": 3}), ("per_head", {}),
-                           ("pull", {"grid": 7})):
+                           ("fixed_split", {"num_splits": 3}), ("fixed_split", {"num_splits": 1}),
+                           ("per_head", {}), ("pull", {"grid": 7})):
             say(f"[phase {dtype} d={d} offset={r} rows {kind} {opts}]")
             check(run(la, view, kind, **opts), ref, tag=f"d={d}/offset={r}/{kind}/{opts}")
 
