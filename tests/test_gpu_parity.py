@@ -263,6 +263,24 @@ def test_determinism(la):
             assert np.array_equal(a, b, equal_nan=True)
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f16")])
+def test_wide_merge(la, d, dtype):
+    """Heads spread over many workgroups: a host with more than 16 peers
+    merges on all four waves, each folding a quarter of the peers, then wave
+    0 folds the waves' states in wave order. The result meets the oracle and
+    is bitwise the same from launch to launch (the order is fixed)."""
+    cap = la.la_max_grid(d, la.LA_BF16 if dtype == "bf16" else la.LA_F16)
+    for lens, H, grid in (([200000], 1, 256), ([100000, 3], 2, cap), ([70000], 1, 19)):
+        inp = W.make_custom(lens, H=H, d=d, dtype=dtype, seed=31, device="cuda")
+        say(f"[wide merge] d={d} lens={lens} H={H} grid={grid}")
+        first = run(la, inp, "lean", grid=grid)
+        check(first, reference(inp), tag=f"wide/{lens}/{grid}")
+        for _ in range(5):
+            again = run(la, inp, "lean", grid=grid)
+            for a, b in zip(first, again):
+                assert np.array_equal(a, b, equal_nan=True)
+
+
 def test_timeout_path_recovers(la):
     """A 1 us wait bound makes hosts give up waiting (forced from the host);
     the launch still ends, la_sync_check reports or not, and after the reset
