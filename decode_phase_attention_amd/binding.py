@@ -67,6 +67,7 @@ class LaOpts(ctypes.Structure):
         ("host_tables", ctypes.c_int),
         ("kv_stride", ctypes.c_int),
         ("ctx_lens_device", ctypes.c_void_p),
+        ("shared_gpu", ctypes.c_int),
     ]
 
 
@@ -266,7 +267,8 @@ def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=Non
 
 def _marshal(q, k_cache, v_cache, ctx_lens, B, H, d, out, *, dtype, kind, tile_tokens, grid,
              num_splits, cooperative, m_out, l_out, tile_owner, cta_timestamps, ev_start, ev_stop,
-             kv_heads, q_tokens, chunk_tiles, host_tables, kv_stride, ctx_lens_device):
+             kv_heads, q_tokens, chunk_tiles, host_tables, kv_stride, ctx_lens_device,
+             shared_gpu=False):
     """The la_opts of a call and its lengths pointer, after the size checks."""
     o = LaOpts()              # ctypes zero-fills it: the same as la_opts_init
     o.dtype = _dtype_of(q) if dtype is None else int(dtype)
@@ -302,6 +304,8 @@ def _marshal(q, k_cache, v_cache, ctx_lens, B, H, d, out, *, dtype, kind, tile_t
         o.host_tables = 1
     if kv_stride:
         o.kv_stride = int(kv_stride)
+    if shared_gpu:
+        o.shared_gpu = 1
     if ctx_lens_device is not None:
         import torch
         if (isinstance(ctx_lens_device, torch.Tensor) and
@@ -325,7 +329,7 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
                  kind="lean", tile_tokens=0, grid=0, num_splits=0, cooperative=False,
                  m_out=None, l_out=None, tile_owner=None, cta_timestamps=None, ev_start=None,
                  ev_stop=None, kv_heads=0, q_tokens=0, chunk_tiles=0, host_tables=False,
-                 kv_stride=0, ctx_lens_device=None):
+                 kv_stride=0, ctx_lens_device=None, shared_gpu=False):
     """la_decode_ex with the options as keywords. With ctx_lens_device (a
     device int32 tensor of B lengths), ctx_lens may be None."""
     o, arr, p = _marshal(q, k_cache, v_cache, ctx_lens, B, H, d, out, dtype=dtype, kind=kind,
@@ -334,7 +338,7 @@ def la_decode_ex(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None
                          cta_timestamps=cta_timestamps, ev_start=ev_start, ev_stop=ev_stop,
                          kv_heads=kv_heads, q_tokens=q_tokens, chunk_tiles=chunk_tiles,
                          host_tables=host_tables, kv_stride=kv_stride,
-                         ctx_lens_device=ctx_lens_device)
+                         ctx_lens_device=ctx_lens_device, shared_gpu=shared_gpu)
     _check(lib().la_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                               float(scale), _ptr(out), _stream(stream), ctypes.byref(o)))
 
@@ -396,7 +400,7 @@ def la_select_for(ctx_lens, H, d, cus, coresident, kv_heads=0, q_tokens=0, tile_
     return KIND_NAMES[kind.value], grid.value
 
 
-def la_select(ctx_lens, H, d, dtype, kv_heads=0, q_tokens=0, tile_tokens=0):
+def la_select(ctx_lens, H, d, dtype, kv_heads=0, q_tokens=0, tile_tokens=0, shared_gpu=False):
     """(kind name, grid) that kind="auto" picks on the current device."""
     arr, p = _lens(ctx_lens)
     o = LaOpts()
@@ -405,6 +409,7 @@ def la_select(ctx_lens, H, d, dtype, kv_heads=0, q_tokens=0, tile_tokens=0):
     o.kv_heads = int(kv_heads)
     o.q_tokens = int(q_tokens)
     o.tile_tokens = int(tile_tokens)
+    o.shared_gpu = 1 if shared_gpu else 0
     kind, grid = ctypes.c_int(), ctypes.c_int()
     _check(lib().la_select(p, len(arr), int(H), int(d), ctypes.byref(o), ctypes.byref(kind),
                            ctypes.byref(grid)))

@@ -830,6 +830,11 @@ la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int 
     const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, d, hd.grouped, cus,
                                    cap.coresident, kind, grid, &why);
     if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
+    // other work on the device: chunks pulled as CUs free up, not a static split
+    if (o.shared_gpu != 0 && *kind == LA_KIND_LEAN) {
+        *kind = LA_KIND_PULL;
+        *grid = cap.preferred;
+    }
     return LA_OK;
 }
 

@@ -207,6 +207,20 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               lengths on the same grid. Each workgroup reads every length
  *               once at its start: writes to them must be ordered before the
  *               call (on its stream, or synchronised with it).
+ *   shared_gpu  1 = the caller runs other work on the device at the same time
+ *               (kernels of other streams that may hold CUs), the selector
+ *               input "current GPU contention" of the siliconandsystems
+ *               digest ("A useful control policy"). LA_KIND_AUTO (and
+ *               la_select) then picks LA_KIND_PULL, on one workgroup per CU,
+ *               wherever it would pick LA_KIND_LEAN: an equal static split
+ *               waits for the workgroups that share a CU with other work,
+ *               while chunks pulled from a counter follow the CUs that are
+ *               free (the same digest, "The hardware-aware part"). Measured
+ *               with 1/8 of the CUs taken, pull lost 5-9% against its own
+ *               time on the whole device, lean 31-61%; alone on the device
+ *               pull is 0-9% slower than lean. Per-head picks stay. Ignored
+ *               with ctx_lens_device, where auto means lean. 0 = the launch
+ *               has the device to itself (default).
  *
  * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
  * pieces": workgroups pull the next piece of the global tile order instead of
@@ -246,6 +260,7 @@ typedef struct la_opts {
     int host_tables;
     int kv_stride;
     const int32_t* ctx_lens_device;
+    int shared_gpu;
 } la_opts;
 
 void la_opts_init(la_opts* opts);
@@ -331,7 +346,9 @@ la_status la_select_for(const int32_t* ctx_lens, int B, int H, int d, int kv_hea
                         int tile_tokens, int cus, int coresident, int* kind, int* grid);
 
 /* la_select: la_select_for on the current device, with d, dtype, kv_heads,
- * q_tokens and tile_tokens taken from `opts` (which may be null: defaults). */
+ * q_tokens and tile_tokens taken from `opts` (which may be null: defaults).
+ * With opts->shared_gpu set, a lean pick becomes LA_KIND_PULL on the default
+ * pull grid (one workgroup per CU), as LA_KIND_AUTO does then. */
 la_status la_select(const int32_t* ctx_lens, int B, int H, int d, const la_opts* opts, int* kind,
                     int* grid);
 

@@ -295,3 +295,29 @@ def test_length_marshalling():
     owner, _ = b._lens(np.array([2**30, 2**30], dtype=np.int64))   # total 2^31: past int32
     with pytest.raises(ValueError, match="k_cache"):
         b._check_sizes(q, kv, kv, out, owner, 2, 1, 64)
+
+
+def test_opts_struct_matches_the_header(tmp_path):
+    """The binding's ctypes mirror of la_opts has the header's fields, in its
+    order, at the offsets a C compiler gives them, and the same size."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [name for name, _ in la.binding.LaOpts._fields_]
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct la_opts \{(.*?)\} la_opts;", text, flags=re.S).group(1)
+    assert re.findall(r"(\w+)\s*;", body) == fields
+    src = tmp_path / "opts.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"la_decode.h\"\n"
+                   "int main(void) {\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(la_opts, {f}));\n' for f in fields)
+                   + '  printf("%zu\\n", sizeof(la_opts));\n  return 0;\n}\n')
+    exe = tmp_path / "opts"
+    subprocess.run([cc, "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    S = la.binding.LaOpts
+    assert got == [getattr(S, f).offset for f in fields] + [ctypes.sizeof(S)]

@@ -85,3 +85,49 @@ def test_decode_attention_wrapper(la):
     assert float(np.max(np.abs(out.cpu().numpy() - ref))) <= 1e-3
     with pytest.raises(ValueError):       # K/V sized for 2 heads, called as 8
         la.decode_attention(inp.q, inp.k, inp.v, lens)
+
+
+SHARED = [
+    # (lens, H, Hk, Nq, d, dtype): lean picks become pull; a per-head pick stays
+    ([3000, 17, 60000], 8, 8, 1, 128, "bf16"),
+    ([5000, 900, 33], 32, 8, 1, 128, "bf16"),
+    ([700, 4000], 16, 4, 4, 64, "f16"),
+    ([1024] * 64, 8, 8, 1, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("lens,H,Hk,Nq,d,dtype", SHARED)
+def test_shared_gpu(la, lens, H, Hk, Nq, d, dtype):
+    """shared_gpu: kind auto takes the dynamic pull on one workgroup per CU
+    wherever it would take lean, and the call gives the explicit pull's bits
+    (pull output does not depend on the grid or on which workgroup took a
+    chunk), within the oracle bar."""
+    say(f"[shared] B={len(lens)} H={H} Hk={Hk} Nq={Nq} d={d} {dtype}")
+    dt = la.LA_BF16 if dtype == "bf16" else la.LA_F16
+    base = la.la_select(lens, H, d, dt, kv_heads=Hk, q_tokens=Nq)
+    pick, grid = la.la_select(lens, H, d, dt, kv_heads=Hk, q_tokens=Nq, shared_gpu=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if base[0] == "lean":
+        assert (pick, grid) == ("pull", cus)
+    else:
+        assert (pick, grid) == base
+    inp = W.make_custom(lens, H, d, dtype, seed=len(lens) + 3 * H, device="cuda", kv_heads=Hk,
+                        q_tokens=Nq)
+    shape = tuple(inp.q.shape)
+    rows = int(np.prod(shape[:-1]))
+    outs = []
+    for opts in ({"kind": "auto", "shared_gpu": True}, {"kind": pick, "grid": grid}):
+        out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+        m = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+        l = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+        la.la_decode_ex(inp.q, inp.k, inp.v, lens, len(lens), H, d, inp.scale, out, m_out=m,
+                        l_out=l, kv_heads=Hk, q_tokens=Nq, **opts)
+        la.la_sync_check()
+        outs.append([t.cpu().numpy() for t in (out, m, l)])
+    for x, y in zip(*outs):
+        np.testing.assert_array_equal(x, y)
+    Or = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                            inp.scale, dtype, workers=16, kv_heads=Hk)[0]
+    err = float(np.max(np.abs(outs[0][0] - Or)))
+    assert err <= 1e-3, err
+    say(f"[shared] {base[0]} -> {pick}@{grid}, max|dO|={err:.2e}")
