@@ -196,6 +196,11 @@ la_status get_workspace(hipStream_t stream, Workspace** out) {
     }
     for (auto& s : w->ring) {
         if (hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
+            s.ev = nullptr;
+            for (auto& r : w->ring)
+                if (r.ev != nullptr) (void)hipEventDestroy(r.ev);
+            (void)hipStreamSynchronize(stream);   // the control block's clear may be queued
+            (void)hipFree(w->ctl);
             delete w;
             return fail(LA_EHIP, "hipEventCreate failed");
         }
