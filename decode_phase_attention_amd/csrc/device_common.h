@@ -167,16 +167,19 @@ __device__ __forceinline__ void wait_flag(uint32_t* f, uint32_t epoch, uint64_t 
 // Args must be the kernel's only argument (offset 0).
 typedef const __attribute__((address_space(4))) int32_t* ktp_t;
 typedef const __attribute__((address_space(4))) uint32_t* ktok_t;
+typedef const __attribute__((address_space(4))) SchedArgs* ksa_t;
 struct KSched {
     ktp_t tp;
     ktok_t tok;
+    ksa_t sa;
 };
 template <class Args>
 __device__ __forceinline__ KSched kernarg_sched() {
     typedef const __attribute__((address_space(4))) char* kchar_t;
     const kchar_t base = (kchar_t)__builtin_amdgcn_kernarg_segment_ptr();
     return {(ktp_t)(base + offsetof(Args, sched) + offsetof(SchedArgs, tp)),
-            (ktok_t)(base + offsetof(Args, sched) + offsetof(SchedArgs, tok))};
+            (ktok_t)(base + offsetof(Args, sched) + offsetof(SchedArgs, tok)),
+            (ksa_t)(base + offsetof(Args, sched))};
 }
 
 // LDS for the segment walk over lengths read from device memory.
@@ -267,16 +270,23 @@ struct SegCursor<kSrcDevice> {
 
 template <>
 struct SegCursor<kSrcTables> {
-    const SchedArgs& a;
+    ksa_t ka;
     int si, s1;                 // next segment, end
     int iter;                   // linear iteration of the next segment
 
-    __device__ SegCursor(const SchedArgs& a_, KSched, SchedLds&, int c)
-        : a(a_), si(a_.cta_seg[c]), s1(a_.cta_seg[c + 1]), iter(a_.cta_begin[c]) {}
+    __device__ SegCursor(const SchedArgs& a_, KSched k, SchedLds&, int c)
+        : ka(k.sa), si(a_.cta_seg[c]), s1(a_.cta_seg[c + 1]), iter(a_.cta_begin[c]) {}
     __device__ bool bad() const { return false; }
 
+    // The table pointers are read from the kernel arguments at every segment
+    // (an opaque copy of the kernarg pointer keeps them from being hoisted):
+    // kept live across the grouped kernel's step loop they pushed it past its
+    // scalar registers and into scratch.
     __device__ bool next(LeanSeg& s) {
         if (si >= s1) return false;
+        ksa_t p = ka;
+        asm volatile("" : "+s"(p));
+        const auto& a = *p;
         const int4 sg = a.seg[si++];
         s.u = sg.x;
         s.t0 = sg.y;
