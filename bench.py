@@ -311,8 +311,9 @@ def host_cpu():
     return cpu, len(os.sched_getaffinity(0))
 
 
-# Worker threads of the CPU baseline: the GPU machine allots 16 host CPUs to its
-# one GPU, whatever the affinity mask shows, so pools are sized to that share.
+# Worker threads of the CPU baseline: a one-GPU host share here is 16 CPUs,
+# whatever the affinity mask shows, so pools are sized to that share (and the
+# visible count is reported beside it).
 CPU_SHARE = 16
 
 
