@@ -130,6 +130,7 @@ struct Capacity {
     int coresident;   // occupancy per CU x CUs: the largest grid a launch may use
     int preferred;    // default grid: kWgPerCu workgroups on every CU
     int cus;          // compute units of the device
+    int per_cu;       // workgroups of the kernel one CU holds at once
 };
 std::map<std::pair<int, const void*>, Capacity> g_capacity;
 
@@ -246,9 +247,42 @@ la_status capacity(int dtype, int d, bool grouped, Capacity* out) {
     c.coresident = per_cu * cus;
     c.preferred = (per_cu < kWgPerCu ? per_cu : kWgPerCu) * cus;
     c.cus = cus;
+    c.per_cu = per_cu;
     g_capacity[key] = c;
     *out = c;
     return LA_OK;
+}
+
+// The CUs a stream's kernels may run on: all of the device's, unless the
+// stream was created with a CU mask (hipExtStreamCreateWithCUMask), whose set
+// bits are counted. Asked on every call (a host-side lookup, well under a
+// microsecond), so a stream handle reused for a stream with another mask is
+// never answered from a stale copy.
+int stream_cus(hipStream_t stream, int cus) {
+    constexpr int kMaxWords = 64;
+    uint32_t mask[kMaxWords];
+    const int words = (cus + 31) / 32;
+    if (words > kMaxWords) return cus;
+    if (hipExtStreamGetCUMask(stream, (uint32_t)words, mask) != hipSuccess) {
+        (void)hipGetLastError();   // leave no error for the caller's next check
+        return cus;
+    }
+    int n = 0;
+    for (int i = 0; i < words; ++i) n += __builtin_popcount(mask[i]);
+    return n >= 1 && n < cus ? n : cus;
+}
+
+// A lean kernel's limits on the CUs of one stream. Its hosts wait for their
+// peers, so every workgroup of a launch must be resident at once on the CUs
+// the stream may use: on a CU-masked stream that is per_cu times the masked
+// CUs, not the device's capacity, and the default grid is one workgroup per
+// CU of the stream.
+struct StreamCap {
+    int cus, coresident, preferred;
+};
+StreamCap on_stream(const Capacity& cap, hipStream_t stream) {
+    const int n = stream_cus(stream, cap.cus);
+    return {n, cap.per_cu * n, (cap.per_cu < kWgPerCu ? cap.per_cu : kWgPerCu) * n};
 }
 
 // Pinned staging slot with room for `bytes`; waits until its previous copy is done.
@@ -436,9 +470,10 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
     Capacity cap;
     la_status st = capacity(o.dtype, d, hd.grouped, &cap);
     if (st != LA_OK) return st;
-    if (o.grid < 0 || o.grid > cap.coresident)
-        return fail(LA_EINVAL, "grid %d outside [1, %d] (co-resident capacity)", o.grid,
-                    cap.coresident);
+    const StreamCap sc = on_stream(cap, stream);
+    if (o.grid < 0 || o.grid > sc.coresident)
+        return fail(LA_EINVAL, "grid %d outside [1, %d] (co-resident capacity on the %d CUs "
+                    "the stream may use)", o.grid, sc.coresident, sc.cus);
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
     const int U = hd.units_per_req();
     int64_t I = 0;
@@ -447,10 +482,10 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
     if (dev_lens) {
         // The lengths are known only in the launch: the grid is the requested
         // (or default) one, and workgroups beyond the iterations stay empty.
-        G = o.grid > 0 ? o.grid : cap.preferred;
+        G = o.grid > 0 ? o.grid : sc.preferred;
     } else {
         const char* why = "";
-        const int rc = la::schedule_dims(ctx_lens, B, U, L, o.grid > 0 ? o.grid : cap.preferred,
+        const int rc = la::schedule_dims(ctx_lens, B, U, L, o.grid > 0 ? o.grid : sc.preferred,
                                          &I, &G, &max_rows, &why);
         if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
     }
@@ -464,7 +499,7 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
         if (it != g_dev.end()) budget = it->second.budget;
     }
     if (budget != nullptr) {
-        const int g = budget->admit(w->stream, G, cap.coresident);
+        const int g = budget->admit(w->stream, G, sc.coresident);
         if (g < G) {
             if (dev_lens) {
                 G = g;
@@ -576,7 +611,7 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
         if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
         HIP_TRY(la::launch_lean_gqa(o.dtype, d, a, G, stream, coop));
         if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));
-        lean_launched(w, budget, G, cap.coresident);
+        lean_launched(w, budget, G, sc.coresident);
         return LA_OK;
     }
     la::LeanArgs a{};
@@ -602,7 +637,7 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
     HIP_TRY(la::launch_lean(o.dtype, d, a, G, stream, coop));
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));
-    lean_launched(w, budget, G, cap.coresident);
+    lean_launched(w, budget, G, sc.coresident);
     return LA_OK;
 }
 
@@ -823,20 +858,21 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
 
 // la_select_for with the current device's CU count and lean capacity.
 la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int d,
-                           const la_opts& o, int* kind, int* grid) {
+                           const la_opts& o, hipStream_t stream, int* kind, int* grid) {
     Capacity cap;
     la_status st = capacity(o.dtype, d, hd.grouped, &cap);
     if (st != LA_OK) return st;
-    int dev = 0, cus = 0;
-    HIP_TRY(hipGetDevice(&dev));
-    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    const StreamCap sc = on_stream(cap, stream);
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
     const char* why = "";
-    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, d, hd.grouped, cus,
-                                   cap.coresident, kind, grid, &why);
+    const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, d, hd.grouped, sc.cus,
+                                   sc.coresident, kind, grid, &why);
     if (rc != 0) return fail(rc == 1 ? LA_EINVAL : LA_EUNSUPPORTED, "%s", why);
-    // other work on the device: chunks pulled as CUs free up, not a static split
-    if (o.shared_gpu != 0 && *kind == LA_KIND_LEAN) {
+    // Other work on the device (stated by the caller), or single heads on a
+    // stream confined to part of the CUs: chunks pulled as CUs free up rather
+    // than a static split. Grouped heads on such a stream keep lean on a grid
+    // of the stream's CUs, which measured faster than pull there.
+    if (*kind == LA_KIND_LEAN && (o.shared_gpu != 0 || (sc.cus < cap.cus && !hd.grouped))) {
         *kind = LA_KIND_PULL;
         *grid = cap.preferred;
     }
@@ -998,7 +1034,9 @@ la_status la_decode_ex(const void* q, const void* k, const void* v, const int32_
     }
     if (o.kind == LA_KIND_AUTO) {
         int kind = 0, grid = 0;
-        if ((st = select_on_device(ctx_lens, B, hd, d, o, &kind, &grid)) != LA_OK) return st;
+        if ((st = select_on_device(ctx_lens, B, hd, d, o, (hipStream_t)stream, &kind, &grid)) !=
+            LA_OK)
+            return st;
         o.kind = kind;
         if (o.grid == 0) o.grid = grid;
     }
@@ -1140,7 +1178,8 @@ la_status la_select(const int32_t* ctx_lens, int B, int H, int d, const la_opts*
         return fail(LA_EINVAL, "q_tokens %d outside [0, %d]", o.q_tokens, kMaxQTokens);
     if (o.tile_tokens < 0) return fail(LA_EINVAL, "tile_tokens must be >= 0");
     std::lock_guard<std::mutex> lock(g_mu);
-    return select_on_device(ctx_lens, B, heads_of(H, o.kv_heads, o.q_tokens), d, o, kind, grid);
+    return select_on_device(ctx_lens, B, heads_of(H, o.kv_heads, o.q_tokens), d, o, nullptr, kind,
+                            grid);
 }
 
 int la_default_tile(int d) { return (d == 64 || d == 128) ? la::chunk_rows(d) : 0; }

@@ -48,6 +48,13 @@
  *    la_sync_check() reports.
  *  - Nothing throws across this boundary. On failure la_last_error() returns a
  *    message for the calling thread.
+ *  - Reproducibility: for a given kind, grid and tile size every sum and merge
+ *    runs in a fixed order, so outputs are bitwise the same from call to call,
+ *    with one exception. A single-head lean or pull workgroup whose CU holds
+ *    more of its launch's workgroups than their fair share (other work taking
+ *    CUs, or a CU-masked stream) reads K by whole rows, which adds each score's
+ *    partial products in another order; outputs then stay within the usual
+ *    tolerance, but their last bits depend on where the workgroups ran.
  *  - Workspaces (partials buffer, flags, schedule tables, pinned staging) are
  *    owned by the library, one per (device, stream), allocated on first use and
  *    freed by la_shutdown(). Calls on the same stream are ordered; calls from
@@ -111,11 +118,22 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  * Options for la_decode_ex. Zero-initialise (or call la_opts_init) and set
  * what you need.
  *   kind        la_kind. LA_KIND_AUTO resolves kind and (if grid is 0) the
- *               grid with la_select; it takes no tile_owner or
+ *               grid as la_select does, on the CUs the stream may use: on a
+ *               stream created with a CU mask (hipExtStreamCreateWithCUMask)
+ *               the grid rule counts the masked CUs, and a single-head lean
+ *               pick becomes LA_KIND_PULL on one workgroup per CU of the
+ *               device (grouped heads keep lean there: measured with 7/8 of
+ *               the CUs, lean on their grid took 547 us on the grouped ragged
+ *               batch where pull took 602, and pull 1268 us on 512k where
+ *               lean on the device grid took 1554). It takes no tile_owner or
  *               cta_timestamps, since those depend on the kind
  *   tile_tokens LeanTile size in tokens; 0 = library default for d
- *   grid        lean: workgroups in the persistent grid; 0 = la_default_grid
- *               (one per CU); larger than la_max_grid -> LA_EINVAL
+ *   grid        lean: workgroups in the persistent grid; 0 = one per CU the
+ *               stream may use (la_default_grid on a stream without a CU
+ *               mask). Every workgroup must be resident at once on those
+ *               CUs, so a grid above la_max_grid scaled to the stream's
+ *               share of the CUs (its mask's set bits over the device's
+ *               CUs) -> LA_EINVAL
  *   num_splits  fixed split: pieces per head; 0 = smallest power of two with
  *               B*H*splits >= capacity, capped at 64
  *   cooperative lean: 1 = hipLaunchCooperativeKernel, which refuses a grid
@@ -346,7 +364,9 @@ la_status la_select_for(const int32_t* ctx_lens, int B, int H, int d, int kv_hea
                         int tile_tokens, int cus, int coresident, int* kind, int* grid);
 
 /* la_select: la_select_for on the current device, with d, dtype, kv_heads,
- * q_tokens and tile_tokens taken from `opts` (which may be null: defaults).
+ * q_tokens and tile_tokens taken from `opts` (which may be null: defaults),
+ * for a stream that may use every CU (LA_KIND_AUTO on a CU-masked stream
+ * decides on that stream's CUs; see la_opts.kind).
  * With opts->shared_gpu set, a lean pick becomes LA_KIND_PULL on the default
  * pull grid (one workgroup per CU), as LA_KIND_AUTO does then. */
 la_status la_select(const int32_t* ctx_lens, int B, int H, int d, const la_opts* opts, int* kind,
@@ -385,7 +405,8 @@ int la_default_tile(int d);
  * current device: occupancy per CU times the CU count. Returns <= 0 on error.
  * This is the bound on la_opts.grid for calls with one query column per K/V
  * head; calls with kv_heads < H or q_tokens > 1 run the grouped kernel, whose
- * bound is la_max_grid_grouped.
+ * bound is la_max_grid_grouped. On a CU-masked stream the bound is the
+ * occupancy per CU times the stream's CUs.
  */
 int la_max_grid(int d, int dtype);
 
@@ -394,7 +415,8 @@ int la_max_grid_grouped(int d, int dtype);
 
 /*
  * Grid the lean kind uses when la_opts.grid is 0: one workgroup per CU on the
- * current device (never more than la_max_grid). Returns <= 0 on error.
+ * current device (never more than la_max_grid); on a CU-masked stream, one
+ * per CU of its mask. Returns <= 0 on error.
  */
 int la_default_grid(int d, int dtype);
 

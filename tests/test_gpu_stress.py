@@ -348,3 +348,71 @@ def test_crowded_cus(la, dtype, d, lens, H, n_cus):
     for o in outs:
         err = float(np.max(np.abs(o.cpu().numpy() - ref)))
         assert err <= 1e-3, err
+
+
+@pytest.mark.parametrize("n_cus", [200, 96])
+def test_stream_cus(la, n_cus):
+    """A stream confined to part of the CUs. Lean's default grid is one
+    workgroup per CU of the stream (the executed tile map shows it, and the
+    output has the bits of an explicit call at that grid); a grid beyond what
+    those CUs hold at once is refused before launch; kind auto takes the pull
+    kind for single heads and lean on the stream's CUs for grouped ones, each
+    with the bits of the explicit call. Everything meets the oracle. The
+    single-head shape gives every workgroup fewer than 8 tiles, so the
+    crowding watch is off and the bits cannot depend on where the dispatcher
+    put the workgroups (a wave that finds its CU crowded sums its scores in
+    another order)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_cus = min(n_cus, cus - 1)
+    st = _masked_stream(n_cus)
+
+    def call(inp, out, stream=None, **o):
+        with torch.cuda.stream(stream or torch.cuda.current_stream()):
+            la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d, inp.scale, out,
+                            kv_heads=inp.Hk, **o)
+        (stream or torch.cuda.current_stream()).synchronize()
+        la.la_sync_check((stream or torch.cuda.current_stream()).cuda_stream)
+        return out.cpu().numpy()
+
+    def fresh(inp):
+        return torch.full((inp.B, inp.H, inp.d), float("nan"), dtype=torch.float32, device="cuda")
+
+    # single heads
+    inp = W.make_custom([3000, 17, 6400], 8, 128, "bf16", seed=n_cus, device="cuda")
+    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), inp.ctx_lens,
+                             inp.scale, "bf16", workers=8)[0]
+    L = la.la_default_tile(128)
+    I = inp.H * sum((n + L - 1) // L for n in inp.ctx_lens)
+    assert n_cus < I < 8 * n_cus and I < 8 * cus
+    say(f"[stream cus] {n_cus} of {cus}: lean default grid, I={I}")
+    owner = torch.full((I,), -1, dtype=torch.int32, device="cuda")
+    got = call(inp, fresh(inp), st, kind="lean", tile_owner=owner)
+    own = owner.cpu().numpy()
+    assert own.min() == 0 and own.max() == n_cus - 1 and np.all(np.diff(own) >= 0)
+    np.testing.assert_array_equal(got, call(inp, fresh(inp), kind="lean", grid=n_cus))
+    assert float(np.max(np.abs(got - ref))) <= 1e-3
+
+    per_cu = la.la_max_grid(128, la.LA_BF16) // cus
+    with pytest.raises(la.LaError, match="CUs"):
+        call(inp, fresh(inp), st, kind="lean", grid=per_cu * n_cus + 1)
+    # the largest grid the stream's CUs hold runs
+    assert float(np.max(np.abs(call(inp, fresh(inp), st, kind="lean", grid=per_cu * n_cus) -
+                               ref))) <= 1e-3
+
+    say(f"[stream cus] {n_cus}: auto, single heads")
+    got = call(inp, fresh(inp), st, kind="auto")
+    np.testing.assert_array_equal(got, call(inp, fresh(inp), kind="pull"))
+    assert float(np.max(np.abs(got - ref))) <= 1e-3
+
+    # grouped heads: lean on a grid chosen for the stream's CUs
+    g = W.make_custom([5000, 900, 33, 20000], 32, 128, "bf16", seed=n_cus + 1, device="cuda",
+                      kv_heads=8)
+    gref = oracle.attend_fp64(W.to_bits(g.q), W.to_bits(g.k), W.to_bits(g.v), g.ctx_lens,
+                              g.scale, "bf16", workers=8, kv_heads=8)[0]
+    per_cu_g = la.la_max_grid_grouped(128, la.LA_BF16) // cus
+    pick, grid = la.la_select_for(g.ctx_lens, 32, 128, n_cus, per_cu_g * n_cus, kv_heads=8)
+    say(f"[stream cus] {n_cus}: auto, grouped -> {pick}@{grid}")
+    assert pick == "lean" and grid <= per_cu_g * n_cus
+    got = call(g, fresh(g), st, kind="auto")
+    np.testing.assert_array_equal(got, call(g, fresh(g), kind="lean", grid=grid))
+    assert float(np.max(np.abs(got - gref))) <= 1e-3
