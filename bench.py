@@ -500,10 +500,13 @@ def masked_stream(hip, torch, n_cus, total):
 
 
 def contention(workloads, steps=10, warmup=3):
-    """Each kind on streams that may use only part of the CUs, as when other
-    kernels of a serving step hold the rest: the static schedules keep their
-    one-per-CU grid and split, the pull kinds rebalance. Prints one JSON line
-    with kernel p50 (us) per kind and available-CU count."""
+    """Each kind on streams that may use only part of the CUs (a CU mask), as
+    when other kernels of a serving step hold the rest. Lean takes its
+    default grid on that stream (one workgroup per CU the stream may use;
+    single heads on under 70% of the CUs one per CU of the device) and, as
+    lean_device_grid, one per CU of the whole device; auto is what kind auto
+    picks on that stream; the pull kinds rebalance. Prints one JSON line with
+    kernel p50 (us) per kind and available-CU count."""
     import torch
 
     import decode_phase_attention_amd as la
@@ -524,7 +527,8 @@ def contention(workloads, steps=10, warmup=3):
         units = inp.Hk * ((cols + 15) // 16) if cols > 1 else inp.H
         I = units * sum((n + L - 1) // L for n in inp.ctx_lens)
         G = la.la_default_grid(inp.d, la.LA_BF16 if inp.dtype == "bf16" else la.LA_F16)
-        kinds = [("lean", "lean", {}), ("pull", "pull", {}),
+        kinds = [("lean", "lean", {}), ("lean_device_grid", "lean", {"grid": G}),
+                 ("auto", "auto", {}), ("pull", "pull", {}),
                  ("chunks", "chunks", {"chunk_tiles": -(-I // G)}),
                  ("fixed_split_8", "fixed_split", {"num_splits": 8}),
                  ("fixed_split_16", "fixed_split", {"num_splits": 16})]
@@ -537,6 +541,14 @@ def contention(workloads, steps=10, warmup=3):
         for f in fracs:
             n = total * f // 8
             st = masked_stream(evs.hip, torch, n, total)
+            # a new stream's first launches run slower: a fifth of a second of
+            # untimed ones first
+            with torch.cuda.stream(st):
+                t0 = time.perf_counter()
+                while time.perf_counter() - t0 < 0.2:
+                    la.la_decode_ex(inp.q, inp.k, inp.v, inp.ctx_lens, inp.B, inp.H, inp.d,
+                                    inp.scale, out, kind="lean", kv_heads=inp.Hk, q_tokens=inp.Nq)
+                    st.synchronize()
             row = {}
             for tag, kind, o in kinds:
                 with torch.cuda.stream(st):
@@ -563,7 +575,9 @@ def contention(workloads, steps=10, warmup=3):
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "decode kernel p50 us when only part of the CUs is available",
                       "device": torch.cuda.get_device_name(0), "cus": total,
-                      "grid": "lean/pull one workgroup per CU of the whole device; chunks "
+                      "grid": "lean its default grid (one workgroup per CU of the stream; "
+                              "single heads on under 70% of the CUs one per CU of the device), "
+                              "lean_device_grid and pull one per CU of the device; chunks "
                               "ceil(I / that grid) tiles each; fixed split K pieces per head",
                       "table": table}), flush=True)
 

@@ -275,14 +275,24 @@ int stream_cus(hipStream_t stream, int cus) {
 // A lean kernel's limits on the CUs of one stream. Its hosts wait for their
 // peers, so every workgroup of a launch must be resident at once on the CUs
 // the stream may use: on a CU-masked stream that is per_cu times the masked
-// CUs, not the device's capacity, and the default grid is one workgroup per
-// CU of the stream.
+// CUs, not the device's capacity. The default grid there is one workgroup per
+// CU of the stream, except for single heads on under 70% of the CUs, which
+// keep the device's default (capped at what the stream's CUs hold): one
+// single-head workgroup per CU reads at most ~34.6 GB/s with K in 16-row
+// blocks, while two on a CU switch to whole rows and reach ~48 GB/s, so with
+// n CUs one per CU takes bytes / (n * 34.6 GB/s) and the device grid about
+// bytes / (128 * 48 GB/s) on a 256-CU device: equal near n = 178 (measured on
+// 512k: 1254 against 1557 us at 224 CUs, 1597 against 1526 at 160). Grouped
+// heads were fastest on one per CU of the stream at every count measured.
 struct StreamCap {
     int cus, coresident, preferred;
 };
-StreamCap on_stream(const Capacity& cap, hipStream_t stream) {
+StreamCap on_stream(const Capacity& cap, hipStream_t stream, bool grouped) {
     const int n = stream_cus(stream, cap.cus);
-    return {n, cap.per_cu * n, (cap.per_cu < kWgPerCu ? cap.per_cu : kWgPerCu) * n};
+    int preferred = (cap.per_cu < kWgPerCu ? cap.per_cu : kWgPerCu) * n;
+    if (!grouped && n < cap.cus && 10 * n < 7 * cap.cus)
+        preferred = std::min(cap.preferred, cap.per_cu * n);
+    return {n, cap.per_cu * n, preferred};
 }
 
 // Pinned staging slot with room for `bytes`; waits until its previous copy is done.
@@ -470,7 +480,7 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
     Capacity cap;
     la_status st = capacity(o.dtype, d, hd.grouped, &cap);
     if (st != LA_OK) return st;
-    const StreamCap sc = on_stream(cap, stream);
+    const StreamCap sc = on_stream(cap, stream, hd.grouped);
     if (o.grid < 0 || o.grid > sc.coresident)
         return fail(LA_EINVAL, "grid %d outside [1, %d] (co-resident capacity on the %d CUs "
                     "the stream may use)", o.grid, sc.coresident, sc.cus);
@@ -862,7 +872,7 @@ la_status select_on_device(const int32_t* ctx_lens, int B, const Heads& hd, int 
     Capacity cap;
     la_status st = capacity(o.dtype, d, hd.grouped, &cap);
     if (st != LA_OK) return st;
-    const StreamCap sc = on_stream(cap, stream);
+    const StreamCap sc = on_stream(cap, stream, hd.grouped);
     const int L = o.tile_tokens > 0 ? o.tile_tokens : la::chunk_rows(d);
     const char* why = "";
     const int rc = la::select_kind(ctx_lens, B, hd.units_per_req(), L, d, hd.grouped, sc.cus,

@@ -123,14 +123,17 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               the grid rule counts the masked CUs, and a single-head lean
  *               pick becomes LA_KIND_PULL on one workgroup per CU of the
  *               device (grouped heads keep lean there: measured with 7/8 of
- *               the CUs, lean on their grid took 547 us on the grouped ragged
- *               batch where pull took 602, and pull 1268 us on 512k where
- *               lean on the device grid took 1554). It takes no tile_owner or
+ *               the CUs, lean on their grid took 556 us on the grouped ragged
+ *               batch where pull took 608, and pull 1245 us on 512k where
+ *               lean on the device grid took 1508). It takes no tile_owner or
  *               cta_timestamps, since those depend on the kind
  *   tile_tokens LeanTile size in tokens; 0 = library default for d
  *   grid        lean: workgroups in the persistent grid; 0 = one per CU the
  *               stream may use (la_default_grid on a stream without a CU
- *               mask). Every workgroup must be resident at once on those
+ *               mask), except single heads on a stream with under 70% of the
+ *               CUs, which keep la_default_grid (within what the stream's CUs
+ *               hold): there two workgroups on a CU read faster than one
+ *               per CU does. Every workgroup must be resident at once on those
  *               CUs, so a grid above la_max_grid scaled to the stream's
  *               share of the CUs (its mask's set bits over the device's
  *               CUs) -> LA_EINVAL
@@ -144,7 +147,9 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               Once lean calls have run on two or more streams of a device,
  *               the library also keeps the unfinished lean launches of all
  *               those streams within the co-resident capacity together (each
- *               counted as grid / capacity of its kernel): a call whose grid
+ *               counted as grid / capacity of its kernel on its stream's
+ *               CUs; streams whose CU masks overlap only in part are not
+ *               covered): a call whose grid
  *               does not fit beside the other streams' unfinished launches
  *               runs on the largest grid that does, or waits on the host for
  *               the oldest of them when none fits. Its outputs then follow the
@@ -234,11 +239,14 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               waits for the workgroups that share a CU with other work,
  *               while chunks pulled from a counter follow the CUs that are
  *               free (the same digest, "The hardware-aware part"). Measured
- *               with 1/8 of the CUs taken, pull lost 5-9% against its own
- *               time on the whole device, lean 31-61%; alone on the device
- *               pull is 0-9% slower than lean. Per-head picks stay. Ignored
- *               with ctx_lens_device, where auto means lean. 0 = the launch
- *               has the device to itself (default).
+ *               with 1/8 of the CUs taken, pull lost 3-10% against its own
+ *               time on the whole device, lean on one workgroup per CU of
+ *               the device 28-63%; alone on the device pull is 0-11% slower
+ *               than lean. Per-head picks stay. Ignored with
+ *               ctx_lens_device, where auto means lean. A stream confined to
+ *               part of the CUs by a CU mask needs no flag: kind auto reads
+ *               the mask (see kind). 0 = the launch has the device to itself
+ *               (default).
  *
  * The pull kinds (siliconandsystems digest, "Exact softmax can be reduced in
  * pieces": workgroups pull the next piece of the global tile order instead of
@@ -415,8 +423,8 @@ int la_max_grid_grouped(int d, int dtype);
 
 /*
  * Grid the lean kind uses when la_opts.grid is 0: one workgroup per CU on the
- * current device (never more than la_max_grid); on a CU-masked stream, one
- * per CU of its mask. Returns <= 0 on error.
+ * current device (never more than la_max_grid). On a CU-masked stream the
+ * call's default follows la_opts.grid's description. Returns <= 0 on error.
  */
 int la_default_grid(int d, int dtype);
 
