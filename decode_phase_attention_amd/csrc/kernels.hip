@@ -34,11 +34,13 @@
 //
 // Epilogues run in wave 0. In the lean kernel a peer (a workgroup that holds
 // a head's tiles but not its first one) publishes its (Obar, m, l) record and
-// raises a flag; the head's host polls all its peers' flags at once and folds
+// raises a flag once the record's stores have completed -- after the first
+// step of its workgroup's next segment, so that the wave does not stop to
+// wait for them; the head's host polls all its peers' flags at once and folds
 // their records in ascending workgroup order (§3.5). The other waves meanwhile
-// go on to the workgroup's next segment -- except at a host with more than
-// kMergeBatch peers, whose segment is its workgroup's last: there all four
-// waves share the merge.
+// go on to the workgroup's next segment without waiting for wave 0's fold --
+// except at a host with more than kMergeBatch peers, whose segment is its
+// workgroup's last: there all four waves share the merge.
 //
 // Exponentials are taken base 2 with log2(e) folded into the scale; m is kept
 // in log2 units inside the kernels and converted back to natural-log units
@@ -364,6 +366,25 @@ struct CuWatch {
     bool rows;
 };
 
+// A lean peer's flag whose record stores have been issued but not yet waited
+// for (wave 0 of a peer whose workgroup has another segment; flag == nullptr
+// in every other wave). The wave goes on streaming its next segment and
+// raises the flag after that segment's first step: by then the stores have
+// had a step's time to complete, so the wait for them that must precede the
+// flag store costs the stream nothing.
+struct PendingFlag {
+    uint32_t* flag;
+    uint32_t epoch;
+};
+__device__ __forceinline__ void raise_pending(PendingFlag* pf) {
+    if (pf != nullptr && pf->flag != nullptr) {
+        drain_stores();   // the record's stores have completed
+        if ((threadIdx.x & 63) == 0)
+            __hip_atomic_store(pf->flag, pf->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pf->flag = nullptr;
+    }
+}
+
 // Stream rows [a, e) of one head (kh/vh point at its row 0, qh at its query
 // row) through the lane groups' online softmax; sx is the wave's slice of
 // the score exchange in LDS (Geo<D>::RW floats). A head spans less than
@@ -391,7 +412,7 @@ struct CuWatch {
 template <int DT, int D>
 __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t* vh, int a, int e,
                                              const uint16_t* qh, float sl2e, float* sx, Acc& acc,
-                                             CuWatch* cw = nullptr) {
+                                             CuWatch* cw = nullptr, PendingFlag* pf = nullptr) {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -400,9 +421,12 @@ __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t*
     const uint4 qv = *reinterpret_cast<const uint4*>(qh + (lane % G::LPR) * 8);
     if (e - a < kBlockMinSteps * G::CH) {
         int base = a;
-        for (; base + G::CH <= e; base += G::CH)
+        for (; base + G::CH <= e; base += G::CH) {
             stream_step_rows<DT, D, kStepFull, false>(kc, vc, base, a, e, qv, sl2e, acc);
+            raise_pending(pf);
+        }
         if (base < e) stream_step_rows<DT, D, kStepTail, false>(kc, vc, base, a, e, qv, sl2e, acc);
+        raise_pending(pf);
         return;
     }
     uint4 qk[G::KK];
@@ -420,6 +444,7 @@ __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t*
         else
             stream_step<DT, D, kStepEdge>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
         base += G::CH;
+        raise_pending(pf);
     }
     for (int j = 1; base + G::CH <= e; base += G::CH, ++j) {
         const bool look = watch && (j % kCheckSteps) == 0;
@@ -430,6 +455,7 @@ __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t*
         else
             stream_step<DT, D, kStepFull>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
         if (look) rows = __builtin_amdgcn_readfirstlane(count) > cw->fair;
+        raise_pending(pf);
     }
     if (base < e) {
         if (rows)
@@ -437,14 +463,19 @@ __device__ __forceinline__ void stream_range(const uint16_t* kh, const uint16_t*
         else
             stream_step<DT, D, kStepTail>(kc, vc, base + G::RW * wave, a, e, qk, sl2e, sx, acc);
     }
+    raise_pending(pf);
     if (watch) cw->rows = rows;
 }
 
-template <int D>
+// NS sets of fold state. The lean kernel keeps two, used by alternate
+// segments: its waves 1-3 leave a fold without waiting for wave 0 to read it,
+// since the next fold writes the other set, and the one after that waits at
+// its barrier for wave 0, which has finished reading by then.
+template <int D, int NS = 1>
 struct alignas(16) Smem {
-    float o[Geo<D>::NG][D];
-    float m[Geo<D>::NG];
-    float l[Geo<D>::NG];
+    float o[NS][Geo<D>::NG][D];
+    float m[NS][Geo<D>::NG];
+    float l[NS][Geo<D>::NG];
     float sx[kWaves][Geo<D>::RW];   // per wave: the scores of its step, for its V lanes
 };
 
@@ -453,43 +484,45 @@ struct alignas(16) Smem {
 template <int D>
 constexpr int kDpl = D / 64;
 
-// Fold the lane groups of the workgroup with f. Wave 0 receives
-// (m, l, Obar[lane + 64k]) of everything the workgroup streamed for this
-// range; the other waves return at once after the second barrier.
-template <int D>
-__device__ __forceinline__ void wg_fold(Smem<D>& sm, const Acc& a, int grp, int sub, float& M,
-                                        float& Ls, float (&O)[kDpl<D>]) {
+// Fold the lane groups of the workgroup with f, through fold state set
+// `set` (0 or 1). Wave 0 receives (m, l, Obar[lane + 64k]) of everything the
+// workgroup streamed for this range. With kTrail the other waves return after
+// a second barrier, once wave 0 has read the state; without it they return at
+// once, and the caller's next fold must use the other set.
+template <int D, bool kTrail = true, int NS>
+__device__ __forceinline__ void wg_fold(Smem<D, NS>& sm, int set, const Acc& a, int grp, int sub,
+                                        float& M, float& Ls, float (&O)[kDpl<D>]) {
     using G = Geo<D>;
-    float4* dst = reinterpret_cast<float4*>(&sm.o[grp][sub * 8]);
+    float4* dst = reinterpret_cast<float4*>(&sm.o[set][grp][sub * 8]);
     dst[0] = make_float4(a.o[0], a.o[1], a.o[2], a.o[3]);
     dst[1] = make_float4(a.o[4], a.o[5], a.o[6], a.o[7]);
     if (sub == 0) {
-        sm.m[grp] = a.m;
-        sm.l[grp] = a.l;
+        sm.m[set][grp] = a.m;
+        sm.l[set][grp] = a.l;
     }
     __syncthreads();
     const int t = threadIdx.x;
     if (t < 64) {
         float mx = kNegInf;
 #pragma unroll
-        for (int g = 0; g < G::NG; ++g) mx = fmaxf(mx, sm.m[g]);
+        for (int g = 0; g < G::NG; ++g) mx = fmaxf(mx, sm.m[set][g]);
         const float mu = (mx == kNegInf) ? 0.f : mx;
         float ls = 0.f, o[kDpl<D>];
 #pragma unroll
         for (int k = 0; k < kDpl<D>; ++k) o[k] = 0.f;
 #pragma unroll 8
         for (int g = 0; g < G::NG; ++g) {
-            const float w = fexp2(sm.m[g] - mu);
-            ls = fmaf(w, sm.l[g], ls);
+            const float w = fexp2(sm.m[set][g] - mu);
+            ls = fmaf(w, sm.l[set][g], ls);
 #pragma unroll
-            for (int k = 0; k < kDpl<D>; ++k) o[k] = fmaf(w, sm.o[g][t + 64 * k], o[k]);
+            for (int k = 0; k < kDpl<D>; ++k) o[k] = fmaf(w, sm.o[set][g][t + 64 * k], o[k]);
         }
         M = mx;
         Ls = ls;
 #pragma unroll
         for (int k = 0; k < kDpl<D>; ++k) O[k] = o[k];
     }
-    __syncthreads();
+    if constexpr (kTrail) __syncthreads();
 }
 
 
@@ -512,7 +545,7 @@ template <int DT, int D, int SRC>
 __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     using G = Geo<D>;
     constexpr int P = kDpl<D>;
-    __shared__ Smem<D> sm;
+    __shared__ Smem<D, 2> sm;
     const int c = blockIdx.x;
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -531,6 +564,8 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
     CuWatch cw{a.cu_fair > 0 ? a.ctl : nullptr, cu_slot(), (uint32_t)a.cu_fair, false};
     if (cw.ctl != nullptr && t == 0) cu_add(a.ctl, cw.slot, 1);
     LeanSeg sg;
+    int set = 0;             // fold state set of the next segment (alternates)
+    PendingFlag pf{nullptr, 0u};
     while (cur.next(sg)) {
         const int u = sg.u;
         const int n = sg.n;
@@ -540,14 +575,17 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         Acc acc;
         acc_init(acc);
         stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, a.q + (int64_t)u * D,
-                            a.sl2e, sm.sx[t >> 6], acc, &cw);
+                            a.sl2e, sm.sx[t >> 6], acc, &cw, &pf);
         if (a.tile_owner != nullptr && t == 0)
             for (int i = sg.t0; i < sg.t1; ++i) a.tile_owner[sg.iter0 + i - sg.t0] = c;
 
         float M = kNegInf, Ls = 0.f, O[P];
 #pragma unroll
         for (int k = 0; k < P; ++k) O[k] = 0.f;   // waves 1-3 start a wide merge from zero
-        wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+        // Waves 1-3 leave the fold without waiting for wave 0 to read it and
+        // go on to the next segment, whose fold uses the other state set.
+        wg_fold<D, false>(sm, set, acc, grp, sub, M, Ls, O);
+        set ^= 1;
         // A host's segment is the last of its workgroup's range. With more
         // than kMergeBatch peers, all four waves wait for and fold a quarter
         // of them each; otherwise the epilogue is wave 0's and the others go
@@ -556,8 +594,9 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
         if (t >= 64 && !wide) continue;
 
         if (!sg.host) {
-            // a peer: publish (Obar, m, l) for the head's host, then raise the
-            // flag to this launch's epoch
+            // a peer: publish (Obar, m, l) for the head's host; the flag goes
+            // up to this launch's epoch once the stores have completed -- after
+            // the first step of the workgroup's next segment, or at its end
             float* p = a.part + (int64_t)c * part_stride(D);
 #pragma unroll
             for (int k = 0; k < P; ++k) store_agent(p + lane + 64 * k, O[k]);
@@ -565,8 +604,7 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
                 store_agent(p + D, M);
                 store_agent(p + D + 1, Ls);
             }
-            drain_stores();
-            if (lane == 0) __hip_atomic_store(&a.flags[c], ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pf = PendingFlag{&a.flags[c], ep};
             continue;
         }
         if (!sg.fin) {
@@ -602,12 +640,14 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
                     if (p0 + j <= p_last) merge_into<P>(M, Ls, O, pm[j], pl[j], po[j]);
             }
             if (wide) {
+                // through the state set the fold did not use: wave 0 read
+                // that one before the fold's barrier
                 if (wave > 0) {
 #pragma unroll
-                    for (int k = 0; k < P; ++k) sm.o[wave][lane + 64 * k] = O[k];
+                    for (int k = 0; k < P; ++k) sm.o[set][wave][lane + 64 * k] = O[k];
                     if (lane == 0) {
-                        sm.m[wave] = M;
-                        sm.l[wave] = Ls;
+                        sm.m[set][wave] = M;
+                        sm.l[set][wave] = Ls;
                     }
                 }
                 __syncthreads();
@@ -615,13 +655,14 @@ __global__ __launch_bounds__(kThreads) void lean_kernel(const LeanArgs a) {
                 for (int v = 1; v < kWaves; ++v) {
                     float ov[P];
 #pragma unroll
-                    for (int k = 0; k < P; ++k) ov[k] = sm.o[v][lane + 64 * k];
-                    merge_into<P>(M, Ls, O, sm.m[v], sm.l[v], ov);
+                    for (int k = 0; k < P; ++k) ov[k] = sm.o[set][v][lane + 64 * k];
+                    merge_into<P>(M, Ls, O, sm.m[set][v], sm.l[set][v], ov);
                 }
             }
         }
         write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
     }
+    raise_pending(&pf);   // a peer segment that was its workgroup's last
     if (cw.ctl != nullptr && t == 0) cu_add(a.ctl, cw.slot, -1);
     if (t == 0) launch_exit(a.ctl, ep);
     stamp_end(a.ts, c);
@@ -742,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void pull_kernel(const PullArgs a) {
             if (a.tile_owner != nullptr)
                 for (int i = it + t; i < t1; i += kThreads) a.tile_owner[i] = blockIdx.x;
             float M = kNegInf, Ls = 0.f, O[P];
-            wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+            wg_fold<D>(sm, 0, acc, grp, sub, M, Ls, O);
             const int side = it == c0 ? 0 : 1;
             it = t1;
             if (t >= 64) continue;   // the epilogue is wave 0's
@@ -828,7 +869,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
         stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, tok0, tok1, a.q + (int64_t)u * D,
                             a.sl2e, sm.sx[t >> 6], acc);
     float M = kNegInf, Ls = 0.f, O[P];
-    wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+    wg_fold<D>(sm, 0, acc, grp, sub, M, Ls, O);
     if (t >= 64) return;
     float* p = a.part + (int64_t)blockIdx.x * part_stride(D);
 #pragma unroll
@@ -880,7 +921,7 @@ __global__ __launch_bounds__(kThreads) void per_head_kernel(const SplitArgs a) {
     stream_range<DT, D>(a.k + row0 * D, a.v + row0 * D, 0, n, a.q + (int64_t)u * D, a.sl2e,
                         sm.sx[t >> 6], acc);
     float M = kNegInf, Ls = 0.f, O[kDpl<D>];
-    wg_fold<D>(sm, acc, grp, sub, M, Ls, O);
+    wg_fold<D>(sm, 0, acc, grp, sub, M, Ls, O);
     if (t < 64) write_out<D>(a.out, a.m_out, a.l_out, u, lane, M, Ls, O);
     stamp_end(a.ts, blockIdx.x);
 }
