@@ -623,6 +623,106 @@ def tile_sweep(workloads, steps=20, warmup=3, rounds=3):
                       "device": torch.cuda.get_device_name(0), "table": table}), flush=True)
 
 
+def pages_sweep_shapes():
+    """The single-GPU sweeps of the LeanAttention evaluation (xllm-io paper
+    review, §5.2 and §5.4), at the shapes the pages state, with uniform
+    contexts and one query token per head:
+    - context sweep at 56 heads, batch 1: 1k, 8k, 32k, 64k and 512k tokens;
+    - head sweep at 64k tokens, batch 1: 16 to 192 heads;
+    - batch sweep at 56 heads (the context sweep's) and 64k tokens (the head
+      sweep's; the pages give no context for it): batch 1 to 16;
+    - the extremes the pages quote: 16 and 24 heads at 512k, 24 heads at 1k;
+    - head dimension 128 at 1k and 512k (56 heads, batch 1).
+    The pages state no precision: d = 64 runs in fp16, d = 128 in bf16, as the
+    many-heads and 512k workloads do."""
+    S = []
+    for n in (1024, 8192, 32768, 65536, 524288):
+        S.append(dict(sweep="context", B=1, H=56, d=64, n=n))
+    for H in (16, 24, 32, 64, 128, 192):
+        S.append(dict(sweep="heads", B=1, H=H, d=64, n=65536))
+    for B in (2, 4, 8, 16):
+        S.append(dict(sweep="batch", B=B, H=56, d=64, n=65536))
+    for H, n in ((16, 524288), (24, 524288), (24, 1024)):
+        S.append(dict(sweep="extremes", B=1, H=H, d=64, n=n))
+    for n in (1024, 524288):
+        S.append(dict(sweep="head_dim_128", B=1, H=56, d=128, n=n))
+    return S
+
+
+def pages_sweep(steps=20, warmup=3, rounds=3):
+    """Lean against the per-head kernel (one workgroup per head over its whole
+    context: the FlashAttention-2 decode schedule) and the fixed split
+    (FlashDecoding's: K splits per head chosen to fill the GPU, plus the best K
+    of 2..64) on the pages' sweep shapes; prints one JSON line. Each shape's
+    inputs are drawn, a second of untimed launches follows the allocation, and
+    the kinds are timed in interleaved rounds (best round's median)."""
+    import torch
+
+    import decode_phase_attention_amd as la
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    la.lib()
+    evs = HipEvents()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    kinds = [("lean", "lean", {}), ("auto", "auto", {}), ("pull", "pull", {}),
+             ("per_head", "per_head", {}), ("fixed_split_heuristic", "fixed_split", {})]
+    kinds += [(f"fixed_split_{K}", "fixed_split", {"num_splits": K}) for K in (2, 4, 8, 16, 32, 64)]
+    rows = []
+    for i, s in enumerate(pages_sweep_shapes()):
+        dt = "f16" if s["d"] == 64 else "bf16"
+        log(f"[pages {i}] {s['sweep']}: B={s['B']} H={s['H']} d={s['d']} n={s['n']} {dt}")
+        inp = W.make_custom([s["n"]] * s["B"], s["H"], s["d"], dt, seed=i, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:
+            time_kind(la, torch, evs, inp, "lean", 5, 1)
+        t = {}
+        for r in range(rounds):
+            for j in range(len(kinds)):
+                tag, kind, o = kinds[(j + r * 4) % len(kinds)]
+                us = time_kind(la, torch, evs, inp, kind, steps, warmup, **o)["kernel_us_p50"]
+                t[tag] = round(min(us, t.get(tag, float("inf"))), 2)
+        fs = {k: v for k, v in t.items() if k.startswith("fixed_split_") and k[12:].isdigit()}
+        fs_best = min(fs.items(), key=lambda kv: kv[1])
+        alg = W.algorithmic_bytes(inp.ctx_lens, inp.H, inp.d)
+        lean = t["lean"]
+        row = {**s, "dtype": dt, "units": s["B"] * s["H"], "cus": cus,
+               "lean_grid": la.la_default_grid(s["d"], la.LA_F16 if dt == "f16" else la.LA_BF16),
+               "auto_pick": "%s@%d" % la.la_select(inp.ctx_lens, inp.H, inp.d,
+                                                    la.LA_F16 if dt == "f16" else la.LA_BF16),
+               "bytes": alg, "kernel_us_p50": t,
+               "fixed_split_best": fs_best[0],
+               "lean_TBps": round(alg / lean / 1e6, 3),
+               "lean_frac_of_8TBps": round(alg / lean / 1e6 / 8.0, 4),
+               "speedup_vs_per_head": round(t["per_head"] / lean, 3),
+               "speedup_vs_fixed_split_heuristic": round(t["fixed_split_heuristic"] / lean, 3),
+               "speedup_vs_fixed_split_best": round(fs_best[1] / lean, 3),
+               "auto_speedup_vs_per_head": round(t["per_head"] / t["auto"], 3),
+               "auto_speedup_vs_fixed_split_heuristic": round(t["fixed_split_heuristic"] / t["auto"], 3)}
+        rows.append(row)
+        log(f"   lean {lean} us ({row['lean_TBps']} TB/s), per-head {t['per_head']}, "
+            f"fixed split {t['fixed_split_heuristic']} (best {fs_best[0]} {fs_best[1]}), "
+            f"x{row['speedup_vs_per_head']} / x{row['speedup_vs_fixed_split_heuristic']}")
+        del inp
+        torch.cuda.empty_cache()
+
+    def stats(key):
+        v = [r[key] for r in rows]
+        return {"mean": round(sum(v) / len(v), 3),
+                "geomean": round(math.exp(sum(math.log(x) for x in v) / len(v)), 3),
+                "max": max(v), "min": min(v)}
+
+    print(json.dumps({"metric": "lean kernel speedup over per-head and fixed-split kernels on "
+                                "the pages' sweep shapes (kernel p50)",
+                      "device": torch.cuda.get_device_name(0), "cus": cus, "shapes": len(rows),
+                      "summary": {k: stats(k) for k in
+                                  ("speedup_vs_per_head", "speedup_vs_fixed_split_heuristic",
+                                   "speedup_vs_fixed_split_best", "auto_speedup_vs_per_head",
+                                   "auto_speedup_vs_fixed_split_heuristic")},
+                      "rows": rows}), flush=True)
+
+
 def decode_loop(workloads, steps=64, warmup=4):
     """Decode steps on a [B, Hk, S, d] cache (kv_stride = S) whose contexts
     grow by one token per request every step (the rows are already in the
@@ -768,6 +868,9 @@ def main():
                     help="also append one JSON record per measured kernel kind to this file")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="instead of the headline line: the lean kernel at tile sizes 32..2048")
+    ap.add_argument("--pages-sweep", action="store_true",
+                    help="instead of the headline line: lean against per-head and fixed split "
+                         "on the pages' context, head, batch and head-dim sweeps")
     ap.add_argument("--decode-loop", action="store_true",
                     help="instead of the headline line: decode steps on a [B, Hk, S, d] cache "
                          "whose contexts grow by one token per step")
@@ -784,6 +887,9 @@ def main():
         return
     if args.tile_sweep:
         tile_sweep(["512k", "ragged", "65k", "many-heads", "gqa-512k", "gqa8-ragged"])
+        return
+    if args.pages_sweep:
+        pages_sweep()
         return
     if args.decode_loop:
         decode_loop(["512k", "ragged", "gqa8-ragged", "mqa-32k", "spec4-ragged"]
