@@ -11,7 +11,11 @@
 //      single stream, which is fastest while a workgroup's range holds few
 //      heads. With at least two heads per CU, every workgroup switches heads,
 //      and the fixed costs of a switch (loading q, the cross-wave fold, the
-//      epilogue) stall a CU that runs one workgroup; two per CU hide them.
+//      epilogue) stall a CU that runs one workgroup; two per CU hide them --
+//      unless the heads average kLongUnitTiles tiles or more, where a
+//      workgroup switches heads a few times in a long range and one per CU
+//      is faster again (measured on three draws of the 16-request ragged
+//      batch, 178-423 tiles per head on average: 0.2-1.6%).
 //   2. Kind. If the lean schedule on that grid splits no head, every
 //      workgroup holds whole heads: the per-head decomposition (review §4.3's
 //      FlashAttention-2 case) does the same work with no tables, partials or
@@ -47,6 +51,7 @@
 namespace la {
 
 constexpr int64_t kMinTilesPerUnitGrouped = 4;
+constexpr int64_t kLongUnitTiles = 128;
 constexpr int64_t kShortUnitBytes = 256 * 1024;
 
 int select_kind(const int32_t* ctx_lens, int B, int units, int L, int d, bool grouped, int cus,
@@ -56,16 +61,19 @@ int select_kind(const int32_t* ctx_lens, int B, int units, int L, int d, bool gr
         return 1;
     }
     const int64_t U = (int64_t)B * units;
-    int G = U >= 2 * (int64_t)cus ? 2 * cus : cus;
-    if (G > coresident) G = coresident;
     int32_t n_max = 0;
+    int64_t tiles = 0;   // tiles of one unit of every request
     for (int b = 0; b < B; ++b) {
         if (ctx_lens[b] < 1) {
             *why = "select: every context length must be >= 1";
             return 1;
         }
         n_max = ctx_lens[b] > n_max ? ctx_lens[b] : n_max;
+        tiles += ((int64_t)ctx_lens[b] + L - 1) / L;
     }
+    const bool long_units = tiles >= kLongUnitTiles * (int64_t)B;
+    int G = U >= 2 * (int64_t)cus && !long_units ? 2 * cus : cus;
+    if (G > coresident) G = coresident;
     if (!grouped && U <= cus && (int64_t)n_max * 4 * d <= kShortUnitBytes) {
         *kind = 2;
         *grid = G;

@@ -354,9 +354,10 @@ la_status la_decode_noalloc(const void* q, const void* k_cache, const void* v_ca
  * in the spirit of the siliconandsystems digest ("A useful control policy"),
  * built on the reductions of xllm-io paper review §4.3:
  *   grid  = 2*cus if B * units >= 2*cus (at least two heads per CU, whose
- *           switches a second workgroup per CU hides), else cus; capped at
- *           coresident. units = H, or with kv_heads / q_tokens the grouped
- *           units (K/V head x block of 16 query columns).
+ *           switches a second workgroup per CU hides) and the heads average
+ *           fewer than 128 tiles (sum over b of ceil(n_b / tile) < 128 * B),
+ *           else cus; capped at coresident. units = H, or with kv_heads /
+ *           q_tokens the grouped units (K/V head x block of 16 query columns).
  *   kind  = LA_KIND_PER_HEAD if the lean schedule on that grid splits no
  *           head (every workgroup holds whole heads) and, for grouped units,
  *           they average at least 4 tiles; also LA_KIND_PER_HEAD, with one query column per

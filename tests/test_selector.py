@@ -25,7 +25,8 @@ def expected(lens, H, d, cus, cores, Hk=None, Nq=1, L=None):
     Hk = Hk or H
     U = units(H, Hk, Nq)
     L = L or la.la_default_tile(d)
-    G = 2 * cus if len(lens) * U >= 2 * cus else cus
+    tiles = sum((n + L - 1) // L for n in lens)       # one unit of every request
+    G = 2 * cus if len(lens) * U >= 2 * cus and tiles < 128 * len(lens) else cus
     G = min(G, cores)
     single = H // Hk * Nq == 1
     if single and len(lens) * U <= cus and max(lens) * 4 * d <= 256 * 1024:
@@ -67,10 +68,14 @@ def test_identities_of_the_pages():
     assert la.la_select_for([512] * 128, 64, 128, 256, 1024, kv_heads=8) == ("per_head", 512)
     # uniform lengths that do not divide evenly: heads get split -> lean
     assert la.la_select_for([4096] * 9, 32, 128, 256, 1024) == ("lean", 256)
-    # ragged batch of many heads: lean on two workgroups per CU
-    assert la.la_select_for([1000, 30000, 7, 90000] * 4, 32, 128, 256, 1024) == ("lean", 512)
+    # ragged batch of many heads: lean on two workgroups per CU ...
+    assert la.la_select_for([1000, 3000, 7, 9000] * 4, 32, 128, 256, 1024) == ("lean", 512)
+    # ... on one per CU once the heads average 128 tiles or more (mean 237 here)
+    assert la.la_select_for([1000, 30000, 7, 90000] * 4, 32, 128, 256, 1024) == ("lean", 256)
+    assert la.la_select_for([16129, 16384] * 8, 32, 128, 256, 1024) == ("lean", 512)  # 127.5
+    assert la.la_select_for([16129, 16385] * 8, 32, 128, 256, 1024) == ("lean", 256)  # 128
     # the grid never exceeds the co-resident capacity
-    assert la.la_select_for([1000, 30000, 7, 90000] * 4, 32, 128, 256, 384)[1] == 384
+    assert la.la_select_for([1000, 3000, 7, 9000] * 4, 32, 128, 256, 384)[1] == 384
     # explicit tile size: 64 heads of 5 tiles on 256 workgroups -> split
     assert la.la_select_for([600] * 2, 32, 128, 256, 1024, tile_tokens=128) == ("lean", 256)
     # short heads that all run at once: per head (1024 tokens x 4 x 64 bytes = 256 KiB)
