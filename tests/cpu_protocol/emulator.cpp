@@ -5,7 +5,9 @@
 //   lean  the static stream-K schedule (xllm-io paper review of arXiv
 //         2405.10480, §3.5): the real tables from the library's host
 //         scheduler; a peer publishes its partial (m, l, Obar) and raises its
-//         flag to the launch's epoch; a head's host waits for its peers'
+//         flag to the launch's epoch (after the first step of its
+//         workgroup's next segment, or once the workgroup is done, as the
+//         kernel does); a head's host waits for its peers'
 //         flags to hold that epoch (bounded, like the kernel's watchdog),
 //         folds their partials in workgroup order with f (§3.2) and
 //         normalises. Several launches run back to back on one exchange
@@ -150,22 +152,31 @@ int run_lean(const Problem& P, int grid, int drop, int wait_ms, int launches, un
             std::mt19937 rng(seed * 7919u + c + 104729u * (unsigned)launch);
             uint32_t e = epoch.load(std::memory_order_relaxed) + 1u;
             if (e == 0u) e = 1u;
+            // A peer's flag goes up after the first step of its workgroup's
+            // next segment, as in the kernel, or when the workgroup is done.
+            bool pending = false;
+            auto raise = [&]() {
+                if (!pending) return;
+                pending = false;
+                if (c == drop)
+                    std::this_thread::sleep_for(
+                        std::chrono::milliseconds(launch == 0 ? 2 * wait_ms : wait_ms / 4));
+#ifdef EMU_UNEPOCHED
+                flag[c].store(1, kRelease);
+#else
+                flag[c].store(e, kRelease);
+#endif
+            };
             for (int si = cta_seg[c]; si < cta_seg[c + 1]; ++si) {
                 const int32_t* r = &seg[(size_t)si * 6];
                 const int u = r[1], t0 = r[2], t1 = r[3], is_host = r[4], is_fin = r[5];
-                nap(rng);
+                nap(rng);       // the segment's first step
+                raise();
                 Rec acc = partial(P, u, t0, t1);
                 if (!is_host) {
                     part[c] = acc;
                     nap(rng);
-                    if (c == drop)
-                        std::this_thread::sleep_for(
-                            std::chrono::milliseconds(launch == 0 ? 2 * wait_ms : wait_ms / 4));
-#ifdef EMU_UNEPOCHED
-                    flag[c].store(1, kRelease);
-#else
-                    flag[c].store(e, kRelease);
-#endif
+                    pending = true;
                     continue;
                 }
                 bool gave_up = false;
@@ -196,6 +207,7 @@ int run_lean(const Problem& P, int grid, int drop, int wait_ms, int launches, un
                 }
                 if (!gave_up) finish(P, u, acc, out, mo, lo);
             }
+            raise();
             if (exited.fetch_add(1, std::memory_order_relaxed) == (uint32_t)G - 1) {
                 exited.store(0, std::memory_order_relaxed);
                 epoch.store(e, std::memory_order_relaxed);
