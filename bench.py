@@ -632,7 +632,10 @@ def pages_sweep_shapes():
     - batch sweep at 56 heads (the context sweep's) and 64k tokens (the head
       sweep's; the pages give no context for it): batch 1 to 16;
     - the extremes the pages quote: 16 and 24 heads at 512k, 24 heads at 1k;
-    - head dimension 128 at 1k and 512k (56 heads, batch 1).
+    - head dimension 128 at 1k and 512k (56 heads, batch 1);
+    - few heads at long contexts, where the stream-K schedule departs most
+      from the per-head and fixed-split ones (review §4.3): 1, 2 and 4 heads
+      of 512k tokens, one of 128k, four of 32k (d = 128).
     The pages state no precision: d = 64 runs in fp16, d = 128 in bf16, as the
     many-heads and 512k workloads do."""
     S = []
@@ -646,6 +649,8 @@ def pages_sweep_shapes():
         S.append(dict(sweep="extremes", B=1, H=H, d=64, n=n))
     for n in (1024, 524288):
         S.append(dict(sweep="head_dim_128", B=1, H=56, d=128, n=n))
+    for H, n in ((1, 524288), (2, 524288), (4, 524288), (1, 131072), (4, 32768)):
+        S.append(dict(sweep="few_heads", B=1, H=H, d=128, n=n))
     return S
 
 
@@ -653,7 +658,8 @@ def pages_sweep(steps=20, warmup=3, rounds=3):
     """Lean against the per-head kernel (one workgroup per head over its whole
     context: the FlashAttention-2 decode schedule) and the fixed split
     (FlashDecoding's: K splits per head chosen to fill the GPU, plus the best K
-    of 2..64) on the pages' sweep shapes; prints one JSON line. Each shape's
+    of 2..64, or up to one workgroup per CU for every head) on the pages'
+    sweep shapes; prints one JSON line. Each shape's
     inputs are drawn, a second of untimed launches follows the allocation, and
     the kinds are timed in interleaved rounds (best round's median)."""
     import torch
@@ -667,9 +673,11 @@ def pages_sweep(steps=20, warmup=3, rounds=3):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     kinds = [("lean", "lean", {}), ("auto", "auto", {}), ("pull", "pull", {}),
              ("per_head", "per_head", {}), ("fixed_split_heuristic", "fixed_split", {})]
-    kinds += [(f"fixed_split_{K}", "fixed_split", {"num_splits": K}) for K in (2, 4, 8, 16, 32, 64)]
     rows = []
     for i, s in enumerate(pages_sweep_shapes()):
+        # split counts up to one workgroup per CU for every head
+        Ks = [K for K in (2, 4, 8, 16, 32, 64, 128, 256) if K <= 64 or K * s["B"] * s["H"] <= cus]
+        kinds_s = kinds + [(f"fixed_split_{K}", "fixed_split", {"num_splits": K}) for K in Ks]
         dt = "f16" if s["d"] == 64 else "bf16"
         log(f"[pages {i}] {s['sweep']}: B={s['B']} H={s['H']} d={s['d']} n={s['n']} {dt}")
         inp = W.make_custom([s["n"]] * s["B"], s["H"], s["d"], dt, seed=i, device="cuda")
@@ -679,8 +687,8 @@ def pages_sweep(steps=20, warmup=3, rounds=3):
             time_kind(la, torch, evs, inp, "lean", 5, 1)
         t = {}
         for r in range(rounds):
-            for j in range(len(kinds)):
-                tag, kind, o = kinds[(j + r * 4) % len(kinds)]
+            for j in range(len(kinds_s)):
+                tag, kind, o = kinds_s[(j + r * 4) % len(kinds_s)]
                 us = time_kind(la, torch, evs, inp, kind, steps, warmup, **o)["kernel_us_p50"]
                 t[tag] = round(min(us, t.get(tag, float("inf"))), 2)
         fs = {k: v for k, v in t.items() if k.startswith("fixed_split_") and k[12:].isdigit()}
@@ -707,19 +715,21 @@ def pages_sweep(steps=20, warmup=3, rounds=3):
         del inp
         torch.cuda.empty_cache()
 
-    def stats(key):
-        v = [r[key] for r in rows]
+    def stats(key, sel):
+        v = [r[key] for r in rows if sel(r)]
         return {"mean": round(sum(v) / len(v), 3),
                 "geomean": round(math.exp(sum(math.log(x) for x in v) / len(v)), 3),
                 "max": max(v), "min": min(v)}
 
+    keys = ("speedup_vs_per_head", "speedup_vs_fixed_split_heuristic",
+            "speedup_vs_fixed_split_best", "auto_speedup_vs_per_head",
+            "auto_speedup_vs_fixed_split_heuristic")
+    pages = lambda r: r["sweep"] != "few_heads"   # noqa: E731
     print(json.dumps({"metric": "lean kernel speedup over per-head and fixed-split kernels on "
                                 "the pages' sweep shapes (kernel p50)",
                       "device": torch.cuda.get_device_name(0), "cus": cus, "shapes": len(rows),
-                      "summary": {k: stats(k) for k in
-                                  ("speedup_vs_per_head", "speedup_vs_fixed_split_heuristic",
-                                   "speedup_vs_fixed_split_best", "auto_speedup_vs_per_head",
-                                   "auto_speedup_vs_fixed_split_heuristic")},
+                      "summary": {k: stats(k, pages) for k in keys},
+                      "summary_few_heads": {k: stats(k, lambda r: not pages(r)) for k in keys},
                       "rows": rows}), flush=True)
 
 
