@@ -199,21 +199,30 @@ def _stream(stream) -> int | None:
 
 
 _torch_mod = None
+_TORCH_DTYPES = {}          # LA_F16 / LA_BF16 -> torch dtype, filled with torch
 
 
 def _torch():
     global _torch_mod
     if _torch_mod is None:
         import torch
+        _TORCH_DTYPES.update({LA_F16: torch.float16, LA_BF16: torch.bfloat16})
         _torch_mod = torch
     return _torch_mod
 
 
 def _check_sizes(q, k_cache, v_cache, out, ctx_lens, B, H, d, kv_heads=0, q_tokens=0,
-                 m_out=None, l_out=None, kv_stride=0):
-    """For torch tensors, reject a call that would read or write past them (the
-    library sees only pointers and cannot check)."""
+                 m_out=None, l_out=None, kv_stride=0, dtype=None):
+    """For torch tensors, reject a call that would read or write past them, or
+    whose q, K and V are not all of the call's input type (the library sees
+    only pointers and cannot check)."""
     Tensor = _torch().Tensor
+    ins = [t for t in (q, k_cache, v_cache) if isinstance(t, Tensor)]
+    if ins:
+        want = ins[0].dtype if dtype is None else _TORCH_DTYPES.get(int(dtype))
+        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+            if isinstance(t, Tensor) and want is not None and t.dtype != want:
+                raise ValueError(f"{name} is {t.dtype}; this call reads {want}")
     rows = int(B) * int(q_tokens or 1) * int(H)
     Hk = int(kv_heads or H)
     if kv_stride:
@@ -246,21 +255,21 @@ def la_decode(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None, d
     if dtype is None:
         dtype = _dtype_of(q)
     arr, p = _lens(ctx_lens)
-    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, dtype=dtype)
     _check(lib().la_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                            float(scale), _ptr(out), _stream(stream), int(dtype)))
 
 
 def la_decode_bf16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None):
     arr, p = _lens(ctx_lens)
-    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, dtype=LA_BF16)
     _check(lib().la_decode_bf16(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                                 float(scale), _ptr(out), _stream(stream)))
 
 
 def la_decode_f16(q, k_cache, v_cache, ctx_lens, B, H, d, scale, out, stream=None):
     arr, p = _lens(ctx_lens)
-    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d)
+    _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, dtype=LA_F16)
     _check(lib().la_decode_f16(_ptr(q), _ptr(k_cache), _ptr(v_cache), p, int(B), int(H), int(d),
                                float(scale), _ptr(out), _stream(stream)))
 
@@ -320,7 +329,7 @@ def _marshal(q, k_cache, v_cache, ctx_lens, B, H, d, out, *, dtype, kind, tile_t
     else:
         arr, p = _lens(ctx_lens)
     _check_sizes(q, k_cache, v_cache, out, arr, B, H, d, kv_heads, q_tokens, m_out, l_out,
-                 kv_stride)
+                 kv_stride, o.dtype)
     # keep the lengths array alive with the options until the call returns
     return o, arr, p
 

@@ -188,6 +188,27 @@ def test_binding_rejects_tensors_too_small_for_the_call():
         la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out, kv_heads=2)
 
 
+def test_binding_rejects_mixed_input_types():
+    """q, K and V must all be of the call's input type: the kernels read every
+    input with it, so a bf16 cache under an fp16 query would be decoded as fp16
+    bits (checked on CPU tensors, before any device use)."""
+    import torch
+    q = torch.zeros(2, 8, 64, dtype=torch.float16)
+    kv = torch.zeros(8 * 300, 64, dtype=torch.float16)
+    kvb = kv.bfloat16()
+    out = torch.zeros(2, 8, 64)
+    with pytest.raises(ValueError, match="k_cache is torch.bfloat16"):
+        la.la_decode_ex(q, kvb, kv, [100, 200], 2, 8, 64, 0.125, out)
+    with pytest.raises(ValueError, match="v_cache is torch.bfloat16"):
+        la.la_decode(q, kv, kvb, [100, 200], 2, 8, 64, 0.125, out)
+    with pytest.raises(ValueError, match="q is torch.float16"):
+        la.la_decode_bf16(q, kvb, kvb, [100, 200], 2, 8, 64, 0.125, out)
+    with pytest.raises(ValueError, match="q is torch.float16"):
+        la.la_decode_ex(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out, dtype=la.LA_BF16)
+    with pytest.raises(ValueError, match="device tensors"):        # types agree: the device check
+        la.la_decode_f16(q, kv, kv, [100, 200], 2, 8, 64, 0.125, out)
+
+
 def test_stream_read_validation_before_device_work():
     L = la.lib()
     n = ctypes.c_size_t()
