@@ -123,9 +123,9 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               the grid rule counts the masked CUs, and a single-head lean
  *               pick becomes LA_KIND_PULL on one workgroup per CU of the
  *               device (grouped heads keep lean there: measured with 7/8 of
- *               the CUs, lean on their grid took 556 us on the grouped ragged
- *               batch where pull took 608, and pull 1245 us on 512k where
- *               lean on the device grid took 1508). It takes no tile_owner or
+ *               the CUs, lean on their grid took 563 us on the grouped ragged
+ *               batch where pull took 610, and pull 1264 us on 512k where
+ *               lean on the device grid took 1574). It takes no tile_owner or
  *               cta_timestamps, since those depend on the kind
  *   tile_tokens LeanTile size in tokens; 0 = library default for d
  *   grid        lean: workgroups in the persistent grid; 0 = one per CU the
