@@ -766,6 +766,14 @@ def decode_loop(workloads, steps=64, warmup=4):
             row += Hk * n
         out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device="cuda")
         lens_of = [[n + i + 1 for n in base] for i in range(warmup + steps)]
+        # a second of untimed launches after the allocations, as elsewhere in
+        # this file: kernels run slower for about a second after large ones
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:
+            la.la_decode_ex(inp.q, kc, vc, base, B, H, d, inp.scale, out, kv_heads=Hk,
+                            q_tokens=Nq, kv_stride=S)
+            torch.cuda.synchronize()
         row_out = {}
         for label, ht, grow in (("in_launch_lengths_growing", False, True),
                                 ("host_tables_lengths_growing", True, True),
