@@ -749,19 +749,24 @@ la_status run_pull(Workspace& w, const void* q, const void* k, const void* v,
     for (int b = 0; b < B; ++b) I += (int64_t)U * tiles_of(ctx_lens[b], L);
     if (I > INT32_MAX / 2) return fail(LA_EUNSUPPORTED, "%lld tile iterations do not fit", (long long)I);
     const bool dynamic = o.kind == LA_KIND_PULL;
-    // Default chunk: about eight chunks per workgroup of a one-per-CU grid,
-    // and at least kMinChunkTiles tiles (or one chunk per workgroup).
-    // Measured on MI355X with part of the CUs taken away (a CU-masked
-    // stream): eight to sixteen chunks per workgroup keep a 512k-token decode
-    // within 6% of its full-GPU time with 7/8 of the CUs, where a static split
-    // of the same grid loses a third; chunks of less than about 2 MiB spend
-    // too large a share in the per-chunk fold, publish and merge.
+    // Default chunk: about eight chunks per workgroup of a one-per-CU grid
+    // (four for grouped units), and at least kMinChunkTiles tiles (or one
+    // chunk per workgroup). Measured on MI355X with part of the CUs taken
+    // away (a CU-masked stream): eight to sixteen chunks per workgroup keep a
+    // 512k-token decode within 6% of its full-GPU time with 7/8 of the CUs,
+    // where a static split of the same grid loses a third, and four lose
+    // another 8%; chunks of less than about 2 MiB spend too large a share in
+    // the per-chunk fold, publish and merge. The grouped kernels' per-chunk
+    // costs are higher (16 records per piece): four chunks per workgroup ran
+    // 2.6-3.2% faster than eight on the grouped ragged batches on all of the
+    // CUs, on 7/8 and on half of them.
     const int G0 = dynamic && o.grid > 0 ? o.grid : cap.preferred;
     int C = o.chunk_tiles;
     if (C == 0) {
         const int64_t per_wg = (I + G0 - 1) / G0;   // never fewer chunks than workgroups
+        const int64_t chunks_per_wg = hd.grouped ? 4 : 8;
         C = (int)std::max<int64_t>(std::min<int64_t>(kMinChunkTiles, per_wg),
-                                   (I + 8 * (int64_t)G0 - 1) / (8 * (int64_t)G0));
+                                   (I + chunks_per_wg * G0 - 1) / (chunks_per_wg * G0));
     }
     const int64_t nchunks = (I + C - 1) / C;
     if (nchunks > kMaxPullGrid * 64) return fail(LA_EUNSUPPORTED, "too many chunks (%lld)", (long long)nchunks);

@@ -123,8 +123,8 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               the grid rule counts the masked CUs, and a single-head lean
  *               pick becomes LA_KIND_PULL on one workgroup per CU of the
  *               device (grouped heads keep lean there: measured with 7/8 of
- *               the CUs, lean on their grid took 563 us on the grouped ragged
- *               batch where pull took 610, and pull 1264 us on 512k where
+ *               the CUs, lean on their grid took 561 us on the grouped ragged
+ *               batch where pull took 625, and pull 1264 us on 512k where
  *               lean on the device grid took 1574). It takes no tile_owner or
  *               cta_timestamps, since those depend on the kind
  *   tile_tokens LeanTile size in tokens; 0 = library default for d
@@ -197,9 +197,9 @@ la_status la_decode(const void* q, const void* k_cache, const void* v_cache,
  *               speculative decoding (xllm-io paper review, §7.4) and masked
  *               tokens as a case to qualify (siliconandsystems digest,
  *               "Exactness and numerical qualification") but fix no mask.
- *   chunk_tiles pull kinds: tiles per chunk; 0 = ceil(I / (8 G)) with G the
- *               pull grid (or one workgroup per CU), and at least
- *               min(32, ceil(I / G)).
+ *   chunk_tiles pull kinds: tiles per chunk; 0 = ceil(I / (8 G)), or
+ *               ceil(I / (4 G)) for grouped units, with G the pull grid (or
+ *               one workgroup per CU), and at least min(32, ceil(I / G)).
  *   host_tables lean kind: 1 = the host builds the schedule tables and copies
  *               them to the device on `stream` before the kernel; 0 = with up
  *               to 256 requests and 2^32-1 tokens in all, the per-request

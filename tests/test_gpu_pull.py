@@ -178,7 +178,8 @@ def test_grouped_and_several_tokens(la, H, Hk, Nq, d, dtype, kind, grid, C):
     check((out.cpu().numpy(), m.cpu().numpy().reshape(ref[1].shape),
            l.cpu().numpy().reshape(ref[2].shape)), ref, tag=f"grouped {kind}")
     G = grid if grid > 0 else la.la_default_grid(d, la.LA_BF16 if dtype == "bf16" else la.LA_F16)
-    Ceff = C if C > 0 else max(min(32, -(-I // G)), -(-I // (8 * G)))
+    # the default chunk for grouped units: four per workgroup of the grid
+    Ceff = C if C > 0 else max(min(32, -(-I // G)), -(-I // (4 * G)))
     check_owner(owner, I, Ceff, kind, grid if kind == "pull" and grid > 0 else 1 << 30)
 
 
