@@ -644,6 +644,14 @@ la_status run_lean(Workspace* w, const Exchange* fixed, hipStream_t stream, cons
     a.wait_ticks = (uint64_t)g_wait_us * 100u;   // realtime clock runs at 100 MHz
     // lengths on the device: the ranges are known only in the launch
     a.cu_fair = dev_lens || watch_cus(I, G, L, d) ? (G + cap.cus - 1) / cap.cus : 0;
+    // uniform host lengths: every range starts at the same phase in its head,
+    // and the kernel staggers where each workgroup's long ranges begin
+    a.rotate = 0;
+    if (!dev_lens) {
+        bool uniform = true;
+        for (int b = 1; b < B && uniform; ++b) uniform = ctx_lens[b] == ctx_lens[0];
+        a.rotate = uniform ? 1 : 0;
+    }
     if (o.ev_start != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_start, stream));
     HIP_TRY(la::launch_lean(o.dtype, d, a, G, stream, coop));
     if (o.ev_stop != nullptr) HIP_TRY(hipEventRecord((hipEvent_t)o.ev_stop, stream));

@@ -187,6 +187,7 @@ struct SchedLds {
     int32_t tp[kMaxDeviceB + 1];   // tiles of the requests before b (exclusive prefix)
     int64_t tok[kMaxDeviceB + 1];  // tokens of the requests before b
     int bad;                    // a length was out of range, or the tiles overflow
+    int uniform;                // every request has the same length
 };
 
 // Walks a workgroup's segments in order: derived here (SegWalk over prefix
@@ -205,6 +206,7 @@ struct SegCursor<kSrcArgs> {
         w.init(k.tp, k.tok, a.B, a.U, a.G, c);
     }
     __device__ bool bad() const { return false; }
+    __device__ bool uniform() const { return false; }   // host lengths: the host knows
     __device__ bool next(LeanSeg& s) { return w.next(s); }
 };
 
@@ -212,6 +214,7 @@ template <>
 struct SegCursor<kSrcDevice> {
     SegWalk<const int32_t*, const int64_t*> w;
     int bad_;
+    int uniform_;               // every request has the same length
 
     // Every thread constructs it (a barrier inside). The first wave reads the
     // lengths once (up to 16 consecutive requests per lane), checks them, and
@@ -225,12 +228,19 @@ struct SegCursor<kSrcDevice> {
             const int x0 = min(lane * per, a.B), x1 = min(x0 + per, a.B);
             int bad = 0;
             int64_t tp = 0, tk = 0;
+            int32_t nlo = 0x7fffffff, nhi = -0x7fffffff - 1;
             for (int x = x0; x < x1; ++x) {
                 const int32_t n = a.dlens[x];
                 l.tp[x] = n;
                 bad |= n < a.n_min || n > a.n_max;
                 tp += ((int64_t)n + a.L - 1) / a.L;
                 tk += n;
+                nlo = min(nlo, n);
+                nhi = max(nhi, n);
+            }
+            for (int o = 1; o < 64; o <<= 1) {
+                nlo = min(nlo, __shfl_xor(nlo, o, 64));
+                nhi = max(nhi, __shfl_xor(nhi, o, 64));
             }
             int64_t tpi = tp, tki = tk;
             for (int o = 1; o < 64; o <<= 1) {
@@ -258,13 +268,18 @@ struct SegCursor<kSrcDevice> {
                 l.tp[a.B] = (int32_t)total;
                 l.tok[a.B] = tki;
             }
-            if (lane == 0) l.bad = bad;
+            if (lane == 0) {
+                l.bad = bad;
+                l.uniform = nlo == nhi;
+            }
         }
         __syncthreads();
         bad_ = __builtin_amdgcn_readfirstlane(l.bad);
+        uniform_ = __builtin_amdgcn_readfirstlane(l.uniform);
         if (!bad_) w.init(l.tp, l.tok, a.B, a.U, a.G, c);
     }
     __device__ bool bad() const { return bad_ != 0; }
+    __device__ bool uniform() const { return uniform_ != 0; }
     __device__ bool next(LeanSeg& s) { return bad_ ? false : w.next(s); }
 };
 
@@ -277,6 +292,7 @@ struct SegCursor<kSrcTables> {
     __device__ SegCursor(const SchedArgs& a_, KSched k, SchedLds&, int c)
         : ka(k.sa), si(a_.cta_seg[c]), s1(a_.cta_seg[c + 1]), iter(a_.cta_begin[c]) {}
     __device__ bool bad() const { return false; }
+    __device__ bool uniform() const { return false; }   // host lengths: the host knows
 
     // The table pointers are read from the kernel arguments at every segment
     // (an opaque copy of the kernarg pointer keeps them from being hoisted):

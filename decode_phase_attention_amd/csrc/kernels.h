@@ -94,6 +94,7 @@ struct LeanArgs {
     float sl2e;                // scale * log2(e)
     uint64_t wait_ticks;       // 100 MHz clock ticks before a wait gives up
     int cu_fair;               // ceil(grid / CUs): a CU holding more of the launch's workgroups is crowded
+    int rotate;                // 1: long ranges start at a per-workgroup step (uniform contexts)
 };
 
 struct SplitArgs {
