@@ -330,3 +330,30 @@ def test_graph_captured_with_host_lengths(la):
         la.la_sync_check(s.cuda_stream)
         np.testing.assert_array_equal(out.cpu().numpy(), ref)
     del g
+
+
+@pytest.mark.parametrize("lens", [[262144, 262144], [262144, 262143]],
+                         ids=["uniform", "one-token-apart"])
+def test_staggered_starts_same_bits_from_host_and_device(la, lens):
+    """Long ranges of a launch whose lengths are all equal start at a staggered
+    step in each workgroup (the single-head lean kernel). The host decides that
+    from its lengths and the launch from the lengths it reads itself, so the
+    two sources must give the same bits whether the lengths are equal (ranges
+    of 64 steps here, staggered) or one token apart (not staggered); both
+    meet the oracle."""
+    H, d = 4, 128
+    inp = W.make_custom(lens, H=H, d=d, dtype="bf16", seed=sum(lens) % 997, device="cuda")
+    S = max(lens)
+    kc, vc = strided(inp, S)
+    dl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    say(f"[staggered starts] lens={lens}")
+    host = run(la, inp, kc, vc, S, lens=lens)
+    dev = run(la, inp, kc, vc, S, dlens=dl)
+    for x, y in zip(host, dev):
+        np.testing.assert_array_equal(x, y)
+    ref = oracle.attend_fp64(W.to_bits(inp.q), W.to_bits(inp.k), W.to_bits(inp.v), lens,
+                             inp.scale, "bf16", workers=16)
+    err = float(np.max(np.abs(host[0] - ref[0])))
+    assert err <= 1e-3, err
+    del inp, kc, vc
+    torch.cuda.empty_cache()
