@@ -733,6 +733,84 @@ def pages_sweep(steps=20, warmup=3, rounds=3):
                       "rows": rows}), flush=True)
 
 
+def ragged_draws(workloads, seeds, steps=20, warmup=3, rounds=2):
+    """Lean against the fixed split at every split count of 1..64 (and its
+    fill-the-GPU heuristic), the dynamic pull and the per-head kernel on
+    several seeded draws of each ragged workload's log-uniform lengths (the
+    talk summary's ragged batches; xllm-io paper review §5.2): one JSON line
+    with each draw's kernel p50s and, per workload, how lean compares with the
+    best fixed split picked after the fact for each draw. Each draw's inputs
+    are allocated on their own, followed by a second of untimed launches, and
+    the kinds are timed in interleaved rounds (best round's median)."""
+    import torch
+
+    import decode_phase_attention_amd as la
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    la.lib()
+    evs = HipEvents()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Ks = (1, 2, 4, 8, 16, 32, 64)
+    rows = []
+    for name in workloads:
+        for seed in seeds:
+            log(f"[ragged draws] {name} seed {seed}")
+            inp = W.make_inputs(name, seed=seed, device="cuda")
+            w = inp.meta["workload"]
+            dt = la.LA_BF16 if w.dtype == "bf16" else la.LA_F16
+            _, G = la.la_select(inp.ctx_lens, inp.H, inp.d, dt, kv_heads=inp.Hk, q_tokens=inp.Nq)
+            kinds = [("lean", "lean", {"grid": G}), ("pull", "pull", {}),
+                     ("per_head", "per_head", {}), ("fixed_split_heuristic", "fixed_split", {})]
+            kinds += [(f"fixed_split_{K}", "fixed_split", {"num_splits": K}) for K in Ks]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 1.0:
+                time_kind(la, torch, evs, inp, "lean", 5, 1, grid=G)
+            t = {}
+            for r in range(rounds):
+                for j in range(len(kinds)):
+                    tag, kind, o = kinds[(j + r * 5) % len(kinds)]
+                    us = time_kind(la, torch, evs, inp, kind, steps, warmup, **o)["kernel_us_p50"]
+                    t[tag] = round(min(us, t.get(tag, float("inf"))), 2)
+            fs = {K: t[f"fixed_split_{K}"] for K in Ks}
+            K_best = min(fs, key=fs.get)
+            alg = W.algorithmic_bytes(inp.ctx_lens, inp.H, inp.d, kv_heads=inp.Hk,
+                                      q_tokens=inp.Nq)
+            lens = sorted(inp.ctx_lens)
+            row = {"workload": name, "seed": seed, "B": inp.B, "H": inp.H, "kv_heads": inp.Hk,
+                   "q_tokens": inp.Nq, "d": inp.d, "lens_min": lens[0],
+                   "lens_median": lens[len(lens) // 2], "lens_max": lens[-1],
+                   "sum_n": sum(lens), "bytes": alg, "lean_grid": G, "kernel_us_p50": t,
+                   "lean_TBps": round(alg / t["lean"] / 1e6, 3),
+                   "fixed_split_best_K": K_best, "fixed_split_best_us": fs[K_best],
+                   "lean_over_fixed_split_best": round(t["lean"] / fs[K_best], 4),
+                   "lean_over_fixed_split_heuristic": round(t["lean"] / t["fixed_split_heuristic"], 4),
+                   "lean_over_pull": round(t["lean"] / t["pull"], 4)}
+            rows.append(row)
+            log(f"   lean {t['lean']} us ({row['lean_TBps']} TB/s), best fixed split "
+                f"{fs[K_best]} (K={K_best}), pull {t['pull']}, x{row['lean_over_fixed_split_best']}")
+            del inp
+            torch.cuda.empty_cache()
+
+    def summary(name):
+        rs = [r for r in rows if r["workload"] == name]
+        out = {"draws": len(rs)}
+        for k in ("lean_over_fixed_split_best", "lean_over_fixed_split_heuristic", "lean_over_pull"):
+            v = [r[k] for r in rs]
+            out[k] = {"geomean": round(math.exp(sum(math.log(x) for x in v) / len(v)), 4),
+                      "max": max(v), "min": min(v)}
+        out["draws_lean_faster_than_fixed_split_best"] = sum(
+            r["lean_over_fixed_split_best"] < 1.0 for r in rs)
+        return out
+
+    print(json.dumps({"metric": "lean kernel time over the best fixed split and the dynamic pull "
+                                "on seeded draws of the ragged workloads (kernel p50)",
+                      "device": torch.cuda.get_device_name(0), "cus": cus,
+                      "summary": {name: summary(name) for name in workloads},
+                      "rows": rows}), flush=True)
+
+
 def decode_loop(workloads, steps=64, warmup=4):
     """Decode steps on a [B, Hk, S, d] cache (kv_stride = S) whose contexts
     grow by one token per request every step (the rows are already in the
@@ -892,6 +970,9 @@ def main():
     ap.add_argument("--decode-loop", action="store_true",
                     help="instead of the headline line: decode steps on a [B, Hk, S, d] cache "
                          "whose contexts grow by one token per step")
+    ap.add_argument("--ragged-draws", type=int, default=0, metavar="N",
+                    help="instead of the headline line: lean against every fixed-split count and "
+                         "the pull on N seeded draws of each ragged workload (or --workload)")
     ap.add_argument("--contention", action="store_true",
                     help="instead of the headline line: every kind on streams confined to "
                          "part of the CUs (512k and ragged, or --workload)")
@@ -912,6 +993,10 @@ def main():
     if args.decode_loop:
         decode_loop(["512k", "ragged", "gqa8-ragged", "mqa-32k", "spec4-ragged"]
                     if args.workload == "512k" else [args.workload])
+        return
+    if args.ragged_draws:
+        ragged_draws(["ragged", "gqa8-ragged", "spec4-ragged"] if args.workload == "512k"
+                     else [args.workload], range(args.ragged_draws))
         return
     if args.contention:
         contention(["512k", "ragged"] if args.workload == "512k" else [args.workload])

@@ -26,5 +26,6 @@ def test_help_lists_the_modes():
     r = run("--help")
     assert r.returncode == 0
     for flag in ("--steps", "--warmup", "--workload", "--selector-sweep", "--decode-loop",
-                 "--contention", "--tile-sweep", "--kernel-only", "--pages-sweep"):
+                 "--contention", "--tile-sweep", "--kernel-only", "--pages-sweep",
+                 "--ragged-draws"):
         assert flag in r.stdout
