@@ -173,14 +173,16 @@ def test_random_grids_stress(la):
         assert err <= O_TOL, (i, g, err)
 
 
-@pytest.mark.parametrize("name", ["gqa-512k", "gqa8-ragged", "mqa-32k"])
-def test_full_size(la, name):
-    """Every kind on the full workload, every (request, query head) against
-    the oracle."""
-    say(f"[gqa full {name}]")
-    inp = W.make_inputs(name, seed=0, device="cuda")
+@pytest.mark.parametrize("name,seed", [("gqa-512k", 0), ("gqa8-ragged", 0), ("gqa8-ragged", 3),
+                                       ("mqa-32k", 0)])
+def test_full_size(la, name, seed):
+    """Every kind on the full workload (the grouped ragged batch also at a
+    second draw of its lengths), every (request, query head) against the
+    oracle."""
+    say(f"[gqa full {name} seed {seed}]")
+    inp = W.make_inputs(name, seed=seed, device="cuda")
     res = {k: run(la, inp, k) for k in KINDS}
-    ref = full_reference(name, 0, inp)
+    ref = full_reference(name, seed, inp)
     for k in KINDS:
         err = check(res[k], ref, tag=f"{name}/{k}")
         say(f"[gqa full {name}] {k} max|dO|={err:.2e}")

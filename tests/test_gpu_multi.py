@@ -179,13 +179,14 @@ def test_determinism(la):
             np.testing.assert_array_equal(x, y)
 
 
-@pytest.mark.parametrize("name", ["spec4-ragged", "spec8-64k"])
-def test_full_size(la, name):
-    """Every kind on the full workload, every (request, new token, query
-    head) against the oracle."""
-    say(f"[multi full {name}]")
-    inp = W.make_inputs(name, seed=0, device="cuda")
-    ref = full_reference(name, 0, inp)
+@pytest.mark.parametrize("name,seed", [("spec4-ragged", 0), ("spec4-ragged", 3), ("spec8-64k", 0)])
+def test_full_size(la, name, seed):
+    """Every kind on the full workload (the ragged one also at a second draw
+    of its lengths), every (request, new token, query head) against the
+    oracle."""
+    say(f"[multi full {name} seed {seed}]")
+    inp = W.make_inputs(name, seed=seed, device="cuda")
+    ref = full_reference(name, seed, inp)
     for k in KINDS:
         err = check(run(la, inp, k), ref, tag=f"{name}/{k}")
         say(f"[multi full {name}] {k} max|dO|={err:.2e}")

@@ -347,19 +347,21 @@ def test_timeout_stays_in_its_launch(la, H, Hk):
 
 # ------------------------------------------------------------------ full-size workloads
 
-@pytest.mark.parametrize("name", ["65k", "512k", "ragged", "many-heads", "512k-h4"])
-def test_full_size(la, name):
+# the ragged batch also at two more seeded draws of its lengths
+@pytest.mark.parametrize("name,seed", [("65k", 0), ("512k", 0), ("ragged", 0), ("ragged", 2),
+                                       ("ragged", 3), ("many-heads", 0), ("512k-h4", 0)])
+def test_full_size(la, name, seed):
     """Every kind on the full workload, every (request, head) against the
     oracle; the lean kernel's executed tile map against the schedule oracle."""
-    say(f"[full {name}] generating")
-    inp = W.make_inputs(name, seed=0, device="cuda")
+    say(f"[full {name} seed {seed}] generating")
+    inp = W.make_inputs(name, seed=seed, device="cuda")
     w = inp.meta["workload"]
     say(f"[full {name}] lens={inp.ctx_lens[:4]}... all {inp.B * inp.H} heads checked")
     res = {}
     for kind in KINDS:
         res[kind] = run(la, inp, kind)
         say(f"[full {name}] {kind} done")
-    ref = full_reference(name, 0, inp)
+    ref = full_reference(name, seed, inp)
     say(f"[full {name}] oracle done")
     for kind in KINDS:
         err = check(res[kind], ref, tag=f"{name}/{kind}")
