@@ -1067,8 +1067,11 @@ def main():
     for name, m in extra.items():
         m.pop("_lean")
         rec[name] = m
+    props = torch.cuda.get_device_properties(0)
     rec["env"] = {"torch": torch.__version__, "python": platform.python_version(),
-                  "device": torch.cuda.get_device_name(0)}
+                  "device": torch.cuda.get_device_name(0),
+                  "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+                  "hbm_GiB": round(props.total_memory / 2**30, 1)}
     if args.jsonl:
         write_jsonl(args.jsonl, rec, lean, rec.get("comparators"), rec.get("occupancy"),
                     rec.get("lean_splits_per_head"), rec["roofline"]["bytes_per_launch"],
